@@ -1,0 +1,219 @@
+"""Plain float64 definitions of every step of the sparse-FFN decode path.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Sources ("the pages"):
+  [R] PowerInfer reading report, egguo-blog "PowerInfer_2312.12456",
+      Part A section 2.3 (operational definitions: sparsity, hot/cold split,
+      neuron impact v_i = f_i; the five system modules), section 3.1
+      (power-law finding), section 4.3 (neuron-aware operator avoids sparse
+      formats), Part B (method formula).
+  [B] the benchmark spec of the path this repository builds: a d -> r -> ffn
+      predictor with a sigmoid over a threshold tau, neuron-major W_down rows,
+      ReLU / ReGLU, no output bias.
+
+Readings where the pages are silent (each one is listed with its reason in the
+design notes of this repository):
+  * predictor hidden nonlinearity is ReLU (or none); b1 optional;
+  * "sigmoid(z) > tau" is taken strictly and evaluated as z > ln(tau/(1-tau));
+  * the active index list is ascending with no duplicates;
+  * ReGLU is a = max(W_gate x + b_gate, 0) * (W_up x + b_up), the gated form
+    with the ReLU on the gate; ReLU is a = max(W_up x + b_up, 0);
+  * a neuron "fires" for the profiler when its ReLU input is > 0 (strict);
+  * reorder = stable sort by descending count (ties to the lower index), hot
+    set = shortest prefix whose counts reach hot_share of the total.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+def widen(a) -> Optional[np.ndarray]:
+    """fp16 / fp32 / torch / list -> float64 numpy (exact widening); None stays None."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor, possibly on a device
+        a = a.detach().cpu().numpy()
+    return np.asarray(a, dtype=F64)
+
+
+def logit_threshold(tau: float) -> float:
+    """The predictor marks neuron i active when sigmoid(z_i) > tau [B].
+
+    sigmoid is strictly increasing, so sigmoid(z) > tau  <=>  z > ln(tau/(1-tau)).
+    """
+    if not (0.0 < tau < 1.0):
+        raise ValueError("tau must lie in (0, 1)")
+    return math.log(tau / (1.0 - tau))
+
+
+def predictor_hidden(x, P1, b1=None, act: str = "relu") -> np.ndarray:
+    """Hidden layer of the per-layer predictor MLP ([R] Part A 2.3, module 3).
+
+    s = P1 x + b1 (P1 is r x d), h = ReLU(s) (act "relu") or h = s ("none").
+    """
+    x, P1, b1 = widen(x), widen(P1), widen(b1)
+    s = P1 @ x
+    if b1 is not None:
+        s = s + b1
+    if act == "relu":
+        return np.maximum(s, 0.0)
+    if act == "none":
+        return s
+    raise ValueError(f"unknown predictor activation {act!r}")
+
+
+def predictor_logits(x, P1, b1, act, P2, b2) -> np.ndarray:
+    """z = P2 h + b2 (P2 is ffn x r); one logit per FFN neuron."""
+    h = predictor_hidden(x, P1, b1, act)
+    z = widen(P2) @ h
+    if b2 is not None:
+        z = z + widen(b2)
+    return z
+
+
+def predict(x, P1, b1, act, P2, b2, tau) -> Tuple[np.ndarray, np.ndarray]:
+    """Active-neuron list of one token: ascending i with sigmoid(z_i) > tau.
+
+    Returns (idx int64 ascending, z float64).  count = len(idx).
+    """
+    z = predictor_logits(x, P1, b1, act, P2, b2)
+    idx = np.flatnonzero(z > logit_threshold(tau))
+    return idx, z
+
+
+def neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """u_i = W_up[i] x + b_up_i and (ReGLU) g_i = W_gate[i] x + b_gate_i for i in rows.
+
+    The neuron-aware operator works on whole neuron rows with no sparse
+    format ([R] Part A 2.3 module 4, 4.3): row i of each matrix is neuron i.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    x = widen(x)
+    u = widen(W_up)[rows] @ x
+    if b_up is not None:
+        u = u + widen(b_up)[rows]
+    g = None
+    if kind == "reglu":
+        g = widen(W_gate)[rows] @ x
+        if b_gate is not None:
+            g = g + widen(b_gate)[rows]
+    elif kind != "relu":
+        raise ValueError(f"unknown FFN kind {kind!r}")
+    return u, g
+
+
+def neuron_activations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> np.ndarray:
+    """a_i = max(u_i, 0) (ReLU) or max(g_i, 0) * u_i (ReGLU) for i in rows."""
+    u, g = neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows)
+    if kind == "relu":
+        return np.maximum(u, 0.0)
+    return np.maximum(g, 0.0) * u
+
+
+def sparse_ffn(kind, x, W_up, b_up, W_gate, b_gate, W_down, idx) -> np.ndarray:
+    """y = sum over i in idx (ascending) of a_i * W_down[i, :]; no output bias.
+
+    W_down is neuron-major (ffn x d): row i is neuron i's output vector, so
+    only the rows of active neurons are touched ([R] Part A 2.3 module 4).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    Wd = widen(W_down)
+    y = np.zeros(Wd.shape[1], dtype=F64)
+    if idx.size == 0:
+        return y
+    a = neuron_activations(kind, x, W_up, b_up, W_gate, b_gate, idx)
+    for ai, i in zip(a, idx):          # ascending accumulation order
+        y += ai * Wd[i]
+    return y
+
+
+def dense_ffn(kind, x, W_up, b_up, W_gate, b_gate, W_down) -> np.ndarray:
+    """The dense FFN: every neuron computed, no predictor."""
+    ffn = np.shape(W_up)[0]
+    return sparse_ffn(kind, x, W_up, b_up, W_gate, b_gate, W_down, np.arange(ffn))
+
+
+def decode_step(layer: dict, x) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Predict the active set of one token, then compute only those neurons.
+
+    Returns (y, idx, z).  `layer` holds the tensors named as in the C ABI.
+    """
+    idx, z = predict(x, layer["P1"], layer.get("b1"), layer.get("pred_act", "relu"),
+                     layer["P2"], layer["b2"], layer["tau"])
+    y = sparse_ffn(layer["kind"], x, layer["W_up"], layer.get("b_up"), layer.get("W_gate"),
+                   layer.get("b_gate"), layer["W_down"], idx)
+    return y, idx, z
+
+
+def batched_sparse_ffn(kind, X, W_up, b_up, W_gate, b_gate, W_down,
+                       idx_lists: Sequence[Sequence[int]]) -> np.ndarray:
+    """Batch of B tokens: token t uses only its own active list (per-token masks).
+
+    The result for token t is by definition the single-token result; loading
+    the union of the lists once is an implementation choice that must not
+    change it.
+    """
+    X = widen(X)
+    return np.stack([sparse_ffn(kind, X[t], W_up, b_up, W_gate, b_gate, W_down, idx_lists[t])
+                     for t in range(X.shape[0])])
+
+
+def union_rows(idx_lists: Sequence[Sequence[int]]) -> np.ndarray:
+    """Ascending union of the per-token active lists."""
+    if len(idx_lists) == 0:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.concatenate([np.asarray(l, dtype=np.int64) for l in idx_lists]))
+
+
+def profile_counts(kind, X, W_fire, b_fire) -> np.ndarray:
+    """Offline profiler: per-neuron activation counts over calibration tokens.
+
+    counts_i = #{t : W_fire[i] x_t + b_fire_i > 0}, the number of tokens for
+    which neuron i's ReLU input is positive ([R] Part A 2.2 profiling data,
+    2.3 module 1 and the neuron impact v_i = f_i = counts_i / n).  W_fire is
+    W_up for ReLU FFNs and W_gate for ReGLU FFNs.
+    """
+    if kind not in ("relu", "reglu"):
+        raise ValueError(f"unknown FFN kind {kind!r}")
+    X, W = widen(X), widen(W_fire)
+    pre = X @ W.T                       # (n, ffn)
+    if b_fire is not None:
+        pre = pre + widen(b_fire)[None, :]
+    return (pre > 0.0).sum(axis=0).astype(np.int64)
+
+
+def reorder_plan(counts, hot_share: float = 0.8) -> Tuple[np.ndarray, int]:
+    """Hot-first neuron order and the size of the hot set.
+
+    perm (new -> old) sorts neurons by descending count, ties kept in original
+    order.  hot_count is the smallest k whose first k sorted counts reach
+    hot_share of all activations: the hot neurons are the minority that
+    carries 80% of the activations ([R] Part A 2.3 "hot/cold neurons", 3.1).
+    hot_count is 0 when no neuron ever fired.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    perm = np.argsort(-counts, kind="stable")
+    total = int(counts.sum())
+    if total == 0:
+        return perm.astype(np.int64), 0
+    target = float(hot_share) * float(total)
+    running = 0
+    for k, i in enumerate(perm, start=1):
+        running += int(counts[i])
+        if float(running) >= target:
+            return perm.astype(np.int64), k
+    return perm.astype(np.int64), len(perm)
+
+
+def permute_rows(src, perm) -> np.ndarray:
+    """dst[j] = src[perm[j]]: apply a new -> old neuron order to a row-major tensor."""
+    src = np.asarray(src)
+    return src[np.asarray(perm, dtype=np.int64)].copy()
