@@ -1,0 +1,259 @@
+// C ABI of the sparse-FFN library: argument validation, workspace layout and
+// launches.  Every check runs before the first launch, so a rejected call
+// leaves the device untouched.  See include/pi.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <numeric>
+#include <vector>
+
+#include "internal.hpp"
+#include "pi.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pi_status fail(pi_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pi_status ok() {
+    g_err[0] = '\0';
+    return PI_OK;
+}
+
+pi_status hip_fail(hipError_t e, const char* where) {
+    return fail(PI_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define PI_REQUIRE(cond, status, ...) \
+    do {                              \
+        if (!(cond)) return fail(status, __VA_ARGS__); \
+    } while (0)
+
+pi_status check_dims(int B, int d, int ffn) {
+    PI_REQUIRE(B >= 1 && B <= PI_MAX_BATCH, PI_ERR_INVALID_ARG, "B=%d outside [1, %d]", B, PI_MAX_BATCH);
+    PI_REQUIRE(d > 0 && ffn > 0, PI_ERR_INVALID_ARG, "d=%d ffn=%d must be positive", d, ffn);
+    PI_REQUIRE(d % 8 == 0, PI_ERR_UNSUPPORTED, "d=%d is not a multiple of 8", d);
+    PI_REQUIRE(d <= PI_MAX_D, PI_ERR_UNSUPPORTED, "d=%d above PI_MAX_D=%d", d, PI_MAX_D);
+    PI_REQUIRE(ffn <= PI_MAX_FFN, PI_ERR_UNSUPPORTED, "ffn=%d above PI_MAX_FFN=%d", ffn, PI_MAX_FFN);
+    return PI_OK;
+}
+
+pi_status check_half(const void* p, const char* name, bool required) {
+    if (!p) return required ? fail(PI_ERR_INVALID_ARG, "%s is NULL", name) : PI_OK;
+    PI_REQUIRE(aligned(p, 16), PI_ERR_UNSUPPORTED, "%s is not 16-byte aligned", name);
+    return PI_OK;
+}
+
+pi_status check_word(const void* p, const char* name, bool required) {
+    if (!p) return required ? fail(PI_ERR_INVALID_ARG, "%s is NULL", name) : PI_OK;
+    PI_REQUIRE(aligned(p, 4), PI_ERR_UNSUPPORTED, "%s is not 4-byte aligned", name);
+    return PI_OK;
+}
+
+pi_status check_ws(void* ws, size_t ws_bytes, size_t need, const char* op) {
+    if (need == 0) return PI_OK;
+    PI_REQUIRE(ws != nullptr, PI_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", op, need);
+    PI_REQUIRE(ws_bytes >= need, PI_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", op,
+               ws_bytes, need);
+    PI_REQUIRE(aligned(ws, 256), PI_ERR_UNSUPPORTED, "%s: workspace is not 256-byte aligned", op);
+    return PI_OK;
+}
+
+#define PI_TRY(expr)                  \
+    do {                              \
+        pi_status _s = (expr);        \
+        if (_s != PI_OK) return _s;   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* pi_status_string(pi_status s) {
+    switch (s) {
+        case PI_OK: return "PI_OK";
+        case PI_ERR_INVALID_ARG: return "PI_ERR_INVALID_ARG";
+        case PI_ERR_UNSUPPORTED: return "PI_ERR_UNSUPPORTED";
+        case PI_ERR_WORKSPACE: return "PI_ERR_WORKSPACE";
+        case PI_ERR_HIP: return "PI_ERR_HIP";
+    }
+    return "PI_ERR_UNKNOWN";
+}
+
+const char* pi_last_error(void) { return g_err; }
+
+pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes) {
+    PI_REQUIRE(bytes != nullptr, PI_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    switch (op) {
+        case PI_OP_PREDICT:
+            PI_TRY(check_dims(B, d, ffn));
+            PI_REQUIRE(r > 0 && r <= PI_MAX_R, PI_ERR_INVALID_ARG, "r=%d outside [1, %d]", r, PI_MAX_R);
+            *bytes = pi::predict_layout(B, r, ffn).total;
+            return ok();
+        case PI_OP_SPARSE:
+            PI_TRY(check_dims(B, d, ffn));
+            *bytes = pi::sparse_layout(B, d, ffn).total;
+            return ok();
+        case PI_OP_PROFILE:
+            *bytes = 0;
+            return ok();
+    }
+    return fail(PI_ERR_INVALID_ARG, "unknown op %d", op);
+}
+
+pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, const float* b1,
+                         int act, const pi_half* P2, const float* b2, int r, int ffn, float tau,
+                         int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+    PI_TRY(check_dims(B, d, ffn));
+    PI_REQUIRE(r > 0, PI_ERR_INVALID_ARG, "r=%d must be positive", r);
+    PI_REQUIRE(r % 8 == 0, PI_ERR_UNSUPPORTED, "r=%d is not a multiple of 8", r);
+    PI_REQUIRE(r <= PI_MAX_R, PI_ERR_UNSUPPORTED, "r=%d above PI_MAX_R=%d", r, PI_MAX_R);
+    PI_REQUIRE(act == PI_ACT_RELU || act == PI_ACT_NONE, PI_ERR_INVALID_ARG, "act=%d unknown", act);
+    PI_REQUIRE(tau > 0.f && tau < 1.f, PI_ERR_INVALID_ARG, "tau=%g not in (0, 1)", (double)tau);
+    PI_TRY(check_half(x, "x", true));
+    PI_TRY(check_half(P1, "P1", true));
+    PI_TRY(check_half(P2, "P2", true));
+    PI_TRY(check_word(b1, "b1", false));
+    PI_TRY(check_word(b2, "b2", false));
+    PI_TRY(check_word(idx, "idx", true));
+    PI_TRY(check_word(count, "count", true));
+    const pi::PredictLayout L = pi::predict_layout(B, r, ffn);
+    PI_TRY(check_ws(ws, ws_bytes, L.total, "pi_ffn_predict"));
+
+    // sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
+    const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
+    char* w = static_cast<char*>(ws);
+    float* h = reinterpret_cast<float*>(w + L.h);
+    uint32_t* status = reinterpret_cast<uint32_t*>(w + L.status);
+    uint32_t* tickets = status + (size_t)B * L.tiles;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const auto* hx = reinterpret_cast<const pi::h16*>(x);
+    hipError_t e = pi::launch_pred_hidden(hx, B, d, reinterpret_cast<const pi::h16*>(P1), b1,
+                                          act == PI_ACT_RELU, r, h, status, B * L.tiles + B, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict hidden layer");
+    e = pi::launch_pred_compact(reinterpret_cast<const pi::h16*>(P2), b2, h, B, r, ffn, thr, status,
+                                tickets, idx, count, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict logits/compaction");
+    return ok();
+}
+
+pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* W_up,
+                        const float* b_up, const pi_half* W_gate, const float* b_gate,
+                        const pi_half* W_down, const int32_t* idx, const int32_t* count, float* y,
+                        uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+    PI_TRY(check_dims(B, d, ffn));
+    PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU, PI_ERR_INVALID_ARG, "kind=%d unknown", kind);
+    PI_REQUIRE((flags & ~PI_DENSE) == 0u, PI_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    const bool dense = (flags & PI_DENSE) != 0u;
+    const bool reglu = kind == PI_FFN_REGLU;
+    PI_REQUIRE(reglu == (W_gate != nullptr), PI_ERR_INVALID_ARG,
+               reglu ? "W_gate is NULL for a ReGLU FFN" : "W_gate given for a ReLU FFN");
+    PI_REQUIRE(reglu || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
+    PI_TRY(check_half(x, "x", true));
+    PI_TRY(check_half(W_up, "W_up", true));
+    PI_TRY(check_half(W_gate, "W_gate", false));
+    PI_TRY(check_half(W_down, "W_down", true));
+    PI_TRY(check_word(b_up, "b_up", false));
+    PI_TRY(check_word(b_gate, "b_gate", false));
+    PI_TRY(check_word(idx, "idx", !dense));
+    PI_TRY(check_word(count, "count", !dense));
+    PI_REQUIRE(y != nullptr, PI_ERR_INVALID_ARG, "y is NULL");
+    PI_REQUIRE(aligned(y, 16), PI_ERR_UNSUPPORTED, "y is not 16-byte aligned");
+    const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
+    PI_TRY(check_ws(ws, ws_bytes, L.total, "pi_ffn_sparse"));
+
+    char* w = static_cast<char*>(ws);
+    float* a = reinterpret_cast<float*>(w + L.a);
+    float* partial = reinterpret_cast<float*>(w + L.partial);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(w + L.ctr);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = pi::launch_up_act(reglu, dense, reinterpret_cast<const pi::h16*>(x), B, d, ffn,
+                                     reinterpret_cast<const pi::h16*>(W_up), b_up,
+                                     reinterpret_cast<const pi::h16*>(W_gate), b_gate, idx, count,
+                                     a, ctr, L.T, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse up/gate");
+    e = pi::launch_down_acc(dense, reinterpret_cast<const pi::h16*>(W_down), B, d, ffn, idx, count,
+                            a, y, partial, ctr, L.T, L.G, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse down");
+    return ok();
+}
+
+pi_status pi_profile(const pi_half* X, int n, int d, int ffn, const pi_half* W_fire,
+                     const float* b_fire, uint32_t* counts, void* ws, size_t ws_bytes,
+                     void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    PI_REQUIRE(n >= 1, PI_ERR_INVALID_ARG, "n=%d must be >= 1", n);
+    PI_TRY(check_dims(1, d, ffn));
+    PI_TRY(check_half(X, "X", true));
+    PI_TRY(check_half(W_fire, "W_fire", true));
+    PI_TRY(check_word(b_fire, "b_fire", false));
+    PI_TRY(check_word(counts, "counts", true));
+    hipError_t e = pi::launch_profile(reinterpret_cast<const pi::h16*>(X), n, d, ffn,
+                                      reinterpret_cast<const pi::h16*>(W_fire), b_fire, counts,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_profile");
+    return ok();
+}
+
+pi_status pi_reorder(const uint32_t* counts, int ffn, double hot_share, int32_t* perm,
+                     int32_t* hot_count) {
+    PI_REQUIRE(counts && perm && hot_count, PI_ERR_INVALID_ARG, "NULL pointer argument");
+    PI_REQUIRE(ffn > 0 && ffn <= PI_MAX_FFN, PI_ERR_INVALID_ARG, "ffn=%d outside [1, %d]", ffn, PI_MAX_FFN);
+    PI_REQUIRE(hot_share > 0.0 && hot_share <= 1.0, PI_ERR_INVALID_ARG,
+               "hot_share=%g not in (0, 1]", hot_share);
+    std::vector<int32_t> order(ffn);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+    uint64_t total = 0;
+    for (int i = 0; i < ffn; ++i) total += counts[i];
+    int32_t hot = 0;
+    if (total > 0) {
+        const double target = hot_share * (double)total;
+        uint64_t running = 0;
+        hot = ffn;
+        for (int k = 0; k < ffn; ++k) {
+            running += counts[order[k]];
+            if ((double)running >= target) {
+                hot = k + 1;
+                break;
+            }
+        }
+    }
+    std::copy(order.begin(), order.end(), perm);
+    *hot_count = hot;
+    return ok();
+}
+
+pi_status pi_permute_rows(const void* src, void* dst, int rows, int row_bytes,
+                          const int32_t* perm, void* stream) {
+    PI_REQUIRE(src && dst && perm, PI_ERR_INVALID_ARG, "NULL pointer argument");
+    PI_REQUIRE(rows > 0 && row_bytes > 0, PI_ERR_INVALID_ARG, "rows=%d row_bytes=%d must be positive",
+               rows, row_bytes);
+    PI_REQUIRE(row_bytes % 4 == 0, PI_ERR_UNSUPPORTED, "row_bytes=%d is not a multiple of 4", row_bytes);
+    PI_REQUIRE(aligned(src, 4) && aligned(dst, 4) && aligned(perm, 4), PI_ERR_UNSUPPORTED,
+               "pointers must be 4-byte aligned");
+    const char* s0 = static_cast<const char*>(src);
+    const char* d0 = static_cast<const char*>(dst);
+    const size_t bytes = (size_t)rows * row_bytes;
+    PI_REQUIRE(s0 + bytes <= d0 || d0 + bytes <= s0, PI_ERR_INVALID_ARG, "src and dst overlap");
+    hipError_t e = pi::launch_permute(src, dst, rows, row_bytes, perm, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_permute_rows");
+    return ok();
+}
+
+}  // extern "C"

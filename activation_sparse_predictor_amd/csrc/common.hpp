@@ -1,0 +1,105 @@
+// Device helpers shared by the gfx950 kernels of the sparse-FFN library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pi {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// 16-byte global load (8 fp16 values).
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// 16-byte streaming load: data read once, marked non-temporal so it does not
+// displace reused lines (x, h, partial sums) from the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ f16x2 as_h2(unsigned int v) { return __builtin_bit_cast(f16x2, v); }
+
+// acc + sum_k w[k] * x[k] over 8 fp16 pairs, fp16 products accumulated in fp32
+// (v_dot2_f32_f16: the products of two fp16 values are exact in fp32).
+__device__ __forceinline__ float dot8_h(u32x4 w, u32x4 x, float acc) {
+    acc = __builtin_amdgcn_fdot2(as_h2(w.x), as_h2(x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w.y), as_h2(x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w.z), as_h2(x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(as_h2(w.w), as_h2(x.w), acc, false);
+    return acc;
+}
+
+// acc + sum_k w[k] * h[k] with fp16 weights and fp32 activations.
+__device__ __forceinline__ float dot8_hf(u32x4 w, const float* h, float acc) {
+    f16x2 a = as_h2(w.x), b = as_h2(w.y), c = as_h2(w.z), d = as_h2(w.w);
+    acc = fmaf((float)a.x, h[0], acc);
+    acc = fmaf((float)a.y, h[1], acc);
+    acc = fmaf((float)b.x, h[2], acc);
+    acc = fmaf((float)b.y, h[3], acc);
+    acc = fmaf((float)c.x, h[4], acc);
+    acc = fmaf((float)c.y, h[5], acc);
+    acc = fmaf((float)d.x, h[6], acc);
+    acc = fmaf((float)d.y, h[7], acc);
+    return acc;
+}
+
+// acc[k] += s * w[k] for 8 fp16 weights.
+__device__ __forceinline__ void axpy8(float* acc, float s, u32x4 w) {
+    f16x2 a = as_h2(w.x), b = as_h2(w.y), c = as_h2(w.z), d = as_h2(w.w);
+    acc[0] = fmaf(s, (float)a.x, acc[0]);
+    acc[1] = fmaf(s, (float)a.y, acc[1]);
+    acc[2] = fmaf(s, (float)b.x, acc[2]);
+    acc[3] = fmaf(s, (float)b.y, acc[3]);
+    acc[4] = fmaf(s, (float)c.x, acc[4]);
+    acc[5] = fmaf(s, (float)c.y, acc[5]);
+    acc[6] = fmaf(s, (float)d.x, acc[6]);
+    acc[7] = fmaf(s, (float)d.y, acc[7]);
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of a
+// group ends with the group sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ uint32_t group_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of m strictly below this lane.
+__device__ __forceinline__ uint32_t rank_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Device-coherent relaxed accesses for cross-workgroup flags.
+__device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add_acq_rel(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace pi

@@ -1,0 +1,141 @@
+"""Device-buffer plumbing around the C ABI: workspaces, outputs, layer bundles.
+
+Nothing here computes part of the path.  torch provides device memory and the
+stream; every arithmetic step runs in libpi's HIP kernels via `binding`.
+A layer is a dict of device tensors named as in the C ABI (W_up, W_gate,
+W_down, b_up, b_gate, P1, b1, P2, b2) plus kind, tau and sizes.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import binding as B
+
+
+class Workspace:
+    """A grow-only device byte buffer, 256-byte aligned (torch allocations are)."""
+
+    def __init__(self, device="cuda"):
+        self.device = torch.device(device)
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> Tuple[Optional[torch.Tensor], int]:
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf, self.buf.numel()
+
+
+_WS: Dict[Tuple[str, int], Workspace] = {}
+
+
+def workspace(tag: str, device=None) -> Workspace:
+    dev = torch.device(device or "cuda")
+    key = (tag, dev.index if dev.index is not None else torch.cuda.current_device())
+    if key not in _WS:
+        _WS[key] = Workspace(dev)
+    return _WS[key]
+
+
+def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    """fp16 tensors are passed by address; make sure they are contiguous fp16."""
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpi must be contiguous")
+    return t
+
+
+def predict(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
+            count: Optional[torch.Tensor] = None, act: str = "relu",
+            tau: Optional[float] = None, stream=None):
+    """idx (B x ffn int32) and count (B int32) for tokens x (B x d fp16)."""
+    Bt, d = x.shape
+    ffn, r = layer["ffn"], layer["r"]
+    if idx is None:
+        idx = torch.empty(Bt, ffn, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(Bt, dtype=torch.int32, device=x.device)
+    nbytes = B.pi_workspace_size(B.PI_OP_PREDICT, Bt, d, r, ffn)
+    ws, wsb = workspace("predict", x.device).get(nbytes)
+    st = B.pi_ffn_predict(_bits(x), Bt, d, layer["P1"], layer.get("b1"), B.ACTS[act], layer["P2"],
+                          layer.get("b2"), r, ffn, float(layer["tau"] if tau is None else tau),
+                          idx, count, ws, wsb, stream)
+    B.check(st, "pi_ffn_predict")
+    return idx, count
+
+
+def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
+           count: Optional[torch.Tensor], y: Optional[torch.Tensor] = None,
+           dense: bool = False, stream=None) -> torch.Tensor:
+    """y (B x d fp32) from the active rows (or every row with dense=True)."""
+    Bt, d = x.shape
+    ffn = layer["ffn"]
+    if y is None:
+        y = torch.empty(Bt, d, dtype=torch.float32, device=x.device)
+    nbytes = B.pi_workspace_size(B.PI_OP_SPARSE, Bt, d, layer.get("r", 8), ffn)
+    ws, wsb = workspace("sparse", x.device).get(nbytes)
+    st = B.pi_ffn_sparse(B.KINDS[layer["kind"]], _bits(x), Bt, d, ffn, layer["W_up"],
+                         layer.get("b_up"), layer.get("W_gate"), layer.get("b_gate"),
+                         layer["W_down"], None if dense else idx, None if dense else count, y,
+                         B.PI_DENSE if dense else 0, ws, wsb, stream)
+    B.check(st, "pi_ffn_sparse")
+    return y
+
+
+def decode(layer: dict, x: torch.Tensor, stream=None):
+    """One decode step: predict the active set, then the sparse FFN. Returns (y, idx, count)."""
+    idx, count = predict(layer, x, stream=stream)
+    y = sparse(layer, x, idx, count, stream=stream)
+    return y, idx, count
+
+
+def profile(X: torch.Tensor, W_fire: torch.Tensor, b_fire: Optional[torch.Tensor],
+            counts: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    n, d = X.shape
+    ffn = W_fire.shape[0]
+    if counts is None:
+        counts = torch.zeros(ffn, dtype=torch.int32, device=X.device)
+    B.check(B.pi_profile(_bits(X), n, d, ffn, W_fire, b_fire, counts, None, 0, stream), "pi_profile")
+    return counts
+
+
+def reorder(counts_host, hot_share: float = 0.8):
+    """Host plan: (perm int32 numpy new->old, hot_count)."""
+    import numpy as np
+    c = np.ascontiguousarray(np.asarray(counts_host, dtype=np.uint32))
+    perm = np.empty(c.size, dtype=np.int32)
+    hot = np.zeros(1, dtype=np.int32)
+    B.check(B.pi_reorder(c, c.size, hot_share, perm, hot), "pi_reorder")
+    return perm, int(hot[0])
+
+
+def permute_rows(src: torch.Tensor, perm_dev: torch.Tensor, stream=None) -> torch.Tensor:
+    dst = torch.empty_like(src)
+    rows = src.shape[0]
+    row_bytes = src[0].numel() * src.element_size() if src.dim() > 1 else src.element_size()
+    B.check(B.pi_permute_rows(src, dst, rows, row_bytes, perm_dev, stream), "pi_permute_rows")
+    return dst
+
+
+ROW_KEYS = ("W_up", "W_gate", "W_down", "P2", "b_up", "b_gate", "b2")
+
+
+def permute_layer(layer: dict, perm_dev: torch.Tensor, stream=None) -> dict:
+    """Hot-first copy of a layer: every neuron-indexed tensor gathered by perm."""
+    out = dict(layer)
+    for k in ROW_KEYS:
+        if layer.get(k) is not None:
+            out[k] = permute_rows(layer[k], perm_dev, stream)
+    return out
+
+
+def to_device(layer: dict, device="cuda") -> dict:
+    out = {}
+    for k, v in layer.items():
+        out[k] = v.to(device).contiguous() if isinstance(v, torch.Tensor) else v
+    return out

@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MI355X sparse-FFN path.
+
+A step is one token through one layer: pi_ffn_predict (predictor MLP,
+threshold, ordered compaction) then pi_ffn_sparse (gathered up GEMV +
+activation, neuron-major W_down accumulate), inputs already resident in HBM.
+The metric is decode tokens/s per layer, with achieved HBM GB/s on the bytes
+the step must touch:
+
+  T = 2 r d + 2 ffn r + 4 ffn            predictor weights + b2
+    + (m + 1) count 2 d + 4 count        active rows of W_up [W_gate] W_down + bias
+    + 2 d + 4 d + 8 count                x, y, index list write + read
+
+with m = 1 (ReLU) or 2 (ReGLU) and count the step's own active count.
+
+Cache-cold protocol: steps rotate over several distinct layers (default 8,
+about 7 GB for the OPT-30B-shaped layer) so the 256 MB Infinity Cache cannot
+hold a layer between its visits.  Timing uses HIP events on the stream the
+library launches on.  The dense FFN (every neuron, no predictor) through the
+same library, and torch's hipBLASLt GEMVs, are timed the same way.  The CPU
+oracle (plain float64 numpy) is timed on a bounded sample of tokens.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def touched_bytes(kind, d, r, ffn, count):
+    m = 2 if kind == "reglu" else 1
+    return (2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * count * 2 * d + 4 * count
+            + 2 * d + 4 * d + 8 * count)
+
+
+def dense_bytes(kind, d, ffn):
+    m = 2 if kind == "reglu" else 1
+    return (m + 1) * ffn * 2 * d + 4 * ffn + 2 * d + 4 * d
+
+
+def cpu_baseline(cfg, layer_dev, tokens_dev, budget_s):
+    """The oracle as it stands, timed on the host cores over a bounded token sample."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    H = {k: (v.detach().cpu() if hasattr(v, "detach") else v) for k, v in layer_dev.items()}
+    X = tokens_dev.cpu()
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_step(H, X[n % X.shape[0]])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= X.shape[0]:
+            break
+    return {"value": n / el, "unit": "tokens/s per layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} decode tokens of one {cfg.workload} layer (float64 numpy oracle: "
+                      f"predict + sparse FFN), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer copies in the rotation")
+    ap.add_argument("--tokens", type=int, default=64)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path shards by neuron across GPUs but "
+              f"this build runs on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from activation_sparse_predictor_amd import binding as B
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import CONFIGS, make_layer, make_tokens
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.config]
+    kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
+    NL, NT = args.layers, args.tokens
+    t_gen = time.perf_counter()
+    layers = [make_layer(cfg, layer=l, device=dev) for l in range(NL)]
+    tokens = [make_tokens(cfg, NT, device=dev, layer=l) for l in range(NL)]
+    torch.cuda.synchronize()
+    log(f"generated {NL} x {cfg.workload} in {time.perf_counter() - t_gen:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    y = torch.empty(1, d, dtype=torch.float32, device=dev)
+    xs = [[tokens[l][t:t + 1].contiguous() for t in range(NT)] for l in range(NL)]
+
+    def step(s):
+        l, t = s % NL, (s // NL) % NT
+        L = layers[l]
+        R.predict(L, xs[l][t], idx, cnt)
+        R.sparse(L, xs[l][t], idx, cnt, y)
+
+    # active counts of every (layer, token) in the rotation, for the byte accounting
+    counts = torch.empty(NL, NT, dtype=torch.int32, device=dev)
+    for l in range(NL):
+        for t in range(NT):
+            R.predict(layers[l], xs[l][t], idx, counts[l, t:t + 1])
+    torch.cuda.synchronize()
+    counts_h = counts.cpu()
+    if int(counts_h.min()) < 0:
+        raise RuntimeError("compaction reported an error count")
+
+    def steps_bytes(s0, K):
+        tot = 0
+        for s in range(s0, s0 + K):
+            tot += touched_bytes(kind, d, r, ffn, int(counts_h[s % NL, (s // NL) % NT]))
+        return tot
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0 = args.warmup
+    e0.record(stream)
+    for s in range(s0, s0 + args.steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_step = ms_total / args.steps
+    T_avg = steps_bytes(s0, args.steps) / args.steps
+    value = 1000.0 / ms_step
+    log(f"step {ms_step * 1000:.2f} us, {value:.0f} tok/s/layer, T {T_avg / 1e6:.1f} MB -> "
+        f"{T_avg / ms_step / 1e6:.0f} GB/s")
+
+    # per entry point: events between the two calls of each step
+    K2 = min(args.steps, 400)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K2)]
+    for k in range(K2):
+        s = s0 + k
+        l, t = s % NL, (s // NL) % NT
+        ev[3 * k].record(stream)
+        R.predict(layers[l], xs[l][t], idx, cnt)
+        ev[3 * k + 1].record(stream)
+        R.sparse(layers[l], xs[l][t], idx, cnt, y)
+        ev[3 * k + 2].record(stream)
+    torch.cuda.synchronize()
+    t_pred = [ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(K2)]
+    t_sp = [ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(K2)]
+    pred_bytes = 2 * r * d + 2 * ffn * r + 4 * ffn + 2 * d
+    m = 2 if kind == "reglu" else 1
+    sp_bytes = [(m + 1) * int(counts_h[(s0 + k) % NL, ((s0 + k) // NL) % NT]) * (2 * d + 4) + 4 * d
+                for k in range(K2)]
+    ms_pred, ms_sp = statistics.mean(t_pred), statistics.mean(t_sp)
+    gbs_pred = pred_bytes / ms_pred / 1e6
+    gbs_sp = statistics.mean(sp_bytes) / ms_sp / 1e6
+    log(f"predict {ms_pred * 1000:.2f} us ({gbs_pred:.0f} GB/s), sparse {ms_sp * 1000:.2f} us "
+        f"({gbs_sp:.0f} GB/s)")
+
+    stages = {"pi_ffn_predict": (ms_pred, gbs_pred, pred_bytes),
+              "pi_ffn_sparse": (ms_sp, gbs_sp, statistics.mean(sp_bytes))}
+    dom = max(stages, key=lambda k: stages[k][0])
+
+    dense = None
+    if not args.no_dense:
+        Kd = min(args.steps, 200)
+        for s in range(20):
+            l = s % NL
+            R.sparse(layers[l], xs[l][0], None, None, y, dense=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(Kd):
+            l, t = s % NL, (s // NL) % NT
+            R.sparse(layers[l], xs[l][t], None, None, y, dense=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = e0.elapsed_time(e1) / Kd
+        # torch hipBLASLt GEMVs of the same dense FFN (fp16 in, fp32 out via fp16 GEMM)
+        F = torch.nn.functional
+        def torch_dense(L, x):
+            if kind == "reglu":
+                a = torch.relu(F.linear(x, L["W_gate"], None).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
+            else:
+                a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
+            return F.linear(a.half(), L["W_down"].t())
+        for s in range(10):
+            torch_dense(layers[s % NL], xs[s % NL][0])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for s in range(Kd):
+            l, t = s % NL, (s // NL) % NT
+            torch_dense(layers[l], xs[l][t])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_torch = e0.elapsed_time(e1) / Kd
+        db = dense_bytes(kind, d, ffn)
+        dense = {"pi_dense_us": ms_dense * 1000, "pi_dense_GBs": db / ms_dense / 1e6,
+                 "torch_dense_us": ms_torch * 1000, "speedup_vs_pi_dense": ms_dense / ms_step,
+                 "speedup_vs_torch_dense": ms_torch / ms_step,
+                 "ideal_speedup_1_over_active": ffn / float(counts_h.float().mean())}
+        log(f"dense {ms_dense * 1000:.1f} us ({db / ms_dense / 1e6:.0f} GB/s), torch {ms_torch * 1000:.1f} us, "
+            f"speedup {ms_dense / ms_step:.2f}x")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, layers[0], tokens[0], args.cpu_seconds)
+        log(f"cpu oracle {cpu['value']:.2f} tok/s/layer on {cpu['cores']} threads")
+
+    out = {
+        "metric": "sparse-FFN decode tokens/s per layer + achieved HBM GB/s on touched rows",
+        "value": value,
+        "unit": "tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 weights, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": cfg.workload, "kind": kind, "d": d, "ffn": ffn, "r": r,
+                   "batch": 1, "tau": cfg.tau, "layers_rotated": NL, "tokens_per_layer": NT,
+                   "mean_active": float(counts_h.float().mean()),
+                   "touched_MB_per_step": T_avg / 1e6},
+        "achieved_GBs_step": T_avg / ms_step / 1e6,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": stages[dom][1],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": stages[dom][1] / HBM_PEAK_GBS, "traffic": None,
+                     "step_frac": T_avg / ms_step / 1e6 / HBM_PEAK_GBS,
+                     "stages_us": {k: v[0] * 1000 for k, v in stages.items()}},
+        "dense_baseline": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,187 @@
+/*
+ * pi.h -- C ABI of the MI355X (gfx950) neuron-aware sparse-FFN decode library.
+ *
+ * The operation follows the PowerInfer pages (egguo-blog reading report of
+ * arXiv 2312.12456): an online predictor marks the FFN neurons expected to
+ * fire for a token (Part A section 2.3, system module 3); a neuron-aware
+ * operator computes only those neurons' rows, with no sparse format
+ * (module 4, and section 4.3); an offline profiler counts how often each
+ * neuron fires on general text (module 1, section 2.2) and the hot neurons,
+ * the minority carrying 80% of activations, are placed first (section 2.3
+ * "hot/cold neurons", section 3.1 finding 1).  On one GPU the hot/cold split
+ * becomes a hot-first reorder of the rows.
+ *
+ * Conventions for every call:
+ *  - pi_half is an IEEE binary16 bit pattern.  Matrices are row-major.  FFN
+ *    weights are neuron-major: row i of W_up, W_gate and W_down belongs to
+ *    neuron i and has length d.  All tensor arguments are DEVICE pointers
+ *    unless marked "host".
+ *  - The caller owns every buffer.  The library allocates nothing; scratch
+ *    memory is a caller-provided device workspace of at least
+ *    pi_workspace_size() bytes, 256-byte aligned, that must not be used by
+ *    another call running concurrently.  Its contents need no initialisation.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    means the default stream).  Nothing is copied to the host: the active
+ *    count stays in device memory and later kernels read it there.
+ *  - Every argument check runs before any launch; on an error nothing is
+ *    launched and pi_last_error() holds a thread-local description.
+ *  - Results are deterministic: the same inputs give bitwise equal outputs.
+ *  - Limits: 1 <= B <= PI_MAX_BATCH; d and r multiples of 8; d <= PI_MAX_D;
+ *    r <= PI_MAX_R; 1 <= ffn <= PI_MAX_FFN; pi_half tensors 16-byte aligned;
+ *    float / int tensors 4-byte aligned.
+ */
+#ifndef PI_H_
+#define PI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t pi_half;
+
+typedef enum pi_status {
+    PI_OK = 0,
+    PI_ERR_INVALID_ARG = 1,  /* NULL pointer, size or enum out of range, tau not in (0,1) */
+    PI_ERR_UNSUPPORTED = 2,  /* d or r not a multiple of 8, misaligned pointer, size above a limit */
+    PI_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than pi_workspace_size() */
+    PI_ERR_HIP = 4           /* a HIP runtime call or launch failed; text in pi_last_error() */
+} pi_status;
+
+typedef enum pi_ffn_kind {
+    PI_FFN_RELU = 0,   /* a_i = max(W_up[i].x + b_up_i, 0) */
+    PI_FFN_REGLU = 1   /* a_i = max(W_gate[i].x + b_gate_i, 0) * (W_up[i].x + b_up_i) */
+} pi_ffn_kind;
+
+typedef enum pi_pred_act {
+    PI_ACT_RELU = 0,   /* predictor hidden layer h = max(P1 x + b1, 0) */
+    PI_ACT_NONE = 1    /* h = P1 x + b1 (linear low-rank predictor) */
+} pi_pred_act;
+
+typedef enum pi_op {
+    PI_OP_PREDICT = 0,
+    PI_OP_SPARSE = 1,
+    PI_OP_PROFILE = 2
+} pi_op;
+
+/* pi_ffn_sparse flags */
+#define PI_DENSE 0x1u      /* ignore idx/count and compute every neuron (dense FFN baseline) */
+
+#define PI_MAX_BATCH 256
+#define PI_MAX_D 16384
+#define PI_MAX_R 8192
+#define PI_MAX_FFN (1 << 24)
+
+/*
+ * pi_ffn_predict -- which neurons fire for each token.
+ *
+ * Per token t (x_t = row t of x):
+ *   h = act(P1 x_t + b1)            P1: r x d, b1: r floats or NULL (= 0)
+ *   z = P2 h + b2                   P2: ffn x r, b2: ffn floats or NULL (= 0)
+ *   neuron i is active  <=>  sigmoid(z_i) > tau  <=>  z_i > ln(tau / (1 - tau))
+ * (the per-layer predictor MLP of Part A section 2.3, module 3).  h and z are
+ * accumulated in fp32; h is never rounded to fp16.
+ *
+ * Outputs (device): idx[t * ffn + j], j < count[t], the active neurons of
+ * token t in strictly ascending order; count[t] in [0, ffn].  Entries of idx
+ * at j >= count[t] are left unspecified.  idx holds B * ffn int32, count B.
+ *
+ * Errors: INVALID_ARG for NULL x/P1/P2/idx/count, B/d/r/ffn out of range,
+ * act not a pi_pred_act, tau not in (0,1); UNSUPPORTED for d or r not a
+ * multiple of 8, misalignment, sizes above the limits; WORKSPACE if ws is
+ * NULL or ws_bytes < pi_workspace_size(PI_OP_PREDICT, B, d, r, ffn).
+ */
+pi_status pi_ffn_predict(const pi_half* x, int B, int d,
+                         const pi_half* P1, const float* b1, int act,
+                         const pi_half* P2, const float* b2, int r, int ffn,
+                         float tau, int32_t* idx, int32_t* count,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * pi_ffn_sparse -- the neuron-aware FFN over the active rows only.
+ *
+ * Per token t, over j < count[t] with i = idx[t * ffn + j]:
+ *   u_i = W_up[i].x_t + b_up_i ;  ReGLU: g_i = W_gate[i].x_t + b_gate_i
+ *   a_i = max(u_i, 0)  (RELU)   or   max(g_i, 0) * u_i  (REGLU)
+ *   y_t = sum_j a_i * W_down[i, :]                (no output bias)
+ * (the neuron-aware operator of Part A section 2.3 module 4 / section 4.3;
+ * W_down is neuron-major so each active neuron is one contiguous row).
+ * With flags & PI_DENSE, idx and count are ignored (may be NULL) and every
+ * neuron is computed: the dense FFN.  Biases may be NULL (= 0).  W_gate must
+ * be non-NULL for REGLU and NULL for RELU.  Products are fp16 x fp16 with
+ * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0).
+ * idx must hold valid, strictly ascending neuron ids (as written by
+ * pi_ffn_predict); the call does not re-check them.
+ *
+ * Errors: as pi_ffn_predict, plus INVALID_ARG for an unknown kind or flag,
+ * or a W_gate that does not match the kind.
+ */
+pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn,
+                        const pi_half* W_up, const float* b_up,
+                        const pi_half* W_gate, const float* b_gate,
+                        const pi_half* W_down,
+                        const int32_t* idx, const int32_t* count,
+                        float* y, uint32_t flags,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * pi_profile -- offline activation counts (Part A section 2.2 "offline
+ * profiling data", section 2.3 module 1 and the neuron impact v_i = f_i).
+ *
+ *   counts[i] += #{ t < n : W_fire[i].X_t + b_fire_i > 0 }
+ *
+ * X: n x d calibration tokens; W_fire: ffn x d, the matrix whose output goes
+ * through the ReLU (W_up for RELU FFNs, W_gate for REGLU); b_fire: ffn
+ * floats or NULL.  counts (device, uint32, ffn) ACCUMULATES, so several
+ * calls over chunks of calibration tokens sum up; zero it before the first.
+ * Pre-activations are fp32 accumulations of fp16 products (matrix cores).
+ * Errors: as above; n must be >= 1.  ws: pi_workspace_size(PI_OP_PROFILE, ...)
+ * (currently 0 bytes; ws may be NULL).
+ */
+pi_status pi_profile(const pi_half* X, int n, int d, int ffn,
+                     const pi_half* W_fire, const float* b_fire,
+                     uint32_t* counts, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * pi_reorder -- HOST-ONLY hot-first order from profile counts.
+ *
+ * perm (host, ffn int32, new -> old) lists neurons by descending count, ties
+ * in ascending original index.  *hot_count (host) is the smallest k such that
+ * the first k sorted counts sum to at least hot_share * sum(counts), computed
+ * in double precision; 0 when every count is 0.  hot_share in (0, 1]; the
+ * pages' hot set is hot_share = 0.8 (Part A section 2.3).
+ * Errors: INVALID_ARG for NULL pointers, ffn out of range, hot_share not in
+ * (0, 1].  Deterministic; no HIP call.
+ */
+pi_status pi_reorder(const uint32_t* counts, int ffn, double hot_share,
+                     int32_t* perm, int32_t* hot_count);
+
+/*
+ * pi_permute_rows -- dst[j, :] = src[perm[j], :] for j < rows (device).
+ *
+ * Applies a pi_reorder plan to any row-major tensor (W_up, W_gate, W_down,
+ * P2: row_bytes = 2 * cols; biases: row_bytes = 4).  Out of place: src and
+ * dst must not overlap.  perm is a device int32 array of length rows whose
+ * entries lie in [0, rows).  row_bytes must be a multiple of 4 and both
+ * pointers 16-byte aligned (4-byte when row_bytes is not a multiple of 16).
+ * With perm[j] = j it is a plain copy.
+ */
+pi_status pi_permute_rows(const void* src, void* dst, int rows, int row_bytes,
+                          const int32_t* perm, void* stream);
+
+/* Workspace bytes that `op` needs for these sizes (op is a pi_op). */
+pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes);
+
+/* Static description of a status code. */
+const char* pi_status_string(pi_status status);
+
+/* Thread-local description of the last error returned on this thread. */
+const char* pi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PI_H_ */

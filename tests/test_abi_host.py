@@ -1,0 +1,177 @@
+"""C ABI checks that need no GPU: exports, host-only reorder, argument validation.
+
+Every validation case below fails before the library makes any HIP call, so
+these run on a machine without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from activation_sparse_predictor_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pi.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpi.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pi_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = _declared()
+    for want in ("pi_ffn_predict", "pi_ffn_sparse", "pi_profile", "pi_reorder", "pi_permute_rows",
+                 "pi_workspace_size", "pi_status_string", "pi_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    assert B.status_string(0) == "PI_OK"
+    assert B.status_string(3) == "PI_ERR_WORKSPACE"
+    assert B.status_string(99) == "PI_ERR_UNKNOWN"
+
+
+def _reorder(counts, share):
+    return __import__("activation_sparse_predictor_amd.runtime", fromlist=["reorder"]).reorder(counts, share)
+
+
+def test_reorder_matches_oracle_on_golden_cases():
+    import json
+    cases = json.load(open(os.path.join(ROOT, "tests", "golden", "reorder_cases.json")))["cases"]
+    for c in cases:
+        perm, hot = _reorder(c["counts"], c["hot_share"])
+        assert perm.tolist() == c["perm"] and hot == c["hot_count"], c
+
+
+@pytest.mark.parametrize("n", [1, 5, 64, 1000, 28672])
+def test_reorder_matches_oracle_random(n):
+    rng = np.random.default_rng(n)
+    for share in (0.5, 0.8, 0.95, 1.0):
+        counts = (rng.zipf(1.3, size=n) * rng.integers(0, 2, size=n)).clip(max=4096).astype(np.uint32)
+        perm, hot = _reorder(counts, share)
+        operm, ohot = oracle.reorder_plan(counts, share)
+        assert np.array_equal(perm, operm) and hot == ohot
+
+
+def test_reorder_rejects_bad_arguments():
+    c = np.ones(4, np.uint32)
+    perm = np.empty(4, np.int32)
+    hot = np.zeros(1, np.int32)
+    assert B.pi_reorder(c, 4, 0.0, perm, hot) == B.PI_ERR_INVALID_ARG
+    assert B.pi_reorder(c, 4, 1.5, perm, hot) == B.PI_ERR_INVALID_ARG
+    assert B.pi_reorder(c, 0, 0.8, perm, hot) == B.PI_ERR_INVALID_ARG
+    assert B.pi_reorder(None, 4, 0.8, perm, hot) == B.PI_ERR_INVALID_ARG
+    assert "hot_share" in B.last_error() or "NULL" in B.last_error() or "ffn" in B.last_error()
+
+
+def test_workspace_size_queries():
+    p = B.pi_workspace_size(B.PI_OP_PREDICT, 1, 7168, 1024, 28672)
+    s = B.pi_workspace_size(B.PI_OP_SPARSE, 1, 7168, 1024, 28672)
+    assert p >= 1024 * 4 and s >= 28672 * 4
+    assert B.pi_workspace_size(B.PI_OP_SPARSE, 4, 7168, 1024, 28672) > s
+    out = ctypes.c_size_t(0)
+    assert B.load().pi_workspace_size(9, 1, 8, 8, 8, ctypes.byref(out)) == B.PI_ERR_INVALID_ARG
+    assert B.load().pi_workspace_size(0, 0, 8, 8, 8, ctypes.byref(out)) == B.PI_ERR_INVALID_ARG
+
+
+# Fake, aligned, never-dereferenced addresses: validation rejects each call first.
+A = 1 << 20          # 16-byte aligned
+W = (1 << 20) + 4096
+
+
+def _predict(**kw):
+    args = dict(x=A, B=1, d=64, P1=A, b1=None, act=B.PI_ACT_RELU, P2=A, b2=None, r=16, ffn=128,
+                tau=0.5, idx=A, count=A, ws=A, ws_bytes=0, stream=0)
+    args.update(kw)
+    return B.pi_ffn_predict(*args.values())
+
+
+def _sparse(**kw):
+    args = dict(kind=B.PI_FFN_RELU, x=A, B=1, d=64, ffn=128, W_up=A, b_up=None, W_gate=None,
+                b_gate=None, W_down=A, idx=A, count=A, y=A, flags=0, ws=A, ws_bytes=0, stream=0)
+    args.update(kw)
+    return B.pi_ffn_sparse(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), B.PI_ERR_INVALID_ARG),
+    (dict(P1=None), B.PI_ERR_INVALID_ARG),
+    (dict(P2=None), B.PI_ERR_INVALID_ARG),
+    (dict(idx=None), B.PI_ERR_INVALID_ARG),
+    (dict(count=None), B.PI_ERR_INVALID_ARG),
+    (dict(B=0), B.PI_ERR_INVALID_ARG),
+    (dict(B=257), B.PI_ERR_INVALID_ARG),
+    (dict(d=0), B.PI_ERR_INVALID_ARG),
+    (dict(r=0), B.PI_ERR_INVALID_ARG),
+    (dict(ffn=-1), B.PI_ERR_INVALID_ARG),
+    (dict(tau=0.0), B.PI_ERR_INVALID_ARG),
+    (dict(tau=1.0), B.PI_ERR_INVALID_ARG),
+    (dict(tau=float("nan")), B.PI_ERR_INVALID_ARG),
+    (dict(act=7), B.PI_ERR_INVALID_ARG),
+    (dict(d=60), B.PI_ERR_UNSUPPORTED),
+    (dict(r=12), B.PI_ERR_UNSUPPORTED),
+    (dict(x=A + 8), B.PI_ERR_UNSUPPORTED),
+    (dict(P2=A + 2), B.PI_ERR_UNSUPPORTED),
+    (dict(b2=A + 2), B.PI_ERR_UNSUPPORTED),
+    (dict(d=32768), B.PI_ERR_UNSUPPORTED),
+    (dict(ws=None), B.PI_ERR_WORKSPACE),
+    (dict(ws_bytes=16), B.PI_ERR_WORKSPACE),
+])
+def test_predict_rejects_before_launch(kw, code):
+    assert _predict(**kw) == code
+    assert B.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=5), B.PI_ERR_INVALID_ARG),
+    (dict(x=None), B.PI_ERR_INVALID_ARG),
+    (dict(W_up=None), B.PI_ERR_INVALID_ARG),
+    (dict(W_down=None), B.PI_ERR_INVALID_ARG),
+    (dict(y=None), B.PI_ERR_INVALID_ARG),
+    (dict(idx=None), B.PI_ERR_INVALID_ARG),
+    (dict(count=None), B.PI_ERR_INVALID_ARG),
+    (dict(W_gate=A), B.PI_ERR_INVALID_ARG),                 # gate given for ReLU
+    (dict(kind=B.PI_FFN_REGLU), B.PI_ERR_INVALID_ARG),      # gate missing for ReGLU
+    (dict(b_gate=W), B.PI_ERR_INVALID_ARG),                 # gate bias for ReLU
+    (dict(flags=0x80), B.PI_ERR_INVALID_ARG),
+    (dict(B=300), B.PI_ERR_INVALID_ARG),
+    (dict(d=12), B.PI_ERR_UNSUPPORTED),
+    (dict(W_down=A + 4), B.PI_ERR_UNSUPPORTED),
+    (dict(y=A + 4), B.PI_ERR_UNSUPPORTED),
+    (dict(idx=A + 2), B.PI_ERR_UNSUPPORTED),
+    (dict(ws=None), B.PI_ERR_WORKSPACE),
+    (dict(ws_bytes=64), B.PI_ERR_WORKSPACE),
+])
+def test_sparse_rejects_before_launch(kw, code):
+    assert _sparse(**kw) == code
+    assert B.last_error() != ""
+
+
+def test_dense_flag_allows_null_index_list():
+    # with PI_DENSE the index list is not required: the call gets as far as the workspace check
+    assert _sparse(flags=B.PI_DENSE, idx=None, count=None, ws=None) == B.PI_ERR_WORKSPACE
+
+
+def test_profile_and_permute_reject_before_launch():
+    assert B.pi_profile(None, 4, 64, 128, A, None, A, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_profile(A, 0, 64, 128, A, None, A, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_profile(A, 4, 60, 128, A, None, A, stream=0) == B.PI_ERR_UNSUPPORTED
+    assert B.pi_profile(A, 4, 64, 128, A + 2, None, A, stream=0) == B.PI_ERR_UNSUPPORTED
+    assert B.pi_permute_rows(A, None, 4, 16, A, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_permute_rows(A, W, 4, 6, A, stream=0) == B.PI_ERR_UNSUPPORTED
+    assert B.pi_permute_rows(A, A + 16, 4, 16, A, stream=0) == B.PI_ERR_INVALID_ARG   # overlap
+    assert B.pi_permute_rows(A, W, 0, 16, A, stream=0) == B.PI_ERR_INVALID_ARG

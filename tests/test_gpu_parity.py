@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Small ragged shapes span several tiles plus a tail on every axis (d vs the
+512-wide row steps and 1024-wide column tiles, ffn vs the 64-neuron
+compaction tiles, r vs the per-row lane groups).  Full-size layers are
+checked on sampled tokens.  Rules (tests/parity.py): index lists bit-exact
+outside a 1e-3 band around the logit threshold; y within rel-L2 1e-3 and
+max-abs 2e-3 * ||y||_inf of the oracle evaluated on the GPU's own list.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from activation_sparse_predictor_amd import binding as B
+from activation_sparse_predictor_amd import runtime as R
+from synthetic import CONFIGS, custom_config, make_calibration, make_layer, make_tokens
+from tests.parity import check_counts, check_idx, check_y
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _host(layer):
+    return {k: (v.detach().cpu() if isinstance(v, torch.Tensor) else v) for k, v in layer.items()}
+
+
+def _oracle_y(H, x, idx):
+    return O.sparse_ffn(H["kind"], x, H["W_up"], H.get("b_up"), H.get("W_gate"), H.get("b_gate"),
+                        H["W_down"], idx)
+
+
+def _check_tokens(L, X, act="relu", where=""):
+    """Predict + sparse one token at a time; full parity per token. Returns active counts."""
+    H = _host(L)
+    thr = O.logit_threshold(L["tau"])
+    counts = []
+    for t in range(X.shape[0]):
+        x = X[t:t + 1].contiguous()
+        idx, cnt = R.predict(L, x, act=act)
+        y = R.sparse(L, x, idx, cnt)
+        torch.cuda.synchronize()
+        c = int(cnt.cpu()[0])
+        assert 0 <= c <= L["ffn"], f"{where} t={t}: count {c}"
+        gi = idx[0, :c].cpu().numpy()
+        xh = X[t].cpu()
+        z = O.predictor_logits(xh, H["P1"], H.get("b1"), act, H["P2"], H.get("b2"))
+        check_idx(gi, z, thr, where=f"{where} t={t}")
+        check_y(y[0].cpu().numpy(), _oracle_y(H, xh, gi), where=f"{where} t={t}")
+        counts.append(c)
+    return counts
+
+
+SHAPES = [
+    ("relu", 64, 64, 8, 0.10),
+    ("relu", 256, 1024, 64, 0.10),
+    ("relu", 520, 1000, 72, 0.10),
+    ("relu", 1032, 2080, 136, 0.30),
+    ("reglu", 520, 1000, 16, 0.20),
+    ("reglu", 256, 1024, 64, 0.50),
+    ("relu", 2048, 4160, 256, 0.05),
+]
+
+
+@pytest.mark.parametrize("kind,d,ffn,r,mean", SHAPES)
+def test_decode_parity_small(kind, d, ffn, r, mean):
+    cfg = custom_config(kind, d, ffn, r, mean=mean, number=40 + d % 37)
+    L = R.to_device(make_layer(cfg), DEV)
+    X = make_tokens(cfg, 6).to(DEV)
+    counts = _check_tokens(L, X, where=f"{kind} d{d} ffn{ffn} r{r}")
+    assert sum(counts) > 0
+
+
+def test_decode_parity_tiny_config():
+    cfg = CONFIGS["c1"]
+    L = R.to_device(make_layer(cfg), DEV)
+    X = make_tokens(cfg, cfg.tokens).to(DEV)
+    counts = _check_tokens(L, X, where="c1")
+    assert 0.03 * cfg.ffn < np.mean(counts) < 0.3 * cfg.ffn
+
+
+@pytest.mark.parametrize("tau", [0.01, 0.3, 0.5, 0.99])
+def test_tau_values(tau):
+    cfg = custom_config("relu", 256, 1024, 64, mean=0.2, number=51)
+    L = R.to_device(make_layer(cfg), DEV)
+    L["tau"] = tau
+    _check_tokens(L, make_tokens(cfg, 3).to(DEV), where=f"tau={tau}")
+
+
+def test_linear_predictor_and_hidden_bias():
+    cfg = custom_config("relu", 520, 1000, 72, number=52)
+    L = R.to_device(make_layer(cfg), DEV)
+    L["b1"] = torch.linspace(-0.5, 0.5, 72, device=DEV, dtype=torch.float32)
+    X = make_tokens(cfg, 3).to(DEV)
+    _check_tokens(L, X, act="none", where="act=none")
+    _check_tokens(L, X, act="relu", where="act=relu b1")
+
+
+def test_zero_token():
+    cfg = custom_config("reglu", 256, 1000, 64, mean=0.3, number=53)
+    L = R.to_device(make_layer(cfg), DEV)
+    X = torch.zeros(1, 256, dtype=torch.float16, device=DEV)
+    _check_tokens(L, X, where="x=0")
+
+
+def _sparse_with(L, x, idx_list):
+    ffn = L["ffn"]
+    idx = torch.zeros(1, ffn, dtype=torch.int32, device=DEV)
+    if len(idx_list):
+        idx[0, :len(idx_list)] = torch.tensor(idx_list, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([len(idx_list)], dtype=torch.int32, device=DEV)
+    y = R.sparse(L, x, idx, cnt)
+    torch.cuda.synchronize()
+    return y[0].cpu().numpy()
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_sparse_edge_lists(kind):
+    cfg = custom_config(kind, 1032, 1000, 16, mean=0.3, number=54)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    x = make_tokens(cfg, 1).to(DEV)
+    xh = x[0].cpu()
+    y = _sparse_with(L, x, [])
+    assert np.all(y == 0.0), "empty list must give exactly 0"
+    for lst in ([cfg.ffn - 1], [0], list(range(cfg.ffn)), list(range(0, cfg.ffn, 7)),
+                list(range(cfg.ffn - 9, cfg.ffn))):
+        check_y(_sparse_with(L, x, lst), _oracle_y(H, xh, lst), where=f"{kind} list len {len(lst)}")
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_dense_flag(kind):
+    cfg = custom_config(kind, 520, 2080, 16, number=55)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    X = make_tokens(cfg, 3).to(DEV)
+    Y = R.sparse(L, X, None, None, dense=True)
+    torch.cuda.synchronize()
+    for t in range(3):
+        xh = X[t].cpu()
+        ref = O.dense_ffn(kind, xh, H["W_up"], H.get("b_up"), H.get("W_gate"), H.get("b_gate"), H["W_down"])
+        check_y(Y[t].cpu().numpy(), ref, where=f"dense t={t}")
+
+
+@pytest.mark.parametrize("Bt", [1, 4, 15, 16, 17, 32])
+def test_batched_matches_single_token(Bt):
+    cfg = custom_config("relu", 520, 1000, 72, mean=0.15, number=56)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    X = make_tokens(cfg, Bt).to(DEV)
+    idx, cnt = R.predict(L, X)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    cnt_h, idx_h, Y_h = cnt.cpu().numpy(), idx.cpu().numpy(), Y.cpu().numpy()
+    for t in range(Bt):
+        x1 = X[t:t + 1].contiguous()
+        i1, c1 = R.predict(L, x1)
+        y1 = R.sparse(L, x1, i1, c1)
+        torch.cuda.synchronize()
+        c = int(cnt_h[t])
+        assert c == int(c1.cpu()[0])
+        assert np.array_equal(idx_h[t, :c], i1[0, :c].cpu().numpy())
+        assert np.array_equal(Y_h[t], y1[0].cpu().numpy()), "batched result differs from single token"
+        xh = X[t].cpu()
+        z = O.predictor_logits(xh, H["P1"], None, "relu", H["P2"], H["b2"])
+        check_idx(idx_h[t, :c], z, thr, where=f"B={Bt} t={t}")
+        check_y(Y_h[t], _oracle_y(H, xh, idx_h[t, :c]), where=f"B={Bt} t={t}")
+
+
+def test_deterministic_repeats():
+    cfg = custom_config("reglu", 1032, 2080, 136, mean=0.3, number=57)
+    L = R.to_device(make_layer(cfg), DEV)
+    x = make_tokens(cfg, 1).to(DEV)
+    outs = []
+    for _ in range(3):
+        idx, cnt = R.predict(L, x)
+        y = R.sparse(L, x, idx, cnt)
+        torch.cuda.synchronize()
+        c = int(cnt.cpu()[0])
+        outs.append((c, idx[0, :c].cpu().numpy().copy(), y.cpu().numpy().copy()))
+    for c, i, y in outs[1:]:
+        assert c == outs[0][0] and np.array_equal(i, outs[0][1]) and np.array_equal(y, outs[0][2])
+
+
+@pytest.mark.parametrize("kind,d,ffn,n", [("relu", 64, 96, 40), ("relu", 520, 1000, 300),
+                                          ("reglu", 256, 1024, 129), ("relu", 1032, 2080, 1024)])
+def test_profile_parity(kind, d, ffn, n):
+    cfg = custom_config(kind, d, ffn, 8, mean=0.2, number=58)
+    L = R.to_device(make_layer(cfg, predictor=False), DEV)
+    Xc = make_calibration(cfg, n).to(DEV)
+    Wf = L["W_up"] if kind == "relu" else L["W_gate"]
+    bf = L["b_up"] if kind == "relu" else L["b_gate"]
+    counts = R.profile(Xc, Wf, bf)
+    torch.cuda.synchronize()
+    pre = O.profile_preactivations(Xc.cpu(), Wf.cpu(), bf.cpu())
+    check_counts(counts.cpu().numpy(), pre, where=f"profile {kind} d{d} ffn{ffn} n{n}")
+    # counts accumulate across calls
+    R.profile(Xc, Wf, bf, counts)
+    torch.cuda.synchronize()
+    lo, hi = (pre > 1e-3).sum(0), (pre > -1e-3).sum(0)
+    c2 = counts.cpu().numpy().astype(np.int64)
+    assert np.all((c2 >= 2 * lo) & (c2 <= 2 * hi))
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(1000, 520, torch.float16), (4160, 1, torch.float32),
+                                              (7, 3, torch.float32), (64, 4096, torch.float16)])
+def test_permute_rows_bit_exact(rows, cols, dtype):
+    g = torch.Generator(device="cpu").manual_seed(rows)
+    src = torch.randn(rows, cols, generator=g).to(dtype).to(DEV)
+    if cols == 1:
+        src = src[:, 0].contiguous()
+    perm = torch.randperm(rows, generator=g).to(torch.int32)
+    out = R.permute_rows(src, perm.to(DEV))
+    ident = R.permute_rows(src, torch.arange(rows, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    want = O.permute_rows(src.cpu().numpy(), perm.numpy())
+    assert np.array_equal(out.cpu().numpy(), want)
+    assert torch.equal(ident, src)
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_profile_reorder_invariance(kind):
+    """Profile -> host plan -> permuted layer: the same y, and idx' = sort(perm^-1[idx])."""
+    cfg = custom_config(kind, 520, 2080, 72, mean=0.15, exponent=1.3, number=59)
+    L = R.to_device(make_layer(cfg), DEV)
+    Xc = make_calibration(cfg, 512).to(DEV)
+    Wf = L["W_up"] if kind == "relu" else L["W_gate"]
+    bf = L["b_up"] if kind == "relu" else L["b_gate"]
+    counts = R.profile(Xc, Wf, bf).cpu().numpy()
+    perm, hot = R.reorder(counts, 0.8)
+    operm, ohot = O.reorder_plan(counts.astype(np.int64), 0.8)
+    assert np.array_equal(perm, operm) and hot == ohot
+    P = R.permute_layer(L, torch.from_numpy(perm).to(DEV))
+    inv = np.argsort(perm)
+    H = _host(L)
+    thr = O.logit_threshold(L["tau"])
+    X = make_tokens(cfg, 4).to(DEV)
+    for t in range(4):
+        x = X[t:t + 1].contiguous()
+        i0, c0 = R.predict(L, x)
+        i1, c1 = R.predict(P, x)
+        y0 = R.sparse(L, x, i0, c0)
+        y1 = R.sparse(P, x, i1, c1)
+        torch.cuda.synchronize()
+        a0 = i0[0, :int(c0.cpu()[0])].cpu().numpy()
+        a1 = i1[0, :int(c1.cpu()[0])].cpu().numpy()
+        z = O.predictor_logits(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"])
+        diff = set(a1.tolist()) ^ set(inv[a0].tolist())
+        assert all(abs(z[perm[j]] - thr) <= 1e-3 for j in diff)
+        check_y(y1[0].cpu().numpy(), _oracle_y(H, X[t].cpu(), np.sort(perm[a1])), where=f"reordered t={t}")
+    # hot prefix holds the most active neurons
+    pc = counts[perm]
+    assert np.all(np.diff(pc.astype(np.int64)) <= 0)
+
+
+# ---------------------------------------------------------------- full-size layers
+def _full(key, layer=0, ntok=3):
+    cfg = CONFIGS[key]
+    L = make_layer(cfg, layer=layer, device=DEV)
+    X = make_tokens(cfg, ntok, device=DEV, layer=layer)
+    return cfg, L, X
+
+
+@pytest.mark.parametrize("key", ["c2", "c3", "c4"])
+def test_full_size_decode(key):
+    cfg, L, X = _full(key)
+    counts = _check_tokens(L, X, where=key)
+    frac = np.mean(counts) / cfg.ffn
+    assert 0.5 * cfg.mean < frac < 1.6 * cfg.mean, frac
+
+
+def test_full_size_stack_layer_and_profile():
+    """One sampled layer of the 64-layer stack shape, plus its profile on 256 calibration tokens."""
+    cfg, L, X = _full("c5", layer=17, ntok=2)
+    _check_tokens(L, X, where="c5 layer 17")
+    Xc = make_calibration(cfg, 256, device=DEV, layer=17)
+    counts = R.profile(Xc, L["W_up"], L["b_up"])
+    torch.cuda.synchronize()
+    pre = O.profile_preactivations(Xc.cpu(), L["W_up"].cpu(), L["b_up"].cpu())
+    check_counts(counts.cpu().numpy(), pre, where="c5 profile")
+
+
+@pytest.mark.parametrize("Bt", [4, 16])
+def test_full_size_batched(Bt):
+    cfg, L, X = _full("c4", ntok=Bt)
+    H = _host(L)
+    idx, cnt = R.predict(L, X)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    for t in (0, Bt - 1):
+        c = int(cnt[t].cpu())
+        gi = idx[t, :c].cpu().numpy()
+        z = O.predictor_logits(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"])
+        check_idx(gi, z, thr, where=f"c4 B={Bt} t={t}")
+        check_y(Y[t].cpu().numpy(), _oracle_y(H, X[t].cpu(), gi), where=f"c4 B={Bt} t={t}")
