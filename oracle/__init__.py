@@ -30,7 +30,9 @@ from .ffn import (  # noqa: F401
     decode_step,
     batched_sparse_ffn,
     union_rows,
+    profile_preactivations,
     profile_counts,
+    rows_of,
     reorder_plan,
     permute_rows,
 )

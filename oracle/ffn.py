@@ -44,6 +44,14 @@ def widen(a) -> Optional[np.ndarray]:
     return np.asarray(a, dtype=F64)
 
 
+def rows_of(W, rows) -> np.ndarray:
+    """W[rows] widened to float64 (rows taken first, so a large matrix is never widened whole)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    if hasattr(W, "detach"):
+        W = W.detach().cpu().numpy()
+    return np.asarray(np.asarray(W)[rows], dtype=F64)
+
+
 def logit_threshold(tau: float) -> float:
     """The predictor marks neuron i active when sigmoid(z_i) > tau [B].
 
@@ -97,14 +105,14 @@ def neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> Tuple[np
     """
     rows = np.asarray(rows, dtype=np.int64)
     x = widen(x)
-    u = widen(W_up)[rows] @ x
+    u = rows_of(W_up, rows) @ x
     if b_up is not None:
-        u = u + widen(b_up)[rows]
+        u = u + rows_of(b_up, rows)
     g = None
     if kind == "reglu":
-        g = widen(W_gate)[rows] @ x
+        g = rows_of(W_gate, rows) @ x
         if b_gate is not None:
-            g = g + widen(b_gate)[rows]
+            g = g + rows_of(b_gate, rows)
     elif kind != "relu":
         raise ValueError(f"unknown FFN kind {kind!r}")
     return u, g
@@ -125,13 +133,13 @@ def sparse_ffn(kind, x, W_up, b_up, W_gate, b_gate, W_down, idx) -> np.ndarray:
     only the rows of active neurons are touched ([R] Part A 2.3 module 4).
     """
     idx = np.asarray(idx, dtype=np.int64)
-    Wd = widen(W_down)
-    y = np.zeros(Wd.shape[1], dtype=F64)
+    y = np.zeros(np.shape(W_down)[1], dtype=F64)
     if idx.size == 0:
         return y
     a = neuron_activations(kind, x, W_up, b_up, W_gate, b_gate, idx)
-    for ai, i in zip(a, idx):          # ascending accumulation order
-        y += ai * Wd[i]
+    Wd = rows_of(W_down, idx)
+    for ai, wrow in zip(a, Wd):        # ascending accumulation order
+        y += ai * wrow
     return y
 
 
@@ -173,6 +181,15 @@ def union_rows(idx_lists: Sequence[Sequence[int]]) -> np.ndarray:
     return np.unique(np.concatenate([np.asarray(l, dtype=np.int64) for l in idx_lists]))
 
 
+def profile_preactivations(X, W_fire, b_fire) -> np.ndarray:
+    """pre[t, i] = W_fire[i] x_t + b_fire_i, the ReLU input of neuron i for token t."""
+    X, W = widen(X), widen(W_fire)
+    pre = X @ W.T                       # (n, ffn)
+    if b_fire is not None:
+        pre = pre + widen(b_fire)[None, :]
+    return pre
+
+
 def profile_counts(kind, X, W_fire, b_fire) -> np.ndarray:
     """Offline profiler: per-neuron activation counts over calibration tokens.
 
@@ -183,11 +200,7 @@ def profile_counts(kind, X, W_fire, b_fire) -> np.ndarray:
     """
     if kind not in ("relu", "reglu"):
         raise ValueError(f"unknown FFN kind {kind!r}")
-    X, W = widen(X), widen(W_fire)
-    pre = X @ W.T                       # (n, ffn)
-    if b_fire is not None:
-        pre = pre + widen(b_fire)[None, :]
-    return (pre > 0.0).sum(axis=0).astype(np.int64)
+    return (profile_preactivations(X, W_fire, b_fire) > 0.0).sum(axis=0).astype(np.int64)
 
 
 def reorder_plan(counts, hot_share: float = 0.8) -> Tuple[np.ndarray, int]:
@@ -215,5 +228,7 @@ def reorder_plan(counts, hot_share: float = 0.8) -> Tuple[np.ndarray, int]:
 
 def permute_rows(src, perm) -> np.ndarray:
     """dst[j] = src[perm[j]]: apply a new -> old neuron order to a row-major tensor."""
+    if hasattr(src, "detach"):
+        src = src.detach().cpu().numpy()
     src = np.asarray(src)
     return src[np.asarray(perm, dtype=np.int64)].copy()
