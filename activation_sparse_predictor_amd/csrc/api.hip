@@ -137,15 +137,15 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, cons
     const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
     char* w = static_cast<char*>(ws);
     float* h = reinterpret_cast<float*>(w + L.h);
-    uint32_t* status = reinterpret_cast<uint32_t*>(w + L.status);
-    uint32_t* tickets = status + (size_t)B * L.tiles;
+    uint64_t* masks = reinterpret_cast<uint64_t*>(w + L.masks);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(w + L.ctr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const auto* hx = reinterpret_cast<const pi::h16*>(x);
     hipError_t e = pi::launch_pred_hidden(hx, B, d, reinterpret_cast<const pi::h16*>(P1), b1,
-                                          act == PI_ACT_RELU, r, h, status, B * L.tiles + B, s);
+                                          act == PI_ACT_RELU, r, h, ctr, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict hidden layer");
-    e = pi::launch_pred_compact(reinterpret_cast<const pi::h16*>(P2), b2, h, B, r, ffn, thr, status,
-                                tickets, idx, count, s);
+    e = pi::launch_pred_compact(reinterpret_cast<const pi::h16*>(P2), b2, h, B, r, ffn, thr, masks,
+                                ctr, idx, count, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict logits/compaction");
     return ok();
 }

@@ -20,7 +20,9 @@ __device__ __forceinline__ int clamp_row(int i, int ffn) { return i < 0 ? 0 : (i
 
 // ---------------------------------------------------------------------------
 // Gathered up(/gate) GEMV.  One wave per active neuron: the row (d fp16) is
-// streamed 1 KB per step, 8 steps in flight per lane, against x held in LDS.
+// streamed 1 KB per step, 16 steps (ReGLU: 8 per matrix) in flight per lane,
+// so a d <= 8192 row is requested in one round.  The first row's loads are
+// issued before x is staged into LDS, so the staging overlaps them.
 // Workgroup 0 of each token also zeroes that token's arrival counters for
 // the accumulate kernel that follows on the stream.
 template <bool REGLU, bool DENSE>
@@ -34,33 +36,51 @@ __global__ __launch_bounds__(256) void k_up_act(const h16* __restrict__ x, int d
                                                 float* __restrict__ a, uint32_t* __restrict__ ctr,
                                                 int T) {
     extern __shared__ u32x4 sx[];
+    constexpr int U = REGLU ? 8 : 16;
     const int tok = blockIdx.y;
+    const int tid = threadIdx.x;
     if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < T; i += 256) ctr[(size_t)tok * T + i] = 0u;
+        for (int i = tid; i < T; i += 256) ctr[((size_t)tok * T + i) * kCtrStride] = 0u;
     const int nch = d >> 3;
-    for (int i = threadIdx.x; i < nch; i += 256) sx[i] = ld16(x + (size_t)tok * d + (size_t)i * 8);
-    __syncthreads();
-
     const int cnt = DENSE ? ffn : clamp_count(count[tok], ffn);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = tid >> 6, lane = tid & 63;
     const int32_t* ip = idx + (size_t)tok * ffn;
-    for (int j = blockIdx.x * 4 + wave; j < cnt; j += gridDim.x * 4) {
-        const int i = DENSE ? j : clamp_row(ip[j], ffn);
+    const int stride = gridDim.x * 4;
+
+    int j = blockIdx.x * 4 + wave;
+    int i = 0;
+    u32x4 wu[U], wg[U];
+    auto issue = [&](int c0) {
         const h16* ru = Wup + (size_t)i * d;
         const h16* rg = REGLU ? Wg + (size_t)i * d : nullptr;
-        float au = 0.f, ag = 0.f;
-        for (int c0 = lane; c0 < nch; c0 += 64 * 8) {
-            u32x4 wu[8], wg[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int c = c0 + u * 64;
-                if (c < nch) {
-                    wu[u] = ld16_stream(ru + (size_t)c * 8);
-                    if (REGLU) wg[u] = ld16_stream(rg + (size_t)c * 8);
-                }
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u * 64;
+            if (c < nch) {
+                wu[u] = ld16_stream(ru + (size_t)c * 8);
+                if (REGLU) wg[u] = ld16_stream(rg + (size_t)c * 8);
             }
+        }
+    };
+    if (j < cnt) {
+        i = DENSE ? j : clamp_row(ip[j], ffn);
+        issue(lane);
+    }
+    for (int k = tid; k < nch; k += 256) sx[k] = ld16(x + (size_t)tok * d + (size_t)k * 8);
+    __syncthreads();
+
+    bool first = true;
+    for (; j < cnt; j += stride) {
+        if (!first) {
+            i = DENSE ? j : clamp_row(ip[j], ffn);
+            issue(lane);
+        }
+        first = false;
+        float au = 0.f, ag = 0.f;
+        for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+            if (c0 != lane) issue(c0);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < U; ++u) {
                 const int c = c0 + u * 64;
                 if (c < nch) {
                     const u32x4 xv = sx[c];
@@ -85,12 +105,18 @@ __global__ __launch_bounds__(256) void k_up_act(const h16* __restrict__ x, int d
 
 // ---------------------------------------------------------------------------
 // W_down accumulate.  Grid = (column tiles, neuron chunks, tokens).  A
-// workgroup of 128 threads owns 1024 output columns (8 per thread) and a
-// contiguous slice of the active list; each active row contributes one
-// coalesced 2 KB segment.  Per-chunk partial sums go to the workspace; the
-// last chunk of a column tile to arrive (atomic arrival counter) adds the
-// partials in chunk order and writes y, so the result does not depend on
-// scheduling, and resets the counter.
+// workgroup of 1024 threads owns 1024 output columns and a contiguous slice
+// of the active list.  The slice's row ids and activations are staged in
+// LDS, then 8 row groups of 128 threads each take every 8th row, so a row
+// contributes one coalesced 2 KB segment and a thread keeps 8 row loads in
+// flight with no dependent global load in between.  The row groups are
+// summed in LDS in a fixed order and the chunk's partial goes to the
+// workspace through device-coherent stores.  Once its stores have completed,
+// one thread per workgroup arrives on the tile's counter (a relaxed atomic on
+// its own 128-byte line); the last chunk to arrive adds the G partials in
+// chunk order (one column per thread, all loads issued together, read from
+// the coherent level), writes y and resets the counter.  The result never
+// depends on scheduling, and no L2 write-back is needed.
 template <bool DENSE>
 __global__ __launch_bounds__(kDownThreads) void k_down_acc(const h16* __restrict__ Wd, int d,
                                                            int ffn,
@@ -101,64 +127,85 @@ __global__ __launch_bounds__(kDownThreads) void k_down_acc(const h16* __restrict
                                                            float* __restrict__ partial,
                                                            uint32_t* __restrict__ ctr, int T,
                                                            int G) {
+    // Staged list slice, transposed so row group g finds its rows (window
+    // entries g, g+8, g+16, ...) contiguous: 8 ids in two 16-byte LDS reads.
+    constexpr int kPerGroup = kDownWindow / kDownGroups;
+    __shared__ float s_red[kDownGroups][kDownCols];
+    __shared__ __align__(16) int32_t s_row[kDownGroups][kPerGroup];
+    __shared__ __align__(16) float s_act[kDownGroups][kPerGroup];
     __shared__ int s_last;
     const int tile = blockIdx.x, chunk = blockIdx.y, tok = blockIdx.z;
+    const int tid = threadIdx.x;
     const int cnt = DENSE ? ffn : clamp_count(count[tok], ffn);
     const int per = (cnt + G - 1) / G;
     const int j0 = min(cnt, chunk * per), j1 = min(cnt, j0 + per);
-    const int col = tile * kDownCols + threadIdx.x * 8;
-    const bool on = col < d;
+    const int ct = tid % kDownColThreads;
+    const int rg = __builtin_amdgcn_readfirstlane(tid / kDownColThreads);
+    const int lcol = ct * 8;
+    const int col = tile * kDownCols + lcol;
     const int32_t* ip = idx + (size_t)tok * ffn;
     const float* ap = a + (size_t)tok * ffn;
 
     float acc[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[k] = 0.f;
-    if (on) {
-        int j = j0;
-        for (; j + 8 <= j1; j += 8) {
-            u32x4 w[8];
-            float s[8];
+    for (int w0 = j0; w0 < j1; w0 += kDownWindow) {
+        const int wn = min(kDownWindow, j1 - w0);
+        if (tid < wn) {
+            s_row[tid % kDownGroups][tid / kDownGroups] = DENSE ? w0 + tid : clamp_row(ip[w0 + tid], ffn);
+            s_act[tid % kDownGroups][tid / kDownGroups] = ap[w0 + tid];
+        }
+        __syncthreads();
+        const int nk = (wn - rg + kDownGroups - 1) / kDownGroups;  // rows of this group
+        if (col < d) {
+            for (int k0 = 0; k0 < nk; k0 += 8) {
+                const i32x4 r0 = *reinterpret_cast<const i32x4*>(&s_row[rg][k0]);
+                const i32x4 r1 = *reinterpret_cast<const i32x4*>(&s_row[rg][k0 + 4]);
+                const f32x4 a0 = *reinterpret_cast<const f32x4*>(&s_act[rg][k0]);
+                const f32x4 a1 = *reinterpret_cast<const f32x4*>(&s_act[rg][k0 + 4]);
+                const int rows[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+                const float s[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                u32x4 w[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = DENSE ? j + u : clamp_row(ip[j + u], ffn);
-                w[u] = ld16_stream(Wd + (size_t)i * d + col);
-                s[u] = ap[j + u];
+                for (int u = 0; u < 8; ++u)
+                    if (k0 + u < nk) w[u] = ld16_stream(Wd + (size_t)rows[u] * d + col);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (k0 + u < nk) axpy8(acc, s[u], w[u]);
             }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) axpy8(acc, s[u], w[u]);
         }
-        for (; j < j1; ++j) {
-            const int i = DENSE ? j : clamp_row(ip[j], ffn);
-            axpy8(acc, ap[j], ld16_stream(Wd + (size_t)i * d + col));
-        }
-        float* pp = partial + ((size_t)tok * G + chunk) * d + col;
-        *reinterpret_cast<f32x4*>(pp) = f32x4{acc[0], acc[1], acc[2], acc[3]};
-        *reinterpret_cast<f32x4*>(pp + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        __syncthreads();
     }
-    __threadfence();
+    *reinterpret_cast<f32x4*>(&s_red[rg][lcol]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(&s_red[rg][lcol + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
     __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = fetch_add_acq_rel(&ctr[(size_t)tok * T + tile], 1u) == (uint32_t)(G - 1);
+
+    const int gc = tile * kDownCols + tid;  // one output column per thread from here on
+    if (gc < d) {
+        float v = 0.f;
+#pragma unroll
+        for (int g = 0; g < kDownGroups; ++g) v += s_red[g][tid];
+        st_coherent(&partial[((size_t)tok * G + chunk) * d + gc], v);
+    }
+    wait_own_memory();
+    __syncthreads();
+    uint32_t* my_ctr = &ctr[((size_t)tok * T + tile) * kCtrStride];
+    if (tid == 0) s_last = fetch_add(my_ctr, 1u) == (uint32_t)(G - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    if (on) {
-        float sum[8];
+    if (gc < d) {
+        const float* q = partial + (size_t)tok * G * d + gc;
+        float sum = 0.f;
+        for (int g0 = 0; g0 < G; g0 += 16) {
+            float v[16];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sum[k] = 0.f;
-        const float* q = partial + (size_t)tok * G * d + col;
-        for (int g = 0; g < G; ++g) {
-            const f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q + (size_t)g * d));
-            const f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(q + (size_t)g * d + 4));
-            sum[0] += v0.x; sum[1] += v0.y; sum[2] += v0.z; sum[3] += v0.w;
-            sum[4] += v1.x; sum[5] += v1.y; sum[6] += v1.z; sum[7] += v1.w;
+            for (int u = 0; u < 16; ++u) v[u] = (g0 + u < G) ? ld_coherent(q + (size_t)(g0 + u) * d) : 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sum += v[u];
         }
-        float* yp = y + (size_t)tok * d + col;
-        *reinterpret_cast<f32x4*>(yp) = f32x4{sum[0], sum[1], sum[2], sum[3]};
-        *reinterpret_cast<f32x4*>(yp + 4) = f32x4{sum[4], sum[5], sum[6], sum[7]};
+        y[(size_t)tok * d + gc] = sum;
     }
-    if (threadIdx.x == 0) ctr[(size_t)tok * T + tile] = 0u;
+    if (tid == 0) st_flag(my_ctr, 0u);
 }
 
 hipError_t launch_up_act(bool reglu, bool dense, const h16* x, int B, int d, int ffn,
