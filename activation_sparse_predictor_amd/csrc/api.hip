@@ -71,6 +71,15 @@ pi_status check_ws(void* ws, size_t ws_bytes, size_t need, const char* op) {
     return PI_OK;
 }
 
+size_t sparse_ws_bytes(int B, int d, int ffn) {
+    size_t n = pi::sparse_layout(B, d, ffn).total;
+    if (B >= 2) {
+        const size_t u = pi::batch_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, d, ffn).total;
+        if (u > n) n = u;
+    }
+    return n;
+}
+
 #define PI_TRY(expr)                  \
     do {                              \
         pi_status _s = (expr);        \
@@ -105,7 +114,7 @@ pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes)
             return ok();
         case PI_OP_SPARSE:
             PI_TRY(check_dims(B, d, ffn));
-            *bytes = pi::sparse_layout(B, d, ffn).total;
+            *bytes = sparse_ws_bytes(B, d, ffn);
             return ok();
         case PI_OP_PROFILE:
             *bytes = 0;
@@ -156,7 +165,7 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
                         uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
     PI_TRY(check_dims(B, d, ffn));
     PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU, PI_ERR_INVALID_ARG, "kind=%d unknown", kind);
-    PI_REQUIRE((flags & ~PI_DENSE) == 0u, PI_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN)) == 0u, PI_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
     const bool dense = (flags & PI_DENSE) != 0u;
     const bool reglu = kind == PI_FFN_REGLU;
     PI_REQUIRE(reglu == (W_gate != nullptr), PI_ERR_INVALID_ARG,
@@ -172,21 +181,32 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
     PI_TRY(check_word(count, "count", !dense));
     PI_REQUIRE(y != nullptr, PI_ERR_INVALID_ARG, "y is NULL");
     PI_REQUIRE(aligned(y, 16), PI_ERR_UNSUPPORTED, "y is not 16-byte aligned");
-    const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
-    PI_TRY(check_ws(ws, ws_bytes, L.total, "pi_ffn_sparse"));
+    PI_TRY(check_ws(ws, ws_bytes, sparse_ws_bytes(B, d, ffn), "pi_ffn_sparse"));
 
     char* w = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const auto* hx = reinterpret_cast<const pi::h16*>(x);
+    const auto* hu = reinterpret_cast<const pi::h16*>(W_up);
+    const auto* hg = reinterpret_cast<const pi::h16*>(W_gate);
+    const auto* hd = reinterpret_cast<const pi::h16*>(W_down);
+    if (B >= 2 && !dense && !(flags & PI_PER_TOKEN)) {
+        for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
+            const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
+            const pi::BatchLayout L = pi::batch_layout(Bg, d, ffn);
+            hipError_t e = pi::launch_union(reglu, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
+                                            idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L, w, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
+        }
+        return ok();
+    }
+    const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
     float* a = reinterpret_cast<float*>(w + L.a);
     float* partial = reinterpret_cast<float*>(w + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(w + L.ctr);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = pi::launch_up_act(reglu, dense, reinterpret_cast<const pi::h16*>(x), B, d, ffn,
-                                     reinterpret_cast<const pi::h16*>(W_up), b_up,
-                                     reinterpret_cast<const pi::h16*>(W_gate), b_gate, idx, count,
-                                     a, ctr, L.T, s);
+    hipError_t e = pi::launch_up_act(reglu, dense, hx, B, d, ffn, hu, b_up, hg, b_gate, idx, count, a,
+                                     ctr, L.T, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse up/gate");
-    e = pi::launch_down_acc(dense, reinterpret_cast<const pi::h16*>(W_down), B, d, ffn, idx, count,
-                            a, y, partial, ctr, L.T, L.G, s);
+    e = pi::launch_down_acc(dense, hd, B, d, ffn, idx, count, a, y, partial, ctr, L.T, L.G, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse down");
     return ok();
 }

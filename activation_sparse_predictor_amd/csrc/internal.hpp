@@ -75,6 +75,44 @@ inline SparseLayout sparse_layout(int B, int d, int ffn) {
     return L;
 }
 
+// ---- batched union path (2 <= B <= kUnionMaxTokens tokens per pass)
+constexpr int kUnionMaxTokens = 128;
+struct BatchLayout {
+    size_t tmask;    // ffn x W uint32 per-neuron token masks
+    size_t umasks;   // tiles uint64 union bitmaps
+    size_t umask;    // |U| x W uint32 token masks in union order
+    size_t ulist;    // ffn int32 ascending union list
+    size_t ucount;   // uint32 |U|
+    size_t a_hi;     // Bp x lda fp16 activations, high part
+    size_t a_lo;     // Bp x lda fp16 activations, low part
+    size_t partial;  // G x Bp x d fp32 split-K partials
+    size_t ctr;      // kCtrWords uint32 arrival counters
+    size_t total;
+    int W, Bp, lda, T, G;
+};
+
+inline BatchLayout batch_layout(int B, int d, int ffn) {
+    BatchLayout L;
+    L.W = (B + 31) / 32;
+    L.Bp = L.W * 32;
+    L.lda = (ffn + 7) & ~7;
+    L.T = (d + 127) / 128;
+    L.G = (ffn + 4087) / 4088;   // chunks of at most 4088 union entries
+    if (L.G < 8) L.G = 8;
+    const size_t tiles = (size_t)(ffn + 63) / 64;
+    L.tmask = 0;
+    L.umasks = L.tmask + align256((size_t)ffn * L.W * 4);
+    L.umask = L.umasks + align256(tiles * 8);
+    L.ulist = L.umask + align256((size_t)ffn * L.W * 4);
+    L.ucount = L.ulist + align256((size_t)ffn * 4);
+    L.a_hi = L.ucount + 256;
+    L.a_lo = L.a_hi + align256((size_t)L.Bp * L.lda * 2);
+    L.partial = L.a_lo + align256((size_t)L.Bp * L.lda * 2);
+    L.ctr = L.partial + align256((size_t)L.G * L.Bp * d * 4);
+    L.total = L.ctr + align256((size_t)kCtrWords * 4);
+    return L;
+}
+
 typedef _Float16 h16;
 
 // predict.hip
@@ -91,6 +129,12 @@ hipError_t launch_up_act(bool reglu, bool dense, const h16* x, int B, int d, int
 hipError_t launch_down_acc(bool dense, const h16* Wd, int B, int d, int ffn, const int32_t* idx,
                            const int32_t* count, const float* a, float* y, float* partial,
                            uint32_t* ctr, int T, int G, hipStream_t s);
+
+// batch.hip
+hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h16* Wup,
+                        const float* bup, const h16* Wg, const float* bg, const h16* Wd,
+                        const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
+                        char* ws, hipStream_t s);
 
 // profile.hip
 hipError_t launch_profile(const h16* X, int n, int d, int ffn, const h16* W, const float* b,

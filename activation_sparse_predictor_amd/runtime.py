@@ -71,8 +71,12 @@ def predict(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
 
 def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
            count: Optional[torch.Tensor], y: Optional[torch.Tensor] = None,
-           dense: bool = False, stream=None) -> torch.Tensor:
-    """y (B x d fp32) from the active rows (or every row with dense=True)."""
+           dense: bool = False, per_token: bool = False, stream=None) -> torch.Tensor:
+    """y (B x d fp32) from the active rows (or every row with dense=True).
+
+    For B >= 2 the library reads the union of the tokens' rows once (matrix
+    cores); per_token=True runs each token through the single-token kernels.
+    """
     Bt, d = x.shape
     ffn = layer["ffn"]
     if y is None:
@@ -82,7 +86,8 @@ def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
     st = B.pi_ffn_sparse(B.KINDS[layer["kind"]], _bits(x), Bt, d, ffn, layer["W_up"],
                          layer.get("b_up"), layer.get("W_gate"), layer.get("b_gate"),
                          layer["W_down"], None if dense else idx, None if dense else count, y,
-                         B.PI_DENSE if dense else 0, ws, wsb, stream)
+                         (B.PI_DENSE if dense else 0) | (B.PI_PER_TOKEN if per_token else 0),
+                         ws, wsb, stream)
     B.check(st, "pi_ffn_sparse")
     return y
 

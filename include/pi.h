@@ -68,6 +68,8 @@ typedef enum pi_op {
 
 /* pi_ffn_sparse flags */
 #define PI_DENSE 0x1u      /* ignore idx/count and compute every neuron (dense FFN baseline) */
+#define PI_PER_TOKEN 0x2u  /* B >= 2: run every token through the single-token kernels instead of
+                              the union path (same results up to fp32 rounding) */
 
 #define PI_MAX_BATCH 256
 #define PI_MAX_D 16384
@@ -114,6 +116,15 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d,
  * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0).
  * idx must hold valid, strictly ascending neuron ids (as written by
  * pi_ffn_predict); the call does not re-check them.
+ *
+ * For B >= 2 (unless PI_DENSE or PI_PER_TOKEN) the tokens are taken in
+ * groups of up to 128: the union U of the group's lists is formed on the
+ * device, the rows of U are read once, and the up/gate and W_down products
+ * run on the matrix cores (fp16 x fp16 -> fp32; a_i is carried as an fp16
+ * hi/lo pair, about 22 significant bits).  A neuron outside token t's own
+ * list contributes exactly 0 to y_t, so y_t matches the single-token result
+ * up to fp32 rounding: the union changes which rows are read, not what is
+ * computed (the batched decode of Part A section 4.4).
  *
  * Errors: as pi_ffn_predict, plus INVALID_ARG for an unknown kind or flag,
  * or a W_gate that does not match the kind.

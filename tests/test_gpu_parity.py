@@ -143,18 +143,24 @@ def test_dense_flag(kind):
         check_y(Y[t].cpu().numpy(), ref, where=f"dense t={t}")
 
 
-@pytest.mark.parametrize("Bt", [1, 4, 15, 16, 17, 32])
-def test_batched_matches_single_token(Bt):
-    cfg = custom_config("relu", 520, 1000, 72, mean=0.15, number=56)
+@pytest.mark.parametrize("kind,Bt", [("relu", 1), ("relu", 2), ("relu", 4), ("relu", 15), ("relu", 16),
+                                     ("relu", 17), ("relu", 32), ("relu", 33), ("reglu", 8), ("reglu", 32),
+                                     ("relu", 100), ("reglu", 128), ("relu", 131)])
+def test_batched_union_path(kind, Bt):
+    """Batch of Bt tokens: lists equal single-token lists bit for bit; y (union
+    path on the matrix cores) matches the oracle on each token's own list; the
+    per-token path is bitwise equal to single-token calls."""
+    cfg = custom_config(kind, 520, 1000, 72, mean=0.15, number=56)
     L = R.to_device(make_layer(cfg), DEV)
     H = _host(L)
     X = make_tokens(cfg, Bt).to(DEV)
     idx, cnt = R.predict(L, X)
     Y = R.sparse(L, X, idx, cnt)
+    Yp = R.sparse(L, X, idx, cnt, per_token=True)
     torch.cuda.synchronize()
     thr = O.logit_threshold(L["tau"])
-    cnt_h, idx_h, Y_h = cnt.cpu().numpy(), idx.cpu().numpy(), Y.cpu().numpy()
-    for t in range(Bt):
+    cnt_h, idx_h, Y_h, Yp_h = cnt.cpu().numpy(), idx.cpu().numpy(), Y.cpu().numpy(), Yp.cpu().numpy()
+    for t in sorted(set([0, Bt // 2, Bt - 1] + list(range(0, Bt, max(1, Bt // 8))))):
         x1 = X[t:t + 1].contiguous()
         i1, c1 = R.predict(L, x1)
         y1 = R.sparse(L, x1, i1, c1)
@@ -162,11 +168,34 @@ def test_batched_matches_single_token(Bt):
         c = int(cnt_h[t])
         assert c == int(c1.cpu()[0])
         assert np.array_equal(idx_h[t, :c], i1[0, :c].cpu().numpy())
-        assert np.array_equal(Y_h[t], y1[0].cpu().numpy()), "batched result differs from single token"
+        assert np.array_equal(Yp_h[t], y1[0].cpu().numpy()), "per-token path differs from single token"
         xh = X[t].cpu()
         z = O.predictor_logits(xh, H["P1"], None, "relu", H["P2"], H["b2"])
         check_idx(idx_h[t, :c], z, thr, where=f"B={Bt} t={t}")
-        check_y(Y_h[t], _oracle_y(H, xh, idx_h[t, :c]), where=f"B={Bt} t={t}")
+        ref = _oracle_y(H, xh, idx_h[t, :c])
+        check_y(Y_h[t], ref, where=f"union B={Bt} t={t}")
+        check_y(Yp_h[t], ref, where=f"per-token B={Bt} t={t}")
+
+
+def test_union_path_edge_lists():
+    """Empty lists, disjoint lists, identical lists and one full list in one batch."""
+    cfg = custom_config("reglu", 1032, 1000, 16, mean=0.3, number=60)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    Bt, ffn = 6, cfg.ffn
+    X = make_tokens(cfg, Bt).to(DEV)
+    lists = [[], list(range(0, ffn, 2)), list(range(1, ffn, 2)), list(range(0, ffn, 2)), list(range(ffn)), [ffn - 1]]
+    idx = torch.zeros(Bt, ffn, dtype=torch.int32, device=DEV)
+    for t, l in enumerate(lists):
+        if l:
+            idx[t, :len(l)] = torch.tensor(l, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([len(l) for l in lists], dtype=torch.int32, device=DEV)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    Yh = Y.cpu().numpy()
+    assert np.all(Yh[0] == 0.0)
+    for t in range(1, Bt):
+        check_y(Yh[t], _oracle_y(H, X[t].cpu(), lists[t]), where=f"edge list t={t}")
 
 
 def test_deterministic_repeats():
@@ -282,7 +311,7 @@ def test_full_size_stack_layer_and_profile():
     check_counts(counts.cpu().numpy(), pre, where="c5 profile")
 
 
-@pytest.mark.parametrize("Bt", [4, 16])
+@pytest.mark.parametrize("Bt", [4, 16, 32])
 def test_full_size_batched(Bt):
     cfg, L, X = _full("c4", ntok=Bt)
     H = _host(L)
