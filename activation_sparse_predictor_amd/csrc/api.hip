@@ -71,6 +71,11 @@ pi_status check_ws(void* ws, size_t ws_bytes, size_t need, const char* op) {
     return PI_OK;
 }
 
+size_t predict_ws_bytes(int B, int r, int ffn) {
+    if (B == 1) return pi::predict_layout(1, r, ffn).total;
+    return pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
+}
+
 size_t sparse_ws_bytes(int B, int d, int ffn) {
     size_t n = pi::sparse_layout(B, d, ffn).total;
     if (B >= 2) {
@@ -110,7 +115,7 @@ pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes)
         case PI_OP_PREDICT:
             PI_TRY(check_dims(B, d, ffn));
             PI_REQUIRE(r > 0 && r <= PI_MAX_R, PI_ERR_INVALID_ARG, "r=%d outside [1, %d]", r, PI_MAX_R);
-            *bytes = pi::predict_layout(B, r, ffn).total;
+            *bytes = predict_ws_bytes(B, r, ffn);
             return ok();
         case PI_OP_SPARSE:
             PI_TRY(check_dims(B, d, ffn));
@@ -139,22 +144,32 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, cons
     PI_TRY(check_word(b2, "b2", false));
     PI_TRY(check_word(idx, "idx", true));
     PI_TRY(check_word(count, "count", true));
-    const pi::PredictLayout L = pi::predict_layout(B, r, ffn);
-    PI_TRY(check_ws(ws, ws_bytes, L.total, "pi_ffn_predict"));
+    PI_TRY(check_ws(ws, ws_bytes, predict_ws_bytes(B, r, ffn), "pi_ffn_predict"));
 
     // sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
     const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
     char* w = static_cast<char*>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const auto* hx = reinterpret_cast<const pi::h16*>(x);
+    const auto* h1 = reinterpret_cast<const pi::h16*>(P1);
+    const auto* h2 = reinterpret_cast<const pi::h16*>(P2);
+    if (B >= 2) {   // batched: both predictor layers on the matrix cores, weights read once per group
+        for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
+            const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
+            const pi::BPredLayout L = pi::bpred_layout(Bg, r, ffn);
+            hipError_t e = pi::launch_bpredict(hx + (size_t)g0 * d, Bg, d, h1, b1, act == PI_ACT_RELU, h2, b2,
+                                               r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L, w, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict batched");
+        }
+        return ok();
+    }
+    const pi::PredictLayout L = pi::predict_layout(B, r, ffn);
     float* h = reinterpret_cast<float*>(w + L.h);
     uint64_t* masks = reinterpret_cast<uint64_t*>(w + L.masks);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(w + L.ctr);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const auto* hx = reinterpret_cast<const pi::h16*>(x);
-    hipError_t e = pi::launch_pred_hidden(hx, B, d, reinterpret_cast<const pi::h16*>(P1), b1,
-                                          act == PI_ACT_RELU, r, h, ctr, s);
+    hipError_t e = pi::launch_pred_hidden(hx, B, d, h1, b1, act == PI_ACT_RELU, r, h, ctr, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict hidden layer");
-    e = pi::launch_pred_compact(reinterpret_cast<const pi::h16*>(P2), b2, h, B, r, ffn, thr, masks,
-                                ctr, idx, count, s);
+    e = pi::launch_pred_compact(h2, b2, h, B, r, ffn, thr, masks, ctr, idx, count, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict logits/compaction");
     return ok();
 }

@@ -80,7 +80,6 @@ constexpr int kUnionMaxTokens = 128;
 struct BatchLayout {
     size_t tmask;    // ffn x W uint32 per-neuron token masks
     size_t umasks;   // tiles uint64 union bitmaps
-    size_t umask;    // |U| x W uint32 token masks in union order
     size_t ulist;    // ffn int32 ascending union list
     size_t ucount;   // uint32 |U|
     size_t a_hi;     // Bp x lda fp16 activations, high part
@@ -102,14 +101,32 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
     const size_t tiles = (size_t)(ffn + 63) / 64;
     L.tmask = 0;
     L.umasks = L.tmask + align256((size_t)ffn * L.W * 4);
-    L.umask = L.umasks + align256(tiles * 8);
-    L.ulist = L.umask + align256((size_t)ffn * L.W * 4);
+    L.ulist = L.umasks + align256(tiles * 8);
     L.ucount = L.ulist + align256((size_t)ffn * 4);
     L.a_hi = L.ucount + 256;
     L.a_lo = L.a_hi + align256((size_t)L.Bp * L.lda * 2);
     L.partial = L.a_lo + align256((size_t)L.Bp * L.lda * 2);
     L.ctr = L.partial + align256((size_t)L.G * L.Bp * d * 4);
     L.total = L.ctr + align256((size_t)kCtrWords * 4);
+    return L;
+}
+
+// ---- batched predictor (2 <= B <= kUnionMaxTokens tokens per pass)
+struct BPredLayout {
+    size_t h_hi, h_lo;   // Bp x ldh fp16 hidden activations (hi + lo)
+    size_t masks32;      // B x ceil(ffn/32) uint32 per-token tile masks
+    size_t total;
+    int Bp, ldh;
+};
+
+inline BPredLayout bpred_layout(int B, int r, int ffn) {
+    BPredLayout L;
+    L.Bp = ((B + 31) / 32) * 32;
+    L.ldh = (r + 7) & ~7;
+    L.h_hi = 0;
+    L.h_lo = align256((size_t)L.Bp * L.ldh * 2);
+    L.masks32 = L.h_lo + align256((size_t)L.Bp * L.ldh * 2);
+    L.total = L.masks32 + align256((size_t)B * ((ffn + 31) / 32) * 4);
     return L;
 }
 
@@ -135,6 +152,10 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
                         char* ws, hipStream_t s);
+
+hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
+                          const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
+                          int32_t* count, const BPredLayout& L, char* ws, hipStream_t s);
 
 // profile.hip
 hipError_t launch_profile(const h16* X, int n, int d, int ffn, const h16* W, const float* b,

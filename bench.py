@@ -77,6 +77,77 @@ def cpu_baseline(cfg, layer_dev, tokens_dev, budget_s):
                       f"predict + sparse FFN), {el:.1f} s"}
 
 
+def batch_sweep(cfg_key, batches, steps, nl, log_fn):
+    """Decode steps of B tokens on the union path, cache-cold over nl layers."""
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import CONFIGS, make_layer, make_tokens
+    cfg = CONFIGS[cfg_key]
+    kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
+    m = 2 if kind == "reglu" else 1
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    layers = [make_layer(cfg, layer=l, device=dev) for l in range(nl)]
+    out = []
+    F = torch.nn.functional
+    for Bt in batches:
+        X = [make_tokens(cfg, Bt, device=dev, layer=l) for l in range(nl)]
+        idx = torch.empty(Bt, ffn, dtype=torch.int32, device=dev)
+        cnt = torch.empty(Bt, dtype=torch.int32, device=dev)
+        y = torch.empty(Bt, d, dtype=torch.float32, device=dev)
+        # union sizes for the byte accounting (host side, once per layer)
+        usize = []
+        for l in range(nl):
+            R.predict(layers[l], X[l], idx, cnt)
+            torch.cuda.synchronize()
+            c = cnt.cpu().tolist()
+            ih = idx.cpu()
+            sel = torch.zeros(ffn, dtype=torch.bool)
+            for t in range(Bt):
+                sel[ih[t, :c[t]].long()] = True
+            usize.append(int(sel.sum()))
+        for s in range(10):
+            R.predict(layers[s % nl], X[s % nl], idx, cnt)
+            R.sparse(layers[s % nl], X[s % nl], idx, cnt, y)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            R.predict(layers[s % nl], X[s % nl], idx, cnt)
+            R.sparse(layers[s % nl], X[s % nl], idx, cnt, y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        U = sum(usize[s % nl] for s in range(steps)) / steps
+        T = 2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * U * 2 * d + 4 * U + Bt * (2 * d + 4 * d)
+        # dense reference: torch GEMMs over every neuron for the same B tokens
+        def torch_dense(L, x):
+            if kind == "reglu":
+                a = torch.relu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
+            else:
+                a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
+            return F.linear(a.half(), L["W_down"].t())
+        for s in range(5):
+            torch_dense(layers[s % nl], X[s % nl])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        kd = max(10, steps // 4)
+        for s in range(kd):
+            torch_dense(layers[s % nl], X[s % nl])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_dense = e0.elapsed_time(e1) / kd
+        row = {"batch": Bt, "us_per_step": ms * 1000, "tokens_per_s_per_layer": Bt * 1000 / ms,
+               "union_rows": U, "touched_MB": T / 1e6, "GBs": T / ms / 1e6,
+               "torch_dense_us": ms_dense * 1000, "speedup_vs_torch_dense": ms_dense / ms}
+        log_fn(f"batch {Bt:3d}: {ms * 1000:8.1f} us  {Bt * 1000 / ms:9.0f} tok/s/layer  |U| {U:8.0f}  "
+               f"T {T / 1e6:6.1f} MB  {T / ms / 1e6:6.0f} GB/s  torch dense {ms_dense * 1000:7.1f} us")
+        out.append(row)
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": cfg.workload, "rows": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +159,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--sweep", default="c4", help="config of the batch sweep ('' to skip)")
+    ap.add_argument("--sweep-batches", default="1,4,8,16,32")
+    ap.add_argument("--sweep-steps", type=int, default=200)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -228,9 +302,18 @@ def main():
         log(f"dense {ms_dense * 1000:.1f} us ({db / ms_dense / 1e6:.0f} GB/s), torch {ms_torch * 1000:.1f} us, "
             f"speedup {ms_dense / ms_step:.2f}x")
 
+    sweep = None
+    if args.sweep:
+        del layers, tokens, xs
+        torch.cuda.empty_cache()
+        sweep = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")],
+                            args.sweep_steps, 4, log)
+
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(cfg, layers[0], tokens[0], args.cpu_seconds)
+        cpu_layer = make_layer(cfg, layer=0, device=dev)
+        cpu_tokens = make_tokens(cfg, NT, device=dev, layer=0)
+        cpu = cpu_baseline(cfg, cpu_layer, cpu_tokens, args.cpu_seconds)
         log(f"cpu oracle {cpu['value']:.2f} tok/s/layer on {cpu['cores']} threads")
 
     out = {
@@ -258,6 +341,7 @@ def main():
                      "stages_us": {k: v[0] * 1000 for k, v in stages.items()}},
         "dense_baseline": dense,
         "cpu_baseline": cpu,
+        "batch_sweep": sweep,
     }
     print(json.dumps(out), flush=True)
 

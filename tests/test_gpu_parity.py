@@ -147,9 +147,11 @@ def test_dense_flag(kind):
                                      ("relu", 17), ("relu", 32), ("relu", 33), ("reglu", 8), ("reglu", 32),
                                      ("relu", 100), ("reglu", 128), ("relu", 131)])
 def test_batched_union_path(kind, Bt):
-    """Batch of Bt tokens: lists equal single-token lists bit for bit; y (union
-    path on the matrix cores) matches the oracle on each token's own list; the
-    per-token path is bitwise equal to single-token calls."""
+    """Batch of Bt tokens.  The batched predictor (matrix cores) must satisfy the
+    index rule per token, and agree with the single-token predictor except
+    inside the threshold band; y of the union path matches the oracle on each
+    token's own list; the per-token sparse path is bitwise equal to a
+    single-token call on the same list."""
     cfg = custom_config(kind, 520, 1000, 72, mean=0.15, number=56)
     L = R.to_device(make_layer(cfg), DEV)
     H = _host(L)
@@ -162,17 +164,20 @@ def test_batched_union_path(kind, Bt):
     cnt_h, idx_h, Y_h, Yp_h = cnt.cpu().numpy(), idx.cpu().numpy(), Y.cpu().numpy(), Yp.cpu().numpy()
     for t in sorted(set([0, Bt // 2, Bt - 1] + list(range(0, Bt, max(1, Bt // 8))))):
         x1 = X[t:t + 1].contiguous()
-        i1, c1 = R.predict(L, x1)
-        y1 = R.sparse(L, x1, i1, c1)
-        torch.cuda.synchronize()
         c = int(cnt_h[t])
-        assert c == int(c1.cpu()[0])
-        assert np.array_equal(idx_h[t, :c], i1[0, :c].cpu().numpy())
-        assert np.array_equal(Yp_h[t], y1[0].cpu().numpy()), "per-token path differs from single token"
+        mine = idx_h[t, :c]
+        i1, c1 = R.predict(L, x1)
+        one = torch.from_numpy(idx_h[t:t + 1].copy()).to(DEV)
+        y1 = R.sparse(L, x1, one, cnt[t:t + 1].clone())
+        torch.cuda.synchronize()
         xh = X[t].cpu()
         z = O.predictor_logits(xh, H["P1"], None, "relu", H["P2"], H["b2"])
-        check_idx(idx_h[t, :c], z, thr, where=f"B={Bt} t={t}")
-        ref = _oracle_y(H, xh, idx_h[t, :c])
+        check_idx(mine, z, thr, where=f"batched predict B={Bt} t={t}")
+        single = i1[0, :int(c1.cpu()[0])].cpu().numpy()
+        diff = set(mine.tolist()) ^ set(single.tolist())
+        assert all(abs(z[j] - thr) <= 1e-3 for j in diff), f"B={Bt} t={t}: lists differ outside the band"
+        assert np.array_equal(Yp_h[t], y1[0].cpu().numpy()), "per-token path differs from single token"
+        ref = _oracle_y(H, xh, mine)
         check_y(Y_h[t], ref, where=f"union B={Bt} t={t}")
         check_y(Yp_h[t], ref, where=f"per-token B={Bt} t={t}")
 
