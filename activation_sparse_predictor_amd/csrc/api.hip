@@ -4,10 +4,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <numeric>
+#include <unordered_map>
 #include <vector>
 
 #include "internal.hpp"
@@ -71,18 +74,60 @@ pi_status check_ws(void* ws, size_t ws_bytes, size_t need, const char* op) {
     return PI_OK;
 }
 
+// Every workspace starts with the fused kernels' synchronisation header; the
+// layouts of all other kernels begin kSyncBytes in.
 size_t predict_ws_bytes(int B, int r, int ffn) {
-    if (B == 1) return pi::predict_layout(1, r, ffn).total;
-    return pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
+    if (B == 1) return pi::kSyncBytes + pi::fused_pred_layout(r, ffn).total;
+    return pi::kSyncBytes + pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
 }
 
 size_t sparse_ws_bytes(int B, int d, int ffn) {
-    size_t n = pi::sparse_layout(B, d, ffn).total;
-    if (B >= 2) {
+    size_t n = pi::sparse_layout(B, d, ffn).total;          // dense baseline
+    const size_t f = pi::fused_sparse_layout(d, ffn).total;  // single token / per token
+    if (f > n) n = f;
+    if (B >= 2) {                                            // union path
         const size_t u = pi::batch_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, d, ffn).total;
         if (u > n) n = u;
     }
-    return n;
+    return pi::kSyncBytes + n;
+}
+
+// Launch epochs of the fused kernels: process-wide, strictly increasing,
+// never 0 (the value of a freshly zeroed word).
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{0};
+    uint32_t e;
+    do {
+        e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+    } while (e == 0u);
+    return e;
+}
+
+// Which tagged layout each workspace last held.  Tags of earlier fused calls
+// can never match a new epoch, but data written by another layout could, so
+// a fused call zeroes its tagged words whenever the workspace last held
+// something else (a different op or shape, an unfused call, or a workspace
+// not seen before).
+std::mutex g_ws_mu;
+std::unordered_map<const void*, uint64_t> g_ws_layout;
+
+uint64_t layout_key(int op, int a, int ffn) {
+    return ((uint64_t)(op + 1) << 48) | ((uint64_t)(uint32_t)a << 25) | (uint64_t)(uint32_t)ffn;
+}
+
+// true if the tagged words must be zeroed before a call with this layout
+bool ws_needs_clear(const void* ws, uint64_t key) {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    auto it = g_ws_layout.find(ws);
+    return it == g_ws_layout.end() || it->second != key;
+}
+void ws_record(const void* ws, uint64_t key) {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    g_ws_layout[ws] = key;
+}
+void ws_forget(const void* ws) {
+    std::lock_guard<std::mutex> g(g_ws_mu);
+    g_ws_layout.erase(ws);
 }
 
 #define PI_TRY(expr)                  \
@@ -154,23 +199,27 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, cons
     const auto* h1 = reinterpret_cast<const pi::h16*>(P1);
     const auto* h2 = reinterpret_cast<const pi::h16*>(P2);
     if (B >= 2) {   // batched: both predictor layers on the matrix cores, weights read once per group
+        ws_forget(ws);
         for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
             const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
             const pi::BPredLayout L = pi::bpred_layout(Bg, r, ffn);
             hipError_t e = pi::launch_bpredict(hx + (size_t)g0 * d, Bg, d, h1, b1, act == PI_ACT_RELU, h2, b2,
-                                               r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L, w, s);
+                                               r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L,
+                                               w + pi::kSyncBytes, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict batched");
         }
         return ok();
     }
-    const pi::PredictLayout L = pi::predict_layout(B, r, ffn);
-    float* h = reinterpret_cast<float*>(w + L.h);
-    uint64_t* masks = reinterpret_cast<uint64_t*>(w + L.masks);
-    uint32_t* ctr = reinterpret_cast<uint32_t*>(w + L.ctr);
-    hipError_t e = pi::launch_pred_hidden(hx, B, d, h1, b1, act == PI_ACT_RELU, r, h, ctr, s);
-    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict hidden layer");
-    e = pi::launch_pred_compact(h2, b2, h, B, r, ffn, thr, masks, ctr, idx, count, s);
-    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict logits/compaction");
+    // one token: a single kernel, hidden rows overlapping the logits tiles
+    const pi::FusedPredLayout L = pi::fused_pred_layout(r, ffn);
+    const uint64_t key = layout_key(PI_OP_PREDICT, r, ffn);
+    hipError_t e = hipSuccess;
+    if (ws_needs_clear(ws, key)) e = pi::launch_zero(w + pi::kSyncBytes, L.total, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict clearing the workspace");
+    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, thr, L, w, next_epoch(), idx,
+                                 count, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict");
+    ws_record(ws, key);
     return ok();
 }
 
@@ -205,15 +254,32 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
     const auto* hg = reinterpret_cast<const pi::h16*>(W_gate);
     const auto* hd = reinterpret_cast<const pi::h16*>(W_down);
     if (B >= 2 && !dense && !(flags & PI_PER_TOKEN)) {
+        ws_forget(ws);
         for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
             const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
             const pi::BatchLayout L = pi::batch_layout(Bg, d, ffn);
             hipError_t e = pi::launch_union(reglu, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
-                                            idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L, w, s);
+                                            idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L,
+                                            w + pi::kSyncBytes, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
         }
         return ok();
     }
+    if (!dense) {   // one token (or PI_PER_TOKEN): one kernel per token, up/gate rows overlapping W_down
+        const pi::FusedSparseLayout L = pi::fused_sparse_layout(d, ffn);
+        const uint64_t key = layout_key(PI_OP_SPARSE, d, ffn);
+        hipError_t e = hipSuccess;
+        if (ws_needs_clear(ws, key)) e = pi::launch_zero(w + pi::kSyncBytes + L.atag, L.partial - L.atag, s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse clearing the workspace");
+        for (int t = 0; t < B && e == hipSuccess; ++t)
+            e = pi::launch_sparse_fused(reglu, hx + (size_t)t * d, d, ffn, hu, b_up, hg, b_gate, hd,
+                                        idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, w, next_epoch(), s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse");
+        ws_record(ws, key);
+        return ok();
+    }
+    ws_forget(ws);
+    w += pi::kSyncBytes;
     const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
     float* a = reinterpret_cast<float*>(w + L.a);
     float* partial = reinterpret_cast<float*>(w + L.partial);

@@ -1,0 +1,509 @@
+// Single-token decode step, one kernel per entry point.
+//
+// pi_ffn_predict (B = 1):  k_predict_fused
+//   workgroups [0, NA)        hidden rows, one wave per row of P1:
+//                             h_k = act(P1[k].x + b1_k), published as a tagged word
+//   workgroups [NA, NA + NT)  logits tiles of 32 neurons: issue the tile's P2 rows,
+//                             collect h, z = P2 h + b2 > thr, publish the tile's
+//                             32-bit mask as a tagged word; the last workgroup
+//                             also gathers every mask and writes idx (ascending)
+//                             and count
+//
+// pi_ffn_sparse (B = 1):   k_sparse_fused
+//   workgroups [0, NU)        up chunks, one wave per active row:
+//                             a_j = act(W_up[i].x + b_up_i [, W_gate[i].x + b_gate_i]),
+//                             published as a tagged word
+//   workgroups [NU, NU + T*G) W_down (column tile, list chunk): stage the chunk's
+//                             ids, issue its row segments, collect the chunk's
+//                             a_j, accumulate; the last chunk of a column tile to
+//                             arrive adds the G partials in chunk order
+// All up chunks precede the W_down workgroups: the up rows, which everything
+// waits for, are all requested first.
+//
+// A tagged word is 64 bits, {epoch, 32-bit payload}, written and read with
+// single-copy-atomic device-coherent accesses: a consumer polls the data
+// itself, so publishing costs one store and consuming one load, with no flag
+// or counter in between.  The epoch is a host counter that never repeats
+// within the process (and is never 0), so a word left over from an earlier
+// call can never pass for a current one.  A workgroup only waits for
+// workgroups with a smaller index, which are dispatched before it, so the
+// roles overlap (P1 with P2, W_up with W_down) without any risk of circular
+// waiting.  Every wait is bounded: on overrun the kernel reports an error
+// (count = -1, or NaN in y) instead of hanging.
+//
+// Loads are issued in batches with no uniform condition around any of them:
+// such a branch makes the compiler wait for every earlier load before the
+// next one.  A slot past the end of its range is masked per lane, or reads a
+// clamped, valid address whose value is not used; an absent bias is read
+// from a zero word in the workspace.  Vector loads complete in order, so small
+// loads that must be consumed early (x, ids) go out before the weight batch
+// they share a counter with.
+#include "common.hpp"
+#include "internal.hpp"
+#include "pi.h"
+
+namespace pi {
+
+constexpr int kWaitLimit = 1 << 16;   // polls (with a short sleep) before a wait gives up
+
+__device__ __forceinline__ uint64_t ld_tag(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_tag(uint64_t* p, uint32_t epoch, uint32_t payload) {
+    __hip_atomic_store(p, ((uint64_t)epoch << 32) | payload, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool is_current(uint64_t v, uint32_t epoch) { return (uint32_t)(v >> 32) == epoch; }
+
+// Re-read *p until it carries the epoch; false on overrun.
+__device__ __forceinline__ bool poll_tag(const uint64_t* p, uint64_t& v, uint32_t epoch) {
+    for (int n = 0; !is_current(v, epoch); ++n) {
+        if (n == kWaitLimit) return false;
+        __builtin_amdgcn_s_sleep(2);
+        v = ld_tag(p);
+    }
+    return true;
+}
+
+// ===========================================================================
+// Predict.
+constexpr int kLTile = 32;    // neurons per logits tile (one 32-bit mask), 8 per wave
+constexpr int kLRows = 8;     // rows per wave
+constexpr int kLCols = 2;     // 64-lane chunk columns per batch: 16 P2 loads in flight per lane
+static_assert(kLRows * 4 == kLTile, "4 waves per logits tile");
+
+// 5 waves per SIMD: at 5 workgroups per CU every hidden row and logits tile of
+// a 1024 x 28672 predictor is resident from the start.
+__global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x, int d,
+                                                       const h16* __restrict__ P1,
+                                                       const float* __restrict__ b1, int relu, int r,
+                                                       const h16* __restrict__ P2,
+                                                       const float* __restrict__ b2, int ffn, float thr,
+                                                       uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
+                                                       uint32_t epoch, int32_t* __restrict__ idx,
+                                                       int32_t* __restrict__ count, const float* __restrict__ zero) {
+    extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
+    __shared__ uint32_t s_act[kLTile];
+    __shared__ uint32_t s_part[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int NA = (r + 3) / 4;
+    const int NT = (ffn + kLTile - 1) / kLTile;
+
+    if ((int)blockIdx.x < NA) {
+        // ---------------- hidden rows
+        const int row = blockIdx.x * 4 + wave;
+        const bool valid = row < r;
+        const h16* prow = P1 + (size_t)min(row, r - 1) * d;
+        const int nch = d >> 3;
+        u32x4 xs[4];   // x chunks tid + 256 q, requested ahead of the P1 rows
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xs[q] = ld16(x + (size_t)min(tid + q * 256, nch - 1) * 8);
+        u32x4 w[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            if (lane + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(lane + u * 64) * 8);
+        const float bias = *(b1 ? b1 + min(row, r - 1) : zero);
+        u32x4* sx = reinterpret_cast<u32x4*>(sh);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (tid + q * 256 < nch) sx[tid + q * 256] = xs[q];
+        for (int i = tid + 1024; i < nch; i += 256) sx[i] = ld16(x + (size_t)i * 8);   // d > 8192
+        __syncthreads();
+        float acc = 0.f;
+        for (int c0 = lane; c0 < nch; c0 += 64 * 16) {
+            if (c0 != lane) {
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    if (c0 + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(c0 + u * 64) * 8);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int c = c0 + u * 64;
+                if (c < nch) acc = dot8_h(w[u], sx[c], acc);
+            }
+        }
+        const float s = group_sum<64>(acc) + bias;
+        if (valid && lane == 0) st_tag(&htag[row], epoch, __float_as_uint(relu ? fmaxf(s, 0.f) : s));
+        return;
+    }
+
+    // ---------------- logits tile: wave w owns neurons tile*32 + 8w + k (k < 8); lane l
+    // takes chunks l + 64m of all eight rows, so an h chunk read from LDS serves
+    // eight rows
+    const int tile = blockIdx.x - NA;
+    const int row0 = tile * kLTile + wave * kLRows;   // wave-uniform
+    const int nch = r >> 3;
+    const int M = (nch + 63) / 64;                     // chunk columns per lane
+    const h16* prow[kLRows];
+#pragma unroll
+    for (int k = 0; k < kLRows; ++k) prow[k] = P2 + (size_t)min(row0 + k, ffn - 1) * r;
+    float bias = 0.f;   // lane k < 8: b2 of row row0 + k
+    float acc[kLRows];
+#pragma unroll
+    for (int k = 0; k < kLRows; ++k) acc[k] = 0.f;
+    bool have_h = false, ok = true;
+    // h (and b2) are collected once the first batch of P2 loads is in flight
+    auto collect_round = [&](int i0) {
+        uint64_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[min(i0 + q * 256, r - 1)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = i0 + q * 256;
+            if (i < r) {
+                ok = poll_tag(&htag[i], v[q], epoch) && ok;
+                sh[i] = __uint_as_float((uint32_t)v[q]);
+            }
+        }
+    };
+    auto collect_h = [&]() {
+        bias = *(b2 ? b2 + min(row0 + (lane & (kLRows - 1)), ffn - 1) : zero);
+        collect_round(tid);   // outside any loop: a loop header would wait for the P2 batch first
+        for (int i0 = tid + 1024; i0 < r; i0 += 1024) collect_round(i0);
+        ok = __syncthreads_and(ok);
+        have_h = true;
+    };
+    auto accumulate = [&](const u32x4 (&w)[kLRows][kLCols], int m0) {
+#pragma unroll
+        for (int m = 0; m < kLCols; ++m) {
+            const int c = lane + (m0 + m) * 64;
+            if (c < nch) {
+                const f32x4* hp = reinterpret_cast<const f32x4*>(sh + c * 8);
+                const f32x4 h0 = hp[0], h1 = hp[1];
+                const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+                for (int k = 0; k < kLRows; ++k) acc[k] = dot8_hf(w[k][m], hv, acc[k]);
+            }
+        }
+    };
+    int m0 = 0;
+    for (; (m0 + kLCols) * 64 <= nch; m0 += kLCols) {   // full batches: every lane in range
+        u32x4 w[kLRows][kLCols];
+#pragma unroll
+        for (int k = 0; k < kLRows; ++k)
+#pragma unroll
+            for (int m = 0; m < kLCols; ++m) w[k][m] = ld16_stream(prow[k] + (size_t)(lane + (m0 + m) * 64) * 8);
+        if (!have_h) collect_h();
+        accumulate(w, m0);
+    }
+    if (m0 < M) {   // the last, partial batch: lanes past the row end are masked
+        u32x4 w[kLRows][kLCols];
+#pragma unroll
+        for (int k = 0; k < kLRows; ++k)
+#pragma unroll
+            for (int m = 0; m < kLCols; ++m) {
+                const int c = lane + (m0 + m) * 64;
+                if (c < nch) w[k][m] = ld16_stream(prow[k] + (size_t)c * 8);
+            }
+        if (!have_h) collect_h();
+        accumulate(w, m0);
+    }
+    if (!have_h) collect_h();
+    float zk = 0.f;   // lane k < 8: z of row row0 + k
+#pragma unroll
+    for (int k = 0; k < kLRows; ++k) {
+        const float z = group_sum<64>(acc[k]);
+        if ((lane & (kLRows - 1)) == k) zk = z;
+    }
+    if (lane < kLRows) s_act[wave * kLRows + lane] = (row0 + lane < ffn) && (zk + bias > thr);
+    __syncthreads();
+    if (wave == 0) {
+        const uint64_t m = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
+        if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)m);
+    }
+    if ((int)blockIdx.x != NA + NT - 1) return;
+
+    // ---------------- the last workgroup: ordered compaction, 1024 tiles per round (4 per thread)
+    uint32_t base = 0;
+    bool good = ok;
+    for (int t0 = 0; t0 < NT; t0 += 1024) {
+        uint64_t m4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + tid * 4 + q, NT - 1)]);
+        uint32_t bits[4];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int t = t0 + tid * 4 + q;
+            bits[q] = 0u;
+            if (t < NT) {
+                if (poll_tag(&mtag[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
+                else good = false;
+            }
+            mine += (uint32_t)__popc(bits[q]);
+        }
+        uint32_t incl = mine;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        if (lane == 63) s_part[wave] = incl;
+        __syncthreads();
+        uint32_t pos = base + incl - mine;
+        for (int w2 = 0; w2 < wave; ++w2) pos += s_part[w2];
+        const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t m = bits[q];
+            const int t = t0 + tid * 4 + q;
+            while (m) {
+                idx[pos++] = t * kLTile + __builtin_ctz(m);
+                m &= m - 1;
+            }
+        }
+        base += total;
+        __syncthreads();
+    }
+    good = __syncthreads_and(good);
+    if (tid == 0) count[0] = good ? (int32_t)base : -1;
+}
+
+// ===========================================================================
+// Sparse FFN.
+constexpr int kSThreads = 512;                       // 8 waves
+constexpr int kSColThreads = kFusedCols / 8;         // column threads of a W_down tile (8 fp16 each)
+constexpr int kSGroups = kSThreads / kSColThreads;   // row groups per W_down workgroup
+constexpr int kSBatch = 8;                           // W_down rows in flight per thread
+constexpr int kSWindow = 2048;                       // list entries staged in LDS at a time
+static_assert(kSColThreads * kSGroups == kSThreads, "tile shape");
+static_assert(kFusedCols <= kSThreads, "one reduction column per thread");
+
+template <bool REGLU>
+__global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restrict__ x, int d, int ffn,
+                                                            const h16* __restrict__ Wup,
+                                                            const float* __restrict__ bup,
+                                                            const h16* __restrict__ Wg,
+                                                            const float* __restrict__ bg,
+                                                            const h16* __restrict__ Wd,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ count, int NU,
+                                                            int T, int G, uint64_t* __restrict__ atag,
+                                                            float* __restrict__ partial,
+                                                            uint32_t* __restrict__ ctr, uint32_t epoch,
+                                                            float* __restrict__ y, const float* __restrict__ zero) {
+    // up role: x (d fp16); W_down role: row-group partials, window ids and activations
+    __shared__ __align__(16) char s_mem[kSGroups * kFusedCols * 4 + kSWindow * 8];
+    static_assert(sizeof(s_mem) >= PI_MAX_D * 2, "x does not fit the up role's LDS");
+    u32x4* s_x = reinterpret_cast<u32x4*>(s_mem);
+    float(*s_red)[kFusedCols] = reinterpret_cast<float(*)[kFusedCols]>(s_mem);
+    int32_t* s_row = reinterpret_cast<int32_t*>(s_mem + kSGroups * kFusedCols * 4);
+    float* s_a = reinterpret_cast<float*>(s_mem + kSGroups * kFusedCols * 4 + kSWindow * 4);
+    __shared__ int s_flag;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cnt = min(max(count[0], 0), ffn);
+    const int PU = (cnt + NU - 1) / NU;   // list positions per up chunk
+
+    if ((int)blockIdx.x < NU) {
+        // ---------------- up chunk: one wave per active row
+        const int u = blockIdx.x;
+        const int j0 = min(cnt, u * PU), j1 = min(cnt, j0 + PU);
+        if (j0 >= j1) return;
+        constexpr int UU = REGLU ? 8 : 16;
+        const int nch = d >> 3;
+        int j = j0 + wave;
+        int i = 0;
+        u32x4 wu[UU], wg[UU];
+        auto issue = [&](int c0) {
+            const h16* ru = Wup + (size_t)i * d;
+            const h16* rg = REGLU ? Wg + (size_t)i * d : nullptr;
+#pragma unroll
+            for (int q = 0; q < UU; ++q) {
+                const int c = c0 + q * 64;
+                if (c < nch) {
+                    wu[q] = ld16_stream(ru + (size_t)c * 8);
+                    if (REGLU) wg[q] = ld16_stream(rg + (size_t)c * 8);
+                }
+            }
+        };
+        float bu = 0.f, bgv = 0.f;   // the row's biases, requested with its weights
+        auto issue_bias = [&]() {
+            bu = *(bup ? bup + i : zero);
+            if (REGLU) bgv = *(bg ? bg + i : zero);
+        };
+        u32x4 xs[2];   // x chunks tid + 512 q, requested ahead of the rows
+#pragma unroll
+        for (int q = 0; q < 2; ++q) xs[q] = ld16(x + (size_t)min(tid + q * kSThreads, nch - 1) * 8);
+        const bool live = j < j1;   // wave-uniform
+        i = min(max(idx[min(j, j1 - 1)], 0), ffn - 1);
+        issue(lane);
+        issue_bias();
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            if (tid + q * kSThreads < nch) s_x[tid + q * kSThreads] = xs[q];
+        for (int k = tid + 2 * kSThreads; k < nch; k += kSThreads) s_x[k] = ld16(x + (size_t)k * 8);   // d > 8192
+        __syncthreads();
+        if (!live) return;
+        bool first = true;
+        for (; j < j1; j += kSThreads / 64) {
+            if (!first) {
+                i = min(max(idx[j], 0), ffn - 1);
+                issue(lane);
+                issue_bias();
+            }
+            first = false;
+            float au = 0.f, ag = 0.f;
+            for (int c0 = lane; c0 < nch; c0 += 64 * UU) {
+                if (c0 != lane) issue(c0);
+#pragma unroll
+                for (int q = 0; q < UU; ++q) {
+                    const int c = c0 + q * 64;
+                    if (c < nch) {
+                        const u32x4 xv = s_x[c];
+                        au = dot8_h(wu[q], xv, au);
+                        if (REGLU) ag = dot8_h(wg[q], xv, ag);
+                    }
+                }
+            }
+            au = group_sum<64>(au);
+            if (REGLU) ag = group_sum<64>(ag);
+            if (lane == 0) {
+                const float uval = au + bu;
+                const float act = REGLU ? fmaxf(ag + bgv, 0.f) * uval : fmaxf(uval, 0.f);
+                st_tag(&atag[j], epoch, __float_as_uint(act));
+            }
+        }
+        return;
+    }
+
+    // ---------------- W_down (column tile, chunk)
+    const int k = blockIdx.x - NU;
+    const int tile = k % T, chunk = k / T;
+    const int PD = (cnt + G - 1) / G;
+    const int j0 = min(cnt, chunk * PD), j1 = min(cnt, j0 + PD);
+    const int ct = tid % kSColThreads;
+    const int rg = __builtin_amdgcn_readfirstlane(tid / kSColThreads);
+    const int col = tile * kFusedCols + ct * 8;
+    const bool on = col < d;
+    const int colc = min(col, d - 8);   // load address of a column past the end
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    bool ok = true;
+    for (int w0 = j0; w0 < j1; w0 += kSWindow) {
+        const int wn = min(kSWindow, j1 - w0);
+        for (int q0 = tid; q0 < wn; q0 += kSThreads * 4) {
+            int32_t v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = idx[w0 + min(q0 + e * kSThreads, wn - 1)];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (q0 + e * kSThreads < wn) s_row[q0 + e * kSThreads] = min(max(v[e], 0), ffn - 1);
+        }
+        __syncthreads();
+        const int nk = (wn - rg + kSGroups - 1) / kSGroups;   // this group's rows: rg + kSGroups * n
+        // the first batch of rows goes out before the activations are collected
+        u32x4 w[kSBatch];
+#pragma unroll
+        for (int q = 0; q < kSBatch; ++q)
+            w[q] = ld16_stream(Wd + (size_t)s_row[min(rg + kSGroups * q, wn - 1)] * d + colc);
+        for (int q0 = tid; q0 < wn; q0 += kSThreads * 4) {
+            uint64_t v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = ld_tag(&atag[w0 + min(q0 + e * kSThreads, wn - 1)]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int q = q0 + e * kSThreads;
+                if (q < wn) {
+                    ok = poll_tag(&atag[w0 + q], v[e], epoch) && ok;
+                    s_a[q] = __uint_as_float((uint32_t)v[e]);
+                }
+            }
+        }
+        __syncthreads();
+        if (on) {
+            for (int k0 = 0; k0 < nk; k0 += kSBatch) {
+                if (k0 > 0) {
+#pragma unroll
+                    for (int q = 0; q < kSBatch; ++q)
+                        w[q] = ld16_stream(Wd + (size_t)s_row[min(rg + kSGroups * (k0 + q), wn - 1)] * d + colc);
+                }
+#pragma unroll
+                for (int q = 0; q < kSBatch; ++q)
+                    if (k0 + q < nk) axpy8(acc, s_a[rg + kSGroups * (k0 + q)], w[q]);
+            }
+        }
+        __syncthreads();
+    }
+    ok = __syncthreads_and(ok);
+    *reinterpret_cast<f32x4*>(&s_red[rg][ct * 8]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(&s_red[rg][ct * 8 + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    __syncthreads();
+    // one column per thread: the chunk's partial (NaN if its activations never arrived)
+    const int gc = tile * kFusedCols + tid;
+    if (tid < kFusedCols && gc < d) {
+        float v = 0.f;
+#pragma unroll
+        for (int g = 0; g < kSGroups; ++g) v += s_red[g][tid];
+        st_coherent(&partial[(size_t)chunk * d + gc], ok ? v : __builtin_nanf(""));
+    }
+    wait_own_memory();
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t* c = &ctr[(size_t)tile * kCtrStride];
+        s_flag = fetch_add(c, 1u) == (uint32_t)(G - 1);
+        if (s_flag) st_flag(c, 0u);   // the last arrival puts the counter back for the next call
+    }
+    __syncthreads();
+    if (!s_flag || tid >= kFusedCols || gc >= d) return;
+    // the tile's last chunk: add the G partials in chunk order, all loads in one round
+    // the partial buffer holds kFusedMaxChunks chunks, so every load is in bounds
+    float v[kFusedMaxChunks];
+#pragma unroll
+    for (int g = 0; g < kFusedMaxChunks; ++g) v[g] = ld_coherent(&partial[(size_t)g * d + gc]);
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < kFusedMaxChunks; ++g)
+        if (g < G) sum += v[g];
+    y[gc] = sum;
+}
+
+hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
+                                const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
+                                char* ws, uint32_t epoch, int32_t* idx, int32_t* count, hipStream_t s) {
+    char* data = ws + kSyncBytes;
+    uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
+    uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
+    const int NA = (r + 3) / 4;
+    const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
+    const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
+    hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
+                       thr, htag, mtag, epoch, idx, count, zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
+                               const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
+                               const int32_t* count, float* y, const FusedSparseLayout& L, char* ws,
+                               uint32_t epoch, hipStream_t s) {
+    char* data = ws + kSyncBytes;
+    uint64_t* atag = reinterpret_cast<uint64_t*>(data + L.atag);
+    float* partial = reinterpret_cast<float*>(data + L.partial);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + Sync::ffn_ctr);
+    const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
+    dim3 grid(L.NU + L.T * L.G);
+    if (reglu)
+        hipLaunchKernelGGL(k_sparse_fused<true>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,
+                           count, L.NU, L.T, L.G, atag, partial, ctr, epoch, y, zero);
+    else
+        hipLaunchKernelGGL(k_sparse_fused<false>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,
+                           count, L.NU, L.T, L.G, atag, partial, ctr, epoch, y, zero);
+    return hipGetLastError();
+}
+
+// Zero n 32-bit words (a fill kernel, so that the call stays capturable in a graph).
+__global__ __launch_bounds__(256) void k_zero(uint32_t* __restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    size_t g = (n + 255) / 256;
+    if (g > 1024) g = 1024;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)g), dim3(256), 0, s, static_cast<uint32_t*>(p), n);
+    return hipGetLastError();
+}
+
+}  // namespace pi

@@ -17,25 +17,7 @@ constexpr int kPredTile = 64;
 constexpr int kArriveGroups = 8;
 constexpr int kCtrStride = 32;   // uint32 words between counters (128 bytes)
 constexpr int kCtrWords = (kArriveGroups + 1) * kCtrStride;   // per token
-inline int pred_tiles(int ffn) { return (ffn + kPredTile - 1) / kPredTile; }
-
-struct PredictLayout {
-    size_t h;        // B x r fp32 hidden activations
-    size_t masks;    // B x tiles uint64 active-neuron bitmaps
-    size_t ctr;      // B x kCtrWords uint32 arrival counters
-    size_t total;
-    int tiles;
-};
-
-inline PredictLayout predict_layout(int B, int r, int ffn) {
-    PredictLayout L;
-    L.tiles = pred_tiles(ffn);
-    L.h = 0;
-    L.masks = align256((size_t)B * r * 4);
-    L.ctr = L.masks + align256((size_t)B * L.tiles * 8);
-    L.total = L.ctr + align256((size_t)B * kCtrWords * 4);
-    return L;
-}
+__host__ __device__ inline int pred_tiles(int ffn) { return (ffn + kPredTile - 1) / kPredTile; }
 
 // ---- W_down accumulate: column tiles of 1024 (128 threads x 8 fp16), each
 // workgroup split into kDownGroups row groups reduced in LDS, and G neuron
@@ -130,13 +112,55 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
     return L;
 }
 
-typedef _Float16 h16;
+// ---- fused single-token kernels.  They publish intermediate values as
+// tagged 64-bit words {launch epoch, payload} in the data area, and keep the
+// W_down arrival counters in a fixed header at the start of every workspace,
+// which no other layout touches: the header is zero-filled once when the
+// workspace is allocated and each counter is put back to 0 by the last
+// arrival of every call.  All other layouts start kSyncBytes in.
+constexpr int kFusedCols = 512;                     // W_down columns per tile
+constexpr int kFusedMaxTiles = 16384 / kFusedCols;  // PI_MAX_D / kFusedCols
+constexpr int kFusedMaxChunks = 48;                 // list chunks per W_down tile
+struct Sync {   // byte offsets inside the header
+    static constexpr size_t ffn_ctr = 0;                                    // one 128-byte line per tile
+    static constexpr size_t zero = ffn_ctr + (size_t)kFusedMaxTiles * kCtrStride * 4;   // never written
+    static constexpr size_t end = zero + 256;
+};
+constexpr size_t kSyncBytes = 8192;
+static_assert(Sync::end <= kSyncBytes, "sync header overflow");
 
-// predict.hip
-hipError_t launch_pred_hidden(const h16* x, int B, int d, const h16* P1, const float* b1,
-                              bool relu, int r, float* h, uint32_t* ctr, hipStream_t s);
-hipError_t launch_pred_compact(const h16* P2, const float* b2, const float* h, int B, int r,
-                               int ffn, float thr, uint64_t* masks, uint32_t* ctr, int32_t* idx, int32_t* count, hipStream_t s);
+struct FusedPredLayout {
+    size_t htag, mtag, total;   // offsets from the data area; the whole layout is tagged words
+    int NT;
+};
+inline FusedPredLayout fused_pred_layout(int r, int ffn) {
+    FusedPredLayout L;
+    L.NT = (ffn + 31) / 32;
+    L.htag = 0;
+    L.mtag = align256((size_t)r * 8);
+    L.total = L.mtag + align256((size_t)L.NT * 8);
+    return L;
+}
+
+struct FusedSparseLayout {
+    size_t atag, partial, total;   // offsets from the data area; [atag, partial) is tagged words
+    int NU, T, G;
+};
+inline FusedSparseLayout fused_sparse_layout(int d, int ffn) {
+    FusedSparseLayout L;
+    L.T = (d + kFusedCols - 1) / kFusedCols;
+    L.G = 672 / L.T;   // about 672 W_down workgroups: 2-3 per CU
+    if (L.G > kFusedMaxChunks) L.G = kFusedMaxChunks;
+    if (L.G > ffn) L.G = ffn;
+    if (L.G < 1) L.G = 1;
+    L.NU = (ffn + 7) / 8 < 384 ? (ffn + 7) / 8 : 384;   // up chunks (8 waves each)
+    L.atag = 0;
+    L.partial = align256((size_t)ffn * 8);
+    L.total = L.partial + align256((size_t)kFusedMaxChunks * d * 4);   // padded: the reduction reads every chunk slot
+    return L;
+}
+
+typedef _Float16 h16;
 
 // sparse.hip
 hipError_t launch_up_act(bool reglu, bool dense, const h16* x, int B, int d, int ffn,
@@ -156,6 +180,16 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
                           const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
                           int32_t* count, const BPredLayout& L, char* ws, hipStream_t s);
+
+// fused.hip
+hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
+                                const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
+                                char* ws, uint32_t epoch, int32_t* idx, int32_t* count, hipStream_t s);
+hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
+                               const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
+                               const int32_t* count, float* y, const FusedSparseLayout& L, char* ws,
+                               uint32_t epoch, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // profile.hip
 hipError_t launch_profile(const h16* X, int n, int d, int ffn, const h16* W, const float* b,

@@ -26,7 +26,8 @@ class Workspace:
         if nbytes == 0:
             return None, 0
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            # zero-filled once: the library keeps epoch-tagged sync words in its header
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
         return self.buf, self.buf.numel()
 
 

@@ -19,7 +19,14 @@
  *  - The caller owns every buffer.  The library allocates nothing; scratch
  *    memory is a caller-provided device workspace of at least
  *    pi_workspace_size() bytes, 256-byte aligned, that must not be used by
- *    another call running concurrently.  Its contents need no initialisation.
+ *    another call running concurrently.  Zero-fill a workspace once when it
+ *    is allocated; after that it belongs to the library: pass it to any
+ *    number of calls (of any operation and shape) and write nothing else into
+ *    it, unless you zero-fill it again.  The library keeps synchronisation
+ *    words in it between calls and remembers, by address, which layout each
+ *    workspace last held (a call that finds a different one clears what it
+ *    needs first, at the cost of one small extra kernel): a separate workspace
+ *    per operation avoids those clears.
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
  *    means the default stream).  Nothing is copied to the host: the active
  *    count stays in device memory and later kernels read it there.
@@ -68,7 +75,7 @@ typedef enum pi_op {
 
 /* pi_ffn_sparse flags */
 #define PI_DENSE 0x1u      /* ignore idx/count and compute every neuron (dense FFN baseline) */
-#define PI_PER_TOKEN 0x2u  /* B >= 2: run every token through the single-token kernels instead of
+#define PI_PER_TOKEN 0x2u  /* B >= 2: run every token through the single-token kernel instead of
                               the union path (same results up to fp32 rounding) */
 
 #define PI_MAX_BATCH 256
@@ -89,6 +96,9 @@ typedef enum pi_op {
  * Outputs (device): idx[t * ffn + j], j < count[t], the active neurons of
  * token t in strictly ascending order; count[t] in [0, ffn].  Entries of idx
  * at j >= count[t] are left unspecified.  idx holds B * ffn int32, count B.
+ * For B = 1 the call is one kernel (the hidden rows overlap the reads of
+ * P2); if one of its bounded internal waits ever ran out, count is set to -1
+ * (pi_ffn_sparse treats a negative count as 0).
  *
  * Errors: INVALID_ARG for NULL x/P1/P2/idx/count, B/d/r/ffn out of range,
  * act not a pi_pred_act, tau not in (0,1); UNSUPPORTED for d or r not a
@@ -116,6 +126,11 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d,
  * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0).
  * idx must hold valid, strictly ascending neuron ids (as written by
  * pi_ffn_predict); the call does not re-check them.
+ *
+ * For B = 1 (and for every token under PI_PER_TOKEN) the step is one kernel:
+ * the up/gate rows of the list are computed while the W_down rows are already
+ * being read, and each column block of y is summed over a fixed partition of
+ * the list in a fixed order.
  *
  * For B >= 2 (unless PI_DENSE or PI_PER_TOKEN) the tokens are taken in
  * groups of up to 128: the union U of the group's lists is formed on the
