@@ -3,11 +3,10 @@
 // pi_ffn_predict (B = 1):  k_predict_fused
 //   workgroups [0, NA)        hidden rows, one wave per row of P1:
 //                             h_k = act(P1[k].x + b1_k), published as a tagged word
-//   workgroups [NA, NA + NT)  logits tiles of 32 neurons: issue the tile's P2 rows,
-//                             collect h, z = P2 h + b2 > thr, publish the tile's
-//                             32-bit mask as a tagged word; the last workgroup
-//                             also gathers every mask and writes idx (ascending)
-//                             and count
+//   workgroups [NA, NA + NT)  logits tiles of 32 neurons: collect h, stream the
+//                             tile's P2 rows, z = P2 h + b2 > thr, publish the
+//                             tile's 32-bit mask as a tagged word
+//   workgroup NA + NT         gathers every mask and writes idx (ascending) and count
 //
 // pi_ffn_sparse (B = 1):   k_sparse_fused
 //   workgroups [0, NU)        up chunks, one wave per active row:
@@ -127,6 +126,54 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         return;
     }
 
+    if ((int)blockIdx.x == NA + NT) {
+        // ---------------- ordered compaction, 1024 tiles per round (4 per thread)
+        uint32_t base = 0;
+        bool good = true;
+        for (int t0 = 0; t0 < NT; t0 += 1024) {
+            uint64_t m4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + tid * 4 + q, NT - 1)]);
+            uint32_t bits[4];
+            uint32_t mine = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = t0 + tid * 4 + q;
+                bits[q] = 0u;
+                if (t < NT) {
+                    if (poll_tag(&mtag[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
+                    else good = false;
+                }
+                mine += (uint32_t)__popc(bits[q]);
+            }
+            uint32_t incl = mine;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t v = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += v;
+            }
+            if (lane == 63) s_part[wave] = incl;
+            __syncthreads();
+            uint32_t pos = base + incl - mine;
+            for (int w2 = 0; w2 < wave; ++w2) pos += s_part[w2];
+            const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t m = bits[q];
+                const int t = t0 + tid * 4 + q;
+                while (m) {
+                    idx[pos++] = t * kLTile + __builtin_ctz(m);
+                    m &= m - 1;
+                }
+            }
+            base += total;
+            __syncthreads();
+        }
+        good = __syncthreads_and(good);
+        if (tid == 0) count[0] = good ? (int32_t)base : -1;
+        return;
+    }
+
     // ---------------- logits tile: wave w owns neurons tile*32 + 8w + k (k < 8); lane l
     // takes chunks l + 64m of all eight rows, so an h chunk read from LDS serves
     // eight rows
@@ -141,12 +188,17 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     float acc[kLRows];
 #pragma unroll
     for (int k = 0; k < kLRows; ++k) acc[k] = 0.f;
-    bool have_h = false, ok = true;
-    // h (and b2) are collected once the first batch of P2 loads is in flight
+    bool ok = true;
+    // h (and b2) are read once the tile's first batch of P2 rows has arrived.
+    // Loads return in order, so a poll issued behind the batch would come back
+    // with it, holding what h was when the poll was served, long before; read
+    // after the batch it is fresh, and the hidden rows (which compete with P2
+    // for bandwidth from the start) are long done by then.
+    bool have_h = false;
     auto collect_round = [&](int i0) {
         uint64_t v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[min(i0 + q * 256, r - 1)]);
+        for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[i0 + q * 256]);   // padded to 1024 words
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i = i0 + q * 256;
@@ -183,7 +235,10 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         for (int k = 0; k < kLRows; ++k)
 #pragma unroll
             for (int m = 0; m < kLCols; ++m) w[k][m] = ld16_stream(prow[k] + (size_t)(lane + (m0 + m) * 64) * 8);
-        if (!have_h) collect_h();
+        if (!have_h) {
+            wait_own_memory();
+            collect_h();
+        }
         accumulate(w, m0);
     }
     if (m0 < M) {   // the last, partial batch: lanes past the row end are masked
@@ -195,10 +250,12 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                 const int c = lane + (m0 + m) * 64;
                 if (c < nch) w[k][m] = ld16_stream(prow[k] + (size_t)c * 8);
             }
-        if (!have_h) collect_h();
+        if (!have_h) {
+            wait_own_memory();
+            collect_h();
+        }
         accumulate(w, m0);
     }
-    if (!have_h) collect_h();
     float zk = 0.f;   // lane k < 8: z of row row0 + k
 #pragma unroll
     for (int k = 0; k < kLRows; ++k) {
@@ -211,52 +268,6 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         const uint64_t m = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
         if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)m);
     }
-    if ((int)blockIdx.x != NA + NT - 1) return;
-
-    // ---------------- the last workgroup: ordered compaction, 1024 tiles per round (4 per thread)
-    uint32_t base = 0;
-    bool good = ok;
-    for (int t0 = 0; t0 < NT; t0 += 1024) {
-        uint64_t m4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + tid * 4 + q, NT - 1)]);
-        uint32_t bits[4];
-        uint32_t mine = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = t0 + tid * 4 + q;
-            bits[q] = 0u;
-            if (t < NT) {
-                if (poll_tag(&mtag[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
-                else good = false;
-            }
-            mine += (uint32_t)__popc(bits[q]);
-        }
-        uint32_t incl = mine;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        if (lane == 63) s_part[wave] = incl;
-        __syncthreads();
-        uint32_t pos = base + incl - mine;
-        for (int w2 = 0; w2 < wave; ++w2) pos += s_part[w2];
-        const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint32_t m = bits[q];
-            const int t = t0 + tid * 4 + q;
-            while (m) {
-                idx[pos++] = t * kLTile + __builtin_ctz(m);
-                m &= m - 1;
-            }
-        }
-        base += total;
-        __syncthreads();
-    }
-    good = __syncthreads_and(good);
-    if (tid == 0) count[0] = good ? (int32_t)base : -1;
 }
 
 // ===========================================================================
@@ -468,7 +479,7 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
     const int NA = (r + 3) / 4;
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
-    hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
+    hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
                        thr, htag, mtag, epoch, idx, count, zero);
     return hipGetLastError();
 }

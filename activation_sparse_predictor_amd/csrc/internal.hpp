@@ -136,8 +136,8 @@ struct FusedPredLayout {
 inline FusedPredLayout fused_pred_layout(int r, int ffn) {
     FusedPredLayout L;
     L.NT = (ffn + 31) / 32;
-    L.htag = 0;
-    L.mtag = align256((size_t)r * 8);
+    L.htag = 0;   // padded to a multiple of 1024 words: the collection reads whole rounds
+    L.mtag = align256((size_t)((r + 1023) / 1024) * 1024 * 8);
     L.total = L.mtag + align256((size_t)L.NT * 8);
     return L;
 }
