@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -90,17 +89,6 @@ size_t sparse_ws_bytes(int B, int d, int ffn) {
         if (u > n) n = u;
     }
     return pi::kSyncBytes + n;
-}
-
-// Launch epochs of the fused kernels: process-wide, strictly increasing,
-// never 0 (the value of a freshly zeroed word).
-uint32_t next_epoch() {
-    static std::atomic<uint32_t> counter{0};
-    uint32_t e;
-    do {
-        e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-    } while (e == 0u);
-    return e;
 }
 
 // Which tagged layout each workspace last held.  Tags of earlier fused calls
@@ -216,8 +204,7 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, cons
     hipError_t e = hipSuccess;
     if (ws_needs_clear(ws, key)) e = pi::launch_zero(w + pi::kSyncBytes, L.total, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict clearing the workspace");
-    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, thr, L, w, next_epoch(), idx,
-                                 count, s);
+    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, thr, L, w, idx, count, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict");
     ws_record(ws, key);
     return ok();
@@ -273,7 +260,7 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
         if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse clearing the workspace");
         for (int t = 0; t < B && e == hipSuccess; ++t)
             e = pi::launch_sparse_fused(reglu, hx + (size_t)t * d, d, ffn, hu, b_up, hg, b_gate, hd,
-                                        idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, w, next_epoch(), s);
+                                        idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, w, s);
         if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse");
         ws_record(ws, key);
         return ok();

@@ -22,9 +22,15 @@
 // A tagged word is 64 bits, {epoch, 32-bit payload}, written and read with
 // single-copy-atomic device-coherent accesses: a consumer polls the data
 // itself, so publishing costs one store and consuming one load, with no flag
-// or counter in between.  The epoch is a host counter that never repeats
-// within the process (and is never 0), so a word left over from an earlier
-// call can never pass for a current one.  A workgroup only waits for
+// or counter in between.  The epoch is one more than the previous launch's
+// (never 0), kept in the workspace header, so a word left over from an
+// earlier call never passes for a current one, also when the launches are
+// replayed from a captured graph.  In predict the compaction workgroup, which
+// provably runs after every other workgroup has read the epoch, stores it
+// back.  In the FFN the last chunk of each column tile stores it into that
+// tile's slot, and a launch takes the oldest slot plus one: while any W_down
+// workgroup of a launch is still running, its tile's slot holds the previous
+// epoch.  A workgroup only waits for
 // workgroups with a smaller index, which are dispatched before it, so the
 // roles overlap (P1 with P2, W_up with W_down) without any risk of circular
 // waiting.  Every wait is bounded: on overrun the kernel reports an error
@@ -53,6 +59,28 @@ __device__ __forceinline__ void st_tag(uint64_t* p, uint32_t epoch, uint32_t pay
 }
 __device__ __forceinline__ bool is_current(uint64_t v, uint32_t epoch) { return (uint32_t)(v >> 32) == epoch; }
 
+// This launch's epoch from the stored one: plus one, skipping 0 (a zeroed
+// word).  Each role requests the stored word right after the loads that gate
+// its next step (never ahead of them: loads complete in order), so it adds no
+// wait of its own.  It is an ordinary (cached) load: the word was last
+// written by an earlier kernel, and this launch writes it only after every
+// workgroup has read it.
+__device__ __forceinline__ uint32_t next_epoch(uint32_t stored) {
+    const uint32_t e = stored + 1u;
+    return e == 0u ? 1u : e;
+}
+
+// The FFN's stored epoch: the oldest of the T per-tile slots (which differ by
+// at most one launch), found across the wave with a wrap-safe minimum.  v is
+// this lane's slot, slots[min(lane, T - 1)].
+__device__ __forceinline__ uint32_t oldest_slot(uint32_t v) {
+    const uint32_t ref = __builtin_amdgcn_readfirstlane(v);
+    int dv = (int)(v - ref);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dv = min(dv, __shfl_xor(dv, off, 64));
+    return ref + (uint32_t)dv;
+}
+
 // Re-read *p until it carries the epoch; false on overrun.
 __device__ __forceinline__ bool poll_tag(const uint64_t* p, uint64_t& v, uint32_t epoch) {
     for (int n = 0; !is_current(v, epoch); ++n) {
@@ -78,7 +106,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        const h16* __restrict__ P2,
                                                        const float* __restrict__ b2, int ffn, float thr,
                                                        uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
-                                                       uint32_t epoch, int32_t* __restrict__ idx,
+                                                       uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ count, const float* __restrict__ zero) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
@@ -101,6 +129,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
 #pragma unroll
         for (int u = 0; u < 16; ++u)
             if (lane + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(lane + u * 64) * 8);
+        const uint32_t stored = *epoch_word;
         const float bias = *(b1 ? b1 + min(row, r - 1) : zero);
         u32x4* sx = reinterpret_cast<u32x4*>(sh);
 #pragma unroll
@@ -122,12 +151,14 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             }
         }
         const float s = group_sum<64>(acc) + bias;
+        const uint32_t epoch = next_epoch(stored);
         if (valid && lane == 0) st_tag(&htag[row], epoch, __float_as_uint(relu ? fmaxf(s, 0.f) : s));
         return;
     }
 
     if ((int)blockIdx.x == NA + NT) {
         // ---------------- ordered compaction, 1024 tiles per round (4 per thread)
+        const uint32_t epoch = next_epoch(*epoch_word);
         uint32_t base = 0;
         bool good = true;
         for (int t0 = 0; t0 < NT; t0 += 1024) {
@@ -170,7 +201,12 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             __syncthreads();
         }
         good = __syncthreads_and(good);
-        if (tid == 0) count[0] = good ? (int32_t)base : -1;
+        if (tid == 0) {
+            count[0] = good ? (int32_t)base : -1;
+            // every other workgroup has read the epoch: each logits tile has
+            // published its mask, after every hidden row its h
+            st_flag(epoch_word, epoch);
+        }
         return;
     }
 
@@ -185,6 +221,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
 #pragma unroll
     for (int k = 0; k < kLRows; ++k) prow[k] = P2 + (size_t)min(row0 + k, ffn - 1) * r;
     float bias = 0.f;   // lane k < 8: b2 of row row0 + k
+    uint32_t epoch = 0;
     float acc[kLRows];
 #pragma unroll
     for (int k = 0; k < kLRows; ++k) acc[k] = 0.f;
@@ -195,10 +232,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     // after the batch it is fresh, and the hidden rows (which compete with P2
     // for bandwidth from the start) are long done by then.
     bool have_h = false;
-    auto collect_round = [&](int i0) {
-        uint64_t v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[i0 + q * 256]);   // padded to 1024 words
+    auto check_round = [&](int i0, uint64_t (&v)[4]) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int i = i0 + q * 256;
@@ -209,9 +243,17 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         }
     };
     auto collect_h = [&]() {
+        uint64_t v[4];
+        epoch = next_epoch(*epoch_word);
         bias = *(b2 ? b2 + min(row0 + (lane & (kLRows - 1)), ffn - 1) : zero);
-        collect_round(tid);   // outside any loop: a loop header would wait for the P2 batch first
-        for (int i0 = tid + 1024; i0 < r; i0 += 1024) collect_round(i0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[tid + q * 256]);   // padded to 1024 words
+        check_round(tid, v);   // outside any loop: a loop header would wait for the P2 batch first
+        for (int i0 = tid + 1024; i0 < r; i0 += 1024) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[i0 + q * 256]);
+            check_round(i0, v);
+        }
         ok = __syncthreads_and(ok);
         have_h = true;
     };
@@ -291,8 +333,9 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
                                                             const int32_t* __restrict__ count, int NU,
                                                             int T, int G, uint64_t* __restrict__ atag,
                                                             float* __restrict__ partial,
-                                                            uint32_t* __restrict__ ctr, uint32_t epoch,
-                                                            float* __restrict__ y, const float* __restrict__ zero) {
+                                                            uint32_t* __restrict__ ctr, uint32_t* __restrict__ slots,
+                                                            float* __restrict__ y,
+                                                            const float* __restrict__ zero) {
     // up role: x (d fp16); W_down role: row-group partials, window ids and activations
     __shared__ __align__(16) char s_mem[kSGroups * kFusedCols * 4 + kSWindow * 8];
     static_assert(sizeof(s_mem) >= PI_MAX_D * 2, "x does not fit the up role's LDS");
@@ -340,6 +383,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         i = min(max(idx[min(j, j1 - 1)], 0), ffn - 1);
         issue(lane);
         issue_bias();
+        const uint32_t slot = slots[min(lane, T - 1)];
 #pragma unroll
         for (int q = 0; q < 2; ++q)
             if (tid + q * kSThreads < nch) s_x[tid + q * kSThreads] = xs[q];
@@ -369,6 +413,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
             }
             au = group_sum<64>(au);
             if (REGLU) ag = group_sum<64>(ag);
+            const uint32_t epoch = next_epoch(oldest_slot(slot));
             if (lane == 0) {
                 const float uval = au + bu;
                 const float act = REGLU ? fmaxf(ag + bgv, 0.f) * uval : fmaxf(uval, 0.f);
@@ -392,30 +437,37 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
     bool ok = true;
+    uint32_t slot = 0;
+    uint32_t epoch = 0;   // set with the first window (an empty chunk sets it after the loop)
     for (int w0 = j0; w0 < j1; w0 += kSWindow) {
         const int wn = min(kSWindow, j1 - w0);
-        for (int q0 = tid; q0 < wn; q0 += kSThreads * 4) {
-            int32_t v[4];
+        {
+            int32_t v[kSWindow / kSThreads];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = idx[w0 + min(q0 + e * kSThreads, wn - 1)];
+            for (int e = 0; e < kSWindow / kSThreads; ++e) v[e] = idx[w0 + min(tid + e * kSThreads, wn - 1)];
+            slot = slots[min(lane, T - 1)];   // with the ids, after them
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (q0 + e * kSThreads < wn) s_row[q0 + e * kSThreads] = min(max(v[e], 0), ffn - 1);
+            for (int e = 0; e < kSWindow / kSThreads; ++e)
+                if (tid + e * kSThreads < wn) s_row[tid + e * kSThreads] = min(max(v[e], 0), ffn - 1);
         }
         __syncthreads();
         const int nk = (wn - rg + kSGroups - 1) / kSGroups;   // this group's rows: rg + kSGroups * n
-        // the first batch of rows goes out before the activations are collected
+        // The first batch of rows goes out before the activations are collected
+        // (overlapping the up rows they depend on).  A row whose activation
+        // turns out to be 0 is still read: skipping it would have to wait for
+        // the activation first, which costs more than the bytes it saves.
         u32x4 w[kSBatch];
 #pragma unroll
         for (int q = 0; q < kSBatch; ++q)
             w[q] = ld16_stream(Wd + (size_t)s_row[min(rg + kSGroups * q, wn - 1)] * d + colc);
-        for (int q0 = tid; q0 < wn; q0 += kSThreads * 4) {
-            uint64_t v[4];
+        {
+            uint64_t v[kSWindow / kSThreads];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = ld_tag(&atag[w0 + min(q0 + e * kSThreads, wn - 1)]);
+            for (int e = 0; e < kSWindow / kSThreads; ++e) v[e] = ld_tag(&atag[w0 + min(tid + e * kSThreads, wn - 1)]);
+            epoch = next_epoch(oldest_slot(slot));   // the slot load is long done by now
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int q = q0 + e * kSThreads;
+            for (int e = 0; e < kSWindow / kSThreads; ++e) {
+                const int q = tid + e * kSThreads;
                 if (q < wn) {
                     ok = poll_tag(&atag[w0 + q], v[e], epoch) && ok;
                     s_a[q] = __uint_as_float((uint32_t)v[e]);
@@ -437,6 +489,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         }
         __syncthreads();
     }
+    if (epoch == 0u) epoch = next_epoch(oldest_slot(slots[min(lane, T - 1)]));   // empty chunk (uniform)
     ok = __syncthreads_and(ok);
     *reinterpret_cast<f32x4*>(&s_red[rg][ct * 8]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4*>(&s_red[rg][ct * 8 + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
@@ -453,11 +506,13 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     __syncthreads();
     if (tid == 0) {
         uint32_t* c = &ctr[(size_t)tile * kCtrStride];
-        s_flag = fetch_add(c, 1u) == (uint32_t)(G - 1);
-        if (s_flag) st_flag(c, 0u);   // the last arrival puts the counter back for the next call
+        const int flag = fetch_add(c, 1u) == (uint32_t)(G - 1);
+        if (flag) st_flag(c, 0u);   // the last arrival puts the counter back for the next call
+        s_flag = flag;
     }
     __syncthreads();
     if (!s_flag || tid >= kFusedCols || gc >= d) return;
+
     // the tile's last chunk: add the G partials in chunk order, all loads in one round
     // the partial buffer holds kFusedMaxChunks chunks, so every load is in bounds
     float v[kFusedMaxChunks];
@@ -468,11 +523,13 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     for (int g = 0; g < kFusedMaxChunks; ++g)
         if (g < G) sum += v[g];
     y[gc] = sum;
+    // every chunk of this tile has read the epoch: the tile's slot advances
+    if (tid == 0) st_flag(&slots[tile], epoch);
 }
 
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
                                 const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
-                                char* ws, uint32_t epoch, int32_t* idx, int32_t* count, hipStream_t s) {
+                                char* ws, int32_t* idx, int32_t* count, hipStream_t s) {
     char* data = ws + kSyncBytes;
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
@@ -480,26 +537,27 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
     hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
-                       thr, htag, mtag, epoch, idx, count, zero);
+                       thr, htag, mtag, reinterpret_cast<uint32_t*>(ws + Sync::pred_epoch), idx, count, zero);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* ws,
-                               uint32_t epoch, hipStream_t s) {
+                               hipStream_t s) {
     char* data = ws + kSyncBytes;
     uint64_t* atag = reinterpret_cast<uint64_t*>(data + L.atag);
     float* partial = reinterpret_cast<float*>(data + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + Sync::ffn_ctr);
+    uint32_t* slots = reinterpret_cast<uint32_t*>(ws + Sync::ffn_epoch);
     const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
     dim3 grid(L.NU + L.T * L.G);
     if (reglu)
         hipLaunchKernelGGL(k_sparse_fused<true>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,
-                           count, L.NU, L.T, L.G, atag, partial, ctr, epoch, y, zero);
+                           count, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero);
     else
         hipLaunchKernelGGL(k_sparse_fused<false>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,
-                           count, L.NU, L.T, L.G, atag, partial, ctr, epoch, y, zero);
+                           count, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero);
     return hipGetLastError();
 }
 

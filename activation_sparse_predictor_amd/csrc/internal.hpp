@@ -113,17 +113,21 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
 }
 
 // ---- fused single-token kernels.  They publish intermediate values as
-// tagged 64-bit words {launch epoch, payload} in the data area, and keep the
-// W_down arrival counters in a fixed header at the start of every workspace,
-// which no other layout touches: the header is zero-filled once when the
-// workspace is allocated and each counter is put back to 0 by the last
-// arrival of every call.  All other layouts start kSyncBytes in.
+// tagged 64-bit words {launch epoch, payload} in the data area, and keep
+// their epochs and the W_down arrival counters in a fixed header at the start
+// of every workspace, which no other layout touches: the header is zero-filled
+// once when the workspace is allocated; each counter is put back to 0 by the
+// last arrival of every call, and each epoch advances by one per launch on
+// the device (so a captured graph replays with a new epoch each time).  All
+// other layouts start kSyncBytes in.
 constexpr int kFusedCols = 512;                     // W_down columns per tile
 constexpr int kFusedMaxTiles = 16384 / kFusedCols;  // PI_MAX_D / kFusedCols
 constexpr int kFusedMaxChunks = 48;                 // list chunks per W_down tile
-struct Sync {   // byte offsets inside the header
-    static constexpr size_t ffn_ctr = 0;                                    // one 128-byte line per tile
-    static constexpr size_t zero = ffn_ctr + (size_t)kFusedMaxTiles * kCtrStride * 4;   // never written
+struct Sync {   // byte offsets inside the header, each on its own 128-byte line
+    static constexpr size_t ffn_ctr = 0;                                    // one line per W_down tile
+    static constexpr size_t ffn_epoch = ffn_ctr + (size_t)kFusedMaxTiles * kCtrStride * 4;  // per tile
+    static constexpr size_t pred_epoch = ffn_epoch + kFusedMaxTiles * 4;    // last predict launch's epoch
+    static constexpr size_t zero = pred_epoch + 128;                        // never written
     static constexpr size_t end = zero + 256;
 };
 constexpr size_t kSyncBytes = 8192;
@@ -184,11 +188,11 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
 // fused.hip
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
                                 const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
-                                char* ws, uint32_t epoch, int32_t* idx, int32_t* count, hipStream_t s);
+                                char* ws, int32_t* idx, int32_t* count, hipStream_t s);
 hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* ws,
-                               uint32_t epoch, hipStream_t s);
+                               hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // profile.hip

@@ -222,17 +222,47 @@ def main():
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s0 = args.warmup
+
+    # Eager: one host call per entry point per step.
     e0.record(stream)
     for s in range(s0, s0 + args.steps):
         step(s)
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_total = e0.elapsed_time(e1)
-    ms_step = ms_total / args.steps
-    T_avg = steps_bytes(s0, args.steps) / args.steps
+    ms_eager = e0.elapsed_time(e1) / args.steps
+
+    # Graph: one rotation of steps (every layer, several tokens each) captured
+    # once and replayed, so the timed region holds only the GPU work of the
+    # steps (the library's kernels take their launch epoch from the workspace,
+    # so replays are valid).  This is the headline number.
+    Kg = NL * max(1, min(NT, 8))
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        for s in range(Kg):
+            step(s)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for s in range(Kg):
+                step(s)
+    torch.cuda.synchronize()
+    reps = max(1, (args.steps + Kg - 1) // Kg)
+    for _ in range(max(1, args.warmup // Kg)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n_graph = reps * Kg
+    ms_step = e0.elapsed_time(e1) / n_graph
+    T_avg = steps_bytes(0, Kg) / Kg
     value = 1000.0 / ms_step
-    log(f"step {ms_step * 1000:.2f} us, {value:.0f} tok/s/layer, T {T_avg / 1e6:.1f} MB -> "
-        f"{T_avg / ms_step / 1e6:.0f} GB/s")
+    log(f"step {ms_step * 1000:.2f} us (graph; eager {ms_eager * 1000:.2f} us), {value:.0f} tok/s/layer, "
+        f"T {T_avg / 1e6:.1f} MB -> {T_avg / ms_step / 1e6:.0f} GB/s")
+    del graph
 
     # per entry point: events between the two calls of each step
     K2 = min(args.steps, 400)
@@ -321,7 +351,7 @@ def main():
         "value": value,
         "unit": "tokens/s per layer",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": n_graph,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
@@ -334,6 +364,8 @@ def main():
                    "mean_active": float(counts_h.float().mean()),
                    "touched_MB_per_step": T_avg / 1e6},
         "achieved_GBs_step": T_avg / ms_step / 1e6,
+        "timing": {"method": f"hipGraph of {Kg} steps replayed {reps} times, HIP events around the replays",
+                   "ms_per_step_eager": ms_eager},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": stages[dom][1],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": stages[dom][1] / HBM_PEAK_GBS, "traffic": None,

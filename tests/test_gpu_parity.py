@@ -1,8 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
 Small ragged shapes span several tiles plus a tail on every axis (d vs the
-512-wide row steps and 1024-wide column tiles, ffn vs the 64-neuron
-compaction tiles, r vs the per-row lane groups).  Full-size layers are
+512-column W_down tiles and 1024-element row steps, ffn vs the 32-neuron
+logits tiles, r vs the 64-lane chunk columns).  Full-size layers are
 checked on sampled tokens.  Rules (tests/parity.py): index lists bit-exact
 outside a 1e-3 band around the logit threshold; y within rel-L2 1e-3 and
 max-abs 2e-3 * ||y||_inf of the oracle evaluated on the GPU's own list.
@@ -216,6 +216,108 @@ def test_deterministic_repeats():
         outs.append((c, idx[0, :c].cpu().numpy().copy(), y.cpu().numpy().copy()))
     for c, i, y in outs[1:]:
         assert c == outs[0][0] and np.array_equal(i, outs[0][1]) and np.array_equal(y, outs[0][2])
+
+
+def _decode_args(L, x, idx, cnt, y, ws, ws_bytes):
+    kind = B.PI_FFN_REGLU if L["kind"] == "reglu" else B.PI_FFN_RELU
+    p = (x, x.shape[0], L["d"], L["P1"], L.get("b1"), B.PI_ACT_RELU, L["P2"], L.get("b2"), L["r"], L["ffn"],
+         float(L["tau"]), idx, cnt, ws, ws_bytes)
+    q = (kind, x, x.shape[0], L["d"], L["ffn"], L["W_up"], L.get("b_up"), L.get("W_gate"), L.get("b_gate"),
+         L["W_down"], idx, cnt, y, 0, ws, ws_bytes)
+    return p, q
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_graph_replay(kind):
+    """Single-token predict + sparse captured in a HIP graph and replayed several
+    times, with eager calls on the same workspaces (other tokens) between the
+    replays: every replay must equal the eager result bitwise (the kernels take
+    their launch epoch from the workspace, not from the captured arguments)."""
+    cfg = custom_config(kind, 520, 1000, 72, mean=0.2, number=60)
+    L = R.to_device(make_layer(cfg), DEV)
+    X = make_tokens(cfg, 6).to(DEV)
+    ffn, d = L["ffn"], L["d"]
+    wsb = max(B.pi_workspace_size(B.PI_OP_PREDICT, 1, d, L["r"], ffn),
+              B.pi_workspace_size(B.PI_OP_SPARSE, 1, d, L["r"], ffn))
+    ws_p = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    ws_s = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    bufs = [(torch.empty(1, ffn, dtype=torch.int32, device=DEV), torch.empty(1, dtype=torch.int32, device=DEV),
+             torch.empty(1, d, dtype=torch.float32, device=DEV)) for _ in range(3)]
+
+    def run(t, b):
+        p, _ = _decode_args(L, X[t:t + 1], b[0], b[1], b[2], ws_p, wsb)
+        _, q = _decode_args(L, X[t:t + 1], b[0], b[1], b[2], ws_s, wsb)
+        B.check(B.pi_ffn_predict(*p), "predict")
+        B.check(B.pi_ffn_sparse(*q), "sparse")
+
+    for t in range(3):   # eager reference (also settles the workspaces' layouts)
+        run(t, bufs[t])
+    torch.cuda.synchronize()
+    ref = [(int(b[1].item()), b[0][0, :int(b[1].item())].cpu().clone(), b[2].cpu().clone()) for b in bufs]
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for t in range(3):
+                run(t, bufs[t])
+    torch.cuda.synchronize()
+    scratch = (torch.empty(1, ffn, dtype=torch.int32, device=DEV), torch.empty(1, dtype=torch.int32, device=DEV),
+               torch.empty(1, d, dtype=torch.float32, device=DEV))
+    for rep in range(4):
+        for b in bufs:
+            b[1].fill_(-7)
+            b[2].fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for t, b in enumerate(bufs):
+            c = int(b[1].item())
+            assert c == ref[t][0], f"replay {rep} token {t}: count {c} vs {ref[t][0]}"
+            assert torch.equal(b[0][0, :c].cpu(), ref[t][1]), f"replay {rep} token {t}: idx differs"
+            assert torch.equal(b[2].cpu(), ref[t][2]), f"replay {rep} token {t}: y differs"
+        run(3 + rep % 3, scratch)   # eager work on the same workspaces between replays
+        torch.cuda.synchronize()
+    H = _host(L)
+    for t in range(3):
+        check_y(ref[t][2][0].numpy(), _oracle_y(H, X[t].cpu(), ref[t][1].numpy()), where=f"graph t={t}")
+
+
+def test_one_workspace_for_everything():
+    """One zero-filled workspace shared by every operation and two shapes, in
+    an order that makes each single-token call find a different layout than it
+    left: results must match the oracle throughout."""
+    cfgs = [custom_config("relu", 520, 1000, 72, mean=0.2, number=61),
+            custom_config("reglu", 264, 2080, 136, mean=0.3, number=62)]
+    Ls = [R.to_device(make_layer(c), DEV) for c in cfgs]
+    Xs = [make_tokens(c, 5).to(DEV) for c in cfgs]
+    wsb = 0
+    for L in Ls:
+        for op in (B.PI_OP_PREDICT, B.PI_OP_SPARSE):
+            for Bt in (1, 5):
+                wsb = max(wsb, B.pi_workspace_size(op, Bt, L["d"], L["r"], L["ffn"]))
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    thr = O.logit_threshold(0.5)
+    for rnd in range(3):
+        for li, (L, X) in enumerate(zip(Ls, Xs)):
+            H = _host(L)
+            ffn, d = L["ffn"], L["d"]
+            for Bt in ((1, 5) if rnd % 2 == 0 else (5, 1)):
+                x = X[:Bt].contiguous()
+                idx = torch.empty(Bt, ffn, dtype=torch.int32, device=DEV)
+                cnt = torch.empty(Bt, dtype=torch.int32, device=DEV)
+                y = torch.empty(Bt, d, dtype=torch.float32, device=DEV)
+                p, q = _decode_args(L, x, idx, cnt, y, ws, wsb)
+                B.check(B.pi_ffn_predict(*p), "predict")
+                B.check(B.pi_ffn_sparse(*q), "sparse")
+                torch.cuda.synchronize()
+                for t in range(Bt):
+                    c = int(cnt[t].item())
+                    gi = idx[t, :c].cpu().numpy()
+                    xh = X[t].cpu()
+                    z = O.predictor_logits(xh, H["P1"], None, "relu", H["P2"], H["b2"])
+                    where = f"round {rnd} layer {li} B={Bt} t={t}"
+                    check_idx(gi, z, thr, where=where)
+                    check_y(y[t].cpu().numpy(), _oracle_y(H, xh, gi), where=where)
 
 
 @pytest.mark.parametrize("kind,d,ffn,n", [("relu", 64, 96, 40), ("relu", 520, 1000, 300),
