@@ -193,7 +193,7 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, cons
             const pi::BPredLayout L = pi::bpred_layout(Bg, r, ffn);
             hipError_t e = pi::launch_bpredict(hx + (size_t)g0 * d, Bg, d, h1, b1, act == PI_ACT_RELU, h2, b2,
                                                r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L,
-                                               w + pi::kSyncBytes, s);
+                                               w + pi::kSyncBytes, w, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict batched");
         }
         return ok();

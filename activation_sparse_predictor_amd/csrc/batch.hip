@@ -275,42 +275,63 @@ __global__ __launch_bounds__(256) void k_union_up(const h16* __restrict__ x, int
 
 // ---------------------------------------------------------------------------
 // Batched predictor.  Hidden layer: H = act(P1 X^T + b1), rows of P1 against
-// the tokens; h is written token-major as an fp16 hi/lo pair (h itself is
-// never rounded to fp16: hi + lo carries about 22 significant bits).
+// the tokens.  Grid = (32-row blocks, KS splits of K): each workgroup writes
+// the fp32 partial of its K range with device-coherent stores and arrives on
+// its row block's counter; the last of the KS to arrive adds the partials in
+// split order, applies b1 and the activation, writes h token-major as an fp16
+// hi/lo pair (h itself is never rounded to fp16: hi + lo carries about 22
+// significant bits) and puts the counter back to 0.
 template <int NB>
 __global__ __launch_bounds__(256) void k_bpred_hidden(const h16* __restrict__ x, int B, int d,
                                                       const h16* __restrict__ P1,
                                                       const float* __restrict__ b1, int relu, int r,
                                                       int ldh, h16* __restrict__ h_hi,
-                                                      h16* __restrict__ h_lo) {
+                                                      h16* __restrict__ h_lo, float* __restrict__ part,
+                                                      uint32_t* __restrict__ ctr, int KS) {
     __shared__ float s_red[4][16][64];
     __shared__ float s_sum[32][33];
+    __shared__ int s_last;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int li = lane & 31, half = lane >> 5;
-    const int nrb = (r + 31) / 32;
-    for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-        const h16* wrow[1] = {P1 + (size_t)min(rb * 32 + li, r - 1) * d};
-        const h16* xs[1] = {x};
-        f32x16 acc[1][NB];
+    const int rb = blockIdx.x, ks = blockIdx.y;
+    const int nch = d >> 3;
+    const int c0 = (int)(((long long)nch * ks) / KS), c1 = (int)(((long long)nch * (ks + 1)) / KS);
+    const int Bp = NB * 32;
+    const h16* wrow[1] = {P1 + (size_t)min(rb * 32 + li, r - 1) * d + (size_t)c0 * 8};
+    const h16* xs[1] = {x + (size_t)c0 * 8};
+    f32x16 acc[1][NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[0][nb] = f32x16{};
-        gemm_quarters<1, 1, NB>(acc, wrow, xs, d, d >> 3, B, wave, li, half);
+    for (int nb = 0; nb < NB; ++nb) acc[0][nb] = f32x16{};
+    gemm_quarters<1, 1, NB>(acc, wrow, xs, d, c1 - c0, B, wave, li, half);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            sum_quarters(acc[0][nb], s_red, s_sum, wave, lane);
-            for (int o = threadIdx.x; o < 1024; o += 256) {
-                const int rr = o >> 5, n = o & 31;
-                const int j = rb * 32 + rr, t = nb * 32 + n;
-                if (j < r && t < B) {
-                    const float sv = s_sum[rr][n] + (b1 ? b1[j] : 0.f);
-                    const float hv = relu ? fmaxf(sv, 0.f) : sv;
-                    const h16 hi = (h16)hv;
-                    h_hi[(size_t)t * ldh + j] = hi;
-                    h_lo[(size_t)t * ldh + j] = (h16)(hv - (float)hi);
-                }
-            }
-            __syncthreads();
+    for (int nb = 0; nb < NB; ++nb) {
+        sum_quarters(acc[0][nb], s_red, s_sum, wave, lane);
+        for (int o = threadIdx.x; o < 1024; o += 256) {
+            const int rr = o >> 5, n = o & 31;
+            const int j = rb * 32 + rr, t = nb * 32 + n;
+            if (j < r && t < B) st_coherent(&part[((size_t)ks * Bp + t) * r + j], s_sum[rr][n]);
         }
+        __syncthreads();
+    }
+    wait_own_memory();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int last = fetch_add(&ctr[rb], 1u) == (uint32_t)(KS - 1);
+        if (last) st_flag(&ctr[rb], 0u);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    for (int o = threadIdx.x; o < 32 * B; o += 256) {
+        const int rr = o / B, t = o % B;
+        const int j = rb * 32 + rr;
+        if (j >= r) continue;
+        float sv = b1 ? b1[j] : 0.f;
+        for (int k = 0; k < KS; ++k) sv += ld_coherent(&part[((size_t)k * Bp + t) * r + j]);
+        const float hv = relu ? fmaxf(sv, 0.f) : sv;
+        const h16 hi = (h16)hv;
+        h_hi[(size_t)t * ldh + j] = hi;
+        h_lo[(size_t)t * ldh + j] = (h16)(hv - (float)hi);
     }
 }
 
@@ -573,16 +594,17 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
 
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
                           const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
-                          int32_t* count, const BPredLayout& L, char* ws, hipStream_t s) {
+                          int32_t* count, const BPredLayout& L, char* ws, char* hdr, hipStream_t s) {
     h16* h_hi = reinterpret_cast<h16*>(ws + L.h_hi);
     h16* h_lo = reinterpret_cast<h16*>(ws + L.h_lo);
     uint32_t* masks32 = reinterpret_cast<uint32_t*>(ws + L.masks32);
+    float* hpart = reinterpret_cast<float*>(ws + L.hpart);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(hdr + Sync::bpred_ctr);
     const int NB = L.Bp / 32;
-    int gh = (r + 31) / 32;
-    if (gh > 1024) gh = 1024;
+    const dim3 gh((r + 31) / 32, L.KS);
     int gl = (ffn + 31) / 32;
     if (gl > 2048) gl = 2048;
-#define PI_BH(N) hipLaunchKernelGGL((k_bpred_hidden<N>), dim3(gh), dim3(256), 0, s, x, B, d, P1, b1, (int)relu, r, L.ldh, h_hi, h_lo)
+#define PI_BH(N) hipLaunchKernelGGL((k_bpred_hidden<N>), gh, dim3(256), 0, s, x, B, d, P1, b1, (int)relu, r, L.ldh, h_hi, h_lo, hpart, ctr, L.KS)
 #define PI_BL(N) hipLaunchKernelGGL((k_bpred_logits<N>), dim3(gl), dim3(256), 0, s, P2, b2, B, r, ffn, thr, L.ldh, h_hi, h_lo, masks32)
     if (NB == 1) { PI_BH(1); PI_BL(1); }
     else if (NB == 2) { PI_BH(2); PI_BL(2); }

@@ -97,8 +97,9 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
 struct BPredLayout {
     size_t h_hi, h_lo;   // Bp x ldh fp16 hidden activations (hi + lo)
     size_t masks32;      // B x ceil(ffn/32) uint32 per-token tile masks
+    size_t hpart;        // KS x Bp x r fp32 split-K partials of the hidden layer
     size_t total;
-    int Bp, ldh;
+    int Bp, ldh, KS;
 };
 
 inline BPredLayout bpred_layout(int B, int r, int ffn) {
@@ -108,7 +109,9 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
     L.h_hi = 0;
     L.h_lo = align256((size_t)L.Bp * L.ldh * 2);
     L.masks32 = L.h_lo + align256((size_t)L.Bp * L.ldh * 2);
-    L.total = L.masks32 + align256((size_t)B * ((ffn + 31) / 32) * 4);
+    L.KS = 8;   // K splits of the hidden layer: r/32 x 8 workgroups
+    L.hpart = L.masks32 + align256((size_t)B * ((ffn + 31) / 32) * 4);
+    L.total = L.hpart + align256((size_t)L.KS * L.Bp * r * 4);
     return L;
 }
 
@@ -123,12 +126,13 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
 constexpr int kFusedCols = 512;                     // W_down columns per tile
 constexpr int kFusedMaxTiles = 16384 / kFusedCols;  // PI_MAX_D / kFusedCols
 constexpr int kFusedMaxChunks = 48;                 // list chunks per W_down tile
-struct Sync {   // byte offsets inside the header, each on its own 128-byte line
+struct Sync {   // byte offsets inside the header
     static constexpr size_t ffn_ctr = 0;                                    // one line per W_down tile
     static constexpr size_t ffn_epoch = ffn_ctr + (size_t)kFusedMaxTiles * kCtrStride * 4;  // per tile
     static constexpr size_t pred_epoch = ffn_epoch + kFusedMaxTiles * 4;    // last predict launch's epoch
     static constexpr size_t zero = pred_epoch + 128;                        // never written
-    static constexpr size_t end = zero + 256;
+    static constexpr size_t bpred_ctr = zero + 256;                         // batched predictor: one per 32 rows of P1
+    static constexpr size_t end = bpred_ctr + (size_t)(8192 / 32) * 4;
 };
 constexpr size_t kSyncBytes = 8192;
 static_assert(Sync::end <= kSyncBytes, "sync header overflow");
@@ -183,7 +187,7 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
 
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
                           const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
-                          int32_t* count, const BPredLayout& L, char* ws, hipStream_t s);
+                          int32_t* count, const BPredLayout& L, char* ws, char* hdr, hipStream_t s);
 
 // fused.hip
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
