@@ -247,7 +247,7 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
             const pi::BatchLayout L = pi::batch_layout(Bg, d, ffn);
             hipError_t e = pi::launch_union(reglu, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
                                             idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L,
-                                            w + pi::kSyncBytes, s);
+                                            w + pi::kSyncBytes, w, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
         }
         return ok();

@@ -15,6 +15,7 @@
 // fp16 matrix-core down product loses no accuracy against fp32 activations.
 #include "common.hpp"
 #include "internal.hpp"
+#include "ring.hpp"
 
 namespace pi {
 
@@ -25,8 +26,10 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_union_clear(uint32_t* __restrict__ tmask, size_t n,
-                                                     uint32_t* __restrict__ ctr) {
+                                                     uint32_t* __restrict__ ctr, uint32_t* __restrict__ upctr,
+                                                     int nup) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) tmask[i] = 0u;
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nup; i += gridDim.x * 256) upctr[i] = 0u;
     if (blockIdx.x == 0 && threadIdx.x <= kArriveGroups) ctr[threadIdx.x * kCtrStride] = 0u;
 }
 
@@ -116,262 +119,103 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Rows x tokens on the matrix cores.  A workgroup owns 32 weight rows; its 4
-// waves split K in quarters and each computes the 32 x 32 products for every
-// 32-token block with v_mfma_f32_32x32x8_f16 (lane l: row l%32 of the
-// weight block, token l%32 of the activation block, K slice by l/32).  Both
-// operands are K-contiguous in memory: a 16-byte load gives a lane 8 values;
-// the two lane halves take the two chunks of a chunk pair, and every MFMA sums
-// over both halves' slices.  The loop runs over whole pairs in batches, so
-// every lane executes the same MFMAs (an odd final chunk is fed as zero
-// weights by half 1).  NM weight matrices share the activation loads (gate +
-// up); NX activation arrays share the weight loads and add into the same
-// accumulators (an fp32 activation carried as fp16 hi + lo).
-constexpr int kUpBatch = 8;   // loads per operand kind in flight per lane
-
-template <int NM, int NX, int NB>
-__device__ __forceinline__ void gemm_quarters(f32x16 (&acc)[NM][NB], const h16* const (&wrow)[NM],
-                                              const h16* const (&xs)[NX], int ldx, int nch, int B,
-                                              int wave, int li, int half) {
-    const int npair = nch >> 1;
-    const int p0 = (npair * wave) / 4, p1 = (npair * (wave + 1)) / 4;
-    constexpr int UB = kUpBatch / (NB * NX) > 1 ? kUpBatch / (NB * NX) : 2;   // pairs per batch
-    auto ldx_ = [&](int ix, int nb, int c) {
-        return ld16(xs[ix] + (size_t)min(nb * 32 + li, B - 1) * ldx + (size_t)c * 8);
-    };
-    auto mfma = [&](const u32x4 (&wv)[NM], const u32x4 (&xv)[NX][NB]) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            const f16x8 a8 = __builtin_bit_cast(f16x8, wv[m]);
-            const f16x4 alo = {a8[0], a8[1], a8[2], a8[3]}, ahi = {a8[4], a8[5], a8[6], a8[7]};
-#pragma unroll
-            for (int ix = 0; ix < NX; ++ix)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const f16x8 x8 = __builtin_bit_cast(f16x8, xv[ix][nb]);
-                    const f16x4 xlo = {x8[0], x8[1], x8[2], x8[3]}, xhi = {x8[4], x8[5], x8[6], x8[7]};
-                    acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x8f16(alo, xlo, acc[m][nb], 0, 0, 0);
-                    acc[m][nb] = __builtin_amdgcn_mfma_f32_32x32x8f16(ahi, xhi, acc[m][nb], 0, 0, 0);
-                }
-        }
-    };
-    int p = p0;
-    for (; p + UB <= p1; p += UB) {
-        u32x4 wv[UB][NM], xv[UB][NX][NB];
-#pragma unroll
-        for (int k = 0; k < UB; ++k) {
-            const int c = 2 * (p + k) + half;
-#pragma unroll
-            for (int m = 0; m < NM; ++m) wv[k][m] = ld16_stream(wrow[m] + (size_t)c * 8);
-#pragma unroll
-            for (int ix = 0; ix < NX; ++ix)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) xv[k][ix][nb] = ldx_(ix, nb, c);
-        }
-#pragma unroll
-        for (int k = 0; k < UB; ++k) mfma(wv[k], xv[k]);
-        // keep the batch's loads ahead of its MFMAs: left alone, the scheduler
-        // interleaves them and only one or two loads are ever in flight
-        __builtin_amdgcn_sched_group_barrier(0x0020, UB * (NM + NX * NB), 0);   // VMEM reads
-        __builtin_amdgcn_sched_group_barrier(0x0008, UB * 2 * NM * NX * NB, 0); // MFMA
-    }
-    for (; p < p1; ++p) {
-        const int c = 2 * p + half;
-        u32x4 wv[NM], xv[NX][NB];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) wv[m] = ld16_stream(wrow[m] + (size_t)c * 8);
-#pragma unroll
-        for (int ix = 0; ix < NX; ++ix)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) xv[ix][nb] = ldx_(ix, nb, c);
-        mfma(wv, xv);
-    }
-    if ((nch & 1) && wave == 3) {   // odd chunk count: the last chunk, half 1 feeds zero weights
-        const int c = nch - 1;
-        u32x4 wv[NM], xv[NX][NB];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) wv[m] = half ? u32x4{0u, 0u, 0u, 0u} : ld16_stream(wrow[m] + (size_t)c * 8);
-#pragma unroll
-        for (int ix = 0; ix < NX; ++ix)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) xv[ix][nb] = ldx_(ix, nb, c);
-        mfma(wv, xv);
-    }
+// Skinny GEMMs of the batched path (rows x tokens on the matrix cores, see
+// ring.hpp), by XG = 8-token groups loaded: 32-row blocks and a ring of three
+// stages of 512-byte row segments, or 256 or 128 where three stages of the
+// larger ones would not fit in LDS.
+constexpr int ring_seg(int nm, int nx, int xg) {
+    return 3 * (nm * 4 + nx * xg) * 4 <= 156 ? 4 : (3 * (nm * 4 + nx * xg) * 2 <= 156 ? 2 : 1);
 }
+template <int XG> using HidCfg = RingCfg<1, 1, XG, 1, ring_seg(1, 1, XG), 3>;
+template <int XG> using LogCfg = RingCfg<1, 2, XG, 1, ring_seg(1, 2, XG), 3>;
+template <bool REGLU, int XG> using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, 1, ring_seg(REGLU ? 2 : 1, 1, XG), 3>;
 
-// Sum the four K quarters of accumulator block acc (one matrix, one token
-// block) into out[32][33]: output (row r, token n) lives at element
-// e = (r/8)*4 + r%4, lane n + 32*((r/4)%2) of every wave.  Two barriers.
-__device__ __forceinline__ void sum_quarters(const f32x16& acc, float (&red)[4][16][64], float (&out)[32][33],
-                                             int wave, int lane) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[e];
-    __syncthreads();
-    for (int o = threadIdx.x; o < 1024; o += 256) {
-        const int r = o >> 5, n = o & 31;
-        const int e = (r >> 3) * 4 + (r & 3), ln = n + 32 * ((r >> 2) & 1);
-        out[r][n] = red[0][e][ln] + red[1][e][ln] + red[2][e][ln] + red[3][e][ln];
-    }
-    __syncthreads();
+// Up GEMM over the union rows: A[u][t] = W_up[U_u] . x_t (+ the gate
+// product for ReGLU), then bias, activation and the token mask (zero where
+// token t did not select neuron U_u), stored token-major as an fp16 hi/lo
+// pair: aT[t][u], for every token slot t < Bp (zero past B) and for u up to
+// the next multiple of 8 past |U| (zero past |U|).
+template <class C, bool REGLU>
+__global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __restrict__ ucount, int ffn,
+                                                  const float* __restrict__ bup, const float* __restrict__ bg,
+                                                  const uint32_t* __restrict__ tmask, int W, int Bp, int lda,
+                                                  h16* __restrict__ a_hi, h16* __restrict__ a_lo) {
+    __shared__ __align__(16) char lds[C::LDS];
+    const int U = (int)min(*ucount, (uint32_t)ffn), B = a.B;
+    const int32_t* ulist = a.rowlist;
+    const int U8 = min((U + 7) & ~7, lda);
+    ring_gemm<C, true, true>(a, U, lds, [&](int uu, int t, float vu, float vg) {
+        if (t >= Bp || uu >= U8) return;
+        if (uu >= U) {   // the down GEMM reads whole 8-entry chunks: the tail past U is zero
+            a_hi[(size_t)t * lda + uu] = (h16)0.f;
+            a_lo[(size_t)t * lda + uu] = (h16)0.f;
+            return;
+        }
+        float av = 0.f;
+        const int nrow = ulist[uu];
+        if (t < B && ((tmask[(size_t)nrow * W + (t >> 5)] >> (t & 31)) & 1u)) {
+            const float uval = vu + (bup ? bup[nrow] : 0.f);
+            av = REGLU ? fmaxf(vg + (bg ? bg[nrow] : 0.f), 0.f) * uval : fmaxf(uval, 0.f);
+        }
+        const h16 hi = (h16)av;
+        a_hi[(size_t)t * lda + uu] = hi;
+        a_lo[(size_t)t * lda + uu] = (h16)(av - (float)hi);
+    });
 }
 
 // ---------------------------------------------------------------------------
-// Up GEMM over the union rows: bias, activation and the token mask give A,
-// stored token-major as hi/lo fp16 pairs: aT[t][u].
-template <bool REGLU, int NB>
-__global__ __launch_bounds__(256) void k_union_up(const h16* __restrict__ x, int B, int d, int ffn,
-                                                  const h16* __restrict__ Wup,
-                                                  const float* __restrict__ bup,
-                                                  const h16* __restrict__ Wg,
-                                                  const float* __restrict__ bg,
-                                                  const int32_t* __restrict__ ulist,
-                                                  const uint32_t* __restrict__ tmask,
-                                                  const uint32_t* __restrict__ ucount, int W,
-                                                  int Bp, int lda, h16* __restrict__ a_hi,
-                                                  h16* __restrict__ a_lo) {
-    constexpr int NM = REGLU ? 2 : 1;
-    __shared__ float s_red[4][16][64];
-    __shared__ float s_sum[NM][32][33];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int li = lane & 31, half = lane >> 5;
-    const int U = (int)min(*ucount, (uint32_t)ffn);
-    const int nrb = (U + 31) / 32;
-    for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-        const int row = ulist[min(rb * 32 + li, U - 1)];
-        const h16* wrow[NM];
-        wrow[0] = Wup + (size_t)row * d;
-        if (REGLU) wrow[NM - 1] = Wg + (size_t)row * d;
-        const h16* xs[1] = {x};
-        f32x16 acc[NM][NB];
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[m][nb] = f32x16{};
-        gemm_quarters<NM, 1, NB>(acc, wrow, xs, d, d >> 3, B, wave, li, half);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-            for (int m = 0; m < NM; ++m) sum_quarters(acc[m][nb], s_red, s_sum[m], wave, lane);
-            for (int o = threadIdx.x; o < 1024; o += 256) {
-                const int r = o >> 5, n = o & 31;
-                const int uu = rb * 32 + r, t = nb * 32 + n;
-                if (uu < U && t < Bp) {
-                    float av = 0.f;
-                    const int nrow = ulist[uu];
-                    if (t < B && ((tmask[(size_t)nrow * W + (t >> 5)] >> (t & 31)) & 1u)) {
-                        const float uval = s_sum[0][r][n] + (bup ? bup[nrow] : 0.f);
-                        av = REGLU ? fmaxf(s_sum[NM - 1][r][n] + (bg ? bg[nrow] : 0.f), 0.f) * uval
-                                   : fmaxf(uval, 0.f);
-                    }
-                    const h16 hi = (h16)av;
-                    a_hi[(size_t)t * lda + uu] = hi;
-                    a_lo[(size_t)t * lda + uu] = (h16)(av - (float)hi);
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Batched predictor.  Hidden layer: H = act(P1 X^T + b1), rows of P1 against
-// the tokens.  Grid = (32-row blocks, KS splits of K): each workgroup writes
-// the fp32 partial of its K range with device-coherent stores and arrives on
-// its row block's counter; the last of the KS to arrive adds the partials in
-// split order, applies b1 and the activation, writes h token-major as an fp16
-// hi/lo pair (h itself is never rounded to fp16: hi + lo carries about 22
-// significant bits) and puts the counter back to 0.
-template <int NB>
-__global__ __launch_bounds__(256) void k_bpred_hidden(const h16* __restrict__ x, int B, int d,
-                                                      const h16* __restrict__ P1,
-                                                      const float* __restrict__ b1, int relu, int r,
-                                                      int ldh, h16* __restrict__ h_hi,
-                                                      h16* __restrict__ h_lo, float* __restrict__ part,
-                                                      uint32_t* __restrict__ ctr, int KS) {
-    __shared__ float s_red[4][16][64];
-    __shared__ float s_sum[32][33];
-    __shared__ int s_last;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int li = lane & 31, half = lane >> 5;
-    const int rb = blockIdx.x, ks = blockIdx.y;
-    const int nch = d >> 3;
-    const int c0 = (int)(((long long)nch * ks) / KS), c1 = (int)(((long long)nch * (ks + 1)) / KS);
-    const int Bp = NB * 32;
-    const h16* wrow[1] = {P1 + (size_t)min(rb * 32 + li, r - 1) * d + (size_t)c0 * 8};
-    const h16* xs[1] = {x + (size_t)c0 * 8};
-    f32x16 acc[1][NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[0][nb] = f32x16{};
-    gemm_quarters<1, 1, NB>(acc, wrow, xs, d, c1 - c0, B, wave, li, half);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        sum_quarters(acc[0][nb], s_red, s_sum, wave, lane);
-        for (int o = threadIdx.x; o < 1024; o += 256) {
-            const int rr = o >> 5, n = o & 31;
-            const int j = rb * 32 + rr, t = nb * 32 + n;
-            if (j < r && t < B) st_coherent(&part[((size_t)ks * Bp + t) * r + j], s_sum[rr][n]);
-        }
-        __syncthreads();
-    }
-    wait_own_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int last = fetch_add(&ctr[rb], 1u) == (uint32_t)(KS - 1);
-        if (last) st_flag(&ctr[rb], 0u);
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    for (int o = threadIdx.x; o < 32 * B; o += 256) {
-        const int rr = o / B, t = o % B;
-        const int j = rb * 32 + rr;
-        if (j >= r) continue;
-        float sv = b1 ? b1[j] : 0.f;
-        for (int k = 0; k < KS; ++k) sv += ld_coherent(&part[((size_t)k * Bp + t) * r + j]);
+// Batched predictor.  Hidden layer: H = act(P1 X^T + b1), written token-major
+// as an fp16 hi/lo pair (h itself is never rounded to fp16: hi + lo carries
+// about 22 significant bits).  P1 has few rows and long ones, so every row
+// block is split over many workgroups and k_bpred_hidden_finish adds the
+// pieces.  Workgroup 0 also zeroes the logits kernel's row-block counters,
+// which that kernel (next but one on the stream) expects at 0.
+struct HiddenEpi {
+    const float* b1;
+    int relu, r, B, ldh;
+    h16* h_hi;
+    h16* h_lo;
+    __device__ void operator()(int j, int t, float v, float) const {
+        if (j >= r || t >= B) return;
+        const float sv = v + (b1 ? b1[j] : 0.f);
         const float hv = relu ? fmaxf(sv, 0.f) : sv;
         const h16 hi = (h16)hv;
         h_hi[(size_t)t * ldh + j] = hi;
         h_lo[(size_t)t * ldh + j] = (h16)(hv - (float)hi);
     }
+};
+
+template <class C>
+__global__ __launch_bounds__(256) void k_bpred_hidden(RingArgs a, HiddenEpi epi, uint32_t* __restrict__ lctr,
+                                                      int nlctr) {
+    __shared__ __align__(16) char lds[C::LDS];
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < nlctr; i += 256) lctr[i] = 0u;
+    ring_gemm<C, false, false>(a, a.nrows, lds, epi);
+}
+
+template <class C>
+__global__ __launch_bounds__(256) void k_bpred_hidden_finish(RingArgs a, HiddenEpi epi, int G0) {
+    ring_finish<C>(a, a.nrows, G0, epi);
 }
 
 // Logits: Z = P2 H^T + b2 with both halves of h, then the strict test
-// z > thr per (neuron, token); each 32-neuron tile gives one 32-bit mask per
-// token (bit r = neuron 32*tile + r).
-template <int NB>
-__global__ __launch_bounds__(256) void k_bpred_logits(const h16* __restrict__ P2,
-                                                      const float* __restrict__ b2, int B, int r,
-                                                      int ffn, float thr, int ldh,
-                                                      const h16* __restrict__ h_hi,
-                                                      const h16* __restrict__ h_lo,
+// z > thr per (neuron, token); every 32 neurons give one 32-bit mask word per
+// token (bit k = neuron 32*word + k).  Each half of a wave holds 32 neurons
+// of one token: one ballot gives two words.
+template <class C>
+__global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* __restrict__ b2, float thr,
                                                       uint32_t* __restrict__ masks32) {
-    __shared__ float s_red[4][16][64];
-    __shared__ float s_sum[32][33];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int li = lane & 31, half = lane >> 5;
-    const int nrb = (ffn + 31) / 32;
-    for (int rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-        const h16* wrow[1] = {P2 + (size_t)min(rb * 32 + li, ffn - 1) * r};
-        const h16* xs[2] = {h_hi, h_lo};
-        f32x16 acc[1][NB];
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[0][nb] = f32x16{};
-        gemm_quarters<1, 2, NB>(acc, wrow, xs, ldh, r >> 3, B, wave, li, half);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            sum_quarters(acc[0][nb], s_red, s_sum, wave, lane);
-            if (threadIdx.x < 32) {
-                const int n = threadIdx.x, t = nb * 32 + n;
-                uint32_t m = 0;
-                for (int rr = 0; rr < 32; ++rr) {
-                    const int i = rb * 32 + rr;
-                    if (i < ffn && s_sum[rr][n] + (b2 ? b2[i] : 0.f) > thr) m |= 1u << rr;
-                }
-                if (t < B) masks32[(size_t)t * nrb + rb] = m;
-            }
-            __syncthreads();
-        }
-    }
+    __shared__ __align__(16) char lds[C::LDS];
+    static_assert(C::RB % 32 == 0, "a half-wave must hold 32 neurons of one token");
+    const int ffn = a.nrows, B = a.B;
+    const int nw = (ffn + 31) / 32;
+    ring_gemm<C, false, true>(a, ffn, lds, [&](int i, int t, float v, float) {
+        const bool on = i < ffn && t < B && v + (b2 ? b2[i] : 0.f) > thr;
+        const uint64_t m = __ballot(on);
+        const int lane = threadIdx.x & 63;
+        if ((lane & 31) == 0 && i < ffn && t < B) masks32[(size_t)t * nw + (i >> 5)] = (uint32_t)(m >> (lane & 32));
+    });
 }
 
 // One workgroup per token: the token's 32-bit tile masks in neuron order ->
@@ -421,110 +265,203 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Down GEMM.  Grid = (128-column tiles, G chunks of the union).  Rows of
-// W_down are neuron-major, so the contraction index (the union entry) runs
-// across rows: each stage of KS union rows x 128 columns, and the stage's
-// activations (hi and lo, KS entries x 32*NB tokens), are loaded with
-// coalesced 16-byte loads into registers and written to LDS; the next
-// stage's loads are issued before the current one is multiplied.  The MFMA
-// operands come from LDS: 4 consecutive union rows of one column per lane
-// (W) and 4 consecutive union entries of one token per lane (A).  Wave w
-// owns columns 32w..32w+31 of the tile.  Chunk partials go to the
-// workspace; k_union_reduce adds them in chunk order.
+// Down GEMM.  Y[t][c] = sum_u A[t][u] W_down[U_u][c]: the contraction runs
+// over union entries, i.e. across rows of W_down.  Grid = (128-column tiles,
+// G chunks of the union list); a workgroup streams its chunk's rows of its
+// column tile through an LDS ring, stages of 64 union entries: 8-row x
+// 128-byte blocks of W_down (the ring.hpp block layout, by direct-to-LDS
+// loads, row ids taken from the chunk's list staged in LDS) and the stage's
+// activations, hi and lo (8 tokens x 64 entries per block).
+//
+// The matrix cores need K (union entries) along each lane's operand, while
+// W_down holds columns along a row: ds_read_b64_tr_b16 transposes on the LDS
+// read.  Within each 16-lane group, lane l gets element l % 4 of the 64-bit
+// words read by lanes l/4, 4 + l/4, 8 + l/4 and 12 + l/4 (measured on
+// gfx950); so when lane 4k + m reads row k, columns 4m .. 4m+3 of a 16-column
+// group, lane j receives column j of rows 0..3.  Two such reads give a lane
+// column l % 32 of the 8 union entries of its half (l / 32) of a 16-entry
+// step, the A operand of v_mfma_f32_32x32x16_f16 (columns x entries); the B
+// operand is 16 bytes of A[t][.] per lane.  Wave w owns columns 32w..32w+31
+// of the tile for every token.  Chunk partials go to the workspace and
+// k_union_reduce adds them in chunk order.
 constexpr int kDnCols = 128;
 constexpr int kDnIds = 4096;   // union entries per chunk staged in LDS (G is sized for it)
 
-template <int NB>
+template <int XG_>
+struct DownCfg {
+    static constexpr int XG = XG_;
+    static constexpr int NB = (XG + 3) / 4, BP = 32 * NB;
+    static constexpr int KR = 64;                                  // union entries per stage
+    static constexpr int WBLK = (KR / 8) * (kDnCols / 64);         // W_down blocks per stage
+    static constexpr int ABLK = 2 * XG;                            // activation blocks (hi, lo)
+    static constexpr int NBLK = ((WBLK + ABLK + 3) / 4) * 4;       // padded to whole waves
+    static constexpr int IPW = NBLK / 4;
+    static constexpr int STAGE = NBLK * 1024;
+    static constexpr int NS = 3 * STAGE + kDnIds * 4 <= 156 * 1024 ? 3 : 2;
+    static_assert(WBLK % 4 == 0 && IPW * (NS - 2) < 64, "loads per stage");
+};
+
+__device__ __forceinline__ f16x4 lds_read8_tr(uint32_t addr) {
+    f16x4 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ void lds_ready4(f16x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ int lds_read_i32(uint32_t addr) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ void lds_ready_i(int& v) { asm volatile("" : "+v"(v)); }
+
+template <class C>
 __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, int d, int ffn,
                                                     const int32_t* __restrict__ ulist,
                                                     const uint32_t* __restrict__ ucount,
                                                     const h16* __restrict__ a_hi,
-                                                    const h16* __restrict__ a_lo, int Bp, int lda,
-                                                    float* __restrict__ partial, int G) {
-    constexpr int KS = NB == 1 ? 128 : (NB == 2 ? 64 : 32);   // union rows per stage
-    constexpr int BT = NB * 32;                               // tokens in the tile
-    constexpr int NW = KS / 16;                               // W loads per thread per stage
-    constexpr int NA = 2 * BT * KS / 8 / 256;                 // A loads per thread per stage (= 4)
-    static_assert(NA * 256 * 8 == 2 * BT * KS, "A stage must split evenly");
-    __shared__ h16 s_w[KS][kDnCols + 8];
-    __shared__ __align__(16) h16 s_a[2][BT][KS + 8];          // [hi/lo][token][entry]
+                                                    const h16* __restrict__ a_lo, int B, int Bp, int lda,
+                                                    float* __restrict__ partial, int G,
+                                                    const h16* __restrict__ zsrc) {
+    __shared__ __align__(16) char lds[C::NS * C::STAGE];
     __shared__ int32_t s_ids[kDnIds];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, kh = lane >> 5;
     const int tile = blockIdx.x, chunk = blockIdx.y;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int li = lane & 31, half = lane >> 5;
     const int U = (int)min(*ucount, (uint32_t)ffn);
-    // chunk starts are multiples of 8 so 16-byte A loads stay aligned
+    // chunk starts are multiples of 8: 16-byte activation loads stay aligned
     const int per = min((((U + G - 1) / G) + 7) & ~7, kDnIds);
     const int u0 = min(U, chunk * per), u1 = min(U, u0 + per);
     const int n_ids = u1 - u0;
+    const int n = (n_ids + C::KR - 1) / C::KR;
     const int c0 = tile * kDnCols;
-    for (int i = tid; i < n_ids; i += 256) s_ids[i] = ulist[u0 + i];
+    for (int i0 = 0; i0 < n_ids; i0 += 256 * 8) {   // 8 loads in flight per thread
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = ulist[u0 + min(i0 + k * 256 + tid, max(n_ids - 1, 0))];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (i0 + k * 256 + tid < n_ids) s_ids[i0 + k * 256 + tid] = v[k];
+    }
     __syncthreads();
+    const uint32_t lbase = (uint32_t)(size_t)(lds_void_ptr)lds;
+    const uint32_t ibase = (uint32_t)(size_t)(lds_void_ptr)s_ids;
 
-    f32x16 acc[NB];
+    // this thread's loads: block b = wave + 4i; weight blocks first (WBLK is a
+    // multiple of 4, so block i is a weight block exactly when i < WBLK / 4)
+    int wofs[C::IPW];       // weight: row-in-stage; activation: token row offset
+    int kofs[C::IPW];       // weight: column offset; activation: entry offset in the stage
+    const h16* abase[C::IPW];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-
-    const int sr = tid >> 4, sc = (tid & 15) * 8;   // W staging: rows sr + 16k, 8 columns at sc
-    const bool col_ok = c0 + sc < d;
-    u32x4 vw[NW], va[NA];
-    auto issue = [&](int s0) {
-#pragma unroll
-        for (int k = 0; k < NW; ++k) {
-            const int rr = s0 + sr + 16 * k;   // chunk-relative union row
-            vw[k] = (rr < n_ids && col_ok) ? ld16_stream(Wd + (size_t)s_ids[rr] * d + c0 + sc)
-                                           : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < C::IPW; ++i) {
+        const int b = wave + 4 * i;
+        if (i < C::WBLK / 4) {
+            const int rg = b / (kDnCols / 64), cs = b % (kDnCols / 64);
+            wofs[i] = rg * 8 + (lane & 7);
+            kofs[i] = c0 + cs * 64 + (((lane >> 3) ^ (rg & 7)) << 3);
+            abase[i] = nullptr;
+        } else {
+            const int bx = b - C::WBLK;
+            const int ix = bx / C::XG, tg = bx % C::XG;
+            const int t = tg * 8 + (lane & 7);
+            const bool real = bx < C::ABLK && t < B;
+            abase[i] = real ? (ix ? a_lo : a_hi) + (size_t)t * lda : nullptr;
+            wofs[i] = 0;
+            kofs[i] = ((lane >> 3) ^ (tg & 3)) << 3;
         }
+    }
+    auto issue = [&](int st, int q) {
+        int id[C::WBLK / 4];
 #pragma unroll
-        for (int k = 0; k < NA; ++k) {
-            const int q = tid + 256 * k;
-            const int which = q / (BT * KS / 8), rem = q % (BT * KS / 8);
-            const int t = rem / (KS / 8), e = (rem % (KS / 8)) * 8;   // entries s0+e .. +7
-            const h16* src = (which ? a_lo : a_hi) + (size_t)t * lda + u0 + s0 + e;
-            va[k] = (s0 + e < n_ids) ? *reinterpret_cast<const u32x4*>(src) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < C::WBLK / 4; ++i) id[i] = lds_read_i32(ibase + 4 * min(st * C::KR + wofs[i], kDnIds - 1));
+        lds_wait();
+#pragma unroll
+        for (int i = 0; i < C::WBLK / 4; ++i) lds_ready_i(id[i]);
+        char* dst = lds + q * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i) {
+            const h16* p;
+            if (i < C::WBLK / 4) {
+                const bool ok = st * C::KR + wofs[i] < n_ids && kofs[i] < d;
+                p = ok ? Wd + (size_t)id[i] * d + kofs[i] : zsrc;
+            } else {
+                const int e = st * C::KR + kofs[i];
+                p = (abase[i] && e < n_ids) ? abase[i] + u0 + e : zsrc;
+            }
+            __builtin_amdgcn_global_load_lds(p, (lds_void_ptr)(dst + (wave + 4 * i) * 1024), 16, 0, 0);
         }
     };
-    if (n_ids > 0) issue(0);
-    const int col = wave * 32 + li;   // column within the tile
-    for (int s0 = 0; s0 < n_ids; s0 += KS) {
-        __syncthreads();   // the previous stage is no longer read from LDS
+
+    f32x16 acc[C::NB];
 #pragma unroll
-        for (int k = 0; k < NW; ++k) *reinterpret_cast<u32x4*>(&s_w[sr + 16 * k][sc]) = vw[k];
+    for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
+    const int g = lane >> 4, j = lane & 15;
+    const int col = wave * 32 + 16 * (g & 1) + 4 * (j & 3);     // first of this lane's 4 columns
+    const int cs = col >> 6, ch = (col & 63) >> 3, quad = (col >> 2) & 1;
+
+    wait_vm<0>();
 #pragma unroll
-        for (int k = 0; k < NA; ++k) {
-            const int q = tid + 256 * k;
-            const int which = q / (BT * KS / 8), rem = q % (BT * KS / 8);
-            const int t = rem / (KS / 8), e = (rem % (KS / 8)) * 8;
-            f16x8 v = __builtin_bit_cast(f16x8, va[k]);
+    for (int jj = 0; jj < C::NS - 1; ++jj)
+        if (jj < n) issue(jj, jj);
+    for (int s = 0; s < n; ++s) {
+        if (s + C::NS - 2 < n) wait_vm<(C::NS - 2) * C::IPW>();
+        else wait_vm<0>();
+        ring_barrier();
+        if (s + C::NS - 1 < n) issue(s + C::NS - 1, (s + C::NS - 1) % C::NS);
+        const uint32_t buf = lbase + (s % C::NS) * C::STAGE;
+        f16x4 w0[C::KR / 16], w1[C::KR / 16];
+        f16x8 av[C::KR / 16][C::NB][2];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)   // entries past the chunk hold stale data: zero them
-                if (s0 + e + j >= n_ids) v[j] = (h16)0.f;
-            *reinterpret_cast<f16x8*>(&s_a[which][t][e]) = v;
+        for (int q = 0; q < C::KR / 16; ++q) {
+            const int rg = 2 * q + kh;   // row group of this lane half's 8 entries
+            const uint32_t wb = buf + (rg * (kDnCols / 64) + cs) * 1024 + ((ch ^ (rg & 7)) << 7) + quad * 8;
+            w0[q] = lds_read8_tr(wb + (j >> 2) * 16);
+            w1[q] = lds_read8_tr(wb + ((j >> 2) + 4) * 16);
+            const int c = 2 * q + kh;    // activation chunk (8 entries)
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                const int t = nb * 32 + li, tg = min(t >> 3, C::XG - 1);
+#pragma unroll
+                for (int ix = 0; ix < 2; ++ix) {
+                    const int blk = C::WBLK + ix * C::XG + tg;
+                    av[q][nb][ix] = lds_read16(buf + blk * 1024 + ((c ^ (tg & 3)) << 7) + ((t & 7) << 4));
+                }
+            }
         }
-        __syncthreads();
-        if (s0 + KS < n_ids) issue(s0 + KS);
-        const int sn = min(KS, n_ids - s0);
-        for (int kk = 0; kk < sn; kk += 8) {
-            const int kr = kk + 4 * half;     // this lane's 4 union rows: kr .. kr+3 (zero past sn)
-            const f16x4 wv = {s_w[kr][col], s_w[kr + 1][col], s_w[kr + 2][col], s_w[kr + 3][col]};
+        lds_wait();
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int t = nb * 32 + li;
-                const f16x4 ah = *reinterpret_cast<const f16x4*>(&s_a[0][t][kr]);
-                const f16x4 al = *reinterpret_cast<const f16x4*>(&s_a[1][t][kr]);
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x8f16(wv, ah, acc[nb], 0, 0, 0);
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x8f16(wv, al, acc[nb], 0, 0, 0);
+        for (int q = 0; q < C::KR / 16; ++q) {
+            lds_ready4(w0[q]);
+            lds_ready4(w1[q]);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                lds_ready(av[q][nb][0]);
+                lds_ready(av[q][nb][1]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < C::KR / 16; ++q) {
+            const f16x8 a8 = {w0[q][0], w0[q][1], w0[q][2], w0[q][3], w1[q][0], w1[q][1], w1[q][2], w1[q][3]};
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][0], acc[nb], 0, 0, 0);
+                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][1], acc[nb], 0, 0, 0);
             }
         }
     }
-    // acc[nb] element e of lane l: column wave*32 + 8*(e/4) + 4*half + e%4, token nb*32 + li
+    // acc[nb] element e of lane l: column wave*32 + 8*(e/4) + 4*(l/32) + e%4 of the
+    // tile, token nb*32 + l%32; four consecutive columns per 16-byte store
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < C::NB; ++nb) {
         const int t = nb * 32 + li;
+        if (t >= B) continue;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int cc = c0 + wave * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            if (cc < d) partial[((size_t)chunk * Bp + t) * d + cc] = acc[nb][e];
+        for (int e4 = 0; e4 < 4; ++e4) {
+            const int cc = c0 + wave * 32 + 8 * e4 + 4 * kh;
+            if (cc < d) {
+                const f32x4 v = {acc[nb][4 * e4], acc[nb][4 * e4 + 1], acc[nb][4 * e4 + 2], acc[nb][4 * e4 + 3]};
+                *reinterpret_cast<f32x4*>(&partial[((size_t)chunk * Bp + t) * d + cc]) = v;
+            }
         }
     }
 }
@@ -547,10 +484,28 @@ __global__ __launch_bounds__(256) void k_union_reduce(const float* __restrict__ 
     y[o] = sum;
 }
 
+// Workgroups of a ring kernel that are resident on the device at once (at
+// most kRingMaxWG, the size the piece areas are laid out for).
+template <auto KERN>
+static int ring_grid() {
+    static const int g = [] {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, reinterpret_cast<const void*>(KERN), 256, 0) != hipSuccess)
+            return kRingMaxWG / 2;
+        const int n = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+        return n < kRingMaxWG ? n : kRingMaxWG;
+    }();
+    return g;
+}
+
+static int ring_xg(int B) { return B <= 8 ? 1 : (B <= 16 ? 2 : (B <= 32 ? 4 : (B <= 64 ? 8 : 16))); }
+
 hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h16* Wup,
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
-                        char* ws, hipStream_t s) {
+                        char* ws, char* hdr, hipStream_t s) {
     uint32_t* tmask = reinterpret_cast<uint32_t*>(ws + L.tmask);
     uint64_t* umasks = reinterpret_cast<uint64_t*>(ws + L.umasks);
     int32_t* ulist = reinterpret_cast<int32_t*>(ws + L.ulist);
@@ -559,31 +514,47 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
     h16* a_lo = reinterpret_cast<h16*>(ws + L.a_lo);
     float* partial = reinterpret_cast<float*>(ws + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + L.ctr);
+    uint32_t* upctr = reinterpret_cast<uint32_t*>(ws + L.upctr);
     const size_t nmask = (size_t)ffn * L.W;
     int gclear = (int)((nmask + 255) / 256);
     if (gclear > 2048) gclear = 2048;
-    hipLaunchKernelGGL(k_union_clear, dim3(gclear), dim3(256), 0, s, tmask, nmask, ctr);
+    hipLaunchKernelGGL(k_union_clear, dim3(gclear), dim3(256), 0, s, tmask, nmask, ctr, upctr,
+                       (ffn + kRingRows - 1) / kRingRows);
     int gm = (ffn + 255) / 256;
     if (gm > 64) gm = 64;
     hipLaunchKernelGGL(k_union_mark, dim3(gm, B), dim3(256), 0, s, idx, count, ffn, L.W, tmask);
     const int ntiles = (ffn + 63) / 64;
     hipLaunchKernelGGL(k_union_compact, dim3((ntiles + 3) / 4), dim3(256), 0, s, tmask, ffn, L.W, umasks,
                        ctr, ulist, ucount);
-    int gu = (ffn + 31) / 32;
-    if (gu > 1024) gu = 1024;
-#define PI_UP(R, N)                                                                                  \
-    hipLaunchKernelGGL((k_union_up<R, N>), dim3(gu), dim3(256), 0, s, x, B, d, ffn, Wup, bup, Wg, bg, \
-                       ulist, tmask, ucount, L.W, L.Bp, L.lda, a_hi, a_lo)
-#define PI_DN(N)                                                                                     \
-    hipLaunchKernelGGL((k_union_down<N>), dim3(L.T, L.G), dim3(256), 0, s, Wd, d, ffn, ulist, ucount, \
-                       a_hi, a_lo, L.Bp, L.lda, partial, L.G)
-    const int NB = L.Bp / 32;
+    RingArgs ra{};
+    ra.W[0] = Wup;
+    ra.W[1] = Wg;
+    ra.ldw = d;
+    ra.rowlist = ulist;
+    ra.nrows = 0;   // |U|, read on the device
+    ra.X[0] = x;
+    ra.ldx = d;
+    ra.B = B;
+    ra.K = d;
+    ra.zsrc = reinterpret_cast<const h16*>(hdr + Sync::zero);
+    ra.part = reinterpret_cast<float*>(ws + L.upart);
+    ra.ctr = upctr;
+#define PI_UP(R, N)                                                                                        \
+    hipLaunchKernelGGL((k_union_up<UpCfg<R, N>, R>), dim3(ring_grid<k_union_up<UpCfg<R, N>, R>>()), dim3(256), \
+                       0, s, ra, ucount, ffn, bup, bg, tmask, L.W, L.Bp, L.lda, a_hi, a_lo)
+#define PI_DN(X)                                                                                        \
+    hipLaunchKernelGGL((k_union_down<DownCfg<X>>), dim3(L.T, L.G), dim3(256), 0, s, Wd, d, ffn, ulist, ucount, \
+                       a_hi, a_lo, B, L.Bp, L.lda, partial, L.G, ra.zsrc)
+    const int xg = ring_xg(B);
     if (reglu) {
-        if (NB == 1) PI_UP(true, 1); else if (NB == 2) PI_UP(true, 2); else if (NB == 3) PI_UP(true, 3); else PI_UP(true, 4);
+        if (xg == 1) PI_UP(true, 1); else if (xg == 2) PI_UP(true, 2); else if (xg == 4) PI_UP(true, 4);
+        else if (xg == 8) PI_UP(true, 8); else PI_UP(true, 16);
     } else {
-        if (NB == 1) PI_UP(false, 1); else if (NB == 2) PI_UP(false, 2); else if (NB == 3) PI_UP(false, 3); else PI_UP(false, 4);
+        if (xg == 1) PI_UP(false, 1); else if (xg == 2) PI_UP(false, 2); else if (xg == 4) PI_UP(false, 4);
+        else if (xg == 8) PI_UP(false, 8); else PI_UP(false, 16);
     }
-    if (NB == 1) PI_DN(1); else if (NB == 2) PI_DN(2); else if (NB == 3) PI_DN(3); else PI_DN(4);
+    if (xg == 1) PI_DN(1); else if (xg == 2) PI_DN(2); else if (xg == 4) PI_DN(4);
+    else if (xg == 8) PI_DN(8); else PI_DN(16);
 #undef PI_UP
 #undef PI_DN
     const size_t nout = (size_t)B * d;
@@ -598,18 +569,49 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
     h16* h_hi = reinterpret_cast<h16*>(ws + L.h_hi);
     h16* h_lo = reinterpret_cast<h16*>(ws + L.h_lo);
     uint32_t* masks32 = reinterpret_cast<uint32_t*>(ws + L.masks32);
-    float* hpart = reinterpret_cast<float*>(ws + L.hpart);
-    uint32_t* ctr = reinterpret_cast<uint32_t*>(hdr + Sync::bpred_ctr);
-    const int NB = L.Bp / 32;
-    const dim3 gh((r + 31) / 32, L.KS);
-    int gl = (ffn + 31) / 32;
-    if (gl > 2048) gl = 2048;
-#define PI_BH(N) hipLaunchKernelGGL((k_bpred_hidden<N>), gh, dim3(256), 0, s, x, B, d, P1, b1, (int)relu, r, L.ldh, h_hi, h_lo, hpart, ctr, L.KS)
-#define PI_BL(N) hipLaunchKernelGGL((k_bpred_logits<N>), dim3(gl), dim3(256), 0, s, P2, b2, B, r, ffn, thr, L.ldh, h_hi, h_lo, masks32)
-    if (NB == 1) { PI_BH(1); PI_BL(1); }
-    else if (NB == 2) { PI_BH(2); PI_BL(2); }
-    else if (NB == 3) { PI_BH(3); PI_BL(3); }
-    else { PI_BH(4); PI_BL(4); }
+    float* part = reinterpret_cast<float*>(ws + L.hpart);
+    uint32_t* lctr = reinterpret_cast<uint32_t*>(ws + L.lctr);
+    const h16* zsrc = reinterpret_cast<const h16*>(hdr + Sync::zero);
+    RingArgs ha{};
+    ha.W[0] = P1;
+    ha.ldw = d;
+    ha.nrows = r;
+    ha.X[0] = x;
+    ha.ldx = d;
+    ha.B = B;
+    ha.K = d;
+    ha.zsrc = zsrc;
+    ha.part = part;
+    ha.ctr = nullptr;   // pieces are added by k_bpred_hidden_finish
+    RingArgs la{};
+    la.W[0] = P2;
+    la.ldw = r;
+    la.nrows = ffn;
+    la.X[0] = h_hi;
+    la.X[1] = h_lo;
+    la.ldx = L.ldh;
+    la.B = B;
+    la.K = r;
+    la.zsrc = zsrc;
+    la.part = part;
+    la.ctr = lctr;
+    const int nlctr = (ffn + kRingRows - 1) / kRingRows;
+    const HiddenEpi he{b1, (int)relu, r, B, L.ldh, h_hi, h_lo};
+    const int gfin = (int)(((size_t)r * B + 255) / 256);
+#define PI_BH(N)                                                                                              \
+    {                                                                                                         \
+        const int gh = ring_grid<k_bpred_hidden<HidCfg<N>>>();                                                \
+        hipLaunchKernelGGL((k_bpred_hidden<HidCfg<N>>), dim3(gh), dim3(256), 0, s, ha, he, lctr, nlctr);      \
+        hipLaunchKernelGGL((k_bpred_hidden_finish<HidCfg<N>>), dim3(gfin), dim3(256), 0, s, ha, he, gh);      \
+    }
+#define PI_BL(N) hipLaunchKernelGGL((k_bpred_logits<LogCfg<N>>), dim3(ring_grid<k_bpred_logits<LogCfg<N>>>()), \
+                                    dim3(256), 0, s, la, b2, thr, masks32)
+    const int xg = ring_xg(B);
+    if (xg == 1) { PI_BH(1); PI_BL(1); }
+    else if (xg == 2) { PI_BH(2); PI_BL(2); }
+    else if (xg == 4) { PI_BH(4); PI_BL(4); }
+    else if (xg == 8) { PI_BH(8); PI_BL(8); }
+    else { PI_BH(16); PI_BL(16); }
 #undef PI_BH
 #undef PI_BL
     hipLaunchKernelGGL(k_bpred_compact, dim3(B), dim3(256), 0, s, masks32, ffn, idx, count);

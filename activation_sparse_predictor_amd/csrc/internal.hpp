@@ -59,6 +59,13 @@ inline SparseLayout sparse_layout(int B, int d, int ffn) {
 
 // ---- batched union path (2 <= B <= kUnionMaxTokens tokens per pass)
 constexpr int kUnionMaxTokens = 128;
+// Skinny GEMMs of the batched path (ring.hpp): at most kRingMaxWG workgroups,
+// 32-row blocks, token slots padded to 32, 64 or 128.  Piece area: two slots
+// per workgroup of (matrices x token slots x 32) fp32 sums.
+constexpr int kRingMaxWG = 1024;
+constexpr int kRingRows = 32;
+inline int ring_slots(int B) { return B <= 32 ? 32 : (B <= 64 ? 64 : 128); }
+inline size_t ring_piece_bytes(int nm, int B) { return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * kRingRows * 4; }
 struct BatchLayout {
     size_t tmask;    // ffn x W uint32 per-neuron token masks
     size_t umasks;   // tiles uint64 union bitmaps
@@ -66,8 +73,10 @@ struct BatchLayout {
     size_t ucount;   // uint32 |U|
     size_t a_hi;     // Bp x lda fp16 activations, high part
     size_t a_lo;     // Bp x lda fp16 activations, low part
-    size_t partial;  // G x Bp x d fp32 split-K partials
+    size_t partial;  // G x Bp x d fp32 split-K partials of the down GEMM
     size_t ctr;      // kCtrWords uint32 arrival counters
+    size_t upctr;    // ceil(ffn/64) uint32 row-block counters of the up GEMM
+    size_t upart;    // pieces of the up GEMM (two matrices for ReGLU)
     size_t total;
     int W, Bp, lda, T, G;
 };
@@ -89,7 +98,9 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
     L.a_lo = L.a_hi + align256((size_t)L.Bp * L.lda * 2);
     L.partial = L.a_lo + align256((size_t)L.Bp * L.lda * 2);
     L.ctr = L.partial + align256((size_t)L.G * L.Bp * d * 4);
-    L.total = L.ctr + align256((size_t)kCtrWords * 4);
+    L.upctr = L.ctr + align256((size_t)kCtrWords * 4);
+    L.upart = L.upctr + align256((size_t)((ffn + kRingRows - 1) / kRingRows) * 4);
+    L.total = L.upart + align256(ring_piece_bytes(2, B));
     return L;
 }
 
@@ -97,9 +108,10 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
 struct BPredLayout {
     size_t h_hi, h_lo;   // Bp x ldh fp16 hidden activations (hi + lo)
     size_t masks32;      // B x ceil(ffn/32) uint32 per-token tile masks
-    size_t hpart;        // KS x Bp x r fp32 split-K partials of the hidden layer
+    size_t hpart;        // pieces of the hidden and logits GEMMs (one after the other)
+    size_t lctr;         // ceil(ffn/64) uint32 row-block counters of the logits GEMM
     size_t total;
-    int Bp, ldh, KS;
+    int Bp, ldh;
 };
 
 inline BPredLayout bpred_layout(int B, int r, int ffn) {
@@ -109,9 +121,10 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
     L.h_hi = 0;
     L.h_lo = align256((size_t)L.Bp * L.ldh * 2);
     L.masks32 = L.h_lo + align256((size_t)L.Bp * L.ldh * 2);
-    L.KS = 8;   // K splits of the hidden layer: r/32 x 8 workgroups
     L.hpart = L.masks32 + align256((size_t)B * ((ffn + 31) / 32) * 4);
-    L.total = L.hpart + align256((size_t)L.KS * L.Bp * r * 4);
+    L.lctr = L.hpart + align256(ring_piece_bytes(1, B));
+    L.total = L.lctr + align256((size_t)((ffn + kRingRows - 1) / kRingRows) * 4);
+    (void)r;
     return L;
 }
 
@@ -131,7 +144,7 @@ struct Sync {   // byte offsets inside the header
     static constexpr size_t ffn_epoch = ffn_ctr + (size_t)kFusedMaxTiles * kCtrStride * 4;  // per tile
     static constexpr size_t pred_epoch = ffn_epoch + kFusedMaxTiles * 4;    // last predict launch's epoch
     static constexpr size_t zero = pred_epoch + 128;                        // never written
-    static constexpr size_t bpred_ctr = zero + 256;                         // batched predictor: one per 32 rows of P1
+    static constexpr size_t bpred_ctr = zero + 256;                         // batched predictor: one per 64 rows of P1
     static constexpr size_t end = bpred_ctr + (size_t)(8192 / 32) * 4;
 };
 constexpr size_t kSyncBytes = 8192;
@@ -183,7 +196,7 @@ hipError_t launch_down_acc(bool dense, const h16* Wd, int B, int d, int ffn, con
 hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h16* Wup,
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
-                        char* ws, hipStream_t s);
+                        char* ws, char* hdr, hipStream_t s);
 
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
                           const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,

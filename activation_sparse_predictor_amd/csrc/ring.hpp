@@ -1,0 +1,371 @@
+// Skinny GEMM core of the batched path: R rows of one or two weight matrices
+// (rows taken in list order, optionally through a row-id list) against up to
+// 128 tokens, on the matrix cores, with both operands streamed through an LDS
+// ring by direct-to-LDS loads.
+//
+// Load geometry.  One "block" is what a single wave-wide 16-byte-per-lane load
+// moves: 8 rows x 128 contiguous bytes (lane j: row j % 8, 16-byte chunk j / 8
+// of the segment), written by global_load_lds_dwordx4 to 1 KB of LDS at
+// [chunk slot][row] x 16 bytes.  Eight full 128-byte lines per instruction
+// keep the gather at the rate of contiguous reads; a matrix-core operand
+// loaded straight from memory would touch 32 rows x 32 bytes per instruction,
+// which runs at well under half that rate.  Chunk c of a row in block group g
+// sits in slot c ^ (g & 3), so the 32 lanes that read one operand (32 rows or
+// tokens, one chunk) hit 4 different 128-byte slots of 4 blocks and the LDS
+// reads are free of bank conflicts.
+//
+// Stages.  A stage covers SEG 128-byte segments (64*SEG halves of K) of every
+// operand row: NM matrices x RB rows and NX activation arrays x 8*XG tokens
+// (the 8-token groups that hold a valid token; the matrix cores take tokens in
+// blocks of 32, and the slots of a block past the loaded groups read a loaded
+// group again: their sums are never used).
+// The ring holds NS stages; stage s + NS - 1 is loaded while stage s is
+// multiplied, and each wave waits only for its own loads of stage s (vmcnt),
+// then a workgroup barrier makes every wave's loads visible.
+//
+// MFMA.  v_mfma_f32_32x32x16_f16: lane l supplies row (or token) l % 32 and 8
+// halves of K from chunk 2p + l / 32 of chunk pair p; the contraction order
+// inside a stage is a permutation of K, the same for both operands.  Wave w
+// takes token block w % NB and the chunk pairs p = w / NB (mod 4 / NB); with
+// NB < 4 the waves that share a token block add their sums in LDS.  An fp32
+// activation array is carried as two fp16 arrays (hi, lo) that add into the
+// same accumulators (NX = 2).
+//
+// Work split (stream-K).  A unit is one stage of one RB-row block.  The
+// T = row blocks x stages units are cut into gridDim.x equal ranges, one per
+// workgroup, so every workgroup streams the same number of bytes whatever the
+// row count.  A row block whose stages all fall in one range is finished in
+// place; otherwise each piece writes its fp32 sums to a slot of its own and
+// the last piece to arrive on the row block's counter adds the pieces in
+// workgroup order (fixed order: deterministic) and finishes the row block,
+// then puts the counter back to 0.  When the rows are few and K is long (every
+// row block split many ways), that one workgroup would read all the pieces
+// alone: there the pieces are left for ring_finish, a kernel of their own
+// that spreads the sums over the whole device.
+#pragma once
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace pi {
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef float ring_f32x16 __attribute__((ext_vector_type(16)));
+
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// at their maximum so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Workgroup barrier without the memory fences of __syncthreads (those would
+// make every wave wait for all of its outstanding loads, the ring's included);
+// the empty asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS reads issued as inline assembly.  With a direct-to-LDS load in flight
+// the compiler makes every LDS read it knows of wait for all outstanding
+// vector-memory loads (it cannot tell which LDS bytes the load writes), which
+// would drain the ring at every stage; these reads are ordered by the ring's
+// own waits and barriers instead.  lds_wait() waits for all of them and
+// lds_ready(v) marks v as produced after that wait.
+__device__ __forceinline__ f16x8 lds_read16(uint32_t addr) {
+    f16x8 v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_ready(f16x8& v) { asm volatile("" : "+v"(v)); }
+
+template <int NM_, int NX_, int XG_, int RBW_, int SEG_, int NS_>
+struct RingCfg {
+    static constexpr int NM = NM_, NX = NX_, XG = XG_, RBW = RBW_, SEG = SEG_, NS = NS_;
+    static constexpr int NB = (XG + 3) / 4;           // 32-token blocks
+    static constexpr int RB = 32 * RBW;               // rows per row block
+    static constexpr int BP = 32 * NB;                // token slots
+    static constexpr int WBLK = NM * (RB / 8) * SEG;  // weight blocks per stage
+    static constexpr int XBLK = NX * XG * SEG;        // activation blocks per stage
+    static constexpr int NBLK = WBLK + XBLK;
+    static constexpr int IPW = NBLK / 4;              // loads per wave per stage
+    static constexpr int STAGE = NBLK * 1024;         // bytes per stage
+    static constexpr int KST = SEG * 64;              // halves of K per stage
+    static constexpr int WK = 4 / NB;                 // waves sharing a token block
+    static constexpr int NPW = 4 * SEG / WK;          // chunk pairs per wave per stage
+    static constexpr int RED = 4 * RBW * NM * 1024 * 4;   // bytes of per-wave sums
+    static constexpr int LDS = NS * STAGE > RED ? NS * STAGE : RED;
+    static_assert(XG == 1 || XG == 2 || XG == 4 || XG == 8 || XG == 16, "token groups: 1, 2 or 4, or whole blocks");
+    static_assert(WBLK % 4 == 0 && XBLK % 4 == 0 && IPW * (NS - 2) < 64, "loads per stage");
+    static_assert(NS >= 2, "ring depth");
+};
+
+struct RingArgs {
+    const h16* W[2];          // NM weight matrices, row stride ldw halves
+    int ldw;
+    const int32_t* rowlist;   // row ids of the list (gathering kernels only)
+    int nrows;                // list length
+    const h16* X[2];          // NX activation arrays [token][ldx]
+    int ldx;
+    int B;                    // valid tokens, at most 8*XG (loads of slots B.. read zeros)
+    int K;                    // contraction length in halves (multiple of 8)
+    const h16* zsrc;          // 16 zero bytes
+    float* part;              // 2 * gridDim.x pieces of NM x BP x RB fp32 sums
+    uint32_t* ctr;            // one arrival counter per row block, 0 between calls
+};
+
+// Host-side sizes of the pieces area for a grid of G workgroups.
+template <class C>
+inline size_t ring_part_bytes(int G) { return (size_t)2 * G * C::NM * C::BP * C::RB * 4; }
+
+// Runs the calling workgroup's range of units over the first nrows rows of
+// the list (a.nrows is not read: a kernel may take the count from memory);
+// GATHER: row i is a.rowlist[i], else row i.  LAST_FINISHES: split row
+// blocks are finished by their last piece's workgroup (else by ring_finish).  epi(i, t, v0, v1) is called by every
+// thread of the workgroup, uniformly, for every (row i of a finished row block,
+// token slot t < BP), rows fastest: rows 64k .. 64k+63 of one token form a wave
+// when RB = 64.  v0 and v1 are the sums for matrices 0 and 1 (v1 = 0 when
+// NM = 1), 0 for t >= B; i runs to the end of the row block, past nrows,
+// where the sums mean nothing.  The caller's LDS
+// area lds must hold C::LDS bytes, 16-byte aligned.
+template <class C, bool GATHER, bool LAST_FINISHES, class Epi>
+__device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* lds, Epi&& epi) {
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar block arithmetic
+    const int li = lane & 31, kh = lane >> 5;
+    const int wn = wave % C::NB, wk = wave / C::NB;
+    const int nrb = (nrows + C::RB - 1) / C::RB;
+    const int nst = (a.K + C::KST - 1) / C::KST;
+    const long long T = (long long)nrb * nst;
+    // no more workgroups than units, so that no range is empty and every
+    // workgroup between the first and last holder of a row block has a piece
+    const int G = (int)min((long long)gridDim.x, T), w = (int)blockIdx.x;
+    if (w >= G) return;
+    const long long ua = T * w / G, ub = T * (w + 1) / G;
+    float* red = reinterpret_cast<float*>(lds);
+    const uint32_t lbase = (uint32_t)(size_t)(lds_void_ptr)lds;
+
+    for (long long u = ua; u < ub;) {
+        const int rb = (int)(u / nst), st0 = (int)(u % nst);
+        const int st1 = (int)min((long long)nst, st0 + (ub - u));
+        u += st1 - st0;
+        const int n = st1 - st0;
+
+        // this thread's loads: block b = wave + 4i of every stage
+        const h16* src[C::IPW];
+        int kofs[C::IPW];
+        bool ok[C::IPW];
+        // (WBLK is a multiple of 4, so block wave + 4i is a weight block
+        // exactly when i < WBLK / 4, whatever the wave: no branches, and all
+        // the row ids are in flight together)
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i) {
+            const int b = wave + 4 * i;
+            if (i < C::WBLK / 4) {
+                const int m = b / ((C::RB / 8) * C::SEG), rem = b % ((C::RB / 8) * C::SEG);
+                const int g = rem / C::SEG, sg = rem % C::SEG;
+                const int row = min(rb * C::RB + g * 8 + (lane & 7), nrows - 1);
+                const int id = GATHER ? a.rowlist[row] : row;
+                src[i] = (m == 0 ? a.W[0] : a.W[1]) + (size_t)id * a.ldw;
+                kofs[i] = sg * 64 + (((lane >> 3) ^ (g & 3)) << 3);
+                ok[i] = true;
+            } else {
+                const int bx = b - C::WBLK;
+                const int ix = bx / (C::XG * C::SEG), rem = bx % (C::XG * C::SEG);
+                const int tg = rem / C::SEG, sg = rem % C::SEG;
+                const int t = tg * 8 + (lane & 7);
+                src[i] = (ix == 0 ? a.X[0] : a.X[1]) + (size_t)min(t, a.B - 1) * a.ldx;
+                kofs[i] = sg * 64 + (((lane >> 3) ^ (tg & 3)) << 3);
+                ok[i] = t < a.B;
+            }
+        }
+        auto issue = [&](int st, int q) {
+            char* dst = lds + q * C::STAGE;
+#pragma unroll
+            for (int i = 0; i < C::IPW; ++i) {
+                const int k = st * C::KST + kofs[i];
+                const h16* p = (ok[i] && k < a.K) ? src[i] + k : a.zsrc;
+                __builtin_amdgcn_global_load_lds(p, (lds_void_ptr)(dst + (wave + 4 * i) * 1024), 16, 0, 0);
+            }
+        };
+
+        ring_f32x16 acc[C::RBW][C::NM];
+#pragma unroll
+        for (int rr = 0; rr < C::RBW; ++rr)
+#pragma unroll
+            for (int m = 0; m < C::NM; ++m) acc[rr][m] = ring_f32x16{};
+
+        wait_vm<0>();   // nothing else outstanding: the ring waits count this unit's loads only
+#pragma unroll
+        for (int j = 0; j < C::NS - 1; ++j)
+            if (j < n) issue(st0 + j, j);
+        for (int s = 0; s < n; ++s) {
+            if (s + C::NS - 2 < n) wait_vm<(C::NS - 2) * C::IPW>();
+            else wait_vm<0>();
+            ring_barrier();   // stage s is in LDS; every wave is done with stage s - 1
+            if (s + C::NS - 1 < n) issue(st0 + s + C::NS - 1, (s + C::NS - 1) % C::NS);
+            const uint32_t buf = lbase + (s % C::NS) * C::STAGE;
+            f16x8 xv[C::NPW][C::NX], wv[C::NPW][C::RBW][C::NM];
+#pragma unroll
+            for (int j = 0; j < C::NPW; ++j) {
+                const int p = wk + j * C::WK;
+                const int c = 2 * p + kh, sg = c >> 3, cc = c & 7;
+                const int t = wn * 32 + li, tg = min(t >> 3, C::XG - 1);
+#pragma unroll
+                for (int ix = 0; ix < C::NX; ++ix) {
+                    const int blk = C::WBLK + (ix * C::XG + tg) * C::SEG + sg;
+                    xv[j][ix] = lds_read16(buf + blk * 1024 + ((cc ^ (tg & 3)) << 7) + ((t & 7) << 4));
+                }
+#pragma unroll
+                for (int rr = 0; rr < C::RBW; ++rr) {
+                    const int rl = rr * 32 + li, g = rl >> 3;
+#pragma unroll
+                    for (int m = 0; m < C::NM; ++m) {
+                        const int blk = (m * (C::RB / 8) + g) * C::SEG + sg;
+                        wv[j][rr][m] = lds_read16(buf + blk * 1024 + ((cc ^ (g & 3)) << 7) + ((rl & 7) << 4));
+                    }
+                }
+            }
+            lds_wait();
+#pragma unroll
+            for (int j = 0; j < C::NPW; ++j) {
+#pragma unroll
+                for (int ix = 0; ix < C::NX; ++ix) lds_ready(xv[j][ix]);
+#pragma unroll
+                for (int rr = 0; rr < C::RBW; ++rr)
+#pragma unroll
+                    for (int m = 0; m < C::NM; ++m) lds_ready(wv[j][rr][m]);
+            }
+#pragma unroll
+            for (int j = 0; j < C::NPW; ++j)
+#pragma unroll
+                for (int rr = 0; rr < C::RBW; ++rr)
+#pragma unroll
+                    for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+                        for (int ix = 0; ix < C::NX; ++ix)
+                            acc[rr][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[j][rr][m], xv[j][ix], acc[rr][m], 0, 0, 0);
+        }
+        ring_barrier();   // the ring is no longer read: its memory holds the sums now
+#pragma unroll
+        for (int rr = 0; rr < C::RBW; ++rr)
+#pragma unroll
+            for (int m = 0; m < C::NM; ++m)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) red[((wave * C::RBW + rr) * C::NM + m) * 1024 + e * 64 + lane] = acc[rr][m][e];
+        __syncthreads();
+        // sum of row rl, token slot t, matrix m: output (r, n) of a 32 x 32
+        // block is element (r/8)*4 + r%4 of lane n + 32*((r/4)%2)
+        auto val = [&](int m, int rl, int t) {
+            const int rr = rl >> 5, r = rl & 31, tb = t >> 5, nn = t & 31;
+            const int e = ((r >> 3) << 2) + (r & 3), ln = nn + (((r >> 2) & 1) << 5);
+            float v = 0.f;
+#pragma unroll
+            for (int k = 0; k < C::WK; ++k) v += red[(((k * C::NB + tb) * C::RBW + rr) * C::NM + m) * 1024 + e * 64 + ln];
+            return v;
+        };
+        if (st0 == 0 && st1 == nst) {
+            for (int o = tid; o < C::RB * C::BP; o += 256) {
+                const int rl = o % C::RB, t = o / C::RB;
+                epi(rb * C::RB + rl, t, val(0, rl, t), C::NM > 1 ? val(C::NM - 1, rl, t) : 0.f);
+            }
+        } else {
+            // piece slot: kind 0 when the range starts inside this row block
+            // (its first piece), 1 when it ends inside it (its last piece)
+            auto slot = [&](int wg) {
+                const int kind = (T * wg / G) >= (long long)rb * nst ? 0 : 1;
+                return a.part + (size_t)(wg * 2 + kind) * C::NM * C::BP * C::RB;
+            };
+            float* mine = slot(w);
+            for (int o = tid; o < C::RB * C::BP; o += 256) {
+                const int rl = o % C::RB, t = o / C::RB;
+                if (t < a.B && rb * C::RB + rl < nrows)
+#pragma unroll
+                    for (int m = 0; m < C::NM; ++m) {
+                        if (LAST_FINISHES) st_coherent(&mine[(m * C::BP + t) * C::RB + rl], val(m, rl, t));
+                        else mine[(m * C::BP + t) * C::RB + rl] = val(m, rl, t);
+                    }
+            }
+            if (!LAST_FINISHES) {
+                __syncthreads();   // the sums are read: the ring may be loaded again
+                continue;
+            }
+            wait_own_memory();
+            __syncthreads();
+            // workgroups holding units rb*nst and (rb+1)*nst - 1
+            const int wf = (int)((((long long)rb * nst + 1) * G + T - 1) / T) - 1;
+            const int wl = (int)((((long long)(rb + 1) * nst) * G + T - 1) / T) - 1;
+            if (tid == 0) {
+                const bool last = fetch_add(&a.ctr[rb], 1u) == (uint32_t)(wl - wf);
+                if (last) st_flag(&a.ctr[rb], 0u);
+                s_last = last;
+            }
+            __syncthreads();
+            if (s_last) {
+                for (int o = tid; o < C::RB * C::BP; o += 256) {
+                    const int rl = o % C::RB, t = o / C::RB;
+                    float v0 = 0.f, v1 = 0.f;
+                    if (t < a.B && rb * C::RB + rl < nrows)
+                        for (int wg = wf; wg <= wl; ++wg) {
+                            const float* pc = slot(wg);
+                            v0 += ld_coherent(&pc[t * C::RB + rl]);
+                            if (C::NM > 1) v1 += ld_coherent(&pc[(C::BP + t) * C::RB + rl]);
+                        }
+                    epi(rb * C::RB + rl, t, v0, v1);
+                }
+            }
+        }
+        __syncthreads();   // the sums are read: the ring may be loaded again
+    }
+}
+
+// Finishes the row blocks that a ring_gemm<C, ..., false> launch of G0
+// workgroups left in pieces: one thread per (row block, token < B, row),
+// grid-stride; each sums its pieces in workgroup order, 8 loads in flight.
+template <class C, class Epi>
+__device__ __forceinline__ void ring_finish(const RingArgs& a, int nrows, int G0, Epi&& epi) {
+    const int nrb = (nrows + C::RB - 1) / C::RB;
+    const int nst = (a.K + C::KST - 1) / C::KST;
+    const long long T = (long long)nrb * nst;
+    if (T == 0) return;
+    const int G = (int)min((long long)G0, T);
+    const long long total = (long long)nrb * a.B * C::RB;
+    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (long long)gridDim.x * blockDim.x) {
+        const int rb = (int)(e / ((long long)a.B * C::RB));
+        const int rem = (int)(e % ((long long)a.B * C::RB));
+        const int t = rem / C::RB, rl = rem % C::RB;
+        const int wf = (int)((((long long)rb * nst + 1) * G + T - 1) / T) - 1;
+        const int wl = (int)((((long long)(rb + 1) * nst) * G + T - 1) / T) - 1;
+        if (wf == wl || rb * C::RB + rl >= nrows) continue;   // finished in place, or past the rows
+        auto piece = [&](int wg, int m) {
+            const int kind = (T * wg / G) >= (long long)rb * nst ? 0 : 1;
+            return a.part[(size_t)(wg * 2 + kind) * C::NM * C::BP * C::RB + (m * C::BP + t) * C::RB + rl];
+        };
+        float v0 = 0.f, v1 = 0.f;
+        for (int w0 = wf; w0 <= wl; w0 += 8) {
+            float x0[8], x1[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int wg = min(w0 + j, wl);
+                x0[j] = piece(wg, 0);
+                x1[j] = C::NM > 1 ? piece(wg, C::NM - 1) : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (w0 + j <= wl) {
+                    v0 += x0[j];
+                    v1 += x1[j];
+                }
+        }
+        epi(rb * C::RB + rl, t, v0, v1);
+    }
+}
+
+}  // namespace pi

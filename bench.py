@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--sweep", default="c4", help="config of the batch sweep ('' to skip)")
     ap.add_argument("--sweep-batches", default="1,4,8,16,32")
     ap.add_argument("--sweep-steps", type=int, default=200)
+    ap.add_argument("--sweep-only", action="store_true",
+                    help="run only the batch sweep (for a per-kernel profile of the union path)")
     ap.add_argument("--profile-run", action="store_true",
                     help="short fixed workload for hardware counters: one rotation of decode steps, "
                          "then 4 identity pi_permute_rows copies of 256 MiB (the calibration copy)")
@@ -241,6 +243,10 @@ def main():
     B.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep_only:
+        sw = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")], args.sweep_steps, 4, log)
+        print(json.dumps({"batch_sweep": sw}), flush=True)
+        return
     cfg = CONFIGS[args.config]
     kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
     NL, NT = args.layers, args.tokens
