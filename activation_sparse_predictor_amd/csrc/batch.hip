@@ -3,7 +3,7 @@
 // Part A section 4.4: the gain falls as the batch grows because the tokens'
 // active sets overlap less than fully; the union is what must be read).
 //
-//   k_union_clear / k_union_mark   per-neuron token bitmask from the lists
+//   k_union_bits                   per-token bitmaps of the lists
 //   k_union_compact                ascending union list U and |U|
 //   k_union_up      (MFMA)         A[u][t] = W_up[U_u].x_t (+ gate), bias,
 //                                  activation, zeroed where t did not select U_u
@@ -25,31 +25,66 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_union_clear(uint32_t* __restrict__ tmask, size_t n,
-                                                     uint32_t* __restrict__ ctr, uint32_t* __restrict__ upctr,
-                                                     int nup) {
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) tmask[i] = 0u;
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < nup; i += gridDim.x * 256) upctr[i] = 0u;
-    if (blockIdx.x == 0 && threadIdx.x <= kArriveGroups) ctr[threadIdx.x * kCtrStride] = 0u;
-}
-
-// tmask[i * W + t / 32] has bit t % 32 set when token t selected neuron i.
-__global__ __launch_bounds__(256) void k_union_mark(const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ count, int ffn, int W,
-                                                    uint32_t* __restrict__ tmask) {
-    const int t = blockIdx.y;
+// Per-token bitmaps of the lists: tokbits[t][w] bit k = token t selected
+// neuron 32w + k.  Every word is written, so no clearing pass is needed: the
+// lists are strictly ascending, so the entries of one word form a run; the
+// run's first entry ORs the run's bits (a segmented OR over the wave, then
+// the entries past the wave's end, at most 31) and writes the word, and also
+// zeroes the words strictly between the previous entry's word and its own;
+// the words before the first entry's word and after the last one's are
+// zeroed grid-wide.  Workgroups of token 0 also zero the arrival counters
+// of the compaction and of the up GEMM's row blocks.
+__global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ count, int ffn, int nw,
+                                                    uint32_t* __restrict__ tokbits, uint32_t* __restrict__ ctr,
+                                                    uint32_t* __restrict__ upctr, int nup) {
+    const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    const int stride = gridDim.x * 256;
+    if (t == 0) {
+        for (int i = blockIdx.x * 256 + tid; i < nup; i += stride) upctr[i] = 0u;
+        if (blockIdx.x == 0 && tid <= kArriveGroups) ctr[tid * kCtrStride] = 0u;
+    }
     const int cnt = clampi(count[t], 0, ffn);
-    for (int j = blockIdx.x * 256 + threadIdx.x; j < cnt; j += gridDim.x * 256) {
-        const int i = clampi(idx[(size_t)t * ffn + j], 0, ffn - 1);
-        atomicOr(&tmask[(size_t)i * W + (t >> 5)], 1u << (t & 31));
+    const int32_t* lst = idx + (size_t)t * ffn;
+    uint32_t* out = tokbits + (size_t)t * nw;
+    const int wfirst = cnt > 0 ? lst[0] >> 5 : nw;
+    const int wlast = cnt > 0 ? lst[cnt - 1] >> 5 : -1;
+    for (int w = blockIdx.x * 256 + tid; w < nw; w += stride)
+        if (w < wfirst || w > wlast) out[w] = 0u;
+    for (int j0 = blockIdx.x * 256 + (tid & ~63); j0 < cnt; j0 += stride) {   // whole waves
+        const int j = j0 + lane;
+        const bool in = j < cnt;
+        const int i = in ? lst[j] : 0;
+        const int w = in ? (i >> 5) : -1 - lane;   // lanes past the list match no one
+        uint32_t bits = in ? (1u << (i & 31)) : 0u;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {   // OR of this lane's entry and the rest of its run in the wave
+            const uint32_t ob = __shfl_down(bits, off, 64);
+            const int ow = __shfl_down(w, off, 64);
+            if (lane + off < 64 && ow == w) bits |= ob;
+        }
+        const int wup = __shfl_up(w, 1, 64);
+        const int w63 = __shfl(w, 63, 64);
+        if (!in) continue;
+        const int wprev = j == 0 ? -1 : (lane == 0 ? lst[j - 1] >> 5 : wup);
+        if (wprev == w) continue;   // not the first entry of its word
+        if (w63 == w)               // the run goes on past this wave
+            for (int jj = j0 + 64; jj < cnt; ++jj) {
+                const int ii = lst[jj];
+                if ((ii >> 5) != w) break;
+                bits |= 1u << (ii & 31);
+            }
+        out[w] = bits;
+        for (int g = max(wprev + 1, wfirst); g < w; ++g) out[g] = 0u;
     }
 }
 
 // Union compaction: each wave turns 64 neurons into one bitmap (any token
-// selected the neuron), published with a coherent store; workgroups arrive on
-// a two-level counter and the last one scans the bitmaps in neuron order and
-// writes the ascending union list and |U|.
-__global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restrict__ tmask, int ffn, int W,
+// selected the neuron: lane l ORs token l's two words, then the wave ORs the
+// lanes), published with a coherent store; workgroups arrive on a two-level
+// counter and the last one scans the bitmaps in neuron order and writes the
+// ascending union list and |U|.
+__global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restrict__ tokbits, int ffn, int nw, int B,
                                                        uint64_t* __restrict__ umasks,
                                                        uint32_t* __restrict__ ctr,
                                                        int32_t* __restrict__ ulist,
@@ -60,11 +95,14 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
     const int ntiles = (ffn + 63) / 64;
     const int tile = blockIdx.x * 4 + wave;
     if (tile < ntiles) {
-        const int i = tile * 64 + lane;
-        bool sel = false;
-        if (i < ffn)
-            for (int w = 0; w < W; ++w) sel = sel || tmask[(size_t)i * W + w] != 0u;
-        const uint64_t m = __ballot(sel);
+        uint64_t m = 0;
+        for (int t = lane; t < B; t += 64) {
+            const uint32_t lo = tokbits[(size_t)t * nw + 2 * tile];
+            const uint32_t hi = 2 * tile + 1 < nw ? tokbits[(size_t)t * nw + 2 * tile + 1] : 0u;
+            m |= lo | ((uint64_t)hi << 32);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m |= __shfl_xor(m, off, 64);
         if (lane == 0) __hip_atomic_store(&umasks[tile], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_own_memory();
@@ -138,7 +176,7 @@ template <bool REGLU, int XG> using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, 1, rin
 template <class C, bool REGLU>
 __global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __restrict__ ucount, int ffn,
                                                   const float* __restrict__ bup, const float* __restrict__ bg,
-                                                  const uint32_t* __restrict__ tmask, int W, int Bp, int lda,
+                                                  const uint32_t* __restrict__ tokbits, int nw, int Bp, int lda,
                                                   h16* __restrict__ a_hi, h16* __restrict__ a_lo) {
     __shared__ __align__(16) char lds[C::LDS];
     const int U = (int)min(*ucount, (uint32_t)ffn), B = a.B;
@@ -153,7 +191,7 @@ __global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __
         }
         float av = 0.f;
         const int nrow = ulist[uu];
-        if (t < B && ((tmask[(size_t)nrow * W + (t >> 5)] >> (t & 31)) & 1u)) {
+        if (t < B && ((tokbits[(size_t)t * nw + (nrow >> 5)] >> (nrow & 31)) & 1u)) {
             const float uval = vu + (bup ? bup[nrow] : 0.f);
             av = REGLU ? fmaxf(vg + (bg ? bg[nrow] : 0.f), 0.f) * uval : fmaxf(uval, 0.f);
         }
@@ -283,7 +321,8 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 // step, the A operand of v_mfma_f32_32x32x16_f16 (columns x entries); the B
 // operand is 16 bytes of A[t][.] per lane.  Wave w owns columns 32w..32w+31
 // of the tile for every token.  Chunk partials go to the workspace and
-// k_union_reduce adds them in chunk order.
+// k_union_reduce adds them in chunk order (a kernel of its own: the sums of
+// a tile's chunks spread over the whole device instead of one workgroup).
 constexpr int kDnCols = 128;
 constexpr int kDnIds = 4096;   // union entries per chunk staged in LDS (G is sized for it)
 
@@ -301,18 +340,12 @@ struct DownCfg {
     static_assert(WBLK % 4 == 0 && IPW * (NS - 2) < 64, "loads per stage");
 };
 
-__device__ __forceinline__ f16x4 lds_read8_tr(uint32_t addr) {
-    f16x4 v;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ f16x4 lds_read8_tr(const char* p) {
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_char*)p));
 }
-__device__ __forceinline__ void lds_ready4(f16x4& v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ int lds_read_i32(uint32_t addr) {
-    int v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
-}
-__device__ __forceinline__ void lds_ready_i(int& v) { asm volatile("" : "+v"(v)); }
 
 template <class C>
 __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, int d, int ffn,
@@ -345,7 +378,6 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     }
     __syncthreads();
     const uint32_t lbase = (uint32_t)(size_t)(lds_void_ptr)lds;
-    const uint32_t ibase = (uint32_t)(size_t)(lds_void_ptr)s_ids;
 
     // this thread's loads: block b = wave + 4i; weight blocks first (WBLK is a
     // multiple of 4, so block i is a weight block exactly when i < WBLK / 4)
@@ -373,11 +405,8 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     auto issue = [&](int st, int q) {
         int id[C::WBLK / 4];
 #pragma unroll
-        for (int i = 0; i < C::WBLK / 4; ++i) id[i] = lds_read_i32(ibase + 4 * min(st * C::KR + wofs[i], kDnIds - 1));
-        lds_wait();
-#pragma unroll
-        for (int i = 0; i < C::WBLK / 4; ++i) lds_ready_i(id[i]);
-        char* dst = lds + q * C::STAGE;
+        for (int i = 0; i < C::WBLK / 4; ++i) id[i] = s_ids[min(st * C::KR + wofs[i], kDnIds - 1)];
+        const uint32_t dst = lbase + q * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i) {
             const h16* p;
@@ -388,7 +417,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
                 const int e = st * C::KR + kofs[i];
                 p = (abase[i] && e < n_ids) ? abase[i] + u0 + e : zsrc;
             }
-            __builtin_amdgcn_global_load_lds(p, (lds_void_ptr)(dst + (wave + 4 * i) * 1024), 16, 0, 0);
+            dma16(p, dst + (wave + 4 * i) * 1024);
         }
     };
 
@@ -408,13 +437,13 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
         else wait_vm<0>();
         ring_barrier();
         if (s + C::NS - 1 < n) issue(s + C::NS - 1, (s + C::NS - 1) % C::NS);
-        const uint32_t buf = lbase + (s % C::NS) * C::STAGE;
+        const char* buf = lds + (s % C::NS) * C::STAGE;
         f16x4 w0[C::KR / 16], w1[C::KR / 16];
         f16x8 av[C::KR / 16][C::NB][2];
 #pragma unroll
         for (int q = 0; q < C::KR / 16; ++q) {
             const int rg = 2 * q + kh;   // row group of this lane half's 8 entries
-            const uint32_t wb = buf + (rg * (kDnCols / 64) + cs) * 1024 + ((ch ^ (rg & 7)) << 7) + quad * 8;
+            const char* wb = buf + (rg * (kDnCols / 64) + cs) * 1024 + ((ch ^ (rg & 7)) << 7) + quad * 8;
             w0[q] = lds_read8_tr(wb + (j >> 2) * 16);
             w1[q] = lds_read8_tr(wb + ((j >> 2) + 4) * 16);
             const int c = 2 * q + kh;    // activation chunk (8 entries)
@@ -424,19 +453,8 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
 #pragma unroll
                 for (int ix = 0; ix < 2; ++ix) {
                     const int blk = C::WBLK + ix * C::XG + tg;
-                    av[q][nb][ix] = lds_read16(buf + blk * 1024 + ((c ^ (tg & 3)) << 7) + ((t & 7) << 4));
+                    av[q][nb][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + ((c ^ (tg & 3)) << 7) + ((t & 7) << 4));
                 }
-            }
-        }
-        lds_wait();
-#pragma unroll
-        for (int q = 0; q < C::KR / 16; ++q) {
-            lds_ready4(w0[q]);
-            lds_ready4(w1[q]);
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
-                lds_ready(av[q][nb][0]);
-                lds_ready(av[q][nb][1]);
             }
         }
 #pragma unroll
@@ -506,7 +524,7 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
                         char* ws, char* hdr, hipStream_t s) {
-    uint32_t* tmask = reinterpret_cast<uint32_t*>(ws + L.tmask);
+    uint32_t* tokbits = reinterpret_cast<uint32_t*>(ws + L.tokbits);
     uint64_t* umasks = reinterpret_cast<uint64_t*>(ws + L.umasks);
     int32_t* ulist = reinterpret_cast<int32_t*>(ws + L.ulist);
     uint32_t* ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
@@ -515,16 +533,13 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
     float* partial = reinterpret_cast<float*>(ws + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + L.ctr);
     uint32_t* upctr = reinterpret_cast<uint32_t*>(ws + L.upctr);
-    const size_t nmask = (size_t)ffn * L.W;
-    int gclear = (int)((nmask + 255) / 256);
-    if (gclear > 2048) gclear = 2048;
-    hipLaunchKernelGGL(k_union_clear, dim3(gclear), dim3(256), 0, s, tmask, nmask, ctr, upctr,
+    const int nw = (ffn + 31) / 32;
+    int gb = (ffn + 1023) / 1024;
+    if (gb > 16) gb = 16;
+    hipLaunchKernelGGL(k_union_bits, dim3(gb, B), dim3(256), 0, s, idx, count, ffn, nw, tokbits, ctr, upctr,
                        (ffn + kRingRows - 1) / kRingRows);
-    int gm = (ffn + 255) / 256;
-    if (gm > 64) gm = 64;
-    hipLaunchKernelGGL(k_union_mark, dim3(gm, B), dim3(256), 0, s, idx, count, ffn, L.W, tmask);
     const int ntiles = (ffn + 63) / 64;
-    hipLaunchKernelGGL(k_union_compact, dim3((ntiles + 3) / 4), dim3(256), 0, s, tmask, ffn, L.W, umasks,
+    hipLaunchKernelGGL(k_union_compact, dim3((ntiles + 3) / 4), dim3(256), 0, s, tokbits, ffn, nw, B, umasks,
                        ctr, ulist, ucount);
     RingArgs ra{};
     ra.W[0] = Wup;
@@ -541,7 +556,7 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
     ra.ctr = upctr;
 #define PI_UP(R, N)                                                                                        \
     hipLaunchKernelGGL((k_union_up<UpCfg<R, N>, R>), dim3(ring_grid<k_union_up<UpCfg<R, N>, R>>()), dim3(256), \
-                       0, s, ra, ucount, ffn, bup, bg, tmask, L.W, L.Bp, L.lda, a_hi, a_lo)
+                       0, s, ra, ucount, ffn, bup, bg, tokbits, nw, L.Bp, L.lda, a_hi, a_lo)
 #define PI_DN(X)                                                                                        \
     hipLaunchKernelGGL((k_union_down<DownCfg<X>>), dim3(L.T, L.G), dim3(256), 0, s, Wd, d, ffn, ulist, ucount, \
                        a_hi, a_lo, B, L.Bp, L.lda, partial, L.G, ra.zsrc)

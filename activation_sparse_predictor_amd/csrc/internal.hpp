@@ -67,13 +67,13 @@ constexpr int kRingRows = 32;
 inline int ring_slots(int B) { return B <= 32 ? 32 : (B <= 64 ? 64 : 128); }
 inline size_t ring_piece_bytes(int nm, int B) { return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * kRingRows * 4; }
 struct BatchLayout {
-    size_t tmask;    // ffn x W uint32 per-neuron token masks
+    size_t tokbits;  // B x ceil(ffn/32) uint32 per-token bitmaps of the lists
     size_t umasks;   // tiles uint64 union bitmaps
     size_t ulist;    // ffn int32 ascending union list
     size_t ucount;   // uint32 |U|
     size_t a_hi;     // Bp x lda fp16 activations, high part
     size_t a_lo;     // Bp x lda fp16 activations, low part
-    size_t partial;  // G x Bp x d fp32 split-K partials of the down GEMM
+    size_t partial;  // G x Bp x d fp32 chunk partials of the down GEMM
     size_t ctr;      // kCtrWords uint32 arrival counters
     size_t upctr;    // ceil(ffn/64) uint32 row-block counters of the up GEMM
     size_t upart;    // pieces of the up GEMM (two matrices for ReGLU)
@@ -90,8 +90,8 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
     L.G = (ffn + 4087) / 4088;   // chunks of at most 4088 union entries
     if (L.G < 8) L.G = 8;
     const size_t tiles = (size_t)(ffn + 63) / 64;
-    L.tmask = 0;
-    L.umasks = L.tmask + align256((size_t)ffn * L.W * 4);
+    L.tokbits = 0;
+    L.umasks = L.tokbits + align256((size_t)B * ((ffn + 31) / 32) * 4);
     L.ulist = L.umasks + align256(tiles * 8);
     L.ucount = L.ulist + align256((size_t)ffn * 4);
     L.a_hi = L.ucount + 256;

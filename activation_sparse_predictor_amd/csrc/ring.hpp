@@ -70,19 +70,16 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// LDS reads issued as inline assembly.  With a direct-to-LDS load in flight
-// the compiler makes every LDS read it knows of wait for all outstanding
-// vector-memory loads (it cannot tell which LDS bytes the load writes), which
-// would drain the ring at every stage; these reads are ordered by the ring's
-// own waits and barriers instead.  lds_wait() waits for all of them and
-// lds_ready(v) marks v as produced after that wait.
-__device__ __forceinline__ f16x8 lds_read16(uint32_t addr) {
-    f16x8 v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+// Direct-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4: lane l's
+// bytes land at lds_addr + 16 l; lds_addr is wave-uniform, it goes to M0),
+// issued as inline assembly.  Were the compiler to see it, it would make every
+// LDS read wait for all outstanding vector-memory loads (it cannot tell which
+// LDS bytes the load writes), draining the ring at every stage; the ring's
+// own waits and barriers order these loads and the reads instead.  (A load
+// the compiler does not count can only make its own waits stricter.)
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_addr), "v"(gptr) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void lds_ready(f16x8& v) { asm volatile("" : "+v"(v)); }
 
 template <int NM_, int NX_, int XG_, int RBW_, int SEG_, int NS_>
 struct RingCfg {
@@ -186,12 +183,12 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
             }
         }
         auto issue = [&](int st, int q) {
-            char* dst = lds + q * C::STAGE;
+            const uint32_t dst = lbase + q * C::STAGE;
 #pragma unroll
             for (int i = 0; i < C::IPW; ++i) {
                 const int k = st * C::KST + kofs[i];
                 const h16* p = (ok[i] && k < a.K) ? src[i] + k : a.zsrc;
-                __builtin_amdgcn_global_load_lds(p, (lds_void_ptr)(dst + (wave + 4 * i) * 1024), 16, 0, 0);
+                dma16(p, dst + (wave + 4 * i) * 1024);
             }
         };
 
@@ -210,7 +207,7 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
             else wait_vm<0>();
             ring_barrier();   // stage s is in LDS; every wave is done with stage s - 1
             if (s + C::NS - 1 < n) issue(st0 + s + C::NS - 1, (s + C::NS - 1) % C::NS);
-            const uint32_t buf = lbase + (s % C::NS) * C::STAGE;
+            const char* buf = lds + (s % C::NS) * C::STAGE;
             f16x8 xv[C::NPW][C::NX], wv[C::NPW][C::RBW][C::NM];
 #pragma unroll
             for (int j = 0; j < C::NPW; ++j) {
@@ -220,7 +217,7 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
                 for (int ix = 0; ix < C::NX; ++ix) {
                     const int blk = C::WBLK + (ix * C::XG + tg) * C::SEG + sg;
-                    xv[j][ix] = lds_read16(buf + blk * 1024 + ((cc ^ (tg & 3)) << 7) + ((t & 7) << 4));
+                    xv[j][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + ((cc ^ (tg & 3)) << 7) + ((t & 7) << 4));
                 }
 #pragma unroll
                 for (int rr = 0; rr < C::RBW; ++rr) {
@@ -228,19 +225,9 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
                     for (int m = 0; m < C::NM; ++m) {
                         const int blk = (m * (C::RB / 8) + g) * C::SEG + sg;
-                        wv[j][rr][m] = lds_read16(buf + blk * 1024 + ((cc ^ (g & 3)) << 7) + ((rl & 7) << 4));
+                        wv[j][rr][m] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + ((cc ^ (g & 3)) << 7) + ((rl & 7) << 4));
                     }
                 }
-            }
-            lds_wait();
-#pragma unroll
-            for (int j = 0; j < C::NPW; ++j) {
-#pragma unroll
-                for (int ix = 0; ix < C::NX; ++ix) lds_ready(xv[j][ix]);
-#pragma unroll
-                for (int rr = 0; rr < C::RBW; ++rr)
-#pragma unroll
-                    for (int m = 0; m < C::NM; ++m) lds_ready(wv[j][rr][m]);
             }
 #pragma unroll
             for (int j = 0; j < C::NPW; ++j)
@@ -312,10 +299,20 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
                     const int rl = o % C::RB, t = o / C::RB;
                     float v0 = 0.f, v1 = 0.f;
                     if (t < a.B && rb * C::RB + rl < nrows)
-                        for (int wg = wf; wg <= wl; ++wg) {
-                            const float* pc = slot(wg);
-                            v0 += ld_coherent(&pc[t * C::RB + rl]);
-                            if (C::NM > 1) v1 += ld_coherent(&pc[(C::BP + t) * C::RB + rl]);
+                        for (int w0 = wf; w0 <= wl; w0 += 4) {   // pieces in order, 4 at a time in flight
+                            float x0[4], x1[4];
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) {
+                                const float* pc = slot(min(w0 + k, wl));
+                                x0[k] = ld_coherent(&pc[t * C::RB + rl]);
+                                x1[k] = C::NM > 1 ? ld_coherent(&pc[(C::BP + t) * C::RB + rl]) : 0.f;
+                            }
+#pragma unroll
+                            for (int k = 0; k < 4; ++k)
+                                if (w0 + k <= wl) {
+                                    v0 += x0[k];
+                                    v1 += x1[k];
+                                }
                         }
                     epi(rb * C::RB + rl, t, v0, v1);
                 }

@@ -183,13 +183,17 @@ def test_batched_union_path(kind, Bt):
 
 
 def test_union_path_edge_lists():
-    """Empty lists, disjoint lists, identical lists and one full list in one batch."""
+    """Empty lists, disjoint lists, identical lists, one full list, a list whose
+    32-neuron words run across the 64-entry waves that build the token
+    bitmaps, and one with a long gap, in one batch."""
     cfg = custom_config("reglu", 1032, 1000, 16, mean=0.3, number=60)
     L = R.to_device(make_layer(cfg), DEV)
     H = _host(L)
-    Bt, ffn = 6, cfg.ffn
+    ffn = cfg.ffn
+    lists = [[], list(range(0, ffn, 2)), list(range(1, ffn, 2)), list(range(0, ffn, 2)), list(range(ffn)), [ffn - 1],
+             list(range(0, 41)) + list(range(100, 300)) + list(range(500, 503)), [3, 600, 601, ffn - 2]]
+    Bt = len(lists)
     X = make_tokens(cfg, Bt).to(DEV)
-    lists = [[], list(range(0, ffn, 2)), list(range(1, ffn, 2)), list(range(0, ffn, 2)), list(range(ffn)), [ffn - 1]]
     idx = torch.zeros(Bt, ffn, dtype=torch.int32, device=DEV)
     for t, l in enumerate(lists):
         if l:
