@@ -32,17 +32,17 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 // the entries past the wave's end, at most 31) and writes the word, and also
 // zeroes the words strictly between the previous entry's word and its own;
 // the words before the first entry's word and after the last one's are
-// zeroed grid-wide.  Workgroups of token 0 also zero the arrival counters
-// of the compaction and of the up GEMM's row blocks.
+// zeroed grid-wide.  Workgroups of token 0 also zero the compaction's count
+// slots and the arrival counters of the up GEMM's row blocks.
 __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ count, int ffn, int nw,
-                                                    uint32_t* __restrict__ tokbits, uint32_t* __restrict__ ctr,
-                                                    uint32_t* __restrict__ upctr, int nup) {
+                                                    uint32_t* __restrict__ tokbits, uint64_t* __restrict__ slots,
+                                                    int nslots, uint32_t* __restrict__ upctr, int nup) {
     const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const int stride = gridDim.x * 256;
     if (t == 0) {
         for (int i = blockIdx.x * 256 + tid; i < nup; i += stride) upctr[i] = 0u;
-        if (blockIdx.x == 0 && tid <= kArriveGroups) ctr[tid * kCtrStride] = 0u;
+        for (int i = blockIdx.x * 256 + tid; i < nslots; i += stride) slots[i] = 0ull;
     }
     const int cnt = clampi(count[t], 0, ffn);
     const int32_t* lst = idx + (size_t)t * ffn;
@@ -79,22 +79,37 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
     }
 }
 
-// Union compaction: each wave turns 64 neurons into one bitmap (any token
-// selected the neuron: lane l ORs token l's two words, then the wave ORs the
-// lanes), published with a coherent store; workgroups arrive on a two-level
-// counter and the last one scans the bitmaps in neuron order and writes the
-// ascending union list and |U|.
+// Union compaction in one pass.  Workgroup g of G (at most kCompactWG, all
+// resident at once) owns a contiguous range of 64-neuron tiles; each wave ORs
+// the tokens' words of its tiles (lane l takes token l) into the tiles'
+// union bitmaps, kept in LDS.  The workgroup publishes its count as one
+// tagged 64-bit word {1, count} (the slots are zeroed by k_union_bits), sums
+// the counts of workgroups 0..g-1 as they appear (a bounded wait: every
+// workgroup publishes before it waits, so the wait ends), and writes its own
+// entries of the ascending union list in parallel, each lane its neuron at
+// its rank.  The last workgroup writes |U|.  A wait that overruns counts the
+// missing workgroup as empty and marks its slot: the list is then short but
+// stays in bounds, and |U| is written as 0.
+constexpr int kCompactWG = 256;
+constexpr int kCompactTiles = 1024;   // tiles per workgroup held in LDS
+constexpr int kCompactWait = 1 << 16;
+
 __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restrict__ tokbits, int ffn, int nw, int B,
-                                                       uint64_t* __restrict__ umasks,
-                                                       uint32_t* __restrict__ ctr,
+                                                       uint64_t* __restrict__ slots,
                                                        int32_t* __restrict__ ulist,
                                                        uint32_t* __restrict__ ucount) {
-    __shared__ uint32_t s_part[4];
-    __shared__ int s_last;
+    __shared__ uint64_t s_m[kCompactTiles];
+    __shared__ uint32_t s_wcnt[4];
+    __shared__ uint32_t s_base, s_err;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ntiles = (ffn + 63) / 64;
-    const int tile = blockIdx.x * 4 + wave;
-    if (tile < ntiles) {
+    const int G = gridDim.x, g = blockIdx.x;
+    const int t0 = (int)((long long)ntiles * g / G), t1 = (int)((long long)ntiles * (g + 1) / G);
+    const int tw = (t1 - t0 + 3) / 4;   // tiles per wave
+    uint32_t cnt = 0;
+    for (int k = 0; k < tw; ++k) {
+        const int tl = wave * tw + k, tile = t0 + tl;
+        if (tile >= t1) break;
         uint64_t m = 0;
         for (int t = lane; t < B; t += 64) {
             const uint32_t lo = tokbits[(size_t)t * nw + 2 * tile];
@@ -103,57 +118,54 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m |= __shfl_xor(m, off, 64);
-        if (lane == 0) __hip_atomic_store(&umasks[tile], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) s_m[tl] = m;
+        cnt += (uint32_t)__popcll(m);
     }
-    wait_own_memory();
+    if (lane == 0) s_wcnt[wave] = cnt;
+    if (tid == 0) s_err = 0u;
     __syncthreads();
-    if (tid == 0) {
-        const int nwg = gridDim.x;
-        const int g = blockIdx.x % kArriveGroups;
-        const uint32_t n1 = (uint32_t)((nwg - g + kArriveGroups - 1) / kArriveGroups);
-        const uint32_t groups = (uint32_t)min(nwg, kArriveGroups);
-        bool last = false;
-        if (fetch_add(&ctr[g * kCtrStride], 1u) == n1 - 1u)
-            last = fetch_add(&ctr[kArriveGroups * kCtrStride], 1u) == groups - 1u;
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    uint32_t base = 0;
-    for (int t0 = 0; t0 < ntiles; t0 += 1024) {
-        uint64_t m4[4];
-        uint32_t mine = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t = t0 + tid * 4 + q;
-            m4[q] = t < ntiles ? __hip_atomic_load(&umasks[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-            mine += (uint32_t)__popcll(m4[q]);
-        }
-        uint32_t incl = mine;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        if (lane == 63) s_part[wave] = incl;
-        __syncthreads();
-        uint32_t pos = base + incl - mine;
-        for (int w2 = 0; w2 < wave; ++w2) pos += s_part[w2];
-        const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            uint64_t m = m4[q];
-            const int t = t0 + tid * 4 + q;
-            while (m) {
-                ulist[pos++] = t * 64 + __builtin_ctzll(m);
-                m &= m - 1;
+    const uint32_t total = s_wcnt[0] + s_wcnt[1] + s_wcnt[2] + s_wcnt[3];
+    if (tid == 0) __hip_atomic_store(&slots[g], (1ull << 32) | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0) {
+        uint32_t sum = 0, err = 0;
+        for (int j0 = 0; j0 < g; j0 += 64) {
+            const int j = j0 + lane;
+            if (j < g) {
+                uint64_t v = __hip_atomic_load(&slots[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int n = 0; (v >> 32) == 0u; ++n) {
+                    if (n == kCompactWait) {
+                        v = 2ull << 32;   // give up: counted as empty, marked as an error
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    v = __hip_atomic_load(&slots[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                sum += (uint32_t)v;
+                err |= (uint32_t)(v >> 32) & 2u;
             }
         }
-        base += total;
-        __syncthreads();
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            sum += __shfl_xor(sum, off, 64);
+            err |= __shfl_xor(err, off, 64);
+        }
+        if (lane == 0) {
+            s_base = sum;
+            s_err = err;
+        }
     }
-    if (tid == 0) *ucount = base;
-    if (tid <= kArriveGroups) st_flag(&ctr[tid * kCtrStride], 0u);
+    __syncthreads();
+    uint32_t pos = s_base;
+    for (int w2 = 0; w2 < wave; ++w2) pos += s_wcnt[w2];
+    for (int k = 0; k < tw; ++k) {
+        const int tl = wave * tw + k, tile = t0 + tl;
+        if (tile >= t1) break;
+        const uint64_t m = s_m[tl];
+        if ((m >> lane) & 1ull) ulist[pos + rank_below(m)] = tile * 64 + lane;
+        pos += (uint32_t)__popcll(m);
+    }
+    if (g == G - 1 && tid == 0) *ucount = s_err ? 0u : s_base + total;
+    if (s_err && tid == 0) __hip_atomic_store(&slots[g], (3ull << 32) | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -405,7 +417,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     auto issue = [&](int st, int q) {
         int id[C::WBLK / 4];
 #pragma unroll
-        for (int i = 0; i < C::WBLK / 4; ++i) id[i] = s_ids[min(st * C::KR + wofs[i], kDnIds - 1)];
+        for (int i = 0; i < C::WBLK / 4; ++i) id[i] = clampi(s_ids[min(st * C::KR + wofs[i], kDnIds - 1)], 0, ffn - 1);
         const uint32_t dst = lbase + q * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i) {
@@ -531,21 +543,22 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
     h16* a_hi = reinterpret_cast<h16*>(ws + L.a_hi);
     h16* a_lo = reinterpret_cast<h16*>(ws + L.a_lo);
     float* partial = reinterpret_cast<float*>(ws + L.partial);
-    uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + L.ctr);
     uint32_t* upctr = reinterpret_cast<uint32_t*>(ws + L.upctr);
     const int nw = (ffn + 31) / 32;
     int gb = (ffn + 1023) / 1024;
     if (gb > 16) gb = 16;
-    hipLaunchKernelGGL(k_union_bits, dim3(gb, B), dim3(256), 0, s, idx, count, ffn, nw, tokbits, ctr, upctr,
-                       (ffn + kRingRows - 1) / kRingRows);
     const int ntiles = (ffn + 63) / 64;
-    hipLaunchKernelGGL(k_union_compact, dim3((ntiles + 3) / 4), dim3(256), 0, s, tokbits, ffn, nw, B, umasks,
-                       ctr, ulist, ucount);
+    int gc = (ntiles + 3) / 4;   // a tile per wave, up to kCompactWG workgroups
+    if (gc > kCompactWG) gc = kCompactWG;
+    hipLaunchKernelGGL(k_union_bits, dim3(gb, B), dim3(256), 0, s, idx, count, ffn, nw, tokbits, umasks, gc, upctr,
+                       (ffn + kRingRows - 1) / kRingRows);
+    hipLaunchKernelGGL(k_union_compact, dim3(gc), dim3(256), 0, s, tokbits, ffn, nw, B, umasks, ulist, ucount);
     RingArgs ra{};
     ra.W[0] = Wup;
     ra.W[1] = Wg;
     ra.ldw = d;
     ra.rowlist = ulist;
+    ra.wrows = ffn;
     ra.nrows = 0;   // |U|, read on the device
     ra.X[0] = x;
     ra.ldx = d;

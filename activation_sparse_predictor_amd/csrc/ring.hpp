@@ -106,6 +106,7 @@ struct RingArgs {
     const h16* W[2];          // NM weight matrices, row stride ldw halves
     int ldw;
     const int32_t* rowlist;   // row ids of the list (gathering kernels only)
+    int wrows;                // rows of W (a gathered id is clamped to them)
     int nrows;                // list length
     const h16* X[2];          // NX activation arrays [token][ldx]
     int ldx;
@@ -168,7 +169,7 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
                 const int m = b / ((C::RB / 8) * C::SEG), rem = b % ((C::RB / 8) * C::SEG);
                 const int g = rem / C::SEG, sg = rem % C::SEG;
                 const int row = min(rb * C::RB + g * 8 + (lane & 7), nrows - 1);
-                const int id = GATHER ? a.rowlist[row] : row;
+                const int id = GATHER ? min(max(a.rowlist[row], 0), a.wrows - 1) : row;
                 src[i] = (m == 0 ? a.W[0] : a.W[1]) + (size_t)id * a.ldw;
                 kofs[i] = sg * 64 + (((lane >> 3) ^ (g & 3)) << 3);
                 ok[i] = true;
