@@ -170,15 +170,19 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
 
 // ---------------------------------------------------------------------------
 // Skinny GEMMs of the batched path (rows x tokens on the matrix cores, see
-// ring.hpp), by XG = 8-token groups loaded: 32-row blocks and a ring of three
-// stages of 512-byte row segments, or 256 or 128 where three stages of the
-// larger ones would not fit in LDS.
-constexpr int ring_seg(int nm, int nx, int xg) {
-    return 3 * (nm * 4 + nx * xg) * 4 <= 156 ? 4 : (3 * (nm * 4 + nx * xg) * 2 <= 156 ? 2 : 1);
+// ring.hpp), by XG = 8-token groups loaded: a ring of three stages of
+// 512-byte row segments, or 256 or 128 where three stages of the larger ones
+// would not fit in LDS.
+constexpr int ring_seg(int nm, int nx, int xg, int rbw) {
+    return 3 * (nm * 4 * rbw + nx * xg) * 4 <= 156 ? 4 : (3 * (nm * 4 * rbw + nx * xg) * 2 <= 156 ? 2 : 1);
 }
-template <int XG> using HidCfg = RingCfg<1, 1, XG, 1, ring_seg(1, 1, XG), 3>;
-template <int XG> using LogCfg = RingCfg<1, 2, XG, 1, ring_seg(1, 2, XG), 3>;
-template <bool REGLU, int XG> using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, 1, ring_seg(REGLU ? 2 : 1, 1, XG), 3>;
+// With 64 or 128 tokens the row block grows to 64 or 128 rows, to keep the
+// activation bytes per weight byte of a stage down.
+constexpr int ring_rbw(int xg) { return xg <= 4 ? 1 : xg / 4; }
+template <int XG> using HidCfg = RingCfg<1, 1, XG, ring_rbw(XG), ring_seg(1, 1, XG, ring_rbw(XG)), 3>;
+template <int XG> using LogCfg = RingCfg<1, 2, XG, ring_rbw(XG), ring_seg(1, 2, XG, ring_rbw(XG)), 3>;
+template <bool REGLU, int XG>
+using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, ring_rbw(XG), ring_seg(REGLU ? 2 : 1, 1, XG, ring_rbw(XG)), 3>;
 
 // Up GEMM over the union rows: A[u][t] = W_up[U_u] . x_t (+ the gate
 // product for ReGLU), then bias, activation and the token mask (zero where
@@ -335,15 +339,18 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 // of the tile for every token.  Chunk partials go to the workspace and
 // k_union_reduce adds them in chunk order (a kernel of its own: the sums of
 // a tile's chunks spread over the whole device instead of one workgroup).
-constexpr int kDnCols = 128;
 constexpr int kDnIds = 4096;   // union entries per chunk staged in LDS (G is sized for it)
 
+// Wave w owns CB blocks of 32 columns (the tile is 128 CB columns): with many
+// tokens, two blocks per wave halve the activation bytes per W_down byte.
 template <int XG_>
 struct DownCfg {
     static constexpr int XG = XG_;
     static constexpr int NB = (XG + 3) / 4, BP = 32 * NB;
+    static constexpr int CB = XG >= 8 ? 2 : 1;
+    static constexpr int CT = 128 * CB;                            // columns per tile
     static constexpr int KR = 64;                                  // union entries per stage
-    static constexpr int WBLK = (KR / 8) * (kDnCols / 64);         // W_down blocks per stage
+    static constexpr int WBLK = (KR / 8) * (CT / 64);              // W_down blocks per stage
     static constexpr int ABLK = 2 * XG;                            // activation blocks (hi, lo)
     static constexpr int NBLK = ((WBLK + ABLK + 3) / 4) * 4;       // padded to whole waves
     static constexpr int IPW = NBLK / 4;
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     const int u0 = min(U, chunk * per), u1 = min(U, u0 + per);
     const int n_ids = u1 - u0;
     const int n = (n_ids + C::KR - 1) / C::KR;
-    const int c0 = tile * kDnCols;
+    const int c0 = tile * C::CT;
     for (int i0 = 0; i0 < n_ids; i0 += 256 * 8) {   // 8 loads in flight per thread
         int v[8];
 #pragma unroll
@@ -400,7 +407,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     for (int i = 0; i < C::IPW; ++i) {
         const int b = wave + 4 * i;
         if (i < C::WBLK / 4) {
-            const int rg = b / (kDnCols / 64), cs = b % (kDnCols / 64);
+            const int rg = b / (C::CT / 64), cs = b % (C::CT / 64);
             wofs[i] = rg * 8 + (lane & 7);
             kofs[i] = c0 + cs * 64 + (((lane >> 3) ^ (rg & 7)) << 3);
             abase[i] = nullptr;
@@ -433,12 +440,12 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
         }
     };
 
-    f32x16 acc[C::NB];
+    f32x16 acc[C::CB][C::NB];
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) acc[nb] = f32x16{};
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) acc[cb][nb] = f32x16{};
     const int g = lane >> 4, j = lane & 15;
-    const int col = wave * 32 + 16 * (g & 1) + 4 * (j & 3);     // first of this lane's 4 columns
-    const int cs = col >> 6, ch = (col & 63) >> 3, quad = (col >> 2) & 1;
 
     wait_vm<0>();
 #pragma unroll
@@ -450,14 +457,20 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
         ring_barrier();
         if (s + C::NS - 1 < n) issue(s + C::NS - 1, (s + C::NS - 1) % C::NS);
         const char* buf = lds + (s % C::NS) * C::STAGE;
-        f16x4 w0[C::KR / 16], w1[C::KR / 16];
+        f16x4 w0[C::KR / 16][C::CB], w1[C::KR / 16][C::CB];
         f16x8 av[C::KR / 16][C::NB][2];
 #pragma unroll
         for (int q = 0; q < C::KR / 16; ++q) {
             const int rg = 2 * q + kh;   // row group of this lane half's 8 entries
-            const char* wb = buf + (rg * (kDnCols / 64) + cs) * 1024 + ((ch ^ (rg & 7)) << 7) + quad * 8;
-            w0[q] = lds_read8_tr(wb + (j >> 2) * 16);
-            w1[q] = lds_read8_tr(wb + ((j >> 2) + 4) * 16);
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) {
+                // first of this lane's 4 columns in column block cb of the wave
+                const int col = (wave * C::CB + cb) * 32 + 16 * (g & 1) + 4 * (j & 3);
+                const int cs = col >> 6, ch = (col & 63) >> 3, quad = (col >> 2) & 1;
+                const char* wb = buf + (rg * (C::CT / 64) + cs) * 1024 + ((ch ^ (rg & 7)) << 7) + quad * 8;
+                w0[q][cb] = lds_read8_tr(wb + (j >> 2) * 16);
+                w1[q][cb] = lds_read8_tr(wb + ((j >> 2) + 4) * 16);
+            }
             const int c = 2 * q + kh;    // activation chunk (8 entries)
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
@@ -470,30 +483,36 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
             }
         }
 #pragma unroll
-        for (int q = 0; q < C::KR / 16; ++q) {
-            const f16x8 a8 = {w0[q][0], w0[q][1], w0[q][2], w0[q][3], w1[q][0], w1[q][1], w1[q][2], w1[q][3]};
+        for (int q = 0; q < C::KR / 16; ++q)
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][0], acc[nb], 0, 0, 0);
-                acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][1], acc[nb], 0, 0, 0);
+            for (int cb = 0; cb < C::CB; ++cb) {
+                const f16x8 a8 = {w0[q][cb][0], w0[q][cb][1], w0[q][cb][2], w0[q][cb][3],
+                                  w1[q][cb][0], w1[q][cb][1], w1[q][cb][2], w1[q][cb][3]};
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][0], acc[cb][nb], 0, 0, 0);
+                    acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][1], acc[cb][nb], 0, 0, 0);
+                }
+            }
+    }
+    // acc[cb][nb] element e of lane l: column (wave*CB + cb)*32 + 8*(e/4) + 4*(l/32) + e%4
+    // of the tile, token nb*32 + l%32; four consecutive columns per 16-byte store
+#pragma unroll
+    for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+            const int t = nb * 32 + li;
+            if (t >= B) continue;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int cc = c0 + (wave * C::CB + cb) * 32 + 8 * e4 + 4 * kh;
+                if (cc < d) {
+                    const f32x4 v = {acc[cb][nb][4 * e4], acc[cb][nb][4 * e4 + 1], acc[cb][nb][4 * e4 + 2],
+                                     acc[cb][nb][4 * e4 + 3]};
+                    *reinterpret_cast<f32x4*>(&partial[((size_t)chunk * Bp + t) * d + cc]) = v;
+                }
             }
         }
-    }
-    // acc[nb] element e of lane l: column wave*32 + 8*(e/4) + 4*(l/32) + e%4 of the
-    // tile, token nb*32 + l%32; four consecutive columns per 16-byte store
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-        const int t = nb * 32 + li;
-        if (t >= B) continue;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-            const int cc = c0 + wave * 32 + 8 * e4 + 4 * kh;
-            if (cc < d) {
-                const f32x4 v = {acc[nb][4 * e4], acc[nb][4 * e4 + 1], acc[nb][4 * e4 + 2], acc[nb][4 * e4 + 3]};
-                *reinterpret_cast<f32x4*>(&partial[((size_t)chunk * Bp + t) * d + cc]) = v;
-            }
-        }
-    }
 }
 
 // y[t][c] = sum over chunks g (in order) of partial[g][t][c]: one output per
@@ -571,7 +590,8 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
     hipLaunchKernelGGL((k_union_up<UpCfg<R, N>, R>), dim3(ring_grid<k_union_up<UpCfg<R, N>, R>>()), dim3(256), \
                        0, s, ra, ucount, ffn, bup, bg, tokbits, nw, L.Bp, L.lda, a_hi, a_lo)
 #define PI_DN(X)                                                                                        \
-    hipLaunchKernelGGL((k_union_down<DownCfg<X>>), dim3(L.T, L.G), dim3(256), 0, s, Wd, d, ffn, ulist, ucount, \
+    hipLaunchKernelGGL((k_union_down<DownCfg<X>>), dim3((d + DownCfg<X>::CT - 1) / DownCfg<X>::CT, L.G), dim3(256), \
+                       0, s, Wd, d, ffn, ulist, ucount, \
                        a_hi, a_lo, B, L.Bp, L.lda, partial, L.G, ra.zsrc)
     const int xg = ring_xg(B);
     if (reglu) {

@@ -60,12 +60,15 @@ inline SparseLayout sparse_layout(int B, int d, int ffn) {
 // ---- batched union path (2 <= B <= kUnionMaxTokens tokens per pass)
 constexpr int kUnionMaxTokens = 128;
 // Skinny GEMMs of the batched path (ring.hpp): at most kRingMaxWG workgroups,
-// 32-row blocks, token slots padded to 32, 64 or 128.  Piece area: two slots
-// per workgroup of (matrices x token slots x 32) fp32 sums.
+// token slots padded to 32, 64 or 128 and row blocks of as many rows.  Piece
+// area: two slots per workgroup of (matrices x token slots x rows) fp32 sums.
 constexpr int kRingMaxWG = 1024;
 constexpr int kRingRows = 32;
 inline int ring_slots(int B) { return B <= 32 ? 32 : (B <= 64 ? 64 : 128); }
-inline size_t ring_piece_bytes(int nm, int B) { return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * kRingRows * 4; }
+// row blocks: 32 rows up to 32 tokens, 64 up to 64, 128 beyond
+inline size_t ring_piece_bytes(int nm, int B) {
+    return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * ring_slots(B) * 4;
+}
 struct BatchLayout {
     size_t tokbits;  // B x ceil(ffn/32) uint32 per-token bitmaps of the lists
     size_t umasks;   // tiles uint64 union bitmaps
