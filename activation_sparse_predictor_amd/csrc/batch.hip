@@ -176,13 +176,10 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
 constexpr int ring_seg(int nm, int nx, int xg, int rbw) {
     return 3 * (nm * 4 * rbw + nx * xg) * 4 <= 156 ? 4 : (3 * (nm * 4 * rbw + nx * xg) * 2 <= 156 ? 2 : 1);
 }
-// With 64 or 128 tokens the row block grows to 64 or 128 rows, to keep the
-// activation bytes per weight byte of a stage down.
-constexpr int ring_rbw(int xg) { return xg <= 4 ? 1 : xg / 4; }
-template <int XG> using HidCfg = RingCfg<1, 1, XG, ring_rbw(XG), ring_seg(1, 1, XG, ring_rbw(XG)), 3>;
-template <int XG> using LogCfg = RingCfg<1, 2, XG, ring_rbw(XG), ring_seg(1, 2, XG, ring_rbw(XG)), 3>;
+template <int XG> using HidCfg = RingCfg<1, 1, XG, rbw_hidden(XG), ring_seg(1, 1, XG, rbw_hidden(XG)), 3>;
+template <int XG> using LogCfg = RingCfg<1, 2, XG, rbw_logits(XG), ring_seg(1, 2, XG, rbw_logits(XG)), 3>;
 template <bool REGLU, int XG>
-using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, ring_rbw(XG), ring_seg(REGLU ? 2 : 1, 1, XG, ring_rbw(XG)), 3>;
+using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, rbw_up(XG), ring_seg(REGLU ? 2 : 1, 1, XG, rbw_up(XG)), 3>;
 
 // Up GEMM over the union rows: A[u][t] = W_up[U_u] . x_t (+ the gate
 // product for ReGLU), then bias, activation and the token mask (zero where
@@ -549,7 +546,6 @@ static int ring_grid() {
     return g;
 }
 
-static int ring_xg(int B) { return B <= 8 ? 1 : (B <= 16 ? 2 : (B <= 32 ? 4 : (B <= 64 ? 8 : 16))); }
 
 hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h16* Wup,
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,

@@ -65,9 +65,19 @@ constexpr int kUnionMaxTokens = 128;
 constexpr int kRingMaxWG = 1024;
 constexpr int kRingRows = 32;
 inline int ring_slots(int B) { return B <= 32 ? 32 : (B <= 64 ? 64 : 128); }
-// row blocks: 32 rows up to 32 tokens, 64 up to 64, 128 beyond
-inline size_t ring_piece_bytes(int nm, int B) {
-    return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * ring_slots(B) * 4;
+// 8-token groups loaded for B tokens, and 32-row blocks per row block for xg
+// groups, by kernel: the row block grows with the tokens, to keep the
+// activation bytes per weight byte of a stage down (the logits read h as two
+// arrays, hi and lo, so theirs grows first; the hidden layer has few rows, so
+// its stays small: a larger one would split each row block more ways)
+__host__ __device__ constexpr int ring_xg(int B) {
+    return B <= 8 ? 1 : (B <= 16 ? 2 : (B <= 32 ? 4 : (B <= 64 ? 8 : 16)));
+}
+__host__ __device__ constexpr int rbw_up(int xg) { return xg <= 2 ? 1 : (xg == 4 ? 2 : xg / 4); }
+__host__ __device__ constexpr int rbw_hidden(int xg) { return xg <= 4 ? 1 : xg / 4; }
+__host__ __device__ constexpr int rbw_logits(int xg) { return xg <= 4 ? xg : 4; }
+inline size_t ring_piece_bytes(int nm, int rbw, int B) {
+    return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * (32 * rbw) * 4;
 }
 struct BatchLayout {
     size_t tokbits;  // B x ceil(ffn/32) uint32 per-token bitmaps of the lists
@@ -103,7 +113,7 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
     L.ctr = L.partial + align256((size_t)L.G * L.Bp * d * 4);
     L.upctr = L.ctr + align256((size_t)kCtrWords * 4);
     L.upart = L.upctr + align256((size_t)((ffn + kRingRows - 1) / kRingRows) * 4);
-    L.total = L.upart + align256(ring_piece_bytes(2, B));
+    L.total = L.upart + align256(ring_piece_bytes(2, rbw_up(ring_xg(B)), B));
     return L;
 }
 
@@ -125,7 +135,8 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
     L.h_lo = align256((size_t)L.Bp * L.ldh * 2);
     L.masks32 = L.h_lo + align256((size_t)L.Bp * L.ldh * 2);
     L.hpart = L.masks32 + align256((size_t)B * ((ffn + 31) / 32) * 4);
-    L.lctr = L.hpart + align256(ring_piece_bytes(1, B));
+    const int rbw = rbw_hidden(ring_xg(B)) > rbw_logits(ring_xg(B)) ? rbw_hidden(ring_xg(B)) : rbw_logits(ring_xg(B));
+    L.lctr = L.hpart + align256(ring_piece_bytes(1, rbw, B));
     L.total = L.lctr + align256((size_t)((ffn + kRingRows - 1) / kRingRows) * 4);
     (void)r;
     return L;
