@@ -338,13 +338,15 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 // a tile's chunks spread over the whole device instead of one workgroup).
 constexpr int kDnIds = 4096;   // union entries per chunk staged in LDS (G is sized for it)
 
-// Wave w owns CB blocks of 32 columns (the tile is 128 CB columns): with many
-// tokens, two blocks per wave halve the activation bytes per W_down byte.
+// Wave w owns CB blocks of 32 columns (the tile is 128 CB columns): with 128
+// tokens, two blocks per wave halve the activation bytes per W_down byte (the
+// ring is then two stages deep either way; with 64 tokens one block keeps
+// it three deep, which measured faster).
 template <int XG_>
 struct DownCfg {
     static constexpr int XG = XG_;
     static constexpr int NB = (XG + 3) / 4, BP = 32 * NB;
-    static constexpr int CB = XG >= 8 ? 2 : 1;
+    static constexpr int CB = XG >= 16 ? 2 : 1;
     static constexpr int CT = 128 * CB;                            // columns per tile
     static constexpr int KR = 64;                                  // union entries per stage
     static constexpr int WBLK = (KR / 8) * (CT / 64);              // W_down blocks per stage
