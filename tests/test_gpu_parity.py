@@ -143,8 +143,9 @@ def test_dense_flag(kind):
         check_y(Y[t].cpu().numpy(), ref, where=f"dense t={t}")
 
 
-@pytest.mark.parametrize("kind,Bt", [("relu", 1), ("relu", 2), ("relu", 4), ("relu", 15), ("relu", 16),
-                                     ("relu", 17), ("relu", 32), ("relu", 33), ("reglu", 8), ("reglu", 32),
+@pytest.mark.parametrize("kind,Bt", [("relu", 1), ("relu", 2), ("relu", 4), ("relu", 9), ("relu", 15),
+                                     ("relu", 16), ("relu", 17), ("relu", 32), ("relu", 33), ("reglu", 8),
+                                     ("reglu", 12), ("reglu", 20), ("reglu", 32), ("reglu", 64), ("relu", 65),
                                      ("relu", 100), ("reglu", 128), ("relu", 131)])
 def test_batched_union_path(kind, Bt):
     """Batch of Bt tokens.  The batched predictor (matrix cores) must satisfy the
@@ -422,7 +423,7 @@ def test_full_size_stack_layer_and_profile():
     check_counts(counts.cpu().numpy(), pre, where="c5 profile")
 
 
-@pytest.mark.parametrize("Bt", [4, 16, 32])
+@pytest.mark.parametrize("Bt", [4, 16, 32, 64, 128])
 def test_full_size_batched(Bt):
     cfg, L, X = _full("c4", ntok=Bt)
     H = _host(L)
