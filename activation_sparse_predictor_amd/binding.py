@@ -31,6 +31,8 @@ PI_OP_SPARSE = 1
 PI_OP_PROFILE = 2
 PI_DENSE = 0x1
 PI_PER_TOKEN = 0x2
+PI_DETERMINISTIC = 0x4
+PI_CHECK_IDX = 0x8
 
 KINDS = {"relu": PI_FFN_RELU, "reglu": PI_FFN_REGLU}
 ACTS = {"relu": PI_ACT_RELU, "none": PI_ACT_NONE}

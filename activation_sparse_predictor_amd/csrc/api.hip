@@ -216,8 +216,10 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
                         uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
     PI_TRY(check_dims(B, d, ffn));
     PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU, PI_ERR_INVALID_ARG, "kind=%d unknown", kind);
-    PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN)) == 0u, PI_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN | PI_DETERMINISTIC | PI_CHECK_IDX)) == 0u, PI_ERR_INVALID_ARG,
+               "unknown flags 0x%x", flags);
     const bool dense = (flags & PI_DENSE) != 0u;
+    const bool check = !dense && (flags & PI_CHECK_IDX) != 0u;
     const bool reglu = kind == PI_FFN_REGLU;
     PI_REQUIRE(reglu == (W_gate != nullptr), PI_ERR_INVALID_ARG,
                reglu ? "W_gate is NULL for a ReGLU FFN" : "W_gate given for a ReLU FFN");
@@ -250,6 +252,10 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
                                             w + pi::kSyncBytes, w, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
         }
+        if (check) {
+            hipError_t e = pi::launch_check_idx(idx, count, B, ffn, d, y, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse index check");
+        }
         return ok();
     }
     if (!dense) {   // one token (or PI_PER_TOKEN): one kernel per token, up/gate rows overlapping W_down
@@ -263,6 +269,10 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const
                                         idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, w, s);
         if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse");
         ws_record(ws, key);
+        if (check) {
+            e = pi::launch_check_idx(idx, count, B, ffn, d, y, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse index check");
+        }
         return ok();
     }
     ws_forget(ws);

@@ -47,14 +47,16 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
     const int cnt = clampi(count[t], 0, ffn);
     const int32_t* lst = idx + (size_t)t * ffn;
     uint32_t* out = tokbits + (size_t)t * nw;
-    const int wfirst = cnt > 0 ? lst[0] >> 5 : nw;
-    const int wlast = cnt > 0 ? lst[cnt - 1] >> 5 : -1;
+    // ids are read clamped to [0, ffn): a list that breaks the contract gives
+    // wrong bits but no access outside the bitmaps (PI_CHECK_IDX reports it)
+    const int wfirst = cnt > 0 ? clampi(lst[0], 0, ffn - 1) >> 5 : nw;
+    const int wlast = cnt > 0 ? clampi(lst[cnt - 1], 0, ffn - 1) >> 5 : -1;
     for (int w = blockIdx.x * 256 + tid; w < nw; w += stride)
         if (w < wfirst || w > wlast) out[w] = 0u;
     for (int j0 = blockIdx.x * 256 + (tid & ~63); j0 < cnt; j0 += stride) {   // whole waves
         const int j = j0 + lane;
         const bool in = j < cnt;
-        const int i = in ? lst[j] : 0;
+        const int i = in ? clampi(lst[j], 0, ffn - 1) : 0;
         const int w = in ? (i >> 5) : -1 - lane;   // lanes past the list match no one
         uint32_t bits = in ? (1u << (i & 31)) : 0u;
 #pragma unroll
@@ -66,11 +68,11 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
         const int wup = __shfl_up(w, 1, 64);
         const int w63 = __shfl(w, 63, 64);
         if (!in) continue;
-        const int wprev = j == 0 ? -1 : (lane == 0 ? lst[j - 1] >> 5 : wup);
+        const int wprev = j == 0 ? -1 : (lane == 0 ? clampi(lst[j - 1], 0, ffn - 1) >> 5 : wup);
         if (wprev == w) continue;   // not the first entry of its word
         if (w63 == w)               // the run goes on past this wave
             for (int jj = j0 + 64; jj < cnt; ++jj) {
-                const int ii = lst[jj];
+                const int ii = clampi(lst[jj], 0, ffn - 1);
                 if ((ii >> 5) != w) break;
                 bits |= 1u << (ii & 31);
             }
@@ -530,6 +532,33 @@ __global__ __launch_bounds__(256) void k_union_reduce(const float* __restrict__ 
         for (int u = 0; u < 8; ++u) sum += v[u];
     }
     y[o] = sum;
+}
+
+// PI_CHECK_IDX: one workgroup per token checks its list against the contract
+// (count in [0, ffn], ids in [0, ffn), strictly ascending) after the FFN has
+// run, and fills y_t with NaN if it breaks it.  The FFN kernels read ids
+// clamped to [0, ffn), so a broken list never reads outside the weights.
+__global__ __launch_bounds__(256) void k_check_idx(const int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ count, int ffn, int d,
+                                                   float* __restrict__ y) {
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const int c = count[t];
+    const int32_t* lst = idx + (size_t)t * ffn;
+    bool bad = c < 0 || c > ffn;
+    const int n = bad ? 0 : c;
+    for (int j = tid; j < n; j += 256) {
+        const int i = lst[j];
+        bad = bad || i < 0 || i >= ffn || (j > 0 && lst[j - 1] >= i);
+    }
+    if (!__syncthreads_or(bad)) return;
+    const float nan = __builtin_nanf("");
+    for (int k = tid; k < d; k += 256) y[(size_t)t * d + k] = nan;
+}
+
+hipError_t launch_check_idx(const int32_t* idx, const int32_t* count, int B, int ffn, int d, float* y,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(k_check_idx, dim3(B), dim3(256), 0, s, idx, count, ffn, d, y);
+    return hipGetLastError();
 }
 
 // Workgroups of a ring kernel that are resident on the device at once (at

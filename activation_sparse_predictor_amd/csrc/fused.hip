@@ -98,8 +98,10 @@ constexpr int kLRows = 8;     // rows per wave
 constexpr int kLCols = 2;     // 64-lane chunk columns per batch: 16 P2 loads in flight per lane
 static_assert(kLRows * 4 == kLTile, "4 waves per logits tile");
 
-// 5 waves per SIMD: at 5 workgroups per CU every hidden row and logits tile of
-// a 1024 x 28672 predictor is resident from the start.
+// At the 107 VGPRs this needs, 4 workgroups fit per CU: of the 1153 of a
+// 1024 x 28672 predictor, the last 129 logits tiles start as hidden rows
+// retire.  Asking for 5 per CU (102 VGPRs) spills in the logits loop and
+// makes the kernel half again as slow.
 __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x, int d,
                                                        const h16* __restrict__ P1,
                                                        const float* __restrict__ b1, int relu, int r,

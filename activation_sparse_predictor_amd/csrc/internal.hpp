@@ -212,6 +212,9 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
                         char* ws, char* hdr, hipStream_t s);
 
+hipError_t launch_check_idx(const int32_t* idx, const int32_t* count, int B, int ffn, int d, float* y,
+                            hipStream_t s);
+
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
                           const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
                           int32_t* count, const BPredLayout& L, char* ws, char* hdr, hipStream_t s);

@@ -72,11 +72,14 @@ def predict(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
 
 def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
            count: Optional[torch.Tensor], y: Optional[torch.Tensor] = None,
-           dense: bool = False, per_token: bool = False, stream=None) -> torch.Tensor:
+           dense: bool = False, per_token: bool = False, check_idx: bool = False,
+           stream=None) -> torch.Tensor:
     """y (B x d fp32) from the active rows (or every row with dense=True).
 
     For B >= 2 the library reads the union of the tokens' rows once (matrix
     cores); per_token=True runs each token through the single-token kernels.
+    check_idx=True has the device check each list afterwards and fill y_t with
+    NaN where it breaks the contract (ids in [0, ffn), strictly ascending).
     """
     Bt, d = x.shape
     ffn = layer["ffn"]
@@ -87,7 +90,8 @@ def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
     st = B.pi_ffn_sparse(B.KINDS[layer["kind"]], _bits(x), Bt, d, ffn, layer["W_up"],
                          layer.get("b_up"), layer.get("W_gate"), layer.get("b_gate"),
                          layer["W_down"], None if dense else idx, None if dense else count, y,
-                         (B.PI_DENSE if dense else 0) | (B.PI_PER_TOKEN if per_token else 0),
+                         (B.PI_DENSE if dense else 0) | (B.PI_PER_TOKEN if per_token else 0)
+                         | (B.PI_CHECK_IDX if check_idx else 0),
                          ws, wsb, stream)
     B.check(st, "pi_ffn_sparse")
     return y

@@ -77,6 +77,13 @@ typedef enum pi_op {
 #define PI_DENSE 0x1u      /* ignore idx/count and compute every neuron (dense FFN baseline) */
 #define PI_PER_TOKEN 0x2u  /* B >= 2: run every token through the single-token kernel instead of
                               the union path (same results up to fp32 rounding) */
+#define PI_DETERMINISTIC 0x4u  /* accepted for callers that ask for it: every path is deterministic
+                                  already (fixed reduction orders, no floating-point atomics) */
+#define PI_CHECK_IDX 0x8u  /* after the FFN, check each token's list against the contract
+                              (count in [0, ffn], ids in [0, ffn), strictly ascending) on the
+                              device and fill y_t with NaN when it breaks it; without the flag a
+                              broken list gives unspecified y (ids are read clamped to [0, ffn),
+                              so never an access outside the weights).  Ignored with PI_DENSE. */
 
 #define PI_MAX_BATCH 256
 #define PI_MAX_D 16384
@@ -125,7 +132,8 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d,
  * be non-NULL for REGLU and NULL for RELU.  Products are fp16 x fp16 with
  * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0).
  * idx must hold valid, strictly ascending neuron ids (as written by
- * pi_ffn_predict); the call does not re-check them.
+ * pi_ffn_predict); the call does not re-check them unless flags has
+ * PI_CHECK_IDX (then a token whose list breaks this gets y_t = NaN).
  *
  * For B = 1 (and for every token under PI_PER_TOKEN) the step is one kernel:
  * the up/gate rows of the list are computed while the W_down rows are already

@@ -166,6 +166,19 @@ def test_dense_flag_allows_null_index_list():
     assert _sparse(flags=B.PI_DENSE, idx=None, count=None, ws=None) == B.PI_ERR_WORKSPACE
 
 
+def test_flag_values_match_the_header():
+    text = open(HEADER).read()
+    for name in ("PI_DENSE", "PI_PER_TOKEN", "PI_DETERMINISTIC", "PI_CHECK_IDX"):
+        m = re.search(r"#define\s+%s\s+(0x[0-9a-fA-F]+)u" % name, text)
+        assert m, name
+        assert int(m.group(1), 16) == getattr(B, name), name
+
+
+def test_check_and_deterministic_flags_are_accepted():
+    # both flags pass the flag check: the call gets as far as the workspace check
+    assert _sparse(flags=B.PI_CHECK_IDX | B.PI_DETERMINISTIC, ws=None) == B.PI_ERR_WORKSPACE
+
+
 def test_profile_and_permute_reject_before_launch():
     assert B.pi_profile(None, 4, 64, 128, A, None, A, stream=0) == B.PI_ERR_INVALID_ARG
     assert B.pi_profile(A, 0, 64, 128, A, None, A, stream=0) == B.PI_ERR_INVALID_ARG

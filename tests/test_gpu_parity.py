@@ -208,6 +208,42 @@ def test_union_path_edge_lists():
         check_y(Yh[t], _oracle_y(H, X[t].cpu(), lists[t]), where=f"edge list t={t}")
 
 
+@pytest.mark.parametrize("per_token", [False, True])
+def test_check_idx_flag(per_token):
+    """PI_CHECK_IDX: tokens whose lists break the contract (an id out of range,
+    out of order, repeated, a count above ffn or below 0) get y = NaN; valid
+    tokens are bitwise equal to the call without the flag.  The batched path
+    (per_token=False) and the single-token kernel (per_token=True) both."""
+    cfg = custom_config("relu", 264, 600, 16, mean=0.2, number=62)
+    L = R.to_device(make_layer(cfg), DEV)
+    ffn = cfg.ffn
+    good = [list(range(3, ffn, 7)), [], [0, ffn - 1]]
+    bad = [[5, ffn, 9], [1, 8, 4], [2, 2, 3], [-1, 4]]
+    lists = good + bad
+    Bt = len(lists)
+    X = make_tokens(cfg, Bt).to(DEV)
+    idx = torch.zeros(Bt, ffn, dtype=torch.int32, device=DEV)
+    for t, l in enumerate(lists):
+        if l:
+            idx[t, :len(l)] = torch.tensor(l, dtype=torch.int32, device=DEV)
+    counts = [len(l) for l in lists]
+    cnt = torch.tensor(counts, dtype=torch.int32, device=DEV)
+    cnt_over = cnt.clone()
+    cnt_over[1] = ffn + 1     # a count above ffn on an otherwise empty list
+    cnt_neg = cnt.clone()
+    cnt_neg[1] = -3
+    Y0 = R.sparse(L, X, idx, cnt, per_token=per_token).cpu().numpy()
+    Y1 = R.sparse(L, X, idx, cnt, per_token=per_token, check_idx=True).cpu().numpy()
+    Y2 = R.sparse(L, X, idx, cnt_over, per_token=per_token, check_idx=True).cpu().numpy()
+    Y3 = R.sparse(L, X, idx, cnt_neg, per_token=per_token, check_idx=True).cpu().numpy()
+    for t in range(len(good)):
+        assert np.array_equal(Y1[t], Y0[t]), f"valid token {t} changed by the check"
+    for t in range(len(good), Bt):
+        assert np.all(np.isnan(Y1[t])), f"broken list {t} not flagged"
+    assert np.all(np.isnan(Y2[1])) and np.all(np.isnan(Y3[1])), "count outside [0, ffn] not flagged"
+    assert np.array_equal(Y2[0], Y0[0]) and np.array_equal(Y3[2], Y0[2])
+
+
 def test_deterministic_repeats():
     cfg = custom_config("reglu", 1032, 2080, 136, mean=0.3, number=57)
     L = R.to_device(make_layer(cfg), DEV)
