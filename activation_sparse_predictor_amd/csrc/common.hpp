@@ -112,4 +112,33 @@ __device__ __forceinline__ void st_coherent(float* p, float v) {
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_own_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// at their maximum so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+// Direct-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4: lane l's
+// bytes land at lds_addr + 16 l; lds_addr is wave-uniform, it goes to M0),
+// issued as inline assembly.  Were the compiler to see it, it would make every
+// LDS read wait for all outstanding vector-memory loads (it cannot tell which
+// LDS bytes the load writes); the caller orders the load and the reads with
+// its own waits and barriers instead.  (A load the compiler does not count can
+// only make its own waits stricter.)  dma16_coherent reads the device-coherent
+// value, as the relaxed agent-scope atomic loads do.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_addr), "v"(gptr) : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_coherent(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1" : : "s"(lds_addr), "v"(gptr)
+                 : "memory", "m0");
+}
+// The 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const char*)(const char*)p;
+}
+
 }  // namespace pi

@@ -52,15 +52,6 @@ namespace pi {
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef float ring_f32x16 __attribute__((ext_vector_type(16)));
 
-// Wait until at most N vector-memory loads of this wave are outstanding
-// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
-// at their maximum so they are not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
-}
-
 // Workgroup barrier without the memory fences of __syncthreads (those would
 // make every wave wait for all of its outstanding loads, the ring's included);
 // the empty asm keeps the compiler from moving LDS accesses across it.
@@ -70,16 +61,9 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Direct-to-LDS load of 16 bytes per lane (global_load_lds_dwordx4: lane l's
-// bytes land at lds_addr + 16 l; lds_addr is wave-uniform, it goes to M0),
-// issued as inline assembly.  Were the compiler to see it, it would make every
-// LDS read wait for all outstanding vector-memory loads (it cannot tell which
-// LDS bytes the load writes), draining the ring at every stage; the ring's
-// own waits and barriers order these loads and the reads instead.  (A load
-// the compiler does not count can only make its own waits stricter.)
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_addr), "v"(gptr) : "memory", "m0");
-}
+// (dma16 and wait_vm, common.hpp: the ring's direct-to-LDS loads are issued
+// as inline assembly, so that the compiler does not make every LDS read wait
+// for all outstanding loads, which would drain the ring at every stage.)
 
 template <int NM_, int NX_, int XG_, int RBW_, int SEG_, int NS_>
 struct RingCfg {
