@@ -101,20 +101,19 @@ struct RingArgs {
     uint32_t* ctr;            // one arrival counter per row block, 0 between calls
 };
 
-// Host-side sizes of the pieces area for a grid of G workgroups.
-template <class C>
-inline size_t ring_part_bytes(int G) { return (size_t)2 * G * C::NM * C::BP * C::RB * 4; }
-
 // Runs the calling workgroup's range of units over the first nrows rows of
-// the list (a.nrows is not read: a kernel may take the count from memory);
-// GATHER: row i is a.rowlist[i], else row i.  LAST_FINISHES: split row
-// blocks are finished by their last piece's workgroup (else by ring_finish).  epi(i, t, v0, v1) is called by every
-// thread of the workgroup, uniformly, for every (row i of a finished row block,
-// token slot t < BP), rows fastest: rows 64k .. 64k+63 of one token form a wave
-// when RB = 64.  v0 and v1 are the sums for matrices 0 and 1 (v1 = 0 when
-// NM = 1), 0 for t >= B; i runs to the end of the row block, past nrows,
-// where the sums mean nothing.  The caller's LDS
-// area lds must hold C::LDS bytes, 16-byte aligned.
+// the list (a.nrows is not read: a kernel may take the count from memory).
+// GATHER: row i is a.rowlist[i], else row i.  LAST_FINISHES: a split row
+// block is finished by the workgroup of its last piece (else by ring_finish,
+// in a launch of its own).  The caller's LDS area lds holds C::LDS bytes,
+// 16-byte aligned; the pieces area (a.part) holds two slots per workgroup of
+// NM x BP x RB fp32 sums.
+//
+// epi(i, t, v0, v1) is called by every thread of the workgroup, uniformly,
+// for every (row i of a finished row block, token slot t < BP), rows fastest:
+// the 32 rows of a half-wave belong to one token.  v0 and v1 are the sums for
+// matrices 0 and 1 (v1 = 0 when NM = 1), 0 for t >= B; i runs to the end of
+// the row block, past nrows, where the sums mean nothing.
 template <class C, bool GATHER, bool LAST_FINISHES, class Epi>
 __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* lds, Epi&& epi) {
     __shared__ int s_last;
