@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 // of the tile for every token.  Chunk partials go to the workspace and
 // k_union_reduce adds them in chunk order (a kernel of its own: the sums of
 // a tile's chunks spread over the whole device instead of one workgroup).
-constexpr int kDnIds = 4096;   // union entries per chunk staged in LDS (G is sized for it)
+constexpr int kDnIds = 4096;   // union ids staged in LDS at a time (a window of the chunk)
 
 // Wave w owns CB blocks of 32 columns (the tile is 128 CB columns): with 128
 // tokens, two blocks per wave halve the activation bytes per W_down byte (the
@@ -383,19 +383,26 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     const int tile = blockIdx.x, chunk = blockIdx.y;
     const int U = (int)min(*ucount, (uint32_t)ffn);
     // chunk starts are multiples of 8: 16-byte activation loads stay aligned
-    const int per = min((((U + G - 1) / G) + 7) & ~7, kDnIds);
+    const int per = (((U + G - 1) / G) + 7) & ~7;
     const int u0 = min(U, chunk * per), u1 = min(U, u0 + per);
     const int n_ids = u1 - u0;
     const int n = (n_ids + C::KR - 1) / C::KR;
     const int c0 = tile * C::CT;
-    for (int i0 = 0; i0 < n_ids; i0 += 256 * 8) {   // 8 loads in flight per thread
-        int v[8];
+    // the chunk's union ids, kDnIds at a time (a window: kDnIds / KR stages)
+    auto load_ids = [&](int w0) {
+        const int nw = min(n_ids - w0, kDnIds);
+        for (int i0 = 0; i0 < nw; i0 += 256 * 8) {   // 8 loads in flight per thread
+            int v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = ulist[u0 + min(i0 + k * 256 + tid, max(n_ids - 1, 0))];
+            for (int k = 0; k < 8; ++k) v[k] = ulist[u0 + w0 + min(i0 + k * 256 + tid, max(nw - 1, 0))];
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (i0 + k * 256 + tid < n_ids) s_ids[i0 + k * 256 + tid] = v[k];
-    }
+            for (int k = 0; k < 8; ++k)
+                if (i0 + k * 256 + tid < nw) s_ids[i0 + k * 256 + tid] = v[k];
+        }
+    };
+    static_assert(kDnIds % C::KR == 0, "whole stages per id window");
+    int window = 0;
+    load_ids(0);
     __syncthreads();
     const uint32_t lbase = (uint32_t)(size_t)(lds_void_ptr)lds;
 
@@ -423,9 +430,19 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
         }
     }
     auto issue = [&](int st, int q) {
+        const int wst = st * C::KR / kDnIds;   // uniform: every wave issues the same stage
+        if (wst != window) {
+            // every wave has issued the previous window's last stage (it read
+            // its ids then), so the window can be replaced; a rare stall
+            __syncthreads();
+            load_ids(wst * kDnIds);
+            __syncthreads();
+            window = wst;
+        }
         int id[C::WBLK / 4];
 #pragma unroll
-        for (int i = 0; i < C::WBLK / 4; ++i) id[i] = clampi(s_ids[min(st * C::KR + wofs[i], kDnIds - 1)], 0, ffn - 1);
+        for (int i = 0; i < C::WBLK / 4; ++i)
+            id[i] = clampi(s_ids[min(st * C::KR + wofs[i] - window * kDnIds, kDnIds - 1)], 0, ffn - 1);
         const uint32_t dst = lbase + q * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i) {

@@ -100,8 +100,11 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
     L.Bp = L.W * 32;
     L.lda = (ffn + 7) & ~7;
     L.T = (d + 127) / 128;
-    L.G = (ffn + 4087) / 4088;   // chunks of at most 4088 union entries
+    // union chunks per 128-column tile: about 512 down workgroups in all,
+    // 8 to 64 chunks (the partials stay G x Bp x d whatever ffn is)
+    L.G = 512 / L.T;
     if (L.G < 8) L.G = 8;
+    if (L.G > 64) L.G = 64;
     const size_t tiles = (size_t)(ffn + 63) / 64;
     L.tokbits = 0;
     L.umasks = L.tokbits + align256((size_t)B * ((ffn + 31) / 32) * 4);

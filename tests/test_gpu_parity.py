@@ -440,6 +440,26 @@ def _full(key, layer=0, ntok=3):
     return cfg, L, X
 
 
+def test_union_down_id_windows():
+    """A union larger than one LDS window of ids per down chunk (d = 8192 gives
+    8 chunks per column tile, so |U| = 40960 means 5120 entries per chunk: the
+    down GEMM reloads its ids mid-chunk).  Lists: token t takes every neuron
+    i with (i + t) % 3 != 0, so the union is every neuron."""
+    cfg = custom_config("relu", 8192, 40960, 64, mean=0.1, number=63)
+    L = make_layer(cfg, device=DEV)
+    H = _host(L)
+    Bt, ffn = 6, cfg.ffn
+    X = make_tokens(cfg, Bt, device=DEV)
+    lists = [[i for i in range(ffn) if (i + t) % 3 != 0] for t in range(Bt)]
+    idx = torch.zeros(Bt, ffn, dtype=torch.int32, device=DEV)
+    for t, l in enumerate(lists):
+        idx[t, :len(l)] = torch.tensor(l, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([len(l) for l in lists], dtype=torch.int32, device=DEV)
+    Y = R.sparse(L, X, idx, cnt).cpu().numpy()
+    for t in (0, Bt - 1):
+        check_y(Y[t], _oracle_y(H, X[t].cpu(), lists[t]), where=f"union windows t={t}")
+
+
 @pytest.mark.parametrize("key", ["c2", "c3", "c4"])
 def test_full_size_decode(key):
     cfg, L, X = _full(key)
