@@ -395,12 +395,16 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
             int v[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) v[k] = ulist[u0 + w0 + min(i0 + k * 256 + tid, max(nw - 1, 0))];
+            // unconditional stores (i0 <= kDnIds - 2048 keeps them in the
+            // window; slots past nw hold a repeated id that no stage uses):
+            // a conditional store would leave loads pending across the branch
+            // and the compiler would then drain every DMA before the MFMA reads
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (i0 + k * 256 + tid < nw) s_ids[i0 + k * 256 + tid] = v[k];
+            for (int k = 0; k < 8; ++k) s_ids[i0 + k * 256 + tid] = v[k];
         }
     };
     static_assert(kDnIds % C::KR == 0, "whole stages per id window");
+    static_assert(kDnIds % (256 * 8) == 0, "id window loads cover whole 2048-id rounds");
     int window = 0;
     load_ids(0);
     __syncthreads();
