@@ -29,6 +29,7 @@ PI_ACT_NONE = 1
 PI_OP_PREDICT = 0
 PI_OP_SPARSE = 1
 PI_OP_PROFILE = 2
+PI_OP_DECODE = 3
 PI_DENSE = 0x1
 PI_PER_TOKEN = 0x2
 PI_DETERMINISTIC = 0x4
@@ -44,6 +45,8 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "pi_ffn_predict": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "pi_ffn_sparse": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "pi_ffn_decode": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
+                           _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "pi_profile": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "pi_reorder": (_I, [_P, _I, ctypes.c_double, _P, _P]),
     "pi_permute_rows": (_I, [_P, _P, _I, _I, _P, _P]),
@@ -125,6 +128,13 @@ def pi_ffn_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, c
     return load().pi_ffn_sparse(kind, _ptr(x), B, d, ffn, _ptr(W_up), _ptr(b_up), _ptr(W_gate),
                                 _ptr(b_gate), _ptr(W_down), _ptr(idx), _ptr(count), _ptr(y), flags,
                                 _ptr(ws), ws_bytes, _stream(stream))
+
+
+def pi_ffn_decode(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down,
+                  idx, count, y, flags, ws, ws_bytes, stream=None) -> int:
+    return load().pi_ffn_decode(kind, _ptr(x), B, d, ffn, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r, tau,
+                                _ptr(W_up), _ptr(b_up), _ptr(W_gate), _ptr(b_gate), _ptr(W_down), _ptr(idx),
+                                _ptr(count), _ptr(y), flags, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def pi_profile(X, n, d, ffn, W_fire, b_fire, counts, ws=None, ws_bytes=0, stream=None) -> int:

@@ -73,14 +73,15 @@ pi_status check_ws(void* ws, size_t ws_bytes, size_t need, const char* op) {
     return PI_OK;
 }
 
-// Every workspace starts with the fused kernels' synchronisation header; the
-// layouts of all other kernels begin kSyncBytes in.
-size_t predict_ws_bytes(int B, int r, int ffn) {
-    if (B == 1) return pi::kSyncBytes + pi::fused_pred_layout(r, ffn).total;
-    return pi::kSyncBytes + pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
+// Every workspace starts with the fused kernels' synchronisation header; a
+// call's data area follows it.
+size_t predict_data_bytes(int B, int r, int ffn) {
+    if (B == 1) return pi::fused_pred_layout(r, ffn).total;
+    return pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
 }
+size_t predict_ws_bytes(int B, int r, int ffn) { return pi::kSyncBytes + predict_data_bytes(B, r, ffn); }
 
-size_t sparse_ws_bytes(int B, int d, int ffn) {
+size_t sparse_data_bytes(int B, int d, int ffn) {
     size_t n = pi::sparse_layout(B, d, ffn).total;          // dense baseline
     const size_t f = pi::fused_sparse_layout(d, ffn).total;  // single token / per token
     if (f > n) n = f;
@@ -88,28 +89,36 @@ size_t sparse_ws_bytes(int B, int d, int ffn) {
         const size_t u = pi::batch_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, d, ffn).total;
         if (u > n) n = u;
     }
-    return pi::kSyncBytes + n;
+    return n;
 }
+size_t sparse_ws_bytes(int B, int d, int ffn) { return pi::kSyncBytes + sparse_data_bytes(B, d, ffn); }
 
-// Which tagged layout each workspace last held.  Tags of earlier fused calls
-// can never match a new epoch, but data written by another layout could, so
-// a fused call zeroes its tagged words whenever the workspace last held
-// something else (a different op or shape, an unfused call, or a workspace
-// not seen before).
+// pi_ffn_decode: one header, the predictor's data area, then the FFN's, so
+// that repeated steps never find another layout in either area.
+size_t decode_ffn_offset(int B, int r, int ffn) { return pi::kSyncBytes + pi::align256(predict_data_bytes(B, r, ffn)); }
+size_t decode_ws_bytes(int B, int d, int r, int ffn) { return decode_ffn_offset(B, r, ffn) + sparse_data_bytes(B, d, ffn); }
+
+// Which layout each workspace last held, by its address.  Tags of earlier
+// fused calls can never match a new epoch, but data written by another
+// layout could, so a call that uses tagged words zeroes them whenever the
+// workspace last held something else (another operation or shape, an
+// unfused call, or a workspace not seen before).
+struct LayoutKey {
+    int op, B, d, r, ffn;
+    bool operator==(const LayoutKey& o) const {
+        return op == o.op && B == o.B && d == o.d && r == o.r && ffn == o.ffn;
+    }
+};
 std::mutex g_ws_mu;
-std::unordered_map<const void*, uint64_t> g_ws_layout;
-
-uint64_t layout_key(int op, int a, int ffn) {
-    return ((uint64_t)(op + 1) << 48) | ((uint64_t)(uint32_t)a << 25) | (uint64_t)(uint32_t)ffn;
-}
+std::unordered_map<const void*, LayoutKey> g_ws_layout;
 
 // true if the tagged words must be zeroed before a call with this layout
-bool ws_needs_clear(const void* ws, uint64_t key) {
+bool ws_needs_clear(const void* ws, const LayoutKey& key) {
     std::lock_guard<std::mutex> g(g_ws_mu);
     auto it = g_ws_layout.find(ws);
-    return it == g_ws_layout.end() || it->second != key;
+    return it == g_ws_layout.end() || !(it->second == key);
 }
-void ws_record(const void* ws, uint64_t key) {
+void ws_record(const void* ws, const LayoutKey& key) {
     std::lock_guard<std::mutex> g(g_ws_mu);
     g_ws_layout[ws] = key;
 }
@@ -118,11 +127,146 @@ void ws_forget(const void* ws) {
     g_ws_layout.erase(ws);
 }
 
+// Whether a call's path keeps tagged words in its data area.
+bool sparse_is_fused(int B, uint32_t flags) {
+    return (flags & PI_DENSE) == 0u && (B == 1 || (flags & PI_PER_TOKEN) != 0u);
+}
+
 #define PI_TRY(expr)                  \
     do {                              \
         pi_status _s = (expr);        \
         if (_s != PI_OK) return _s;   \
     } while (0)
+
+pi_status check_predict_args(const pi_half* x, int B, int d, const pi_half* P1, const float* b1, int act,
+                             const pi_half* P2, const float* b2, int r, int ffn, float tau, const int32_t* idx,
+                             const int32_t* count) {
+    PI_TRY(check_dims(B, d, ffn));
+    PI_REQUIRE(r > 0, PI_ERR_INVALID_ARG, "r=%d must be positive", r);
+    PI_REQUIRE(r % 8 == 0, PI_ERR_UNSUPPORTED, "r=%d is not a multiple of 8", r);
+    PI_REQUIRE(r <= PI_MAX_R, PI_ERR_UNSUPPORTED, "r=%d above PI_MAX_R=%d", r, PI_MAX_R);
+    PI_REQUIRE(act == PI_ACT_RELU || act == PI_ACT_NONE, PI_ERR_INVALID_ARG, "act=%d unknown", act);
+    PI_REQUIRE(tau > 0.f && tau < 1.f, PI_ERR_INVALID_ARG, "tau=%g not in (0, 1)", (double)tau);
+    PI_TRY(check_half(x, "x", true));
+    PI_TRY(check_half(P1, "P1", true));
+    PI_TRY(check_half(P2, "P2", true));
+    PI_TRY(check_word(b1, "b1", false));
+    PI_TRY(check_word(b2, "b2", false));
+    PI_TRY(check_word(idx, "idx", true));
+    PI_TRY(check_word(count, "count", true));
+    return PI_OK;
+}
+
+pi_status check_sparse_args(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* W_up,
+                            const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
+                            const int32_t* idx, const int32_t* count, const float* y, uint32_t flags) {
+    PI_TRY(check_dims(B, d, ffn));
+    PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU, PI_ERR_INVALID_ARG, "kind=%d unknown", kind);
+    PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN | PI_DETERMINISTIC | PI_CHECK_IDX)) == 0u, PI_ERR_INVALID_ARG,
+               "unknown flags 0x%x", flags);
+    const bool dense = (flags & PI_DENSE) != 0u;
+    const bool reglu = kind == PI_FFN_REGLU;
+    PI_REQUIRE(reglu == (W_gate != nullptr), PI_ERR_INVALID_ARG,
+               reglu ? "W_gate is NULL for a ReGLU FFN" : "W_gate given for a ReLU FFN");
+    PI_REQUIRE(reglu || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
+    PI_TRY(check_half(x, "x", true));
+    PI_TRY(check_half(W_up, "W_up", true));
+    PI_TRY(check_half(W_gate, "W_gate", false));
+    PI_TRY(check_half(W_down, "W_down", true));
+    PI_TRY(check_word(b_up, "b_up", false));
+    PI_TRY(check_word(b_gate, "b_gate", false));
+    PI_TRY(check_word(idx, "idx", !dense));
+    PI_TRY(check_word(count, "count", !dense));
+    PI_REQUIRE(y != nullptr, PI_ERR_INVALID_ARG, "y is NULL");
+    PI_REQUIRE(aligned(y, 16), PI_ERR_UNSUPPORTED, "y is not 16-byte aligned");
+    return PI_OK;
+}
+
+
+// The calls proper, on a checked workspace: hdr is its synchronisation header,
+// data the call's data area; clear: zero the tagged words first (single-token
+// paths only).
+pi_status run_predict(const pi_half* x, int B, int d, const pi_half* P1, const float* b1, int act,
+                      const pi_half* P2, const float* b2, int r, int ffn, float tau, int32_t* idx, int32_t* count,
+                      char* hdr, char* data, bool clear, hipStream_t s) {
+    // sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
+    const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
+    const auto* hx = reinterpret_cast<const pi::h16*>(x);
+    const auto* h1 = reinterpret_cast<const pi::h16*>(P1);
+    const auto* h2 = reinterpret_cast<const pi::h16*>(P2);
+    if (B >= 2) {   // batched: both predictor layers on the matrix cores, weights read once per group
+        for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
+            const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
+            const pi::BPredLayout L = pi::bpred_layout(Bg, r, ffn);
+            hipError_t e = pi::launch_bpredict(hx + (size_t)g0 * d, Bg, d, h1, b1, act == PI_ACT_RELU, h2, b2,
+                                               r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L,
+                                               data, hdr, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict batched");
+        }
+        return ok();
+    }
+    // one token: a single kernel, hidden rows overlapping the logits tiles
+    const pi::FusedPredLayout L = pi::fused_pred_layout(r, ffn);
+    hipError_t e = hipSuccess;
+    if (clear) e = pi::launch_zero(data, L.total, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict clearing the workspace");
+    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, thr, L, hdr, data, idx, count, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict");
+    return ok();
+}
+
+pi_status run_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* W_up, const float* b_up,
+                     const pi_half* W_gate, const float* b_gate, const pi_half* W_down, const int32_t* idx,
+                     const int32_t* count, float* y, uint32_t flags, char* hdr, char* data, bool clear,
+                     hipStream_t s) {
+    const bool dense = (flags & PI_DENSE) != 0u;
+    const bool check = !dense && (flags & PI_CHECK_IDX) != 0u;
+    const bool reglu = kind == PI_FFN_REGLU;
+    const auto* hx = reinterpret_cast<const pi::h16*>(x);
+    const auto* hu = reinterpret_cast<const pi::h16*>(W_up);
+    const auto* hg = reinterpret_cast<const pi::h16*>(W_gate);
+    const auto* hd = reinterpret_cast<const pi::h16*>(W_down);
+    if (B >= 2 && !dense && !(flags & PI_PER_TOKEN)) {
+        for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
+            const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
+            const pi::BatchLayout L = pi::batch_layout(Bg, d, ffn);
+            hipError_t e = pi::launch_union(reglu, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
+                                            idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L,
+                                            data, hdr, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
+        }
+        if (check) {
+            hipError_t e = pi::launch_check_idx(idx, count, B, ffn, d, y, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse index check");
+        }
+        return ok();
+    }
+    if (!dense) {   // one token (or PI_PER_TOKEN): one kernel per token, up/gate rows overlapping W_down
+        const pi::FusedSparseLayout L = pi::fused_sparse_layout(d, ffn);
+        hipError_t e = hipSuccess;
+        if (clear) e = pi::launch_zero(data + L.atag, L.partial - L.atag, s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse clearing the workspace");
+        for (int t = 0; t < B && e == hipSuccess; ++t)
+            e = pi::launch_sparse_fused(reglu, hx + (size_t)t * d, d, ffn, hu, b_up, hg, b_gate, hd,
+                                        idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, hdr, data, s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse");
+        if (check) {
+            e = pi::launch_check_idx(idx, count, B, ffn, d, y, s);
+            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse index check");
+        }
+        return ok();
+    }
+    const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
+    float* a = reinterpret_cast<float*>(data + L.a);
+    float* partial = reinterpret_cast<float*>(data + L.partial);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(data + L.ctr);
+    hipError_t e = pi::launch_up_act(reglu, dense, hx, B, d, ffn, hu, b_up, hg, b_gate, idx, count, a,
+                                     ctr, L.T, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse up/gate");
+    e = pi::launch_down_acc(dense, hd, B, d, ffn, idx, count, a, y, partial, ctr, L.T, L.G, s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse down");
+    return ok();
+}
 
 }  // namespace
 
@@ -157,6 +301,11 @@ pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes)
         case PI_OP_PROFILE:
             *bytes = 0;
             return ok();
+        case PI_OP_DECODE:
+            PI_TRY(check_dims(B, d, ffn));
+            PI_REQUIRE(r > 0 && r <= PI_MAX_R, PI_ERR_INVALID_ARG, "r=%d outside [1, %d]", r, PI_MAX_R);
+            *bytes = decode_ws_bytes(B, d, r, ffn);
+            return ok();
     }
     return fail(PI_ERR_INVALID_ARG, "unknown op %d", op);
 }
@@ -164,129 +313,58 @@ pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes)
 pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, const float* b1,
                          int act, const pi_half* P2, const float* b2, int r, int ffn, float tau,
                          int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
-    PI_TRY(check_dims(B, d, ffn));
-    PI_REQUIRE(r > 0, PI_ERR_INVALID_ARG, "r=%d must be positive", r);
-    PI_REQUIRE(r % 8 == 0, PI_ERR_UNSUPPORTED, "r=%d is not a multiple of 8", r);
-    PI_REQUIRE(r <= PI_MAX_R, PI_ERR_UNSUPPORTED, "r=%d above PI_MAX_R=%d", r, PI_MAX_R);
-    PI_REQUIRE(act == PI_ACT_RELU || act == PI_ACT_NONE, PI_ERR_INVALID_ARG, "act=%d unknown", act);
-    PI_REQUIRE(tau > 0.f && tau < 1.f, PI_ERR_INVALID_ARG, "tau=%g not in (0, 1)", (double)tau);
-    PI_TRY(check_half(x, "x", true));
-    PI_TRY(check_half(P1, "P1", true));
-    PI_TRY(check_half(P2, "P2", true));
-    PI_TRY(check_word(b1, "b1", false));
-    PI_TRY(check_word(b2, "b2", false));
-    PI_TRY(check_word(idx, "idx", true));
-    PI_TRY(check_word(count, "count", true));
+    PI_TRY(check_predict_args(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count));
     PI_TRY(check_ws(ws, ws_bytes, predict_ws_bytes(B, r, ffn), "pi_ffn_predict"));
-
-    // sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
-    const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
     char* w = static_cast<char*>(ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const auto* hx = reinterpret_cast<const pi::h16*>(x);
-    const auto* h1 = reinterpret_cast<const pi::h16*>(P1);
-    const auto* h2 = reinterpret_cast<const pi::h16*>(P2);
-    if (B >= 2) {   // batched: both predictor layers on the matrix cores, weights read once per group
-        ws_forget(ws);
-        for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
-            const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
-            const pi::BPredLayout L = pi::bpred_layout(Bg, r, ffn);
-            hipError_t e = pi::launch_bpredict(hx + (size_t)g0 * d, Bg, d, h1, b1, act == PI_ACT_RELU, h2, b2,
-                                               r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L,
-                                               w + pi::kSyncBytes, w, s);
-            if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict batched");
-        }
-        return ok();
-    }
-    // one token: a single kernel, hidden rows overlapping the logits tiles
-    const pi::FusedPredLayout L = pi::fused_pred_layout(r, ffn);
-    const uint64_t key = layout_key(PI_OP_PREDICT, r, ffn);
-    hipError_t e = hipSuccess;
-    if (ws_needs_clear(ws, key)) e = pi::launch_zero(w + pi::kSyncBytes, L.total, s);
-    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict clearing the workspace");
-    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, thr, L, w, idx, count, s);
-    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict");
-    ws_record(ws, key);
-    return ok();
+    const LayoutKey key{PI_OP_PREDICT, 1, 0, r, ffn};
+    const bool fused = B == 1;
+    const bool clear = fused && ws_needs_clear(ws, key);
+    if (!fused) ws_forget(ws);
+    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count, w, w + pi::kSyncBytes, clear,
+                       static_cast<hipStream_t>(stream)));
+    if (fused) ws_record(ws, key);
+    return PI_OK;
 }
 
 pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* W_up,
                         const float* b_up, const pi_half* W_gate, const float* b_gate,
                         const pi_half* W_down, const int32_t* idx, const int32_t* count, float* y,
                         uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
-    PI_TRY(check_dims(B, d, ffn));
-    PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU, PI_ERR_INVALID_ARG, "kind=%d unknown", kind);
-    PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN | PI_DETERMINISTIC | PI_CHECK_IDX)) == 0u, PI_ERR_INVALID_ARG,
-               "unknown flags 0x%x", flags);
-    const bool dense = (flags & PI_DENSE) != 0u;
-    const bool check = !dense && (flags & PI_CHECK_IDX) != 0u;
-    const bool reglu = kind == PI_FFN_REGLU;
-    PI_REQUIRE(reglu == (W_gate != nullptr), PI_ERR_INVALID_ARG,
-               reglu ? "W_gate is NULL for a ReGLU FFN" : "W_gate given for a ReLU FFN");
-    PI_REQUIRE(reglu || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
-    PI_TRY(check_half(x, "x", true));
-    PI_TRY(check_half(W_up, "W_up", true));
-    PI_TRY(check_half(W_gate, "W_gate", false));
-    PI_TRY(check_half(W_down, "W_down", true));
-    PI_TRY(check_word(b_up, "b_up", false));
-    PI_TRY(check_word(b_gate, "b_gate", false));
-    PI_TRY(check_word(idx, "idx", !dense));
-    PI_TRY(check_word(count, "count", !dense));
-    PI_REQUIRE(y != nullptr, PI_ERR_INVALID_ARG, "y is NULL");
-    PI_REQUIRE(aligned(y, 16), PI_ERR_UNSUPPORTED, "y is not 16-byte aligned");
+    PI_TRY(check_sparse_args(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags));
     PI_TRY(check_ws(ws, ws_bytes, sparse_ws_bytes(B, d, ffn), "pi_ffn_sparse"));
+    char* w = static_cast<char*>(ws);
+    const LayoutKey key{PI_OP_SPARSE, 1, d, 0, ffn};
+    const bool fused = sparse_is_fused(B, flags);
+    const bool clear = fused && ws_needs_clear(ws, key);
+    if (!fused) ws_forget(ws);
+    PI_TRY(run_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w,
+                      w + pi::kSyncBytes, clear, static_cast<hipStream_t>(stream)));
+    if (fused) ws_record(ws, key);
+    return PI_OK;
+}
 
+pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1, const float* b1,
+                        int act, const pi_half* P2, const float* b2, int r, float tau, const pi_half* W_up,
+                        const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
+                        int32_t* idx, int32_t* count, float* y, uint32_t flags, void* ws, size_t ws_bytes,
+                        void* stream) {
+    PI_TRY(check_predict_args(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count));
+    PI_TRY(check_sparse_args(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags));
+    PI_REQUIRE((flags & PI_DENSE) == 0u, PI_ERR_INVALID_ARG, "PI_DENSE has no predictor step: call pi_ffn_sparse");
+    PI_TRY(check_ws(ws, ws_bytes, decode_ws_bytes(B, d, r, ffn), "pi_ffn_decode"));
     char* w = static_cast<char*>(ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const auto* hx = reinterpret_cast<const pi::h16*>(x);
-    const auto* hu = reinterpret_cast<const pi::h16*>(W_up);
-    const auto* hg = reinterpret_cast<const pi::h16*>(W_gate);
-    const auto* hd = reinterpret_cast<const pi::h16*>(W_down);
-    if (B >= 2 && !dense && !(flags & PI_PER_TOKEN)) {
-        ws_forget(ws);
-        for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
-            const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
-            const pi::BatchLayout L = pi::batch_layout(Bg, d, ffn);
-            hipError_t e = pi::launch_union(reglu, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
-                                            idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L,
-                                            w + pi::kSyncBytes, w, s);
-            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
-        }
-        if (check) {
-            hipError_t e = pi::launch_check_idx(idx, count, B, ffn, d, y, s);
-            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse index check");
-        }
-        return ok();
-    }
-    if (!dense) {   // one token (or PI_PER_TOKEN): one kernel per token, up/gate rows overlapping W_down
-        const pi::FusedSparseLayout L = pi::fused_sparse_layout(d, ffn);
-        const uint64_t key = layout_key(PI_OP_SPARSE, d, ffn);
-        hipError_t e = hipSuccess;
-        if (ws_needs_clear(ws, key)) e = pi::launch_zero(w + pi::kSyncBytes + L.atag, L.partial - L.atag, s);
-        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse clearing the workspace");
-        for (int t = 0; t < B && e == hipSuccess; ++t)
-            e = pi::launch_sparse_fused(reglu, hx + (size_t)t * d, d, ffn, hu, b_up, hg, b_gate, hd,
-                                        idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, w, s);
-        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse");
-        ws_record(ws, key);
-        if (check) {
-            e = pi::launch_check_idx(idx, count, B, ffn, d, y, s);
-            if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse index check");
-        }
-        return ok();
-    }
-    ws_forget(ws);
-    w += pi::kSyncBytes;
-    const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
-    float* a = reinterpret_cast<float*>(w + L.a);
-    float* partial = reinterpret_cast<float*>(w + L.partial);
-    uint32_t* ctr = reinterpret_cast<uint32_t*>(w + L.ctr);
-    hipError_t e = pi::launch_up_act(reglu, dense, hx, B, d, ffn, hu, b_up, hg, b_gate, idx, count, a,
-                                     ctr, L.T, s);
-    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse up/gate");
-    e = pi::launch_down_acc(dense, hd, B, d, ffn, idx, count, a, y, partial, ctr, L.T, L.G, s);
-    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse down");
-    return ok();
+    // one key for both data areas: where the FFN's starts depends on B, r and ffn
+    const LayoutKey key{PI_OP_DECODE, B, d, r, ffn};
+    const bool fused = B == 1 || sparse_is_fused(B, flags);
+    const bool clear = fused && ws_needs_clear(ws, key);
+    if (!fused) ws_forget(ws);
+    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count, w, w + pi::kSyncBytes,
+                       clear && B == 1, s));
+    PI_TRY(run_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w,
+                      w + decode_ffn_offset(B, r, ffn), clear && sparse_is_fused(B, flags), s));
+    if (fused) ws_record(ws, key);
+    return PI_OK;
 }
 
 pi_status pi_profile(const pi_half* X, int n, int d, int ffn, const pi_half* W_fire,

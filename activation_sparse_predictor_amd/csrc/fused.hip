@@ -531,28 +531,26 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
                                 const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
-                                char* ws, int32_t* idx, int32_t* count, hipStream_t s) {
-    char* data = ws + kSyncBytes;
+                                char* hdr, char* data, int32_t* idx, int32_t* count, hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
     const int NA = (r + 3) / 4;
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
-    const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
+    const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
-                       thr, htag, mtag, reinterpret_cast<uint32_t*>(ws + Sync::pred_epoch), idx, count, zero);
+                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
-                               const int32_t* count, float* y, const FusedSparseLayout& L, char* ws,
-                               hipStream_t s) {
-    char* data = ws + kSyncBytes;
+                               const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
+                               char* data, hipStream_t s) {
     uint64_t* atag = reinterpret_cast<uint64_t*>(data + L.atag);
     float* partial = reinterpret_cast<float*>(data + L.partial);
-    uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + Sync::ffn_ctr);
-    uint32_t* slots = reinterpret_cast<uint32_t*>(ws + Sync::ffn_epoch);
-    const float* zero = reinterpret_cast<const float*>(ws + Sync::zero);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_ctr);
+    uint32_t* slots = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_epoch);
+    const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     dim3 grid(L.NU + L.T * L.G);
     if (reglu)
         hipLaunchKernelGGL(k_sparse_fused<true>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,

@@ -151,8 +151,10 @@ inline BPredLayout bpred_layout(int B, int r, int ffn) {
 // of every workspace, which no other layout touches: the header is zero-filled
 // once when the workspace is allocated; each counter is put back to 0 by the
 // last arrival of every call, and each epoch advances by one per launch on
-// the device (so a captured graph replays with a new epoch each time).  All
-// other layouts start kSyncBytes in.
+// the device (so a captured graph replays with a new epoch each time).  A
+// call's data area starts kSyncBytes in (pi_ffn_decode puts the FFN's data
+// area after the predictor's, behind the one header they share: predict and
+// the FFN use disjoint header fields).
 constexpr int kFusedCols = 512;                     // W_down columns per tile
 constexpr int kFusedMaxTiles = 16384 / kFusedCols;  // PI_MAX_D / kFusedCols
 constexpr int kFusedMaxChunks = 48;                 // list chunks per W_down tile
@@ -161,8 +163,7 @@ struct Sync {   // byte offsets inside the header
     static constexpr size_t ffn_epoch = ffn_ctr + (size_t)kFusedMaxTiles * kCtrStride * 4;  // per tile
     static constexpr size_t pred_epoch = ffn_epoch + kFusedMaxTiles * 4;    // last predict launch's epoch
     static constexpr size_t zero = pred_epoch + 128;                        // never written
-    static constexpr size_t bpred_ctr = zero + 256;                         // batched predictor: one per 64 rows of P1
-    static constexpr size_t end = bpred_ctr + (size_t)(8192 / 32) * 4;
+    static constexpr size_t end = zero + 256;
 };
 constexpr size_t kSyncBytes = 8192;
 static_assert(Sync::end <= kSyncBytes, "sync header overflow");
@@ -225,11 +226,11 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
 // fused.hip
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
                                 const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
-                                char* ws, int32_t* idx, int32_t* count, hipStream_t s);
+                                char* hdr, char* data, int32_t* idx, int32_t* count, hipStream_t s);
 hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
-                               const int32_t* count, float* y, const FusedSparseLayout& L, char* ws,
-                               hipStream_t s);
+                               const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
+                               char* data, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // profile.hip

@@ -97,10 +97,29 @@ def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
     return y
 
 
-def decode(layer: dict, x: torch.Tensor, stream=None):
-    """One decode step: predict the active set, then the sparse FFN. Returns (y, idx, count)."""
-    idx, count = predict(layer, x, stream=stream)
-    y = sparse(layer, x, idx, count, stream=stream)
+def decode(layer: dict, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+           idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+           act: str = "relu", tau: Optional[float] = None, per_token: bool = False,
+           check_idx: bool = False, stream=None):
+    """One decode step through pi_ffn_decode: the predicted list and the sparse
+    FFN over it (one kernel for a single token).  Returns (y, idx, count)."""
+    Bt, d = x.shape
+    ffn, r = layer["ffn"], layer["r"]
+    if y is None:
+        y = torch.empty(Bt, d, dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty(Bt, ffn, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(Bt, dtype=torch.int32, device=x.device)
+    nbytes = B.pi_workspace_size(B.PI_OP_DECODE, Bt, d, r, ffn)
+    ws, wsb = workspace("decode", x.device).get(nbytes)
+    st = B.pi_ffn_decode(B.KINDS[layer["kind"]], _bits(x), Bt, d, ffn, layer["P1"], layer.get("b1"),
+                         B.ACTS[act], layer["P2"], layer.get("b2"), r,
+                         float(layer["tau"] if tau is None else tau), layer["W_up"], layer.get("b_up"),
+                         layer.get("W_gate"), layer.get("b_gate"), layer["W_down"], idx, count, y,
+                         (B.PI_PER_TOKEN if per_token else 0) | (B.PI_CHECK_IDX if check_idx else 0),
+                         ws, wsb, stream)
+    B.check(st, "pi_ffn_decode")
     return y, idx, count
 
 

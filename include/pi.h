@@ -70,7 +70,8 @@ typedef enum pi_pred_act {
 typedef enum pi_op {
     PI_OP_PREDICT = 0,
     PI_OP_SPARSE = 1,
-    PI_OP_PROFILE = 2
+    PI_OP_PROFILE = 2,
+    PI_OP_DECODE = 3
 } pi_op;
 
 /* pi_ffn_sparse flags */
@@ -158,6 +159,33 @@ pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn,
                         const pi_half* W_down,
                         const int32_t* idx, const int32_t* count,
                         float* y, uint32_t flags,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * pi_ffn_decode -- one decode step of the layer: pi_ffn_predict followed by
+ * pi_ffn_sparse on its list (the predictor, then the neuron-aware operator on
+ * the predicted neurons only: Part A section 2.3 modules 3 and 4).
+ *
+ * Arguments are those of the two calls, with the same meaning, layouts and
+ * checks; idx and count are outputs (the predicted list, as pi_ffn_predict
+ * writes it) and y is computed from them.  flags: as pi_ffn_sparse, except
+ * PI_DENSE, which is INVALID_ARG here (a dense step has no predictor).
+ *
+ * The call is pi_ffn_predict then pi_ffn_sparse on the same stream, so its
+ * results are bitwise theirs (two kernels for B = 1).  The workspace is split
+ * between the two, each part laid out as that call's own workspace, so that
+ * repeated steps never clear it.
+ *
+ * ws: at least pi_workspace_size(PI_OP_DECODE, B, d, r, ffn) bytes (the
+ * workspace rules above apply).
+ */
+pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn,
+                        const pi_half* P1, const float* b1, int act,
+                        const pi_half* P2, const float* b2, int r, float tau,
+                        const pi_half* W_up, const float* b_up,
+                        const pi_half* W_gate, const float* b_gate,
+                        const pi_half* W_down,
+                        int32_t* idx, int32_t* count, float* y, uint32_t flags,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*

@@ -28,8 +28,8 @@ def _declared():
 
 def test_header_declares_the_expected_entry_points():
     names = _declared()
-    for want in ("pi_ffn_predict", "pi_ffn_sparse", "pi_profile", "pi_reorder", "pi_permute_rows",
-                 "pi_workspace_size", "pi_status_string", "pi_last_error"):
+    for want in ("pi_ffn_predict", "pi_ffn_sparse", "pi_ffn_decode", "pi_profile", "pi_reorder",
+                 "pi_permute_rows", "pi_workspace_size", "pi_status_string", "pi_last_error"):
         assert want in names
 
 
@@ -83,6 +83,10 @@ def test_workspace_size_queries():
     s = B.pi_workspace_size(B.PI_OP_SPARSE, 1, 7168, 1024, 28672)
     assert p >= 1024 * 4 and s >= 28672 * 4
     assert B.pi_workspace_size(B.PI_OP_SPARSE, 4, 7168, 1024, 28672) > s
+    for Bt in (1, 4):   # the decode step's workspace: both calls' data areas behind one 8 KB header
+        dec = B.pi_workspace_size(B.PI_OP_DECODE, Bt, 7168, 1024, 28672)
+        assert dec >= B.pi_workspace_size(B.PI_OP_PREDICT, Bt, 7168, 1024, 28672) + \
+            B.pi_workspace_size(B.PI_OP_SPARSE, Bt, 7168, 1024, 28672) - 8192
     out = ctypes.c_size_t(0)
     assert B.load().pi_workspace_size(9, 1, 8, 8, 8, ctypes.byref(out)) == B.PI_ERR_INVALID_ARG
     assert B.load().pi_workspace_size(0, 0, 8, 8, 8, ctypes.byref(out)) == B.PI_ERR_INVALID_ARG
@@ -158,6 +162,34 @@ def test_predict_rejects_before_launch(kw, code):
 ])
 def test_sparse_rejects_before_launch(kw, code):
     assert _sparse(**kw) == code
+    assert B.last_error() != ""
+
+
+def _decode(**kw):
+    args = dict(kind=B.PI_FFN_RELU, x=A, B=1, d=64, ffn=128, P1=A, b1=None, act=B.PI_ACT_RELU, P2=A, b2=None,
+                r=16, tau=0.5, W_up=A, b_up=None, W_gate=None, b_gate=None, W_down=A, idx=A, count=A, y=A,
+                flags=0, ws=A, ws_bytes=0, stream=0)
+    args.update(kw)
+    return B.pi_ffn_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), B.PI_ERR_INVALID_ARG),
+    (dict(P1=None), B.PI_ERR_INVALID_ARG),
+    (dict(W_up=None), B.PI_ERR_INVALID_ARG),
+    (dict(y=None), B.PI_ERR_INVALID_ARG),
+    (dict(idx=None), B.PI_ERR_INVALID_ARG),
+    (dict(tau=1.5), B.PI_ERR_INVALID_ARG),
+    (dict(kind=B.PI_FFN_REGLU), B.PI_ERR_INVALID_ARG),      # gate missing for ReGLU
+    (dict(flags=B.PI_DENSE), B.PI_ERR_INVALID_ARG),         # a dense step has no predictor
+    (dict(flags=0x80), B.PI_ERR_INVALID_ARG),
+    (dict(r=12), B.PI_ERR_UNSUPPORTED),
+    (dict(y=A + 4), B.PI_ERR_UNSUPPORTED),
+    (dict(ws=None), B.PI_ERR_WORKSPACE),
+    (dict(ws_bytes=64), B.PI_ERR_WORKSPACE),
+])
+def test_decode_rejects_before_launch(kw, code):
+    assert _decode(**kw) == code
     assert B.last_error() != ""
 
 
