@@ -12,7 +12,8 @@
 //   workgroups [0, NU)        up chunks, one wave per active row:
 //                             a_j = act(W_up[i].x + b_up_i [, W_gate[i].x + b_gate_i]),
 //                             published as a tagged word
-//   workgroups [NU, NU + T*G) W_down (column tile, list chunk): stage the chunk's
+//   workgroups [NU, NU + T*G) W_down (column tile, list chunk; chunks past
+//                             ceil(count / kSChunkRows) exit at once): stage the chunk's
 //                             ids, issue its row segments, collect the chunk's
 //                             a_j, accumulate; the last chunk of a column tile to
 //                             arrive adds the G partials in chunk order
@@ -319,7 +320,8 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
 constexpr int kSThreads = 512;                       // 8 waves
 constexpr int kSColThreads = kFusedCols / 8;         // column threads of a W_down tile (8 fp16 each)
 constexpr int kSGroups = kSThreads / kSColThreads;   // row groups per W_down workgroup
-constexpr int kSBatch = 8;                           // W_down rows in flight per thread
+constexpr int kSBatch = 16;                          // W_down rows in flight per thread
+constexpr int kSChunkRows = kSGroups * kSBatch;      // list entries of a chunk that fill one batch per group
 constexpr int kSWindow = 2048;                       // list entries staged in LDS at a time
 static_assert(kSColThreads * kSGroups == kSThreads, "tile shape");
 static_assert(kFusedCols <= kSThreads, "one reduction column per thread");
@@ -428,7 +430,12 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     // ---------------- W_down (column tile, chunk)
     const int k = blockIdx.x - NU;
     const int tile = k % T, chunk = k / T;
-    const int PD = (cnt + G - 1) / G;
+    // Chunks in use: as many as give every row group at most one batch of
+    // rows (the launch has G, the most).  Fewer, fuller chunks stream better,
+    // and a second, mostly empty batch would cost as much as a full one.
+    const int Ge = min(G, max(1, (cnt + kSChunkRows - 1) / kSChunkRows));
+    if (chunk >= Ge) return;
+    const int PD = (cnt + Ge - 1) / Ge;
     const int j0 = min(cnt, chunk * PD), j1 = min(cnt, j0 + PD);
     const int ct = tid % kSColThreads;
     const int rg = __builtin_amdgcn_readfirstlane(tid / kSColThreads);
@@ -508,7 +515,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     __syncthreads();
     if (tid == 0) {
         uint32_t* c = &ctr[(size_t)tile * kCtrStride];
-        const int flag = fetch_add(c, 1u) == (uint32_t)(G - 1);
+        const int flag = fetch_add(c, 1u) == (uint32_t)(Ge - 1);
         if (flag) st_flag(c, 0u);   // the last arrival puts the counter back for the next call
         s_flag = flag;
     }
@@ -523,7 +530,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     float sum = 0.f;
 #pragma unroll
     for (int g = 0; g < kFusedMaxChunks; ++g)
-        if (g < G) sum += v[g];
+        if (g < Ge) sum += v[g];
     y[gc] = sum;
     // every chunk of this tile has read the epoch: the tile's slot advances
     if (tid == 0) st_flag(&slots[tile], epoch);

@@ -188,8 +188,7 @@ struct FusedSparseLayout {
 inline FusedSparseLayout fused_sparse_layout(int d, int ffn) {
     FusedSparseLayout L;
     L.T = (d + kFusedCols - 1) / kFusedCols;
-    L.G = 672 / L.T;   // about 672 W_down workgroups: 2-3 per CU
-    if (L.G > kFusedMaxChunks) L.G = kFusedMaxChunks;
+    L.G = kFusedMaxChunks;   // launched; the kernel uses as many as the count needs
     if (L.G > ffn) L.G = ffn;
     if (L.G < 1) L.G = 1;
     L.NU = (ffn + 7) / 8 < 384 ? (ffn + 7) / 8 : 384;   // up chunks (8 waves each)

@@ -129,6 +129,20 @@ def test_sparse_edge_lists(kind):
         check_y(_sparse_with(L, x, lst), _oracle_y(H, xh, lst), where=f"{kind} list len {len(lst)}")
 
 
+@pytest.mark.parametrize("n", [127, 128, 129, 6143, 6144, 6145, 16000])
+def test_sparse_list_lengths_around_chunking(n):
+    """The single-token FFN uses ceil(n / 128) list chunks per column tile (at
+    most 48): lengths at the chunk-count steps, and past 48 x 128 where each
+    row group takes several batches of 16 rows in turn."""
+    cfg = custom_config("relu", 520, 16384, 16, mean=0.3, number=59)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    x = make_tokens(cfg, 1).to(DEV)
+    rng = np.random.default_rng(n)
+    lst = np.sort(rng.choice(cfg.ffn, size=n, replace=False)).tolist()
+    check_y(_sparse_with(L, x, lst), _oracle_y(H, x[0].cpu(), lst), where=f"list len {n}")
+
+
 @pytest.mark.parametrize("kind", ["relu", "reglu"])
 def test_dense_flag(kind):
     cfg = custom_config(kind, 520, 2080, 16, number=55)
