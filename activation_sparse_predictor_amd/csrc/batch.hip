@@ -252,6 +252,65 @@ __global__ __launch_bounds__(256) void k_bpred_hidden_finish(RingArgs a, HiddenE
     ring_finish<C>(a, a.nrows, G0, epi);
 }
 
+// Hidden layer for groups of at most 8 tokens, on the vector units: one wave
+// per P1 row streams the whole row once and takes the TB dot products against
+// the group's x, staged in LDS by direct-to-LDS loads that go out behind the
+// row's loads (tokens past B repeat token B - 1; their sums are dropped).  It
+// writes h straight into the hi/lo pair the logits GEMM reads, so no K-split
+// pieces and no finishing kernel.  Workgroup 0 zeroes the logits counters.
+// x takes TB x roundup(d/8, 64) x 16 bytes of LDS: kHidValuChunks bounds d.
+constexpr int hid_valu_chunks(int TB) { return TB <= 4 ? 2048 : 1152; }   // d <= 16384 / 9216
+template <int TB>
+__global__ __launch_bounds__(256) void k_bpred_hidden_valu(const h16* __restrict__ x, int B, int d,
+                                                           const h16* __restrict__ P1, HiddenEpi epi,
+                                                           uint32_t* __restrict__ lctr, int nlctr) {
+    __shared__ __align__(16) u32x4 sx[TB * hid_valu_chunks(TB)];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0)
+        for (int i = tid; i < nlctr; i += 256) lctr[i] = 0u;
+    const int r = epi.r;
+    const int row = blockIdx.x * 4 + wave;
+    const h16* prow = P1 + (size_t)min(row, r - 1) * d;
+    const int nch = d >> 3;
+    const int ncp = (nch + 63) & ~63;   // LDS chunks per token
+    u32x4 w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w[u] = ld16_stream(prow + (size_t)min(lane + u * 64, nch - 1) * 8);
+    // x behind the row: block b = (token, 64 chunks) -> LDS [token][chunk]
+    const uint32_t sbase = lds_addr(sx);
+    const int nbt = ncp / 64;
+    for (int b = wave; b < TB * nbt; b += 4) {
+        const int t = b / nbt, c0 = (b % nbt) * 64;
+        dma16(x + (size_t)min(t, B - 1) * d + (size_t)min(c0 + lane, nch - 1) * 8,
+              sbase + (uint32_t)(t * ncp + c0) * 16u);
+    }
+    wait_vm<0>();
+    ring_barrier();
+    float acc[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) acc[t] = 0.f;
+    for (int c0 = lane; c0 < nch; c0 += 64 * 16) {
+        if (c0 != lane) {   // rows longer than 8192: the next 16 chunks per lane
+#pragma unroll
+            for (int u = 0; u < 16; ++u) w[u] = ld16_stream(prow + (size_t)min(c0 + u * 64, nch - 1) * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int c = c0 + u * 64;
+            if (c < nch) {
+#pragma unroll
+                for (int t = 0; t < TB; ++t) acc[t] = dot8_h(w[u], sx[t * ncp + c], acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+        const float v = group_sum<64>(acc[t]);
+        if (lane == t && row < r) epi(row, t, v, 0.f);   // drops t >= B
+    }
+}
+
 // Logits: Z = P2 H^T + b2 with both halves of h, then the strict test
 // z > thr per (neuron, token); every 32 neurons give one 32-bit mask word per
 // token (bit k = neuron 32*word + k).  Each half of a wave holds 32 neurons
@@ -700,15 +759,26 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
         hipLaunchKernelGGL((k_bpred_hidden<HidCfg<N>>), dim3(gh), dim3(256), 0, s, ha, he, lctr, nlctr);      \
         hipLaunchKernelGGL((k_bpred_hidden_finish<HidCfg<N>>), dim3(gfin), dim3(256), 0, s, ha, he, gh);      \
     }
+    // up to 8 tokens: the hidden layer on the vector units when the group's x fits in LDS
+    const int nch = d / 8;
+    const int gv = (r + 3) / 4;
+    const bool valu = B <= 8 && nch <= hid_valu_chunks(B <= 4 ? 4 : 8);
+#define PI_BHV(TB) hipLaunchKernelGGL(k_bpred_hidden_valu<TB>, dim3(gv), dim3(256), 0, s, x, B, d, P1, he, lctr, nlctr)
 #define PI_BL(N) hipLaunchKernelGGL((k_bpred_logits<LogCfg<N>>), dim3(ring_grid<k_bpred_logits<LogCfg<N>>>()), \
                                     dim3(256), 0, s, la, b2, thr, masks32)
     const int xg = ring_xg(B);
-    if (xg == 1) { PI_BH(1); PI_BL(1); }
+    if (valu) {
+        if (B <= 2) PI_BHV(2);
+        else if (B <= 4) PI_BHV(4);
+        else PI_BHV(8);
+    }
+    if (xg == 1) { if (!valu) PI_BH(1); PI_BL(1); }
     else if (xg == 2) { PI_BH(2); PI_BL(2); }
     else if (xg == 4) { PI_BH(4); PI_BL(4); }
     else if (xg == 8) { PI_BH(8); PI_BL(8); }
     else { PI_BH(16); PI_BL(16); }
 #undef PI_BH
+#undef PI_BHV
 #undef PI_BL
     hipLaunchKernelGGL(k_bpred_compact, dim3(B), dim3(256), 0, s, masks32, ffn, idx, count);
     return hipGetLastError();

@@ -197,6 +197,32 @@ def test_batched_union_path(kind, Bt):
         check_y(Yp_h[t], ref, where=f"per-token B={Bt} t={t}")
 
 
+@pytest.mark.parametrize("Bt,d", [(3, 520), (5, 520), (3, 8200), (7, 9216), (6, 9224), (8, 16384)])
+def test_batched_predictor_hidden_paths(Bt, d):
+    """Groups of up to 8 tokens take the hidden layer on the vector units when
+    their x fits in LDS (B <= 4: d <= 16384; B <= 8: d <= 9216), else on the
+    matrix cores: padding tokens, rows longer than 8192, both sides of the
+    size limit.  The index rule per token against the oracle, and agreement
+    with the single-token predictor outside the threshold band."""
+    cfg = custom_config("relu", d, 1000, 72, mean=0.15, number=58)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    X = make_tokens(cfg, Bt).to(DEV)
+    idx, cnt = R.predict(L, X)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    for t in range(Bt):
+        c = int(cnt[t].item())
+        mine = idx[t, :c].cpu().numpy()
+        z = O.predictor_logits(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"])
+        check_idx(mine, z, thr, where=f"B={Bt} d={d} t={t}")
+        i1, c1 = R.predict(L, X[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        single = i1[0, :int(c1.item())].cpu().numpy()
+        diff = set(mine.tolist()) ^ set(single.tolist())
+        assert all(abs(z[j] - thr) <= 1e-3 for j in diff), f"B={Bt} d={d} t={t}: lists differ outside the band"
+
+
 def test_union_path_edge_lists():
     """Empty lists, disjoint lists, identical lists, one full list, a list whose
     32-neuron words run across the 64-entry waves that build the token
