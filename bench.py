@@ -334,7 +334,82 @@ def main():
         f"T {T_avg / 1e6:.1f} MB -> {T_avg / ms_step / 1e6:.0f} GB/s")
     del graph
 
-    # per entry point: events between the two calls of each step
+    # The same steps through pi_ffn_decode (one call per step), graph-timed.
+    def dstep(s):
+        l, t = s % NL, (s // NL) % NT
+        R.decode(layers[l], xs[l][t], y, idx, cnt)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        for s in range(Kg):
+            dstep(s)
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for s in range(Kg):
+                dstep(s)
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup // Kg)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_decode = e0.elapsed_time(e1) / n_graph
+    del graph
+    log(f"decode step (pi_ffn_decode) {ms_decode * 1000:.2f} us, {1000.0 / ms_decode:.0f} tok/s/layer")
+
+    # Per entry point: a graph of Kg back-to-back launches of that entry point
+    # alone (rotating layers and tokens as above), replayed between HIP events
+    # on the launching stream, so that the average covers the kernel itself
+    # and not the host's launch gap.  The sparse launches read the lists the
+    # predict launches wrote, one list per step.
+    idx_g = torch.empty(Kg, ffn, dtype=torch.int32, device=dev)
+    cnt_g = torch.empty(Kg, dtype=torch.int32, device=dev)
+    lt = [(s % NL, (s // NL) % NT) for s in range(Kg)]
+
+    def run_pred():
+        for s, (l, t) in enumerate(lt):
+            R.predict(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1])
+
+    def run_sparse():
+        for s, (l, t) in enumerate(lt):
+            R.sparse(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1], y)
+
+    def graph_time(fn):
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            fn()
+            cs.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) / (reps * Kg)
+
+    run_pred()
+    torch.cuda.synchronize()
+    ms_pred = graph_time(run_pred)
+    ms_sp = graph_time(run_sparse)
+    pred_bytes = 2 * r * d + 2 * ffn * r + 4 * ffn + 2 * d
+    m = 2 if kind == "reglu" else 1
+    sp_bytes = [(m + 1) * int(counts_h[l, t]) * (2 * d + 4) + 4 * d for (l, t) in lt]
+    gbs_pred = pred_bytes / ms_pred / 1e6
+    gbs_sp = statistics.mean(sp_bytes) / ms_sp / 1e6
+
+    # the same, eagerly: HIP events between the two calls of each step (the
+    # per-call figure includes the host's launch gap)
     K2 = min(args.steps, 400)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K2)]
     for k in range(K2):
@@ -346,17 +421,12 @@ def main():
         R.sparse(layers[l], xs[l][t], idx, cnt, y)
         ev[3 * k + 2].record(stream)
     torch.cuda.synchronize()
-    t_pred = [ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(K2)]
-    t_sp = [ev[3 * k + 1].elapsed_time(ev[3 * k + 2]) for k in range(K2)]
-    pred_bytes = 2 * r * d + 2 * ffn * r + 4 * ffn + 2 * d
-    m = 2 if kind == "reglu" else 1
-    sp_bytes = [(m + 1) * int(counts_h[(s0 + k) % NL, ((s0 + k) // NL) % NT]) * (2 * d + 4) + 4 * d
-                for k in range(K2)]
-    ms_pred, ms_sp = statistics.mean(t_pred), statistics.mean(t_sp)
-    gbs_pred = pred_bytes / ms_pred / 1e6
-    gbs_sp = statistics.mean(sp_bytes) / ms_sp / 1e6
+    eager_us = {"pi_ffn_predict": 1000 * statistics.mean(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(K2)),
+                "pi_ffn_sparse": 1000 * statistics.mean(ev[3 * k + 1].elapsed_time(ev[3 * k + 2])
+                                                        for k in range(K2))}
     log(f"predict {ms_pred * 1000:.2f} us ({gbs_pred:.0f} GB/s), sparse {ms_sp * 1000:.2f} us "
-        f"({gbs_sp:.0f} GB/s)")
+        f"({gbs_sp:.0f} GB/s) per launch in graphs; eager per call {eager_us['pi_ffn_predict']:.2f} / "
+        f"{eager_us['pi_ffn_sparse']:.2f} us")
 
     stages = {"pi_ffn_predict": (ms_pred, gbs_pred, pred_bytes),
               "pi_ffn_sparse": (ms_sp, gbs_sp, statistics.mean(sp_bytes))}
@@ -434,13 +504,18 @@ def main():
                    "mean_active": float(counts_h.float().mean()),
                    "touched_MB_per_step": T_avg / 1e6},
         "achieved_GBs_step": T_avg / ms_step / 1e6,
+        "decode_call": {"us_per_step": ms_decode * 1000, "tokens_per_s_per_layer": 1000.0 / ms_decode,
+                        "GBs": T_avg / ms_decode / 1e6},
         "timing": {"method": f"hipGraph of {Kg} steps replayed {reps} times, HIP events around the replays",
                    "ms_per_step_eager": ms_eager},
         "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dom], "entry_point": dom, "achieved": stages[dom][1],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": stages[dom][1] / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, dom),
                      "step_frac": T_avg / ms_step / 1e6 / HBM_PEAK_GBS,
-                     "stages_us": {k: v[0] * 1000 for k, v in stages.items()}},
+                     "stages_us": {k: v[0] * 1000 for k, v in stages.items()},
+                     "stages_method": f"graph of {Kg} back-to-back launches of one entry point, "
+                                      f"replayed {reps} times between HIP events",
+                     "stages_us_eager_per_call": eager_us},
         "dense_baseline": dense,
         "cpu_baseline": cpu,
         "batch_sweep": sweep,

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 from activation_sparse_predictor_amd import binding as B
 from activation_sparse_predictor_amd import runtime as R
-from synthetic import CONFIGS, custom_config, make_layer, make_tokens
+from synthetic import CONFIGS, custom_config, make_calibration, make_layer, make_tokens
 from tests.parity import check_idx, check_y
 
 pytestmark = pytest.mark.gpu
@@ -219,6 +219,26 @@ def test_decode_dense_flag_rejected():
     wsb = B.pi_workspace_size(B.PI_OP_DECODE, 1, 64, 8, 64)
     ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     assert B.pi_ffn_decode(*_args(L, x, idx, cnt, y, ws, wsb, flags=B.PI_DENSE)) == B.PI_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kind", ["relu", "reglu"])
+def test_decode_step_hot_first_layer(kind):
+    """A hot-first reordered layer: the active neurons crowd into the first
+    logits tiles, so a few tiles append most of the up workers' queue."""
+    cfg = custom_config(kind, 1032, 4160, 136, mean=0.15, exponent=1.3, number=95)
+    L = R.to_device(make_layer(cfg), DEV)
+    Xc = make_calibration(cfg, 512).to(DEV)
+    Wf = L["W_up"] if kind == "relu" else L["W_gate"]
+    bf = L["b_up"] if kind == "relu" else L["b_gate"]
+    counts = R.profile(Xc, Wf, bf).cpu().numpy()
+    perm, _ = R.reorder(counts, 0.8)
+    P = R.permute_layer(L, torch.from_numpy(perm).to(DEV))
+    X = make_tokens(cfg, 4).to(DEV)
+    got = _check_step(P, X, where=f"hot-first {kind}")
+    # most of each list sits in the first quarter of the neurons
+    idx, cnt = R.predict(P, X[:1].contiguous())
+    c = int(cnt.cpu()[0])
+    assert sum(got) > 0 and np.mean(idx[0, :c].cpu().numpy() < cfg.ffn // 4) > 0.5
 
 
 @pytest.mark.parametrize("key", ["c2", "c3"])
