@@ -517,7 +517,8 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
                 const int e = st * C::KR + kofs[i];
                 p = (abase[i] && e < n_ids) ? abase[i] + u0 + e : zsrc;
             }
-            dma16(p, dst + (wave + 4 * i) * 1024);
+            if (i < C::WBLK / 4) dma16_stream(p, dst + (wave + 4 * i) * 1024);   // W_down: read once
+            else dma16(p, dst + (wave + 4 * i) * 1024);
         }
     };
 

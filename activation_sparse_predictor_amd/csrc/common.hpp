@@ -132,6 +132,12 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds_addr), "v"(gptr) : "memory", "m0");
 }
+// dma16_stream marks the line non-temporal: a weight byte is read once, so
+// the line is the first to go from L2, and the activations that every
+// workgroup re-reads stay resident there.
+__device__ __forceinline__ void dma16_stream(const void* gptr, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" : : "s"(lds_addr), "v"(gptr) : "memory", "m0");
+}
 __device__ __forceinline__ void dma16_coherent(const void* gptr, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1" : : "s"(lds_addr), "v"(gptr)
                  : "memory", "m0");

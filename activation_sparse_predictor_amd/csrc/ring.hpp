@@ -172,7 +172,8 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
             for (int i = 0; i < C::IPW; ++i) {
                 const int k = st * C::KST + kofs[i];
                 const h16* p = (ok[i] && k < a.K) ? src[i] + k : a.zsrc;
-                dma16(p, dst + (wave + 4 * i) * 1024);
+                if (i < C::WBLK / 4) dma16_stream(p, dst + (wave + 4 * i) * 1024);   // weights: read once
+                else dma16(p, dst + (wave + 4 * i) * 1024);
             }
         };
 
