@@ -24,6 +24,7 @@ PI_ERR_HIP = 4
 
 PI_FFN_RELU = 0
 PI_FFN_REGLU = 1
+PI_FFN_SWIGLU = 2
 PI_ACT_RELU = 0
 PI_ACT_NONE = 1
 PI_OP_PREDICT = 0
@@ -35,7 +36,7 @@ PI_PER_TOKEN = 0x2
 PI_DETERMINISTIC = 0x4
 PI_CHECK_IDX = 0x8
 
-KINDS = {"relu": PI_FFN_RELU, "reglu": PI_FFN_REGLU}
+KINDS = {"relu": PI_FFN_RELU, "reglu": PI_FFN_REGLU, "swiglu": PI_FFN_SWIGLU}
 ACTS = {"relu": PI_ACT_RELU, "none": PI_ACT_NONE}
 
 _P = ctypes.c_void_p

@@ -161,14 +161,15 @@ pi_status check_sparse_args(int kind, const pi_half* x, int B, int d, int ffn, c
                             const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
                             const int32_t* idx, const int32_t* count, const float* y, uint32_t flags) {
     PI_TRY(check_dims(B, d, ffn));
-    PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU, PI_ERR_INVALID_ARG, "kind=%d unknown", kind);
+    PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU || kind == PI_FFN_SWIGLU, PI_ERR_INVALID_ARG,
+               "kind=%d unknown", kind);
     PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN | PI_DETERMINISTIC | PI_CHECK_IDX)) == 0u, PI_ERR_INVALID_ARG,
                "unknown flags 0x%x", flags);
     const bool dense = (flags & PI_DENSE) != 0u;
-    const bool reglu = kind == PI_FFN_REGLU;
-    PI_REQUIRE(reglu == (W_gate != nullptr), PI_ERR_INVALID_ARG,
-               reglu ? "W_gate is NULL for a ReGLU FFN" : "W_gate given for a ReLU FFN");
-    PI_REQUIRE(reglu || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
+    const bool gated = kind != PI_FFN_RELU;   // ReGLU and SwiGLU take a W_gate row per neuron
+    PI_REQUIRE(gated == (W_gate != nullptr), PI_ERR_INVALID_ARG,
+               gated ? "W_gate is NULL for a gated (ReGLU / SwiGLU) FFN" : "W_gate given for a ReLU FFN");
+    PI_REQUIRE(gated || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
     PI_TRY(check_half(x, "x", true));
     PI_TRY(check_half(W_up, "W_up", true));
     PI_TRY(check_half(W_gate, "W_gate", false));
@@ -221,7 +222,6 @@ pi_status run_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi
                      hipStream_t s) {
     const bool dense = (flags & PI_DENSE) != 0u;
     const bool check = !dense && (flags & PI_CHECK_IDX) != 0u;
-    const bool reglu = kind == PI_FFN_REGLU;
     const auto* hx = reinterpret_cast<const pi::h16*>(x);
     const auto* hu = reinterpret_cast<const pi::h16*>(W_up);
     const auto* hg = reinterpret_cast<const pi::h16*>(W_gate);
@@ -230,7 +230,7 @@ pi_status run_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi
         for (int g0 = 0; g0 < B; g0 += pi::kUnionMaxTokens) {
             const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
             const pi::BatchLayout L = pi::batch_layout(Bg, d, ffn);
-            hipError_t e = pi::launch_union(reglu, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
+            hipError_t e = pi::launch_union(kind, hx + (size_t)g0 * d, Bg, d, ffn, hu, b_up, hg, b_gate, hd,
                                             idx + (size_t)g0 * ffn, count + g0, y + (size_t)g0 * d, L,
                                             data, hdr, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse union path");
@@ -247,7 +247,7 @@ pi_status run_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi
         if (clear) e = pi::launch_zero(data + L.atag, L.partial - L.atag, s);
         if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse clearing the workspace");
         for (int t = 0; t < B && e == hipSuccess; ++t)
-            e = pi::launch_sparse_fused(reglu, hx + (size_t)t * d, d, ffn, hu, b_up, hg, b_gate, hd,
+            e = pi::launch_sparse_fused(kind, hx + (size_t)t * d, d, ffn, hu, b_up, hg, b_gate, hd,
                                         idx + (size_t)t * ffn, count + t, y + (size_t)t * d, L, hdr, data, s);
         if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse");
         if (check) {
@@ -260,7 +260,7 @@ pi_status run_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi
     float* a = reinterpret_cast<float*>(data + L.a);
     float* partial = reinterpret_cast<float*>(data + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(data + L.ctr);
-    hipError_t e = pi::launch_up_act(reglu, dense, hx, B, d, ffn, hu, b_up, hg, b_gate, idx, count, a,
+    hipError_t e = pi::launch_up_act(kind, dense, hx, B, d, ffn, hu, b_up, hg, b_gate, idx, count, a,
                                      ctr, L.T, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse up/gate");
     e = pi::launch_down_acc(dense, hd, B, d, ffn, idx, count, a, y, partial, ctr, L.T, L.G, s);

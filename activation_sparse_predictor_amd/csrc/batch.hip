@@ -188,7 +188,7 @@ using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, rbw_up(XG), ring_seg(REGLU ? 2 : 1, 
 // token t did not select neuron U_u), stored token-major as an fp16 hi/lo
 // pair: aT[t][u], for every token slot t < Bp (zero past B) and for u up to
 // the next multiple of 8 past |U| (zero past |U|).
-template <class C, bool REGLU>
+template <class C, int KIND>
 __global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __restrict__ ucount, int ffn,
                                                   const float* __restrict__ bup, const float* __restrict__ bg,
                                                   const uint32_t* __restrict__ tokbits, int nw, int Bp, int lda,
@@ -207,8 +207,7 @@ __global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __
         float av = 0.f;
         const int nrow = ulist[uu];
         if (t < B && ((tokbits[(size_t)t * nw + (nrow >> 5)] >> (nrow & 31)) & 1u)) {
-            const float uval = vu + (bup ? bup[nrow] : 0.f);
-            av = REGLU ? fmaxf(vg + (bg ? bg[nrow] : 0.f), 0.f) * uval : fmaxf(uval, 0.f);
+            av = ffn_act<KIND>(vu + (bup ? bup[nrow] : 0.f), KIND != 0 ? vg + (bg ? bg[nrow] : 0.f) : 0.f);
         }
         const h16 hi = (h16)av;
         a_hi[(size_t)t * lda + uu] = hi;
@@ -659,7 +658,7 @@ static int ring_grid() {
 }
 
 
-hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h16* Wup,
+hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16* Wup,
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
                         char* ws, char* hdr, hipStream_t s) {
@@ -694,20 +693,24 @@ hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h
     ra.zsrc = reinterpret_cast<const h16*>(hdr + Sync::zero);
     ra.part = reinterpret_cast<float*>(ws + L.upart);
     ra.ctr = upctr;
-#define PI_UP(R, N)                                                                                        \
-    hipLaunchKernelGGL((k_union_up<UpCfg<R, N>, R>), dim3(ring_grid<k_union_up<UpCfg<R, N>, R>>()), dim3(256), \
+#define PI_UP(K, N)                                                                                        \
+    hipLaunchKernelGGL((k_union_up<UpCfg<(K != 0), N>, K>), dim3(ring_grid<k_union_up<UpCfg<(K != 0), N>, K>>()), \
+                       dim3(256), \
                        0, s, ra, ucount, ffn, bup, bg, tokbits, nw, L.Bp, L.lda, a_hi, a_lo)
 #define PI_DN(X)                                                                                        \
     hipLaunchKernelGGL((k_union_down<DownCfg<X>>), dim3((d + DownCfg<X>::CT - 1) / DownCfg<X>::CT, L.G), dim3(256), \
                        0, s, Wd, d, ffn, ulist, ucount, \
                        a_hi, a_lo, B, L.Bp, L.lda, partial, L.G, ra.zsrc)
     const int xg = ring_xg(B);
-    if (reglu) {
-        if (xg == 1) PI_UP(true, 1); else if (xg == 2) PI_UP(true, 2); else if (xg == 4) PI_UP(true, 4);
-        else if (xg == 8) PI_UP(true, 8); else PI_UP(true, 16);
+    if (kind == 2) {
+        if (xg == 1) PI_UP(2, 1); else if (xg == 2) PI_UP(2, 2); else if (xg == 4) PI_UP(2, 4);
+        else if (xg == 8) PI_UP(2, 8); else PI_UP(2, 16);
+    } else if (kind == 1) {
+        if (xg == 1) PI_UP(1, 1); else if (xg == 2) PI_UP(1, 2); else if (xg == 4) PI_UP(1, 4);
+        else if (xg == 8) PI_UP(1, 8); else PI_UP(1, 16);
     } else {
-        if (xg == 1) PI_UP(false, 1); else if (xg == 2) PI_UP(false, 2); else if (xg == 4) PI_UP(false, 4);
-        else if (xg == 8) PI_UP(false, 8); else PI_UP(false, 16);
+        if (xg == 1) PI_UP(0, 1); else if (xg == 2) PI_UP(0, 2); else if (xg == 4) PI_UP(0, 4);
+        else if (xg == 8) PI_UP(0, 8); else PI_UP(0, 16);
     }
     if (xg == 1) PI_DN(1); else if (xg == 2) PI_DN(2); else if (xg == 4) PI_DN(4);
     else if (xg == 8) PI_DN(8); else PI_DN(16);

@@ -52,6 +52,16 @@ __device__ __forceinline__ float dot8_hf(u32x4 w, const float* h, float acc) {
     return acc;
 }
 
+// A neuron's activation from its up sum u and gate sum g (biases included),
+// by FFN kind: 0 ReLU max(u, 0); 1 ReGLU max(g, 0) * u; 2 SwiGLU SiLU(g) * u
+// with SiLU(g) = g / (1 + e^-g).
+template <int KIND>
+__device__ __forceinline__ float ffn_act(float u, float g) {
+    if (KIND == 0) return fmaxf(u, 0.f);
+    if (KIND == 1) return fmaxf(g, 0.f) * u;
+    return g / (1.f + expf(-g)) * u;
+}
+
 // acc[k] += s * w[k] for 8 fp16 weights.
 __device__ __forceinline__ void axpy8(float* acc, float s, u32x4 w) {
     f16x2 a = as_h2(w.x), b = as_h2(w.y), c = as_h2(w.z), d = as_h2(w.w);

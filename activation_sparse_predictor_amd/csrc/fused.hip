@@ -326,7 +326,7 @@ constexpr int kSWindow = 2048;                       // list entries staged in L
 static_assert(kSColThreads * kSGroups == kSThreads, "tile shape");
 static_assert(kFusedCols <= kSThreads, "one reduction column per thread");
 
-template <bool REGLU>
+template <int KIND>
 __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restrict__ x, int d, int ffn,
                                                             const h16* __restrict__ Wup,
                                                             const float* __restrict__ bup,
@@ -348,6 +348,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     int32_t* s_row = reinterpret_cast<int32_t*>(s_mem + kSGroups * kFusedCols * 4);
     float* s_a = reinterpret_cast<float*>(s_mem + kSGroups * kFusedCols * 4 + kSWindow * 4);
     __shared__ int s_flag;
+    constexpr bool REGLU = KIND != 0;   // gated: a W_gate row per neuron (ReGLU, SwiGLU)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cnt = min(max(count[0], 0), ffn);
@@ -419,9 +420,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
             if (REGLU) ag = group_sum<64>(ag);
             const uint32_t epoch = next_epoch(oldest_slot(slot));
             if (lane == 0) {
-                const float uval = au + bu;
-                const float act = REGLU ? fmaxf(ag + bgv, 0.f) * uval : fmaxf(uval, 0.f);
-                st_tag(&atag[j], epoch, __float_as_uint(act));
+                st_tag(&atag[j], epoch, __float_as_uint(ffn_act<KIND>(au + bu, ag + bgv)));
             }
         }
         return;
@@ -549,7 +548,7 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
     return hipGetLastError();
 }
 
-hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
+hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
                                char* data, hipStream_t s) {
@@ -559,12 +558,13 @@ hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h
     uint32_t* slots = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_epoch);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     dim3 grid(L.NU + L.T * L.G);
-    if (reglu)
-        hipLaunchKernelGGL(k_sparse_fused<true>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,
-                           count, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero);
-    else
-        hipLaunchKernelGGL(k_sparse_fused<false>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx,
-                           count, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero);
+#define PI_SF(K)                                                                                               \
+    hipLaunchKernelGGL(k_sparse_fused<K>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx, count, \
+                       L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero)
+    if (kind == 2) PI_SF(2);
+    else if (kind == 1) PI_SF(1);
+    else PI_SF(0);
+#undef PI_SF
     return hipGetLastError();
 }
 

@@ -201,7 +201,7 @@ inline FusedSparseLayout fused_sparse_layout(int d, int ffn) {
 typedef _Float16 h16;
 
 // sparse.hip
-hipError_t launch_up_act(bool reglu, bool dense, const h16* x, int B, int d, int ffn,
+hipError_t launch_up_act(int kind, bool dense, const h16* x, int B, int d, int ffn,
                          const h16* Wup, const float* bup, const h16* Wg, const float* bg,
                          const int32_t* idx, const int32_t* count, float* a, uint32_t* ctr,
                          int T, hipStream_t s);
@@ -210,7 +210,7 @@ hipError_t launch_down_acc(bool dense, const h16* Wd, int B, int d, int ffn, con
                            uint32_t* ctr, int T, int G, hipStream_t s);
 
 // batch.hip
-hipError_t launch_union(bool reglu, const h16* x, int B, int d, int ffn, const h16* Wup,
+hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16* Wup,
                         const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                         const int32_t* idx, const int32_t* count, float* y, const BatchLayout& L,
                         char* ws, char* hdr, hipStream_t s);
@@ -226,7 +226,7 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
                                 const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
                                 char* hdr, char* data, int32_t* idx, int32_t* count, hipStream_t s);
-hipError_t launch_sparse_fused(bool reglu, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
+hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
                                char* data, hipStream_t s);

@@ -25,7 +25,7 @@ __device__ __forceinline__ int clamp_row(int i, int ffn) { return i < 0 ? 0 : (i
 // issued before x is staged into LDS, so the staging overlaps them.
 // Workgroup 0 of each token also zeroes that token's arrival counters for
 // the accumulate kernel that follows on the stream.
-template <bool REGLU, bool DENSE>
+template <int KIND, bool DENSE>
 __global__ __launch_bounds__(256) void k_up_act(const h16* __restrict__ x, int d, int ffn,
                                                 const h16* __restrict__ Wup,
                                                 const float* __restrict__ bup,
@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void k_up_act(const h16* __restrict__ x, int d
                                                 float* __restrict__ a, uint32_t* __restrict__ ctr,
                                                 int T) {
     extern __shared__ u32x4 sx[];
+    constexpr bool REGLU = KIND != 0;   // gated: a W_gate row per neuron (ReGLU, SwiGLU)
     constexpr int U = REGLU ? 8 : 16;
     const int tok = blockIdx.y;
     const int tid = threadIdx.x;
@@ -93,12 +94,8 @@ __global__ __launch_bounds__(256) void k_up_act(const h16* __restrict__ x, int d
         if (REGLU) ag = group_sum<64>(ag);
         if (lane == 0) {
             const float uval = au + (bup ? bup[i] : 0.f);
-            float act;
-            if (REGLU)
-                act = fmaxf(ag + (bg ? bg[i] : 0.f), 0.f) * uval;
-            else
-                act = fmaxf(uval, 0.f);
-            a[(size_t)tok * ffn + j] = act;
+            const float gval = REGLU ? ag + (bg ? bg[i] : 0.f) : 0.f;
+            a[(size_t)tok * ffn + j] = ffn_act<KIND>(uval, gval);
         }
     }
 }
@@ -208,7 +205,7 @@ __global__ __launch_bounds__(kDownThreads) void k_down_acc(const h16* __restrict
     if (tid == 0) st_flag(my_ctr, 0u);
 }
 
-hipError_t launch_up_act(bool reglu, bool dense, const h16* x, int B, int d, int ffn,
+hipError_t launch_up_act(int kind, bool dense, const h16* x, int B, int d, int ffn,
                          const h16* Wup, const float* bup, const h16* Wg, const float* bg,
                          const int32_t* idx, const int32_t* count, float* a, uint32_t* ctr,
                          int T, hipStream_t s) {
@@ -219,10 +216,12 @@ hipError_t launch_up_act(bool reglu, bool dense, const h16* x, int B, int d, int
 #define PI_UP(R, D)                                                                          \
     hipLaunchKernelGGL((k_up_act<R, D>), grid, dim3(256), shm, s, x, d, ffn, Wup, bup, Wg, bg, \
                        idx, count, a, ctr, T)
-    if (reglu) {
-        if (dense) PI_UP(true, true); else PI_UP(true, false);
+    if (kind == 2) {
+        if (dense) PI_UP(2, true); else PI_UP(2, false);
+    } else if (kind == 1) {
+        if (dense) PI_UP(1, true); else PI_UP(1, false);
     } else {
-        if (dense) PI_UP(false, true); else PI_UP(false, false);
+        if (dense) PI_UP(0, true); else PI_UP(0, false);
     }
 #undef PI_UP
     return hipGetLastError();

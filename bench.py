@@ -71,13 +71,13 @@ def log(*a):
 
 
 def touched_bytes(kind, d, r, ffn, count):
-    m = 2 if kind == "reglu" else 1
+    m = 1 if kind == "relu" else 2
     return (2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * count * 2 * d + 4 * count
             + 2 * d + 4 * d + 8 * count)
 
 
 def dense_bytes(kind, d, ffn):
-    m = 2 if kind == "reglu" else 1
+    m = 1 if kind == "relu" else 2
     return (m + 1) * ffn * 2 * d + 4 * ffn + 2 * d + 4 * d
 
 
@@ -142,7 +142,7 @@ def batch_sweep(cfg_key, batches, steps, nl, log_fn):
     from synthetic import CONFIGS, make_layer, make_tokens
     cfg = CONFIGS[cfg_key]
     kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
-    m = 2 if kind == "reglu" else 1
+    m = 1 if kind == "relu" else 2
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     layers = [make_layer(cfg, layer=l, device=dev) for l in range(nl)]
@@ -182,6 +182,8 @@ def batch_sweep(cfg_key, batches, steps, nl, log_fn):
         def torch_dense(L, x):
             if kind == "reglu":
                 a = torch.relu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
+            elif kind == "swiglu":
+                a = F.silu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
             else:
                 a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
             return F.linear(a.half(), L["W_down"].t())
@@ -220,6 +222,8 @@ def main():
     ap.add_argument("--sweep", default="c4", help="config of the batch sweep ('' to skip)")
     ap.add_argument("--sweep-batches", default="1,4,8,16,32")
     ap.add_argument("--sweep-steps", type=int, default=200)
+    ap.add_argument("--prompt", default="c5",
+                    help="config of the prompt-phase line: one 128-token batch per layer ('' to skip)")
     ap.add_argument("--sweep-only", action="store_true",
                     help="run only the batch sweep (for a per-kernel profile of the union path)")
     ap.add_argument("--profile-run", action="store_true",
@@ -403,7 +407,7 @@ def main():
     ms_pred = graph_time(run_pred)
     ms_sp = graph_time(run_sparse)
     pred_bytes = 2 * r * d + 2 * ffn * r + 4 * ffn + 2 * d
-    m = 2 if kind == "reglu" else 1
+    m = 1 if kind == "relu" else 2
     sp_bytes = [(m + 1) * int(counts_h[l, t]) * (2 * d + 4) + 4 * d for (l, t) in lt]
     gbs_pred = pred_bytes / ms_pred / 1e6
     gbs_sp = statistics.mean(sp_bytes) / ms_sp / 1e6
@@ -451,6 +455,8 @@ def main():
         def torch_dense(L, x):
             if kind == "reglu":
                 a = torch.relu(F.linear(x, L["W_gate"], None).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
+            elif kind == "swiglu":
+                a = F.silu(F.linear(x, L["W_gate"], None).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
             else:
                 a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
             return F.linear(a.half(), L["W_down"].t())
@@ -478,6 +484,13 @@ def main():
         torch.cuda.empty_cache()
         sweep = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")],
                             args.sweep_steps, 4, log)
+
+    prompt = None
+    if args.prompt:
+        # the prompt of a sequence: 128 tokens through the union path at once,
+        # 3 rotated layers (about 4.4 GB at the OPT-66B shape)
+        torch.cuda.empty_cache()
+        prompt = batch_sweep(args.prompt, [128], 40, 3, log)
 
     cpu = None
     if not args.no_cpu:
@@ -519,6 +532,7 @@ def main():
         "dense_baseline": dense,
         "cpu_baseline": cpu,
         "batch_sweep": sweep,
+        "prompt_phase": prompt,
     }
     print(json.dumps(out), flush=True)
 

@@ -59,7 +59,14 @@ typedef enum pi_status {
 
 typedef enum pi_ffn_kind {
     PI_FFN_RELU = 0,   /* a_i = max(W_up[i].x + b_up_i, 0) */
-    PI_FFN_REGLU = 1   /* a_i = max(W_gate[i].x + b_gate_i, 0) * (W_up[i].x + b_up_i) */
+    PI_FFN_REGLU = 1,  /* a_i = max(W_gate[i].x + b_gate_i, 0) * (W_up[i].x + b_up_i) */
+    PI_FFN_SWIGLU = 2  /* a_i = SiLU(W_gate[i].x + b_gate_i) * (W_up[i].x + b_up_i),
+                          SiLU(g) = g / (1 + exp(-g)): the SiLU-gated models of Part A
+                          sections 2.3 and 4.4.  Their activations outside the list are
+                          small rather than zero (sparsity there is the share of neurons
+                          that can be dropped at a perplexity cost under 1%, about half),
+                          so the sparse result approximates the dense one; which neurons
+                          to list is the predictor's calibration */
 } pi_ffn_kind;
 
 typedef enum pi_pred_act {
@@ -123,14 +130,14 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d,
  * pi_ffn_sparse -- the neuron-aware FFN over the active rows only.
  *
  * Per token t, over j < count[t] with i = idx[t * ffn + j]:
- *   u_i = W_up[i].x_t + b_up_i ;  ReGLU: g_i = W_gate[i].x_t + b_gate_i
- *   a_i = max(u_i, 0)  (RELU)   or   max(g_i, 0) * u_i  (REGLU)
+ *   u_i = W_up[i].x_t + b_up_i ;  gated kinds: g_i = W_gate[i].x_t + b_gate_i
+ *   a_i = max(u_i, 0) (RELU), max(g_i, 0) * u_i (REGLU), or SiLU(g_i) * u_i (SWIGLU)
  *   y_t = sum_j a_i * W_down[i, :]                (no output bias)
  * (the neuron-aware operator of Part A section 2.3 module 4 / section 4.3;
  * W_down is neuron-major so each active neuron is one contiguous row).
  * With flags & PI_DENSE, idx and count are ignored (may be NULL) and every
  * neuron is computed: the dense FFN.  Biases may be NULL (= 0).  W_gate must
- * be non-NULL for REGLU and NULL for RELU.  Products are fp16 x fp16 with
+ * be non-NULL for REGLU and SWIGLU and NULL for RELU.  Products are fp16 x fp16 with
  * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0).
  * idx must hold valid, strictly ascending neuron ids (as written by
  * pi_ffn_predict); the call does not re-check them unless flags has

@@ -25,6 +25,7 @@ from .ffn import (  # noqa: F401
     predict,
     neuron_preactivations,
     neuron_activations,
+    silu,
     sparse_ffn,
     dense_ffn,
     decode_step,

@@ -20,6 +20,9 @@ design notes of this repository):
   * the active index list is ascending with no duplicates;
   * ReGLU is a = max(W_gate x + b_gate, 0) * (W_up x + b_up), the gated form
     with the ReLU on the gate; ReLU is a = max(W_up x + b_up, 0);
+  * SwiGLU ([R] Part A 2.3 and 4.4 name SiLU-gated models and their softer
+    sparsity) is a = SiLU(W_gate x + b_gate) * (W_up x + b_up) with
+    SiLU(g) = g / (1 + e^-g), over the listed neurons only;
   * a neuron "fires" for the profiler when its ReLU input is > 0 (strict);
   * reorder = stable sort by descending count (ties to the lower index), hot
     set = shortest prefix whose counts reach hot_share of the total.
@@ -109,7 +112,7 @@ def neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> Tuple[np
     if b_up is not None:
         u = u + rows_of(b_up, rows)
     g = None
-    if kind == "reglu":
+    if kind in ("reglu", "swiglu"):
         g = rows_of(W_gate, rows) @ x
         if b_gate is not None:
             g = g + rows_of(b_gate, rows)
@@ -118,11 +121,22 @@ def neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> Tuple[np
     return u, g
 
 
+def silu(g) -> np.ndarray:
+    """SiLU(g) = g * sigmoid(g) = g / (1 + e^-g), in float64 (e^-g may overflow
+    to inf for g below about -709, which gives the limit -0)."""
+    g = np.asarray(g, dtype=F64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
 def neuron_activations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> np.ndarray:
-    """a_i = max(u_i, 0) (ReLU) or max(g_i, 0) * u_i (ReGLU) for i in rows."""
+    """a_i = max(u_i, 0) (ReLU), max(g_i, 0) * u_i (ReGLU) or SiLU(g_i) * u_i
+    (SwiGLU) for i in rows."""
     u, g = neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows)
     if kind == "relu":
         return np.maximum(u, 0.0)
+    if kind == "swiglu":
+        return silu(g) * u
     return np.maximum(g, 0.0) * u
 
 

@@ -69,7 +69,7 @@ class WorkloadConfig:
     key: str            # "c1".."c5" or "custom"
     number: int         # k in the seed scheme
     workload: str       # human-readable name with the model shape it mimics
-    kind: str           # "relu" or "reglu"
+    kind: str           # "relu", "reglu" or "swiglu"
     d: int              # hidden size
     ffn: int            # FFN neurons
     r: int              # predictor rank
@@ -99,6 +99,10 @@ CONFIGS: Dict[str, WorkloadConfig] = {
     "c5": WorkloadConfig("c5", 5, "opt66b-shaped-relu-ffn-stack d9216 ffn36864 r1024 x64", "relu",
                          9216, 36864, 1024, 0.10, None, 0.17, tokens=128, layers=64,
                          prompt_tokens=128, decode_steps=128),
+    # SiLU-gated variant of the LLaMA2-70B shape: about half the neurons listed per
+    # token, 75% of them carrying 80% of the activations ([R] Part A 3.1, 4.4)
+    "c3s": WorkloadConfig("c3s", 6, "llama2-70b-shaped-swiglu-ffn d8192 ffn28672 r1024", "swiglu",
+                          8192, 28672, 1024, 0.50, None, 0.75, tokens=64),
 }
 
 
@@ -185,7 +189,7 @@ def make_layer(cfg: WorkloadConfig, layer: int = 0, device="cpu",
                               "d": cfg.d, "ffn": cfg.ffn, "r": cfg.r}
     out["W_up"] = _unit_rows(cfg.ffn, cfg.d, _seed(cfg, "W_up", layer), device)
     out["W_down"] = _unit_rows(cfg.ffn, cfg.d, _seed(cfg, "W_down", layer), device)
-    if cfg.kind == "reglu":
+    if cfg.kind in ("reglu", "swiglu"):
         out["W_gate"] = _unit_rows(cfg.ffn, cfg.d, _seed(cfg, "W_gate", layer), device)
         out["b_gate"], out["b_up"] = bias, None
     elif cfg.kind == "relu":

@@ -150,6 +150,8 @@ def test_predict_rejects_before_launch(kw, code):
     (dict(count=None), B.PI_ERR_INVALID_ARG),
     (dict(W_gate=A), B.PI_ERR_INVALID_ARG),                 # gate given for ReLU
     (dict(kind=B.PI_FFN_REGLU), B.PI_ERR_INVALID_ARG),      # gate missing for ReGLU
+    (dict(kind=B.PI_FFN_SWIGLU), B.PI_ERR_INVALID_ARG),     # gate missing for SwiGLU
+    (dict(kind=3), B.PI_ERR_INVALID_ARG),                   # no such kind
     (dict(b_gate=W), B.PI_ERR_INVALID_ARG),                 # gate bias for ReLU
     (dict(flags=0x80), B.PI_ERR_INVALID_ARG),
     (dict(B=300), B.PI_ERR_INVALID_ARG),
@@ -181,6 +183,8 @@ def _decode(**kw):
     (dict(idx=None), B.PI_ERR_INVALID_ARG),
     (dict(tau=1.5), B.PI_ERR_INVALID_ARG),
     (dict(kind=B.PI_FFN_REGLU), B.PI_ERR_INVALID_ARG),      # gate missing for ReGLU
+    (dict(kind=B.PI_FFN_SWIGLU), B.PI_ERR_INVALID_ARG),     # gate missing for SwiGLU
+    (dict(kind=3), B.PI_ERR_INVALID_ARG),                   # no such kind
     (dict(flags=B.PI_DENSE), B.PI_ERR_INVALID_ARG),         # a dense step has no predictor
     (dict(flags=0x80), B.PI_ERR_INVALID_ARG),
     (dict(r=12), B.PI_ERR_UNSUPPORTED),

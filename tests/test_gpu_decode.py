@@ -67,6 +67,7 @@ SHAPES = [
     ("reglu", 256, 1024, 64, 0.50),
     ("relu", 2048, 4160, 256, 0.05),
     ("relu", 1032, 2080, 136, 0.90),  # nearly every neuron active
+    ("swiglu", 520, 1000, 72, 0.50),  # SiLU gate
 ]
 
 

@@ -60,6 +60,8 @@ SHAPES = [
     ("reglu", 520, 1000, 16, 0.20),
     ("reglu", 256, 1024, 64, 0.50),
     ("relu", 2048, 4160, 256, 0.05),
+    ("swiglu", 520, 1000, 72, 0.50),     # SiLU gate: about half the neurons listed
+    ("swiglu", 2048, 4160, 256, 0.30),
 ]
 
 
@@ -143,7 +145,7 @@ def test_sparse_list_lengths_around_chunking(n):
     check_y(_sparse_with(L, x, lst), _oracle_y(H, x[0].cpu(), lst), where=f"list len {n}")
 
 
-@pytest.mark.parametrize("kind", ["relu", "reglu"])
+@pytest.mark.parametrize("kind", ["relu", "reglu", "swiglu"])
 def test_dense_flag(kind):
     cfg = custom_config(kind, 520, 2080, 16, number=55)
     L = R.to_device(make_layer(cfg), DEV)
@@ -160,7 +162,8 @@ def test_dense_flag(kind):
 @pytest.mark.parametrize("kind,Bt", [("relu", 1), ("relu", 2), ("relu", 4), ("relu", 9), ("relu", 15),
                                      ("relu", 16), ("relu", 17), ("relu", 32), ("relu", 33), ("reglu", 8),
                                      ("reglu", 12), ("reglu", 20), ("reglu", 32), ("reglu", 64), ("relu", 65),
-                                     ("relu", 100), ("reglu", 128), ("relu", 131)])
+                                     ("relu", 100), ("reglu", 128), ("relu", 131), ("swiglu", 4),
+                                     ("swiglu", 20), ("swiglu", 64), ("swiglu", 128)])
 def test_batched_union_path(kind, Bt):
     """Batch of Bt tokens.  The batched predictor (matrix cores) must satisfy the
     index rule per token, and agree with the single-token predictor except
@@ -500,7 +503,7 @@ def test_union_down_id_windows():
         check_y(Y[t], _oracle_y(H, X[t].cpu(), lists[t]), where=f"union windows t={t}")
 
 
-@pytest.mark.parametrize("key", ["c2", "c3", "c4"])
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c3s"])
 def test_full_size_decode(key):
     cfg, L, X = _full(key)
     counts = _check_tokens(L, X, where=key)
@@ -533,3 +536,20 @@ def test_full_size_batched(Bt):
         z = O.predictor_logits(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"])
         check_idx(gi, z, thr, where=f"c4 B={Bt} t={t}")
         check_y(Y[t].cpu().numpy(), _oracle_y(H, X[t].cpu(), gi), where=f"c4 B={Bt} t={t}")
+
+
+def test_full_size_swiglu_batched():
+    """The LLaMA2-70B-shaped SiLU-gated layer through the union path (16 tokens,
+    about half the neurons each, so the union covers nearly every row)."""
+    cfg, L, X = _full("c3s", ntok=16)
+    H = _host(L)
+    idx, cnt = R.predict(L, X)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    for t in (0, 15):
+        c = int(cnt[t].cpu())
+        gi = idx[t, :c].cpu().numpy()
+        z = O.predictor_logits(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"])
+        check_idx(gi, z, thr, where=f"c3s B=16 t={t}")
+        check_y(Y[t].cpu().numpy(), _oracle_y(H, X[t].cpu(), gi), where=f"c3s B=16 t={t}")

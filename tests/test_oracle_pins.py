@@ -379,10 +379,47 @@ def pin_profile_binomial():
     assert np.all(np.abs(counts - n * f) <= 5 * sd + 2), np.max(np.abs(counts - n * f) / (sd + 1))
 
 
+def pin_swiglu():
+    """SiLU and the SiLU-gated FFN against forms that share no code with the oracle.
+
+    SiLU(v) = v * sigmoid(v) = (v / 2) * (1 + tanh(v / 2)), and SiLU(v) - SiLU(-v) = v
+    (sigmoid(v) + sigmoid(-v) = 1).  The FFN is then written out row by row with
+    the tanh form: y = sum_i SiLU(W_gate[i] x + b_gate_i) (W_up[i] x + b_up_i) W_down[i].
+    """
+    v = np.linspace(-30.0, 30.0, 601)
+    s = O.silu(v)
+    assert np.allclose(s - O.silu(-v), v, rtol=0, atol=1e-13)
+    # (1 + tanh(v / 2) cancels for v << 0: an absolute bound there)
+    assert np.allclose(s, 0.5 * v * (1.0 + np.tanh(0.5 * v)), rtol=1e-13, atol=1e-13)
+    assert O.silu(0.0) == 0.0 and O.silu(800.0) == 800.0 and O.silu(-800.0) == 0.0
+    rng = np.random.default_rng(21)
+    for (d, ffn) in ((6, 9), (16, 5), (1, 3)):
+        x = rng.standard_normal(d).astype(np.float16)
+        Wu = rng.standard_normal((ffn, d)).astype(np.float16)
+        Wg = rng.standard_normal((ffn, d)).astype(np.float16)
+        Wd = rng.standard_normal((ffn, d)).astype(np.float16)
+        bu = rng.standard_normal(ffn).astype(np.float32)
+        bg = rng.standard_normal(ffn).astype(np.float32)
+        idx = np.sort(rng.choice(ffn, size=max(1, ffn // 2), replace=False))
+        want = [0.0] * d
+        for i in idx:
+            u = float(bu[i]) + sum(float(Wu[i, k]) * float(x[k]) for k in range(d))
+            g = float(bg[i]) + sum(float(Wg[i, k]) * float(x[k]) for k in range(d))
+            a = 0.5 * g * (1.0 + math.tanh(0.5 * g)) * u
+            for k in range(d):
+                want[k] += a * float(Wd[i, k])
+        got = O.sparse_ffn("swiglu", x, Wu, bu, Wg, bg, Wd, idx)
+        assert np.allclose(got, want, rtol=1e-12, atol=1e-12), (d, ffn)
+        # every neuron listed is the dense FFN; an empty list gives 0
+        assert np.array_equal(O.sparse_ffn("swiglu", x, Wu, bu, Wg, bg, Wd, np.arange(ffn)),
+                              O.dense_ffn("swiglu", x, Wu, bu, Wg, bg, Wd))
+        assert not np.any(O.sparse_ffn("swiglu", x, Wu, bu, Wg, bg, Wd, []))
+
+
 PINS = [pin_golden_ffn, pin_golden_predictor, pin_golden_profile_reorder, pin_exact_predictor,
         pin_exact_ffn, pin_float64_error_bound, pin_closed_forms, pin_sigmoid_threshold,
         pin_invariants, pin_reorder_invariance, pin_reorder_properties, pin_profile_exact,
-        pin_profile_binomial]
+        pin_profile_binomial, pin_swiglu]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -491,7 +528,27 @@ def _mutants():
             return orig["neuron_preactivations"](kind, x, W_up, b_up, W_gate, b_gate, rows)
         return orig["neuron_preactivations"](kind, x, W_up, b_gate, W_gate, b_up, rows)
 
+    def act_swiglu_on_up(kind, x, W_up, b_up, W_gate, b_gate, rows):
+        if kind != "swiglu":
+            return orig["neuron_activations"](kind, x, W_up, b_up, W_gate, b_gate, rows)
+        u, g = O.neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows)
+        return O.silu(u) * g
+
+    def act_swiglu_sigmoid(kind, x, W_up, b_up, W_gate, b_gate, rows):
+        if kind != "swiglu":
+            return orig["neuron_activations"](kind, x, W_up, b_up, W_gate, b_gate, rows)
+        u, g = O.neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows)
+        return u / (1.0 + np.exp(-g))
+
+    def pre_swiglu_no_gate_bias(kind, x, W_up, b_up, W_gate, b_gate, rows):
+        if kind != "swiglu":
+            return orig["neuron_preactivations"](kind, x, W_up, b_up, W_gate, b_gate, rows)
+        return orig["neuron_preactivations"](kind, x, W_up, b_up, W_gate, None, rows)
+
     return {
+        "SwiGLU with SiLU on up": ("neuron_activations", act_swiglu_on_up),
+        "SwiGLU with sigmoid for SiLU": ("neuron_activations", act_swiglu_sigmoid),
+        "SwiGLU gate bias dropped": ("neuron_preactivations", pre_swiglu_no_gate_bias),
         "bias dropped": ("neuron_preactivations", pre_no_bias),
         "bias sign flipped": ("neuron_preactivations", pre_neg_bias),
         "ReGLU without ReLU on the gate": ("neuron_activations", act_gate_no_relu),
