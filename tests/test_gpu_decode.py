@@ -121,7 +121,7 @@ def test_decode_step_repeatable_and_check_flag():
         assert c == outs[0][0] and np.array_equal(i, outs[0][1]) and np.array_equal(y, outs[0][2])
 
 
-@pytest.mark.parametrize("kind", ["relu", "reglu"])
+@pytest.mark.parametrize("kind", ["relu", "reglu", "swiglu"])
 def test_decode_step_graph_replay(kind):
     """pi_ffn_decode for three tokens captured in a HIP graph and replayed
     several times, with eager decode steps on the same workspace between the
