@@ -25,7 +25,7 @@ def _host(layer):
 
 
 def _args(L, x, idx, cnt, y, ws, wsb, act=B.PI_ACT_RELU, flags=0):
-    kind = B.PI_FFN_REGLU if L["kind"] == "reglu" else B.PI_FFN_RELU
+    kind = B.KINDS[L["kind"]]
     return (kind, x, x.shape[0], L["d"], L["ffn"], L["P1"], L.get("b1"), act, L["P2"], L.get("b2"), L["r"],
             float(L["tau"]), L["W_up"], L.get("b_up"), L.get("W_gate"), L.get("b_gate"), L["W_down"], idx, cnt,
             y, flags, ws, wsb)

@@ -303,7 +303,7 @@ def test_deterministic_repeats():
 
 
 def _decode_args(L, x, idx, cnt, y, ws, ws_bytes):
-    kind = B.PI_FFN_REGLU if L["kind"] == "reglu" else B.PI_FFN_RELU
+    kind = B.KINDS[L["kind"]]
     p = (x, x.shape[0], L["d"], L["P1"], L.get("b1"), B.PI_ACT_RELU, L["P2"], L.get("b2"), L["r"], L["ffn"],
          float(L["tau"]), idx, cnt, ws, ws_bytes)
     q = (kind, x, x.shape[0], L["d"], L["ffn"], L["W_up"], L.get("b_up"), L.get("W_gate"), L.get("b_gate"),
