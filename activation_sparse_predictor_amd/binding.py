@@ -45,6 +45,7 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "pi_ffn_predict": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "pi_ffn_predict_hot": (_I, [_P, _I, _I, _P, _P, _I, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "pi_ffn_sparse": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "pi_ffn_decode": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                            _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
@@ -122,6 +123,13 @@ def pi_ffn_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count, ws, ws
     return load().pi_ffn_predict(_ptr(x), B, d, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r,
                                  ffn, tau, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
                                  _stream(stream))
+
+
+def pi_ffn_predict_hot(x, B, d, P1, b1, act, P2, b2, r, ffn, n_hot, tau, idx, count, ws, ws_bytes,
+                       stream=None) -> int:
+    return load().pi_ffn_predict_hot(_ptr(x), B, d, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r,
+                                     ffn, n_hot, tau, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
+                                     _stream(stream))
 
 
 def pi_ffn_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags,

@@ -188,8 +188,8 @@ pi_status check_sparse_args(int kind, const pi_half* x, int B, int d, int ffn, c
 // data the call's data area; clear: zero the tagged words first (single-token
 // paths only).
 pi_status run_predict(const pi_half* x, int B, int d, const pi_half* P1, const float* b1, int act,
-                      const pi_half* P2, const float* b2, int r, int ffn, float tau, int32_t* idx, int32_t* count,
-                      char* hdr, char* data, bool clear, hipStream_t s) {
+                      const pi_half* P2, const float* b2, int r, int ffn, int hot, float tau, int32_t* idx,
+                      int32_t* count, char* hdr, char* data, bool clear, hipStream_t s) {
     // sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
     const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
     const auto* hx = reinterpret_cast<const pi::h16*>(x);
@@ -200,7 +200,7 @@ pi_status run_predict(const pi_half* x, int B, int d, const pi_half* P1, const f
             const int Bg = B - g0 < pi::kUnionMaxTokens ? B - g0 : pi::kUnionMaxTokens;
             const pi::BPredLayout L = pi::bpred_layout(Bg, r, ffn);
             hipError_t e = pi::launch_bpredict(hx + (size_t)g0 * d, Bg, d, h1, b1, act == PI_ACT_RELU, h2, b2,
-                                               r, ffn, thr, idx + (size_t)g0 * ffn, count + g0, L,
+                                               r, ffn, hot, thr, idx + (size_t)g0 * ffn, count + g0, L,
                                                data, hdr, s);
             if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict batched");
         }
@@ -211,7 +211,8 @@ pi_status run_predict(const pi_half* x, int B, int d, const pi_half* P1, const f
     hipError_t e = hipSuccess;
     if (clear) e = pi::launch_zero(data, L.total, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict clearing the workspace");
-    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, thr, L, hdr, data, idx, count, s);
+    e = pi::launch_predict_fused(hx, d, h1, b1, act == PI_ACT_RELU, r, h2, b2, ffn, hot, thr, L, hdr, data, idx,
+                                 count, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict");
     return ok();
 }
@@ -313,14 +314,22 @@ pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes)
 pi_status pi_ffn_predict(const pi_half* x, int B, int d, const pi_half* P1, const float* b1,
                          int act, const pi_half* P2, const float* b2, int r, int ffn, float tau,
                          int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+    return pi_ffn_predict_hot(x, B, d, P1, b1, act, P2, b2, r, ffn, 0, tau, idx, count, ws, ws_bytes, stream);
+}
+
+pi_status pi_ffn_predict_hot(const pi_half* x, int B, int d, const pi_half* P1, const float* b1,
+                             int act, const pi_half* P2, const float* b2, int r, int ffn, int n_hot, float tau,
+                             int32_t* idx, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
     PI_TRY(check_predict_args(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count));
-    PI_TRY(check_ws(ws, ws_bytes, predict_ws_bytes(B, r, ffn), "pi_ffn_predict"));
+    PI_REQUIRE(n_hot >= 0 && n_hot <= ffn, PI_ERR_INVALID_ARG, "n_hot=%d outside [0, ffn=%d]", n_hot, ffn);
+    PI_REQUIRE(n_hot % 32 == 0, PI_ERR_UNSUPPORTED, "n_hot=%d is not a multiple of 32", n_hot);
+    PI_TRY(check_ws(ws, ws_bytes, predict_ws_bytes(B, r, ffn), n_hot ? "pi_ffn_predict_hot" : "pi_ffn_predict"));
     char* w = static_cast<char*>(ws);
     const LayoutKey key{PI_OP_PREDICT, 1, 0, r, ffn};
     const bool fused = B == 1;
     const bool clear = fused && ws_needs_clear(ws, key);
     if (!fused) ws_forget(ws);
-    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count, w, w + pi::kSyncBytes, clear,
+    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, n_hot, tau, idx, count, w, w + pi::kSyncBytes, clear,
                        static_cast<hipStream_t>(stream)));
     if (fused) ws_record(ws, key);
     return PI_OK;
@@ -359,7 +368,7 @@ pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn, const
     const bool fused = B == 1 || sparse_is_fused(B, flags);
     const bool clear = fused && ws_needs_clear(ws, key);
     if (!fused) ws_forget(ws);
-    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count, w, w + pi::kSyncBytes,
+    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, 0, tau, idx, count, w, w + pi::kSyncBytes,
                        clear && B == 1, s));
     PI_TRY(run_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w,
                       w + decode_ffn_offset(B, r, ffn), clear && sparse_is_fused(B, flags), s));

@@ -315,23 +315,28 @@ __global__ __launch_bounds__(256) void k_bpred_hidden_valu(const h16* __restrict
 // token (bit k = neuron 32*word + k).  Each half of a wave holds 32 neurons
 // of one token: one ballot gives two words.
 template <class C>
+// The rows are neurons hot .. ffn - 1 (a.W[0] starts at P2 row hot, a.nrows =
+// ffn - hot; hot is a multiple of 32, so each half-wave's 32 rows are still
+// one mask word).  The words of the hot prefix are the compaction's.
 __global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* __restrict__ b2, float thr,
-                                                      uint32_t* __restrict__ masks32) {
+                                                      uint32_t* __restrict__ masks32, int ffn, int hot) {
     __shared__ __align__(16) char lds[C::LDS];
     static_assert(C::RB % 32 == 0, "a half-wave must hold 32 neurons of one token");
-    const int ffn = a.nrows, B = a.B;
+    const int nr = a.nrows, B = a.B;
     const int nw = (ffn + 31) / 32;
-    ring_gemm<C, false, true>(a, ffn, lds, [&](int i, int t, float v, float) {
-        const bool on = i < ffn && t < B && v + (b2 ? b2[i] : 0.f) > thr;
+    ring_gemm<C, false, true>(a, nr, lds, [&](int i, int t, float v, float) {
+        const int n = hot + i;
+        const bool on = i < nr && t < B && v + (b2 ? b2[n] : 0.f) > thr;
         const uint64_t m = __ballot(on);
         const int lane = threadIdx.x & 63;
-        if ((lane & 31) == 0 && i < ffn && t < B) masks32[(size_t)t * nw + (i >> 5)] = (uint32_t)(m >> (lane & 32));
+        if ((lane & 31) == 0 && i < nr && t < B) masks32[(size_t)t * nw + (n >> 5)] = (uint32_t)(m >> (lane & 32));
     });
 }
 
 // One workgroup per token: the token's 32-bit tile masks in neuron order ->
-// popcount prefix -> ascending idx and count.
-__global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restrict__ masks32, int ffn,
+// popcount prefix -> ascending idx and count.  The first hotw words (the
+// always-listed hot prefix) count as all ones and are not read.
+__global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restrict__ masks32, int ffn, int hotw,
                                                        int32_t* __restrict__ idx, int32_t* __restrict__ count) {
     __shared__ uint32_t s_part[4];
     const int tok = blockIdx.x;
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int t = t0 + tid * 8 + q;
-            m8[q] = t < ntiles ? mk[t] : 0u;
+            m8[q] = t < hotw ? 0xFFFFFFFFu : (t < ntiles ? mk[t] : 0u);
             mine += (uint32_t)__popc(m8[q]);
         }
         uint32_t incl = mine;
@@ -723,7 +728,7 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
 }
 
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
-                          const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
+                          const h16* P2, const float* b2, int r, int ffn, int hot, float thr, int32_t* idx,
                           int32_t* count, const BPredLayout& L, char* ws, char* hdr, hipStream_t s) {
     h16* h_hi = reinterpret_cast<h16*>(ws + L.h_hi);
     h16* h_lo = reinterpret_cast<h16*>(ws + L.h_lo);
@@ -743,9 +748,9 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
     ha.part = part;
     ha.ctr = nullptr;   // pieces are added by k_bpred_hidden_finish
     RingArgs la{};
-    la.W[0] = P2;
+    la.W[0] = P2 + (size_t)hot * r;   // the hot prefix's rows are not read
     la.ldw = r;
-    la.nrows = ffn;
+    la.nrows = ffn - hot;
     la.X[0] = h_hi;
     la.X[1] = h_lo;
     la.ldx = L.ldh;
@@ -769,7 +774,7 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
     const bool valu = B <= 8 && nch <= hid_valu_chunks(B <= 4 ? 4 : 8);
 #define PI_BHV(TB) hipLaunchKernelGGL(k_bpred_hidden_valu<TB>, dim3(gv), dim3(256), 0, s, x, B, d, P1, he, lctr, nlctr)
 #define PI_BL(N) hipLaunchKernelGGL((k_bpred_logits<LogCfg<N>>), dim3(ring_grid<k_bpred_logits<LogCfg<N>>>()), \
-                                    dim3(256), 0, s, la, b2, thr, masks32)
+                                    dim3(256), 0, s, la, b2, thr, masks32, ffn, hot)
     const int xg = ring_xg(B);
     if (valu) {
         if (B <= 2) PI_BHV(2);
@@ -784,7 +789,7 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
 #undef PI_BH
 #undef PI_BHV
 #undef PI_BL
-    hipLaunchKernelGGL(k_bpred_compact, dim3(B), dim3(256), 0, s, masks32, ffn, idx, count);
+    hipLaunchKernelGGL(k_bpred_compact, dim3(B), dim3(256), 0, s, masks32, ffn, hot / 32, idx, count);
     return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@
 //                             h_k = act(P1[k].x + b1_k), published as a tagged word
 //   workgroups [NA, NA + NT)  logits tiles of 32 neurons: collect h, stream the
 //                             tile's P2 rows, z = P2 h + b2 > thr, publish the
-//                             tile's 32-bit mask as a tagged word
+//                             tile's 32-bit mask as a tagged word (a tile of
+//                             the always-listed hot prefix publishes all ones)
 //   workgroup NA + NT         gathers every mask and writes idx (ascending) and count
 //
 // pi_ffn_sparse (B = 1):   k_sparse_fused
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        const float* __restrict__ b2, int ffn, float thr,
                                                        uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
                                                        uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
-                                                       int32_t* __restrict__ count, const float* __restrict__ zero) {
+                                                       int32_t* __restrict__ count, const float* __restrict__ zero,
+                                                       int hot) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
     __shared__ uint32_t s_part[4];
@@ -217,6 +219,12 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     // takes chunks l + 64m of all eight rows, so an h chunk read from LDS serves
     // eight rows
     const int tile = blockIdx.x - NA;
+    if ((tile + 1) * kLTile <= hot) {
+        // a tile of the always-listed hot prefix (hot is a multiple of 32):
+        // every neuron on, no P2 row read, no wait for h
+        if (tid == 0) st_tag(&mtag[tile], next_epoch(*epoch_word), 0xFFFFFFFFu);
+        return;
+    }
     const int row0 = tile * kLTile + wave * kLRows;   // wave-uniform
     const int nch = r >> 3;
     const int M = (nch + 63) / 64;                     // chunk columns per lane
@@ -536,15 +544,16 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 }
 
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
-                                const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
-                                char* hdr, char* data, int32_t* idx, int32_t* count, hipStream_t s) {
+                                const h16* P2, const float* b2, int ffn, int hot, float thr,
+                                const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
+                                hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
     const int NA = (r + 3) / 4;
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
-                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero);
+                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot);
     return hipGetLastError();
 }
 

@@ -219,13 +219,14 @@ hipError_t launch_check_idx(const int32_t* idx, const int32_t* count, int B, int
                             hipStream_t s);
 
 hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const float* b1, bool relu,
-                          const h16* P2, const float* b2, int r, int ffn, float thr, int32_t* idx,
+                          const h16* P2, const float* b2, int r, int ffn, int hot, float thr, int32_t* idx,
                           int32_t* count, const BPredLayout& L, char* ws, char* hdr, hipStream_t s);
 
 // fused.hip
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
-                                const h16* P2, const float* b2, int ffn, float thr, const FusedPredLayout& L,
-                                char* hdr, char* data, int32_t* idx, int32_t* count, hipStream_t s);
+                                const h16* P2, const float* b2, int ffn, int hot, float thr,
+                                const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
+                                hipStream_t s);
 hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,

@@ -53,8 +53,10 @@ def _bits(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
 
 def predict(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
             count: Optional[torch.Tensor] = None, act: str = "relu",
-            tau: Optional[float] = None, stream=None):
-    """idx (B x ffn int32) and count (B int32) for tokens x (B x d fp16)."""
+            tau: Optional[float] = None, n_hot: int = 0, stream=None):
+    """idx (B x ffn int32) and count (B int32) for tokens x (B x d fp16).
+    n_hot > 0: neurons [0, n_hot) of a hot-first layer are always listed and
+    skip the predictor (pi_ffn_predict_hot)."""
     Bt, d = x.shape
     ffn, r = layer["ffn"], layer["r"]
     if idx is None:
@@ -63,10 +65,15 @@ def predict(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
         count = torch.empty(Bt, dtype=torch.int32, device=x.device)
     nbytes = B.pi_workspace_size(B.PI_OP_PREDICT, Bt, d, r, ffn)
     ws, wsb = workspace("predict", x.device).get(nbytes)
-    st = B.pi_ffn_predict(_bits(x), Bt, d, layer["P1"], layer.get("b1"), B.ACTS[act], layer["P2"],
-                          layer.get("b2"), r, ffn, float(layer["tau"] if tau is None else tau),
-                          idx, count, ws, wsb, stream)
-    B.check(st, "pi_ffn_predict")
+    t = float(layer["tau"] if tau is None else tau)
+    if n_hot:
+        st = B.pi_ffn_predict_hot(_bits(x), Bt, d, layer["P1"], layer.get("b1"), B.ACTS[act], layer["P2"],
+                                  layer.get("b2"), r, ffn, int(n_hot), t, idx, count, ws, wsb, stream)
+        B.check(st, "pi_ffn_predict_hot")
+    else:
+        st = B.pi_ffn_predict(_bits(x), Bt, d, layer["P1"], layer.get("b1"), B.ACTS[act], layer["P2"],
+                              layer.get("b2"), r, ffn, t, idx, count, ws, wsb, stream)
+        B.check(st, "pi_ffn_predict")
     return idx, count
 
 

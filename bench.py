@@ -135,6 +135,82 @@ def profile_run(layers, tokens, NL, NT, dev):
                                       "copies": 4}}), flush=True)
 
 
+def hot_prefix_line(cfg_key, nl, ntok, reps, log_fn):
+    """Single-token steps on hot-first layers: each layer profiled on its 4096
+    calibration tokens and reordered, the neurons that fired on >= 99 % of them
+    (whole 32-neuron words) listed without the predictor (pi_ffn_predict_hot),
+    against the same layers with the plain predictor.  Graph-timed, nl rotated
+    layers."""
+    import numpy as np
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import CONFIGS, make_calibration, make_layer, make_tokens
+    cfg = CONFIGS[cfg_key]
+    kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
+    dev = torch.device("cuda:0")
+    layers, hots = [], []
+    for l in range(nl):
+        L = make_layer(cfg, layer=l, device=dev)
+        Wf, bf = (L["W_up"], L["b_up"]) if kind == "relu" else (L["W_gate"], L["b_gate"])
+        counts = R.profile(make_calibration(cfg, device=dev, layer=l), Wf, bf).cpu().numpy()
+        perm, _ = R.reorder(counts, 0.8)
+        P = R.permute_layer(L, torch.from_numpy(perm).to(dev))
+        hots.append(32 * (int(np.count_nonzero(counts[perm] >= 0.99 * cfg.calib_tokens)) // 32))
+        layers.append(P)
+        del L
+    xs = [[make_tokens(cfg, ntok, device=dev, layer=l)[t:t + 1].contiguous() for t in range(ntok)]
+          for l in range(nl)]
+    idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    y = torch.empty(1, d, dtype=torch.float32, device=dev)
+    K = nl * ntok
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {"workload": cfg.workload + " hot-first", "n_hot_mean": float(np.mean(hots)),
+           "calibration_tokens": cfg.calib_tokens}
+    for name, use_hot in (("plain", False), ("hot_prefix", True)):
+        def run():
+            for s in range(K):
+                l, t = s % nl, (s // nl) % ntok
+                R.predict(layers[l], xs[l][t], idx, cnt, n_hot=hots[l] if use_hot else 0)
+                R.sparse(layers[l], xs[l][t], idx, cnt, y)
+        counts = []
+        for s in range(K):
+            l, t = s % nl, (s // nl) % ntok
+            R.predict(layers[l], xs[l][t], idx, cnt, n_hot=hots[l] if use_hot else 0)
+            counts.append(int(cnt.item()))
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            run()
+            cs.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * K)
+        del g
+        m = 1 if kind == "relu" else 2
+        cmean = float(np.mean(counts))
+        skipped = float(np.mean([hots[s % nl] for s in range(K)])) if use_hot else 0.0
+        T = (2 * r * d + (ffn - skipped) * (2 * r + 4) + (m + 1) * cmean * 2 * d + 4 * cmean
+             + 2 * d + 4 * d + 8 * cmean)
+        out[name] = {"us_per_step": ms * 1000, "tokens_per_s_per_layer": 1000.0 / ms, "mean_active": cmean,
+                     "touched_MB": T / 1e6, "GBs": T / ms / 1e6}
+        log_fn(f"{name:10s}: {ms * 1000:7.2f} us  {1000.0 / ms:8.0f} tok/s/layer  active {cmean:7.1f}  "
+               f"T {T / 1e6:6.1f} MB  {T / ms / 1e6:6.0f} GB/s  (n_hot {np.mean(hots):.0f})")
+    del layers, xs
+    torch.cuda.empty_cache()
+    return out
+
+
 def batch_sweep(cfg_key, batches, steps, nl, log_fn):
     """Decode steps of B tokens on the union path, cache-cold over nl layers."""
     import torch
@@ -222,6 +298,8 @@ def main():
     ap.add_argument("--sweep", default="c4", help="config of the batch sweep ('' to skip)")
     ap.add_argument("--sweep-batches", default="1,4,8,16,32")
     ap.add_argument("--sweep-steps", type=int, default=200)
+    ap.add_argument("--hot", default="c2",
+                    help="config of the hot-prefix line: hot-first layers, predictor trimmed ('' to skip)")
     ap.add_argument("--prompt", default="c5",
                     help="config of the prompt-phase line: one 128-token batch per layer ('' to skip)")
     ap.add_argument("--sweep-only", action="store_true",
@@ -485,6 +563,13 @@ def main():
         sweep = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")],
                             args.sweep_steps, 4, log)
 
+    hot = None
+    if args.hot:
+        if not args.sweep:
+            del layers, tokens, xs
+        torch.cuda.empty_cache()
+        hot = hot_prefix_line(args.hot, 8, 8, 16, log)
+
     prompt = None
     if args.prompt:
         # the prompt of a sequence: 128 tokens through the union path at once,
@@ -532,6 +617,7 @@ def main():
         "dense_baseline": dense,
         "cpu_baseline": cpu,
         "batch_sweep": sweep,
+        "hot_prefix": hot,
         "prompt_phase": prompt,
     }
     print(json.dumps(out), flush=True)

@@ -127,6 +127,32 @@ pi_status pi_ffn_predict(const pi_half* x, int B, int d,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * pi_ffn_predict_hot -- pi_ffn_predict on a hot-first layer whose first n_hot
+ * neurons are always active.
+ *
+ * After the offline profile and the hot-first reorder (pi_profile,
+ * pi_reorder, pi_permute_rows), the neurons at the front are the ones that
+ * fire on nearly every token, the hot end of the power law that the
+ * profiler and the placement of Part A section 2.3 (modules 1-2) single out
+ * and preload.  Listing such neurons unconditionally is this library's use
+ * of that split on one GPU: they bypass the predictor, so rows [0, n_hot) of
+ * P2 and b2 are never read, and computing a neuron that turns out inactive
+ * only adds its exact contribution.  The other neurons are predicted exactly
+ * as pi_ffn_predict does:
+ *   idx_t = [0, 1, ..., n_hot - 1] followed by the ascending i >= n_hot with z_i > ln(tau / (1 - tau)).
+ * P2 and b2 still hold all ffn rows (the caller's layout does not change).
+ * n_hot = 0 is pi_ffn_predict.  The workspace is pi_workspace_size(PI_OP_PREDICT, ...).
+ *
+ * Errors: as pi_ffn_predict, plus INVALID_ARG for n_hot outside [0, ffn],
+ * and UNSUPPORTED for n_hot not a multiple of 32 (whole 32-neuron mask words).
+ */
+pi_status pi_ffn_predict_hot(const pi_half* x, int B, int d,
+                             const pi_half* P1, const float* b1, int act,
+                             const pi_half* P2, const float* b2, int r, int ffn, int n_hot,
+                             float tau, int32_t* idx, int32_t* count,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
  * pi_ffn_sparse -- the neuron-aware FFN over the active rows only.
  *
  * Per token t, over j < count[t] with i = idx[t * ffn + j]:

@@ -23,6 +23,7 @@ from .ffn import (  # noqa: F401
     predictor_hidden,
     predictor_logits,
     predict,
+    predict_hot,
     neuron_preactivations,
     neuron_activations,
     silu,

@@ -100,6 +100,24 @@ def predict(x, P1, b1, act, P2, b2, tau) -> Tuple[np.ndarray, np.ndarray]:
     return idx, z
 
 
+def predict_hot(x, P1, b1, act, P2, b2, tau, n_hot) -> Tuple[np.ndarray, np.ndarray]:
+    """The list of a hot-first layer whose first n_hot neurons are always listed.
+
+    After profiling and the hot-first reorder ([R] Part A 2.3 modules 1-2: the
+    hot neurons are the frequent ones, placed up front), neurons 0..n_hot-1 are
+    active without consulting the predictor; the predictor decides the rest
+    from rows n_hot.. of P2 and b2 alone.  idx = 0..n_hot-1, then n_hot + the
+    ascending active positions among the others; z is +inf on the prefix.
+    """
+    n_hot = int(n_hot)
+    P2c = np.asarray(P2)[n_hot:]
+    b2c = None if b2 is None else np.asarray(b2)[n_hot:]
+    z_rest = predictor_logits(x, P1, b1, act, P2c, b2c)
+    rest = n_hot + np.flatnonzero(z_rest > logit_threshold(tau))
+    idx = np.concatenate([np.arange(n_hot, dtype=np.int64), rest.astype(np.int64)])
+    return idx, np.concatenate([np.full(n_hot, np.inf), z_rest])
+
+
 def neuron_preactivations(kind, x, W_up, b_up, W_gate, b_gate, rows) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """u_i = W_up[i] x + b_up_i and (ReGLU) g_i = W_gate[i] x + b_gate_i for i in rows.
 

@@ -140,6 +140,27 @@ def test_predict_rejects_before_launch(kw, code):
     assert B.last_error() != ""
 
 
+def _predict_hot(**kw):
+    args = dict(x=A, B=1, d=64, P1=A, b1=None, act=B.PI_ACT_RELU, P2=A, b2=None, r=16, ffn=128, n_hot=32,
+                tau=0.5, idx=A, count=A, ws=A, ws_bytes=0, stream=0)
+    args.update(kw)
+    return B.pi_ffn_predict_hot(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_hot=-32), B.PI_ERR_INVALID_ARG),
+    (dict(n_hot=160), B.PI_ERR_INVALID_ARG),          # beyond ffn
+    (dict(n_hot=16), B.PI_ERR_UNSUPPORTED),           # not whole 32-neuron mask words
+    (dict(n_hot=97, ffn=100), B.PI_ERR_UNSUPPORTED),  # ffn may be ragged, n_hot may not
+    (dict(x=None), B.PI_ERR_INVALID_ARG),
+    (dict(tau=1.0), B.PI_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), B.PI_ERR_WORKSPACE),
+])
+def test_predict_hot_rejects_before_launch(kw, code):
+    assert _predict_hot(**kw) == code
+    assert B.last_error() != ""
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(kind=5), B.PI_ERR_INVALID_ARG),
     (dict(x=None), B.PI_ERR_INVALID_ARG),

@@ -553,3 +553,76 @@ def test_full_size_swiglu_batched():
         z = O.predictor_logits(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"])
         check_idx(gi, z, thr, where=f"c3s B=16 t={t}")
         check_y(Y[t].cpu().numpy(), _oracle_y(H, X[t].cpu(), gi), where=f"c3s B=16 t={t}")
+
+
+# ---------------------------------------------------------------- hot prefix (pi_ffn_predict_hot)
+def _hot_first(cfg, L, ncal):
+    """Profile on calibration tokens, plan the hot-first order, permute the layer;
+    returns the permuted layer and its counts in the new order."""
+    Xc = make_calibration(cfg, ncal).to(DEV)
+    Wf = L["W_up"] if cfg.kind == "relu" else L["W_gate"]
+    bf = L["b_up"] if cfg.kind == "relu" else L["b_gate"]
+    counts = R.profile(Xc, Wf, bf).cpu().numpy()
+    perm, _ = R.reorder(counts, 0.8)
+    return R.permute_layer(L, torch.from_numpy(perm).to(DEV)), counts[perm]
+
+
+def _check_hot(P, X, n_hot, where):
+    H = _host(P)
+    thr = O.logit_threshold(P["tau"])
+    idx, cnt = R.predict(P, X, n_hot=n_hot)
+    Y = R.sparse(P, X, idx, cnt)
+    torch.cuda.synchronize()
+    for t in sorted({0, X.shape[0] // 2, X.shape[0] - 1}):
+        c = int(cnt[t].cpu())
+        gi = idx[t, :c].cpu().numpy()
+        assert np.array_equal(gi[:n_hot], np.arange(n_hot)), f"{where} t={t}: hot prefix not listed"
+        _, z = O.predict_hot(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"], P["tau"], n_hot)
+        check_idx(gi, z, thr, where=f"{where} t={t}")
+        check_y(Y[t].cpu().numpy(), _oracle_y(H, X[t].cpu(), gi), where=f"{where} t={t}")
+
+
+@pytest.mark.parametrize("kind,Bt,n_hot", [("relu", 1, 64), ("reglu", 1, 256), ("relu", 4, 96),
+                                           ("relu", 20, 64), ("swiglu", 16, 128), ("relu", 1, 2048)])
+def test_hot_prefix(kind, Bt, n_hot):
+    """Neurons [0, n_hot) of a hot-first layer are listed for every token without
+    the predictor; the others follow the oracle's prediction from rows n_hot.."""
+    cfg = custom_config(kind, 520, 2080, 72, mean=0.2, exponent=1.3, number=97)
+    L = R.to_device(make_layer(cfg), DEV)
+    P, _ = _hot_first(cfg, L, 512)
+    X = make_tokens(cfg, Bt).to(DEV)
+    _check_hot(P, X, n_hot, where=f"hot {kind} B={Bt} n_hot={n_hot}")
+
+
+def test_hot_prefix_zero_and_whole():
+    """n_hot = 0 is pi_ffn_predict (bitwise); n_hot = ffn lists every neuron."""
+    cfg = custom_config("relu", 256, 1024, 64, mean=0.1, number=98)
+    L = R.to_device(make_layer(cfg), DEV)
+    for Bt in (1, 5):
+        X = make_tokens(cfg, Bt).to(DEV)
+        i0, c0 = R.predict(L, X)
+        ws = torch.zeros(B.pi_workspace_size(B.PI_OP_PREDICT, Bt, 256, 64, 1024), dtype=torch.uint8, device=DEV)
+        i1 = torch.empty_like(i0)
+        c1 = torch.empty_like(c0)
+        B.check(B.pi_ffn_predict_hot(X, Bt, 256, L["P1"], None, B.PI_ACT_RELU, L["P2"], L["b2"], 64, 1024, 0,
+                                     float(L["tau"]), i1, c1, ws, ws.numel()), "predict_hot 0")
+        i2, c2 = R.predict(L, X, n_hot=1024)
+        torch.cuda.synchronize()
+        assert torch.equal(c0, c1)
+        for t in range(Bt):
+            c = int(c0[t])
+            assert torch.equal(i0[t, :c], i1[t, :c])
+            assert int(c2[t]) == 1024 and torch.equal(i2[t].cpu(), torch.arange(1024, dtype=torch.int32))
+
+
+def test_full_size_hot_prefix():
+    """The OPT-30B-shaped layer profiled on 4096 calibration tokens and reordered;
+    the neurons that fired on at least 99 % of them (rounded down to whole mask
+    words) are the always-listed prefix."""
+    cfg, L, X = _full("c2", ntok=4)
+    P, pc = _hot_first(cfg, L, 4096)
+    n_hot = 32 * (int(np.count_nonzero(pc >= 0.99 * 4096)) // 32)
+    assert n_hot >= 512, n_hot   # about 1157 neurons fire with probability 0.999 by construction
+    del L
+    _check_hot(P, X[:1].contiguous(), n_hot, where="c2 hot B=1")
+    _check_hot(P, X, n_hot, where="c2 hot B=4")

@@ -416,10 +416,33 @@ def pin_swiglu():
         assert not np.any(O.sparse_ffn("swiglu", x, Wu, bu, Wg, bg, Wd, []))
 
 
+def pin_hot_prefix():
+    """The hot-prefix list: no prefix is the plain prediction; a whole prefix is
+    every neuron; otherwise the prefix, then exactly the plain prediction's
+    neurons past it (the predictor's row i depends on row i of P2 and b2 only)."""
+    rng = np.random.default_rng(22)
+    d, r, ffn = 24, 8, 160
+    x = rng.standard_normal(d).astype(np.float16)
+    P1 = rng.standard_normal((r, d)).astype(np.float16)
+    P2 = rng.standard_normal((ffn, r)).astype(np.float16)
+    b2 = (rng.standard_normal(ffn) * 0.5).astype(np.float32)
+    full, zf = O.predict(x, P1, None, "relu", P2, b2, 0.5)
+    idx0, z0 = O.predict_hot(x, P1, None, "relu", P2, b2, 0.5, 0)
+    assert np.array_equal(idx0, full) and np.array_equal(z0, zf)
+    idxa, za = O.predict_hot(x, P1, None, "relu", P2, b2, 0.5, ffn)
+    assert np.array_equal(idxa, np.arange(ffn)) and np.all(np.isinf(za))
+    for n_hot in (32, 64, 96):
+        idx, z = O.predict_hot(x, P1, None, "relu", P2, b2, 0.5, n_hot)
+        want = np.concatenate([np.arange(n_hot), full[full >= n_hot]])
+        assert np.array_equal(idx, want), n_hot
+        assert np.array_equal(z[n_hot:], zf[n_hot:])
+        assert np.all(np.diff(idx) > 0)
+
+
 PINS = [pin_golden_ffn, pin_golden_predictor, pin_golden_profile_reorder, pin_exact_predictor,
         pin_exact_ffn, pin_float64_error_bound, pin_closed_forms, pin_sigmoid_threshold,
         pin_invariants, pin_reorder_invariance, pin_reorder_properties, pin_profile_exact,
-        pin_profile_binomial, pin_swiglu]
+        pin_profile_binomial, pin_swiglu, pin_hot_prefix]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -431,7 +454,7 @@ def test_pin(pin):
 def _mutants():
     orig = {k: getattr(O, k) for k in ("neuron_preactivations", "neuron_activations", "predictor_hidden",
                                        "predict", "profile_counts", "reorder_plan", "sparse_ffn",
-                                       "logit_threshold", "predictor_logits")}
+                                       "logit_threshold", "predictor_logits", "predict_hot")}
 
     def pre_no_bias(kind, x, W_up, b_up, W_gate, b_gate, rows):
         return orig["neuron_preactivations"](kind, x, W_up, None, W_gate, None, rows)
@@ -545,7 +568,17 @@ def _mutants():
             return orig["neuron_preactivations"](kind, x, W_up, b_up, W_gate, b_gate, rows)
         return orig["neuron_preactivations"](kind, x, W_up, b_up, W_gate, None, rows)
 
+    def hot_not_shifted(x, P1, b1, act, P2, b2, tau, n_hot):
+        idx, z = orig["predict_hot"](x, P1, b1, act, P2, b2, tau, n_hot)
+        return np.concatenate([idx[:n_hot], idx[n_hot:] - n_hot]), z
+
+    def hot_prefix_not_listed(x, P1, b1, act, P2, b2, tau, n_hot):
+        idx, z = orig["predict_hot"](x, P1, b1, act, P2, b2, tau, n_hot)
+        return idx[n_hot:], z
+
     return {
+        "hot prefix: rest not shifted by n_hot": ("predict_hot", hot_not_shifted),
+        "hot prefix not listed": ("predict_hot", hot_prefix_not_listed),
         "SwiGLU with SiLU on up": ("neuron_activations", act_swiglu_on_up),
         "SwiGLU with sigmoid for SiLU": ("neuron_activations", act_swiglu_sigmoid),
         "SwiGLU gate bias dropped": ("neuron_preactivations", pre_swiglu_no_gate_bias),
