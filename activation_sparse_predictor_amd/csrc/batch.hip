@@ -334,11 +334,13 @@ __global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* _
 }
 
 // One workgroup per token: the token's 32-bit tile masks in neuron order ->
-// popcount prefix -> ascending idx and count.  The first hotw words (the
-// always-listed hot prefix) count as all ones and are not read.
+// popcount prefix -> ascending idx and count.  Thread k takes words k,
+// k + 256, ... of a round (one block-wide scan per 256 words), so the dense
+// words of a hot-first layer spread over many threads.  The first hotw words
+// (the always-listed hot prefix) count as all ones and are not read.
 __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restrict__ masks32, int ffn, int hotw,
                                                        int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-    __shared__ uint32_t s_part[4];
+    __shared__ uint32_t s_part[32];
     const int tok = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ntiles = (ffn + 31) / 32;
@@ -346,35 +348,39 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
     int32_t* out = idx + (size_t)tok * ffn;
     uint32_t base = 0;
     for (int t0 = 0; t0 < ntiles; t0 += 2048) {
-        uint32_t m8[8];
-        uint32_t mine = 0;
+        uint32_t m8[8], c8[8], i8[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const int t = t0 + tid * 8 + q;
+            const int t = t0 + q * 256 + tid;
             m8[q] = t < hotw ? 0xFFFFFFFFu : (t < ntiles ? mk[t] : 0u);
-            mine += (uint32_t)__popc(m8[q]);
         }
-        uint32_t incl = mine;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t v = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += v;
-        }
-        if (lane == 63) s_part[wave] = incl;
-        __syncthreads();
-        uint32_t pos = base + incl - mine;
-        for (int w2 = 0; w2 < wave; ++w2) pos += s_part[w2];
-        const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
+            c8[q] = (uint32_t)__popc(m8[q]);
+            uint32_t incl = c8[q];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t v = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += v;
+            }
+            i8[q] = incl;
+            if (lane == 63) s_part[q * 4 + wave] = incl;
+        }
+        __syncthreads();
+        uint32_t run = base;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            uint32_t pos = run + i8[q] - c8[q];
+            for (int w2 = 0; w2 < wave; ++w2) pos += s_part[q * 4 + w2];
+            run += s_part[q * 4] + s_part[q * 4 + 1] + s_part[q * 4 + 2] + s_part[q * 4 + 3];
             uint32_t m = m8[q];
-            const int t = t0 + tid * 8 + q;
+            const int t = t0 + q * 256 + tid;
             while (m) {
                 out[pos++] = t * 32 + __builtin_ctz(m);
                 m &= m - 1;
             }
         }
-        base += total;
+        base = run;
         __syncthreads();
     }
     if (tid == 0) count[tok] = (int32_t)base;

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        int hot) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
-    __shared__ uint32_t s_part[4];
+    __shared__ uint32_t s_part[16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int NA = (r + 3) / 4;
@@ -162,47 +162,52 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     }
 
     if ((int)blockIdx.x == NA + NT) {
-        // ---------------- ordered compaction, 1024 tiles per round (4 per thread)
+        // ---------------- ordered compaction, 1024 tiles per round: thread k
+        // takes tiles k, k + 256, k + 512 and k + 768 of the round, so the dense
+        // tiles at the front of a hot-first layer spread over many threads
+        // (each writes its tiles' ids one by one, and a wave runs as long as
+        // its busiest lane); one block-wide scan per quarter gives the offsets.
         const uint32_t epoch = next_epoch(*epoch_word);
         uint32_t base = 0;
         bool good = true;
         for (int t0 = 0; t0 < NT; t0 += 1024) {
             uint64_t m4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + tid * 4 + q, NT - 1)]);
-            uint32_t bits[4];
-            uint32_t mine = 0;
+            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + q * 256 + tid, NT - 1)]);
+            uint32_t bits[4], cnt4[4], incl4[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int t = t0 + tid * 4 + q;
+                const int t = t0 + q * 256 + tid;
                 bits[q] = 0u;
                 if (t < NT) {
                     if (poll_tag(&mtag[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
                     else good = false;
                 }
-                mine += (uint32_t)__popc(bits[q]);
-            }
-            uint32_t incl = mine;
+                cnt4[q] = (uint32_t)__popc(bits[q]);
+                uint32_t incl = cnt4[q];
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t v = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += v;
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t v = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += v;
+                }
+                incl4[q] = incl;
+                if (lane == 63) s_part[q * 4 + wave] = incl;
             }
-            if (lane == 63) s_part[wave] = incl;
             __syncthreads();
-            uint32_t pos = base + incl - mine;
-            for (int w2 = 0; w2 < wave; ++w2) pos += s_part[w2];
-            const uint32_t total = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+            uint32_t run = base;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                uint32_t pos = run + incl4[q] - cnt4[q];
+                for (int w2 = 0; w2 < wave; ++w2) pos += s_part[q * 4 + w2];
+                run += s_part[q * 4] + s_part[q * 4 + 1] + s_part[q * 4 + 2] + s_part[q * 4 + 3];
                 uint32_t m = bits[q];
-                const int t = t0 + tid * 4 + q;
+                const int t = t0 + q * 256 + tid;
                 while (m) {
                     idx[pos++] = t * kLTile + __builtin_ctz(m);
                     m &= m - 1;
                 }
             }
-            base += total;
+            base = run;
             __syncthreads();
         }
         good = __syncthreads_and(good);
