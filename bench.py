@@ -503,6 +503,8 @@ def main():
         R.sparse(layers[l], xs[l][t], idx, cnt, y)
         ev[3 * k + 2].record(stream)
     torch.cuda.synchronize()
+    eager_steps = sorted(1000 * ev[3 * k].elapsed_time(ev[3 * k + 2]) for k in range(K2))
+    pct = {f"p{q}": eager_steps[min(K2 - 1, (q * K2) // 100)] for q in (10, 50, 90)}
     eager_us = {"pi_ffn_predict": 1000 * statistics.mean(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(K2)),
                 "pi_ffn_sparse": 1000 * statistics.mean(ev[3 * k + 1].elapsed_time(ev[3 * k + 2])
                                                         for k in range(K2))}
@@ -605,7 +607,10 @@ def main():
         "decode_call": {"us_per_step": ms_decode * 1000, "tokens_per_s_per_layer": 1000.0 / ms_decode,
                         "GBs": T_avg / ms_decode / 1e6},
         "timing": {"method": f"hipGraph of {Kg} steps replayed {reps} times, HIP events around the replays",
-                   "ms_per_step_eager": ms_eager},
+                   "ms_per_step_eager": ms_eager,
+                   "step_us_eager_percentiles": dict(pct, steps=K2,
+                                                     note="per step from HIP events around each eager "
+                                                          "predict + sparse pair (launch gaps included)")},
         "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dom], "entry_point": dom, "achieved": stages[dom][1],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": stages[dom][1] / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, dom),
