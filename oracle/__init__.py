@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call, link
 or execute anything under this directory: only the test suite, the smoke
-check in the repository's graft entry module, and the benchmark's
-cpu_baseline leg use it.  It shares no code with the HIP library (no kernels,
+check at the repository root (smoke()), and the benchmark's cpu_baseline
+leg use it.  It shares no code with the HIP library (no kernels,
 headers, helpers, tables or pre/post-processing) and never reads a value the
 HIP library produced except the index list it is asked to evaluate y on.
 
