@@ -49,6 +49,9 @@ _SIGNATURES = {
     "pi_ffn_sparse": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "pi_ffn_decode": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                            _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "pi_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P]),
+    "pi_ffn_sparse_q4": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32,
+                              _P, _SZ, _P]),
     "pi_profile": (_I, [_P, _I, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "pi_reorder": (_I, [_P, _I, ctypes.c_double, _P, _P]),
     "pi_permute_rows": (_I, [_P, _P, _I, _I, _P, _P]),
@@ -130,6 +133,17 @@ def pi_ffn_predict_hot(x, B, d, P1, b1, act, P2, b2, r, ffn, n_hot, tau, idx, co
     return load().pi_ffn_predict_hot(_ptr(x), B, d, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r,
                                      ffn, n_hot, tau, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
                                      _stream(stream))
+
+
+def pi_quantize_rows(W, rows, d, q, scales, stream=None) -> int:
+    return load().pi_quantize_rows(_ptr(W), rows, d, _ptr(q), _ptr(scales), _stream(stream))
+
+
+def pi_ffn_sparse_q4(kind, x, B, d, ffn, q_up, s_up, b_up, q_gate, s_gate, b_gate, q_down, s_down, idx, count,
+                     y, flags, ws, ws_bytes, stream=None) -> int:
+    return load().pi_ffn_sparse_q4(kind, _ptr(x), B, d, ffn, _ptr(q_up), _ptr(s_up), _ptr(b_up), _ptr(q_gate),
+                                   _ptr(s_gate), _ptr(b_gate), _ptr(q_down), _ptr(s_down), _ptr(idx), _ptr(count),
+                                   _ptr(y), flags, _ptr(ws), ws_bytes, _stream(stream))
 
 
 def pi_ffn_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags,

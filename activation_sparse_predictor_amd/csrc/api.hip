@@ -376,6 +376,50 @@ pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn, const
     return PI_OK;
 }
 
+pi_status pi_quantize_rows(const pi_half* W, int rows, int d, uint8_t* q, pi_half* scales, void* stream) {
+    PI_REQUIRE(rows >= 1 && rows <= PI_MAX_FFN, PI_ERR_INVALID_ARG, "rows=%d outside [1, %d]", rows, PI_MAX_FFN);
+    PI_REQUIRE(d >= 1, PI_ERR_INVALID_ARG, "d=%d must be positive", d);
+    PI_REQUIRE(d % 64 == 0, PI_ERR_UNSUPPORTED, "d=%d is not a multiple of 64 (the INT4 group)", d);
+    PI_REQUIRE(d <= PI_MAX_D, PI_ERR_UNSUPPORTED, "d=%d above PI_MAX_D=%d", d, PI_MAX_D);
+    PI_TRY(check_half(W, "W", true));
+    PI_REQUIRE(q != nullptr && scales != nullptr, PI_ERR_INVALID_ARG, "q or scales is NULL");
+    PI_REQUIRE(aligned(q, 16), PI_ERR_UNSUPPORTED, "q is not 16-byte aligned");
+    PI_REQUIRE(aligned(scales, 2), PI_ERR_UNSUPPORTED, "scales is not 2-byte aligned");
+    hipError_t e = pi::launch_quantize_rows(reinterpret_cast<const pi::h16*>(W), rows, d, q,
+                                            reinterpret_cast<pi::h16*>(scales), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_quantize_rows");
+    return ok();
+}
+
+pi_status pi_ffn_sparse_q4(int kind, const pi_half* x, int B, int d, int ffn, const uint8_t* q_up,
+                           const pi_half* s_up, const float* b_up, const uint8_t* q_gate, const pi_half* s_gate,
+                           const float* b_gate, const uint8_t* q_down, const pi_half* s_down, const int32_t* idx,
+                           const int32_t* count, float* y, uint32_t flags, void* ws, size_t ws_bytes,
+                           void* stream) {
+    // the fp16 argument checks, with the code arrays standing in for the weight pointers
+    PI_TRY(check_sparse_args(kind, x, B, d, ffn, reinterpret_cast<const pi_half*>(q_up), b_up,
+                             reinterpret_cast<const pi_half*>(q_gate), b_gate,
+                             reinterpret_cast<const pi_half*>(q_down), idx, count, y, flags & ~PI_CHECK_IDX));
+    PI_REQUIRE((flags & ~(PI_DENSE | PI_DETERMINISTIC)) == 0u, PI_ERR_INVALID_ARG,
+               "flags 0x%x: only PI_DENSE and PI_DETERMINISTIC apply to INT4 rows", flags);
+    PI_REQUIRE(d % 64 == 0, PI_ERR_UNSUPPORTED, "d=%d is not a multiple of 64 (the INT4 group)", d);
+    PI_REQUIRE(s_up != nullptr && s_down != nullptr && (kind == PI_FFN_RELU || s_gate != nullptr),
+               PI_ERR_INVALID_ARG, "a scale array is NULL");
+    PI_REQUIRE(aligned(s_up, 2) && aligned(s_down, 2) && aligned(s_gate, 2), PI_ERR_UNSUPPORTED,
+               "a scale array is not 2-byte aligned");
+    PI_TRY(check_ws(ws, ws_bytes, sparse_ws_bytes(B, d, ffn), "pi_ffn_sparse_q4"));
+    ws_forget(ws);
+    char* data = static_cast<char*>(ws) + pi::kSyncBytes;
+    const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
+    hipError_t e = pi::launch_ffn_q4(kind, (flags & PI_DENSE) != 0u, reinterpret_cast<const pi::h16*>(x), B, d, ffn,
+                                     q_up, reinterpret_cast<const pi::h16*>(s_up), b_up, q_gate,
+                                     reinterpret_cast<const pi::h16*>(s_gate), b_gate, q_down,
+                                     reinterpret_cast<const pi::h16*>(s_down), idx, count, y, L, data,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse_q4");
+    return ok();
+}
+
 pi_status pi_profile(const pi_half* X, int n, int d, int ffn, const pi_half* W_fire,
                      const float* b_fire, uint32_t* counts, void* ws, size_t ws_bytes,
                      void* stream) {

@@ -99,6 +99,11 @@ __device__ __forceinline__ uint32_t rank_below(uint64_t m) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// A list length clamped to [0, ffn], a neuron id to [0, ffn): a broken list
+// can never make a kernel read outside the weights.
+__device__ __forceinline__ int clamp_count(int c, int ffn) { return c < 0 ? 0 : (c > ffn ? ffn : c); }
+__device__ __forceinline__ int clamp_row(int i, int ffn) { return i < 0 ? 0 : (i >= ffn ? ffn - 1 : i); }
+
 // Device-coherent relaxed accesses for cross-workgroup flags.
 __device__ __forceinline__ uint32_t ld_flag(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -233,6 +233,13 @@ hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16
                                char* data, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
+// q4.hip
+hipError_t launch_quantize_rows(const h16* W, int rows, int d, uint8_t* q, h16* s, hipStream_t st);
+hipError_t launch_ffn_q4(int kind, bool dense, const h16* x, int B, int d, int ffn, const uint8_t* qu,
+                         const h16* su, const float* bup, const uint8_t* qg, const h16* sg, const float* bg,
+                         const uint8_t* qd, const h16* sd, const int32_t* idx, const int32_t* count, float* y,
+                         const SparseLayout& L, char* data, hipStream_t s);
+
 // profile.hip
 hipError_t launch_profile(const h16* X, int n, int d, int ffn, const h16* W, const float* b,
                           uint32_t* counts, hipStream_t s);

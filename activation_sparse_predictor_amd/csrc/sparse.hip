@@ -15,8 +15,6 @@ namespace pi {
 // The active count and ids come from device memory; a count outside [0, ffn]
 // (the compaction's -1 error marker included) or an id outside [0, ffn) is
 // clamped so that no input can make the kernels read outside the weights.
-__device__ __forceinline__ int clamp_count(int c, int ffn) { return c < 0 ? 0 : (c > ffn ? ffn : c); }
-__device__ __forceinline__ int clamp_row(int i, int ffn) { return i < 0 ? 0 : (i >= ffn ? ffn - 1 : i); }
 
 // ---------------------------------------------------------------------------
 // Gathered up(/gate) GEMV.  One wave per active neuron: the row (d fp16) is

@@ -104,6 +104,44 @@ def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
     return y
 
 
+def quantize_rows(W: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """INT4 codes (rows x d/2 uint8) and scales (rows x d/64 fp16) of fp16 rows W."""
+    rows, d = W.shape
+    q = torch.empty(rows, d // 2, dtype=torch.uint8, device=W.device)
+    s = torch.empty(rows, d // 64, dtype=torch.float16, device=W.device)
+    B.check(B.pi_quantize_rows(_bits(W), rows, d, q, s, stream), "pi_quantize_rows")
+    return q, s
+
+
+def quantize_layer(layer: dict, stream=None) -> dict:
+    """The layer with its W_up, W_gate and W_down as INT4 rows (q_*, s_*); the
+    predictor and the biases are kept."""
+    out = {k: v for k, v in layer.items() if k not in ("W_up", "W_gate", "W_down")}
+    for k, name in (("W_up", "up"), ("W_gate", "gate"), ("W_down", "down")):
+        if layer.get(k) is not None:
+            out["q_" + name], out["s_" + name] = quantize_rows(layer[k], stream)
+        else:
+            out["q_" + name], out["s_" + name] = None, None
+    return out
+
+
+def sparse_q4(layer_q: dict, x: torch.Tensor, idx: Optional[torch.Tensor], count: Optional[torch.Tensor],
+              y: Optional[torch.Tensor] = None, dense: bool = False, stream=None) -> torch.Tensor:
+    """pi_ffn_sparse_q4 over a layer from quantize_layer."""
+    Bt, d = x.shape
+    ffn = layer_q["ffn"]
+    if y is None:
+        y = torch.empty(Bt, d, dtype=torch.float32, device=x.device)
+    nbytes = B.pi_workspace_size(B.PI_OP_SPARSE, Bt, d, layer_q.get("r", 8), ffn)
+    ws, wsb = workspace("sparse_q4", x.device).get(nbytes)
+    st = B.pi_ffn_sparse_q4(B.KINDS[layer_q["kind"]], _bits(x), Bt, d, ffn, layer_q["q_up"], layer_q["s_up"],
+                            layer_q.get("b_up"), layer_q["q_gate"], layer_q["s_gate"], layer_q.get("b_gate"),
+                            layer_q["q_down"], layer_q["s_down"], None if dense else idx,
+                            None if dense else count, y, B.PI_DENSE if dense else 0, ws, wsb, stream)
+    B.check(st, "pi_ffn_sparse_q4")
+    return y
+
+
 def decode(layer: dict, x: torch.Tensor, y: Optional[torch.Tensor] = None,
            idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
            act: str = "relu", tau: Optional[float] = None, per_token: bool = False,

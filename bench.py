@@ -211,6 +211,80 @@ def hot_prefix_line(cfg_key, nl, ntok, reps, log_fn):
     return out
 
 
+def q4_line(cfg_key, nl, ntok, reps, log_fn):
+    """Single-token steps with INT4 FFN rows (pi_quantize_rows once per layer,
+    then pi_ffn_predict + pi_ffn_sparse_q4 per step; the predictor stays fp16),
+    graph-timed over nl rotated layers, beside the INT4 dense FFN."""
+    import numpy as np
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import CONFIGS, make_layer, make_tokens
+    cfg = CONFIGS[cfg_key]
+    kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
+    m = 1 if kind == "relu" else 2
+    dev = torch.device("cuda:0")
+    layers = []
+    for l in range(nl):
+        L = make_layer(cfg, layer=l, device=dev)
+        Q = R.quantize_layer(L)
+        for k in ("W_up", "W_gate", "W_down"):
+            L.pop(k, None)
+        Q.update({k: v for k, v in L.items() if k not in Q})
+        layers.append(Q)
+    xs = [[make_tokens(cfg, ntok, device=dev, layer=l)[t:t + 1].contiguous() for t in range(ntok)]
+          for l in range(nl)]
+    idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    y = torch.empty(1, d, dtype=torch.float32, device=dev)
+    K = nl * ntok
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    counts = []
+    for s in range(K):
+        l, t = s % nl, (s // nl) % ntok
+        R.predict(layers[l], xs[l][t], idx, cnt)
+        counts.append(int(cnt.item()))
+    out = {"workload": cfg.workload + " int4 rows (group 64)"}
+    for name, dense in (("sparse", False), ("dense", True)):
+        def run():
+            for s in range(K):
+                l, t = s % nl, (s // nl) % ntok
+                if not dense:
+                    R.predict(layers[l], xs[l][t], idx, cnt)
+                R.sparse_q4(layers[l], xs[l][t], idx, cnt, y, dense=dense)
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        with torch.cuda.stream(cs):
+            run()
+            cs.synchronize()
+            with torch.cuda.graph(g, stream=cs):
+                run()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * K)
+        del g
+        row = d // 2 + d // 32
+        if dense:
+            T = (m + 1) * ffn * row + 4 * ffn + 6 * d
+        else:
+            c = float(np.mean(counts))
+            T = 2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * c * row + 4 * c + 6 * d + 8 * c
+        out[name] = {"us_per_step": ms * 1000, "tokens_per_s_per_layer": 1000.0 / ms, "touched_MB": T / 1e6,
+                     "GBs": T / ms / 1e6}
+        log_fn(f"int4 {name:6s}: {ms * 1000:7.2f} us  {1000.0 / ms:8.0f} tok/s/layer  T {T / 1e6:6.1f} MB  "
+               f"{T / ms / 1e6:6.0f} GB/s")
+    del layers, xs
+    torch.cuda.empty_cache()
+    return out
+
+
 def batch_sweep(cfg_key, batches, steps, nl, log_fn):
     """Decode steps of B tokens on the union path, cache-cold over nl layers."""
     import torch
@@ -300,6 +374,7 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=200)
     ap.add_argument("--hot", default="c2",
                     help="config of the hot-prefix line: hot-first layers, predictor trimmed ('' to skip)")
+    ap.add_argument("--q4", default="c2", help="config of the INT4-rows line ('' to skip)")
     ap.add_argument("--prompt", default="c5",
                     help="config of the prompt-phase line: one 128-token batch per layer ('' to skip)")
     ap.add_argument("--sweep-only", action="store_true",
@@ -572,6 +647,13 @@ def main():
         torch.cuda.empty_cache()
         hot = hot_prefix_line(args.hot, 8, 8, 16, log)
 
+    q4 = None
+    if args.q4:
+        if not args.sweep and not args.hot:
+            del layers, tokens, xs
+        torch.cuda.empty_cache()
+        q4 = q4_line(args.q4, 8, 8, 16, log)
+
     prompt = None
     if args.prompt:
         # the prompt of a sequence: 128 tokens through the union path at once,
@@ -623,6 +705,7 @@ def main():
         "cpu_baseline": cpu,
         "batch_sweep": sweep,
         "hot_prefix": hot,
+        "int4_rows": q4,
         "prompt_phase": prompt,
     }
     print(json.dumps(out), flush=True)

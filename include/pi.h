@@ -240,6 +240,48 @@ pi_status pi_profile(const pi_half* X, int n, int d, int ffn,
                      uint32_t* counts, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * pi_quantize_rows -- INT4 neuron rows (this library's own format).
+ *
+ * Part A section 3.1 of the pages reports the method with INT4 weights as
+ * well as FP16; no format is given there, so this one is the library's.  Each row
+ * of W (rows x d fp16, d % 64 == 0) is cut into groups of 64 weights.  Group
+ * g gets one fp16 scale
+ *   s = fp16(max |w| / 7)            (fp32 division, then round to nearest even)
+ * and its weights become
+ *   c = clamp(rint(w / s), -8, 7)    (fp32 division, rint rounds half to even; c = 0 when s = 0)
+ * stored as the 4-bit code c + 8, two per byte: weight e of a row is the low
+ * nibble of byte e / 2 for even e, the high nibble for odd e.  The weight the
+ * FFN uses is (code - 8) * s.
+ * Outputs (device, caller-owned): q, rows x d / 2 bytes (16-byte aligned);
+ * scales, rows x d / 64 fp16.  Asynchronous on the stream; no workspace.
+ * Errors: INVALID_ARG for rows or d out of range or a NULL pointer;
+ * UNSUPPORTED for d not a multiple of 64, d > PI_MAX_D, or misalignment.
+ */
+pi_status pi_quantize_rows(const pi_half* W, int rows, int d, uint8_t* q, pi_half* scales, void* stream);
+
+/*
+ * pi_ffn_sparse_q4 -- pi_ffn_sparse over INT4 rows of W_up, W_gate and W_down
+ * (as written by pi_quantize_rows; q_* are the code arrays, s_* their scales).
+ *
+ * The same computation as pi_ffn_sparse with each weight replaced by its
+ * dequantised value (code - 8) * s: per token, over the listed neurons,
+ * a_i = act(u_i, g_i) and y = sum a_i W_down[i, :].  Products and sums are in
+ * fp32.  An active neuron's three rows take 3 * (d / 2 + d / 32) bytes
+ * instead of 3 * 2d.  Flags: PI_DENSE (every neuron), PI_DETERMINISTIC
+ * (accepted; the path is deterministic).  The workspace is
+ * pi_workspace_size(PI_OP_SPARSE, B, d, r, ffn).  Two kernels per call; B
+ * tokens share each launch (one grid row per token).
+ * Errors: as pi_ffn_sparse; UNSUPPORTED for d not a multiple of 64; INVALID_ARG
+ * for a NULL scale array of a matrix that is used, or another flag.
+ */
+pi_status pi_ffn_sparse_q4(int kind, const pi_half* x, int B, int d, int ffn,
+                           const uint8_t* q_up, const pi_half* s_up, const float* b_up,
+                           const uint8_t* q_gate, const pi_half* s_gate, const float* b_gate,
+                           const uint8_t* q_down, const pi_half* s_down,
+                           const int32_t* idx, const int32_t* count, float* y, uint32_t flags,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * pi_reorder -- HOST-ONLY hot-first order from profile counts.
  *
  * perm (host, ffn int32, new -> old) lists neurons by descending count, ties

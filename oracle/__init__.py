@@ -37,4 +37,6 @@ from .ffn import (  # noqa: F401
     rows_of,
     reorder_plan,
     permute_rows,
+    quantize_rows,
+    dequantize_rows,
 )

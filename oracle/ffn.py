@@ -264,3 +264,35 @@ def permute_rows(src, perm) -> np.ndarray:
         src = src.detach().cpu().numpy()
     src = np.asarray(src)
     return src[np.asarray(perm, dtype=np.int64)].copy()
+
+
+def quantize_rows(W) -> Tuple[np.ndarray, np.ndarray]:
+    """INT4 rows, the library's own group-wise format ([R] Part A 3.1 reports
+    INT4 results without a format).  Per group of 64 weights of a row, in fp32:
+    s = fp16(max|w| / 7) (IEEE division, round to nearest even), code =
+    clamp(rint(w / s), -8, 7) + 8 (rint: half to even; 8 when s = 0).  Codes
+    are packed two per byte, the even weight in the low nibble.  Returns
+    (codes rows x d/2 uint8, scales rows x d/64 float16)."""
+    W32 = np.asarray(W, dtype=np.float16).astype(np.float32)
+    rows, d = W32.shape
+    G = W32.reshape(rows, d // 64, 64)
+    amax = np.abs(G).max(axis=2)
+    s16 = (amax / np.float32(7.0)).astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    c = np.zeros(G.shape, dtype=np.int64)
+    nz = np.broadcast_to(s32 != 0, G.shape)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c[nz] = np.clip(np.rint(G / s32), -8, 7)[nz].astype(np.int64)
+    codes = (c + 8).reshape(rows, d)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, s16
+
+
+def dequantize_rows(q, s, d: int) -> np.ndarray:
+    """The weights INT4 rows stand for, in float64: (code - 8) * s."""
+    q = np.asarray(q, dtype=np.uint8)
+    codes = np.empty((q.shape[0], d), dtype=np.int64)
+    codes[:, 0::2] = q & 0xF
+    codes[:, 1::2] = q >> 4
+    scale = np.repeat(np.asarray(s, dtype=np.float16).astype(F64), 64, axis=1)
+    return (codes - 8).astype(F64) * scale

@@ -439,10 +439,42 @@ def pin_hot_prefix():
         assert np.all(np.diff(idx) > 0)
 
 
+def pin_int4_rows():
+    """INT4 rows against values fixed by the format's definition.
+
+    A group whose largest magnitude is 7 * 2^e and whose weights are k * 2^e
+    (|k| <= 7) has scale 2^e and codes k + 8 exactly; halves round to even
+    (w / s = 2.5 -> 2, 3.5 -> 4, -2.5 -> -2); an all-zero group has scale 0 and
+    code 8; weight 0 of a row is the low nibble of byte 0, weight 1 its high
+    nibble.  On random rows the dequantised weight is within s / 2 of w.
+    """
+    e = 2.0 ** -3
+    ks = np.array([7, -7, 0, 1, -1, 3, -5, 2] * 8, dtype=np.int64)
+    row = np.concatenate([(ks * e).astype(np.float16), np.zeros(64, np.float16)])
+    halves = np.zeros(64, np.float16)
+    halves[:5] = [7.0, 2.5, 3.5, -2.5, -7.0]     # scale 1: codes 15, 10, 12, 6, 1
+    W = np.stack([row, np.concatenate([halves, np.zeros(64, np.float16)])])
+    q, sc = O.quantize_rows(W)
+    assert sc.dtype == np.float16 and sc.shape == (2, 2) and q.shape == (2, 64)
+    assert sc[0, 0] == np.float16(e) and sc[0, 1] == 0 and sc[1, 0] == 1
+    codes0 = np.empty(128, np.int64)
+    codes0[0::2], codes0[1::2] = q[0] & 0xF, q[0] >> 4
+    assert np.array_equal(codes0[:64], ks + 8) and np.all(codes0[64:] == 8)
+    assert q[0, 0] == (7 + 8) | ((-7 + 8) << 4)            # low nibble = weight 0
+    assert list((q[1, :3] & 0xF)) == [15, 12, 1] and list(q[1, :2] >> 4) == [10, 6]
+    assert np.array_equal(O.dequantize_rows(q, sc, 128)[0], row.astype(np.float64))
+    rng = np.random.default_rng(23)
+    W = (rng.standard_normal((5, 192)) * np.exp(rng.standard_normal((5, 1)))).astype(np.float16)
+    q, sc = O.quantize_rows(W)
+    back = O.dequantize_rows(q, sc, 192)
+    half = np.repeat(sc.astype(np.float64), 64, axis=1) / 2
+    assert np.all(np.abs(back - W.astype(np.float64)) <= half * (1 + 1e-6))
+
+
 PINS = [pin_golden_ffn, pin_golden_predictor, pin_golden_profile_reorder, pin_exact_predictor,
         pin_exact_ffn, pin_float64_error_bound, pin_closed_forms, pin_sigmoid_threshold,
         pin_invariants, pin_reorder_invariance, pin_reorder_properties, pin_profile_exact,
-        pin_profile_binomial, pin_swiglu, pin_hot_prefix]
+        pin_profile_binomial, pin_swiglu, pin_hot_prefix, pin_int4_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -454,7 +486,8 @@ def test_pin(pin):
 def _mutants():
     orig = {k: getattr(O, k) for k in ("neuron_preactivations", "neuron_activations", "predictor_hidden",
                                        "predict", "profile_counts", "reorder_plan", "sparse_ffn",
-                                       "logit_threshold", "predictor_logits", "predict_hot")}
+                                       "logit_threshold", "predictor_logits", "predict_hot",
+                                       "quantize_rows")}
 
     def pre_no_bias(kind, x, W_up, b_up, W_gate, b_gate, rows):
         return orig["neuron_preactivations"](kind, x, W_up, None, W_gate, None, rows)
@@ -576,7 +609,30 @@ def _mutants():
         idx, z = orig["predict_hot"](x, P1, b1, act, P2, b2, tau, n_hot)
         return idx[n_hot:], z
 
+    def q4_nibbles_swapped(W):
+        q, sc = orig["quantize_rows"](W)
+        return ((q >> 4) | (q << 4)).astype(np.uint8), sc
+
+    def q4_scale_over_8(W):
+        W32 = np.asarray(W, dtype=np.float16).astype(np.float32)
+        q, _ = orig["quantize_rows"](W)
+        amax = np.abs(W32.reshape(W32.shape[0], -1, 64)).max(axis=2)
+        return q, (amax / np.float32(8.0)).astype(np.float16)
+
+    def q4_floor(W):
+        W32 = np.asarray(W, dtype=np.float16).astype(np.float32)
+        rows, d = W32.shape
+        G = W32.reshape(rows, d // 64, 64)
+        s16 = (np.abs(G).max(axis=2) / np.float32(7)).astype(np.float16)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            c = np.where(s16[..., None] == 0, 0, np.clip(np.floor(G / s16.astype(np.float32)[..., None]), -8, 7))
+        codes = (c.astype(np.int64) + 8).reshape(rows, d)
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), s16
+
     return {
+        "INT4 nibbles swapped": ("quantize_rows", q4_nibbles_swapped),
+        "INT4 scale max/8": ("quantize_rows", q4_scale_over_8),
+        "INT4 floor instead of rint": ("quantize_rows", q4_floor),
         "hot prefix: rest not shifted by n_hot": ("predict_hot", hot_not_shifted),
         "hot prefix not listed": ("predict_hot", hot_prefix_not_listed),
         "SwiGLU with SiLU on up": ("neuron_activations", act_swiglu_on_up),
