@@ -408,14 +408,31 @@ pi_status pi_ffn_sparse_q4(int kind, const pi_half* x, int B, int d, int ffn, co
     PI_REQUIRE(aligned(s_up, 2) && aligned(s_down, 2) && aligned(s_gate, 2), PI_ERR_UNSUPPORTED,
                "a scale array is not 2-byte aligned");
     PI_TRY(check_ws(ws, ws_bytes, sparse_ws_bytes(B, d, ffn), "pi_ffn_sparse_q4"));
+    char* hdr = static_cast<char*>(ws);
+    char* data = hdr + pi::kSyncBytes;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (B == 1 && (flags & PI_DENSE) == 0u) {
+        // one token: the fused single-token kernel over INT4 rows (the layout,
+        // header fields and epochs of pi_ffn_sparse's single-token path)
+        const LayoutKey key{PI_OP_SPARSE, 1, d, 0, ffn};
+        const pi::FusedSparseLayout LF = pi::fused_sparse_layout(d, ffn);
+        hipError_t e = hipSuccess;
+        if (ws_needs_clear(ws, key)) e = pi::launch_zero(data + LF.atag, LF.partial - LF.atag, st);
+        if (e == hipSuccess)
+            e = pi::launch_sparse_fused_q4(kind, reinterpret_cast<const pi::h16*>(x), d, ffn, q_up,
+                                           reinterpret_cast<const pi::h16*>(s_up), b_up, q_gate,
+                                           reinterpret_cast<const pi::h16*>(s_gate), b_gate, q_down,
+                                           reinterpret_cast<const pi::h16*>(s_down), idx, count, y, LF, hdr, data, st);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse_q4");
+        ws_record(ws, key);
+        return ok();
+    }
     ws_forget(ws);
-    char* data = static_cast<char*>(ws) + pi::kSyncBytes;
     const pi::SparseLayout L = pi::sparse_layout(B, d, ffn);
     hipError_t e = pi::launch_ffn_q4(kind, (flags & PI_DENSE) != 0u, reinterpret_cast<const pi::h16*>(x), B, d, ffn,
                                      q_up, reinterpret_cast<const pi::h16*>(s_up), b_up, q_gate,
                                      reinterpret_cast<const pi::h16*>(s_gate), b_gate, q_down,
-                                     reinterpret_cast<const pi::h16*>(s_down), idx, count, y, L, data,
-                                     static_cast<hipStream_t>(stream));
+                                     reinterpret_cast<const pi::h16*>(s_down), idx, count, y, L, data, st);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_sparse_q4");
     return ok();
 }

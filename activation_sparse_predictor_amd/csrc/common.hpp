@@ -62,6 +62,35 @@ __device__ __forceinline__ float ffn_act(float u, float g) {
     return g / (1.f + expf(-g)) * u;
 }
 
+// sum_j (code_j - 8) * x_j over the 8 weights of one 32-bit code word and 8
+// fp16 x.  The codes become fp16 pairs without conversions: a byte permute
+// puts codes 2j and 2j + 1 in the low bytes of the two halves, or-ing in
+// 0x6400 makes them 1024 + code (exact in fp16), and one packed subtraction
+// of 1032 leaves code - 8; the pairs go through the fp16 dot product with
+// fp32 accumulation (products of fp16 values are exact in fp32).
+__device__ __forceinline__ float dot8_q4(uint32_t codes, u32x4 x, float acc) {
+    const uint32_t lo = codes & 0x0F0F0F0Fu;          // codes of weights 0, 2, 4, 6 (byte j: weight 2j)
+    const uint32_t hi = (codes >> 4) & 0x0F0F0F0Fu;   // codes of weights 1, 3, 5, 7
+    const f16x2 off = {(f16)1032.0f, (f16)1032.0f};
+    const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // result bytes: lo byte j, 0, hi byte j, 0 (perm: bytes 0-3 of the second
+        // operand are 0-3, of the first 4-7; 0x0C selects a zero byte)
+        const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
+        const uint32_t p = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+        acc = __builtin_amdgcn_fdot2(as_h2(p) - off, as_h2(xs[j]), acc, false);
+    }
+    return acc;
+}
+
+// acc[e] += f * (code_e - 8) for the 8 4-bit codes of one word (INT4 rows;
+// f is the activation times the group's scale).
+__device__ __forceinline__ void axpy8_q4(float* acc, float f, uint32_t codes) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(f, (float)((int)((codes >> (4 * e)) & 0xFu) - 8), acc[e]);
+}
+
 // acc[k] += s * w[k] for 8 fp16 weights.
 __device__ __forceinline__ void axpy8(float* acc, float s, u32x4 w) {
     f16x2 a = as_h2(w.x), b = as_h2(w.y), c = as_h2(w.z), d = as_h2(w.w);

@@ -339,7 +339,12 @@ constexpr int kSWindow = 2048;                       // list entries staged in L
 static_assert(kSColThreads * kSGroups == kSThreads, "tile shape");
 static_assert(kFusedCols <= kSThreads, "one reduction column per thread");
 
-template <int KIND>
+// Q4: the rows are INT4 (pi_quantize_rows: 4-bit codes, d / 2 bytes a row, and
+// one fp16 scale per 64 weights in su / sg / sd); the weight pointers then
+// point at the codes.  The up role takes 16-byte code chunks (32 weights)
+// with their scale, the W_down role one 32-bit code word (8 columns) and one
+// scale per row.
+template <int KIND, bool Q4 = false>
 __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restrict__ x, int d, int ffn,
                                                             const h16* __restrict__ Wup,
                                                             const float* __restrict__ bup,
@@ -352,7 +357,10 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
                                                             float* __restrict__ partial,
                                                             uint32_t* __restrict__ ctr, uint32_t* __restrict__ slots,
                                                             float* __restrict__ y,
-                                                            const float* __restrict__ zero) {
+                                                            const float* __restrict__ zero,
+                                                            const h16* __restrict__ su = nullptr,
+                                                            const h16* __restrict__ sg = nullptr,
+                                                            const h16* __restrict__ sd = nullptr) {
     // up role: x (d fp16); W_down role: row-group partials, window ids and activations
     __shared__ __align__(16) char s_mem[kSGroups * kFusedCols * 4 + kSWindow * 8];
     static_assert(sizeof(s_mem) >= PI_MAX_D * 2, "x does not fit the up role's LDS");
@@ -372,20 +380,40 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         const int u = blockIdx.x;
         const int j0 = min(cnt, u * PU), j1 = min(cnt, j0 + PU);
         if (j0 >= j1) return;
-        constexpr int UU = REGLU ? 8 : 16;
-        const int nch = d >> 3;
+        constexpr int UU = Q4 ? (REGLU ? 2 : 4) : (REGLU ? 8 : 16);   // 16-byte chunks per lane per batch
+        const int nch = d >> 3;                     // 8-weight x chunks
+        const int ncw = Q4 ? d >> 5 : nch;          // 16-byte weight chunks of a row
+        const int ng = d >> 6;                      // INT4 scale groups of a row
         int j = j0 + wave;
         int i = 0;
         u32x4 wu[UU], wg[UU];
+        float cu[UU], cg[UU];   // INT4: the chunks' scales
         auto issue = [&](int c0) {
-            const h16* ru = Wup + (size_t)i * d;
-            const h16* rg = REGLU ? Wg + (size_t)i * d : nullptr;
+            if constexpr (Q4) {
+                const uint8_t* ru = reinterpret_cast<const uint8_t*>(Wup) + (size_t)i * (d / 2);
+                const uint8_t* rg = REGLU ? reinterpret_cast<const uint8_t*>(Wg) + (size_t)i * (d / 2) : nullptr;
 #pragma unroll
-            for (int q = 0; q < UU; ++q) {
-                const int c = c0 + q * 64;
-                if (c < nch) {
-                    wu[q] = ld16_stream(ru + (size_t)c * 8);
-                    if (REGLU) wg[q] = ld16_stream(rg + (size_t)c * 8);
+                for (int q = 0; q < UU; ++q) {
+                    const int c = c0 + q * 64;
+                    if (c < ncw) {
+                        wu[q] = ld16_stream(ru + (size_t)c * 16);
+                        cu[q] = (float)su[(size_t)i * ng + (c >> 1)];
+                        if (REGLU) {
+                            wg[q] = ld16_stream(rg + (size_t)c * 16);
+                            cg[q] = (float)sg[(size_t)i * ng + (c >> 1)];
+                        }
+                    }
+                }
+            } else {
+                const h16* ru = Wup + (size_t)i * d;
+                const h16* rg = REGLU ? Wg + (size_t)i * d : nullptr;
+#pragma unroll
+                for (int q = 0; q < UU; ++q) {
+                    const int c = c0 + q * 64;
+                    if (c < ncw) {
+                        wu[q] = ld16_stream(ru + (size_t)c * 8);
+                        if (REGLU) wg[q] = ld16_stream(rg + (size_t)c * 8);
+                    }
                 }
             }
         };
@@ -417,15 +445,29 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
             }
             first = false;
             float au = 0.f, ag = 0.f;
-            for (int c0 = lane; c0 < nch; c0 += 64 * UU) {
+            for (int c0 = lane; c0 < ncw; c0 += 64 * UU) {
                 if (c0 != lane) issue(c0);
 #pragma unroll
                 for (int q = 0; q < UU; ++q) {
                     const int c = c0 + q * 64;
-                    if (c < nch) {
-                        const u32x4 xv = s_x[c];
-                        au = dot8_h(wu[q], xv, au);
-                        if (REGLU) ag = dot8_h(wg[q], xv, ag);
+                    if (c < ncw) {
+                        if constexpr (Q4) {
+                            const uint32_t cw[4] = {wu[q].x, wu[q].y, wu[q].z, wu[q].w};
+                            const uint32_t gw[4] = {wg[q].x, wg[q].y, wg[q].z, wg[q].w};
+                            float pu = 0.f, pg = 0.f;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const u32x4 xv = s_x[c * 4 + e];
+                                pu = dot8_q4(cw[e], xv, pu);
+                                if (REGLU) pg = dot8_q4(gw[e], xv, pg);
+                            }
+                            au = fmaf(cu[q], pu, au);
+                            if (REGLU) ag = fmaf(cg[q], pg, ag);
+                        } else {
+                            const u32x4 xv = s_x[c];
+                            au = dot8_h(wu[q], xv, au);
+                            if (REGLU) ag = dot8_h(wg[q], xv, ag);
+                        }
                     }
                 }
             }
@@ -478,9 +520,19 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         // turns out to be 0 is still read: skipping it would have to wait for
         // the activation first, which costs more than the bytes it saves.
         u32x4 w[kSBatch];
+        uint32_t wq[kSBatch];   // INT4: the row's code word and scale for the thread's 8 columns
+        float wsc[kSBatch];
+        auto load_row = [&](int q, int r) {
+            if constexpr (Q4) {
+                wq[q] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+                    reinterpret_cast<const uint8_t*>(Wd) + (size_t)r * (d / 2) + colc / 2));
+                wsc[q] = (float)sd[(size_t)r * (d >> 6) + (colc >> 6)];
+            } else {
+                w[q] = ld16_stream(Wd + (size_t)r * d + colc);
+            }
+        };
 #pragma unroll
-        for (int q = 0; q < kSBatch; ++q)
-            w[q] = ld16_stream(Wd + (size_t)s_row[min(rg + kSGroups * q, wn - 1)] * d + colc);
+        for (int q = 0; q < kSBatch; ++q) load_row(q, s_row[min(rg + kSGroups * q, wn - 1)]);
         {
             uint64_t v[kSWindow / kSThreads];
 #pragma unroll
@@ -500,12 +552,14 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
             for (int k0 = 0; k0 < nk; k0 += kSBatch) {
                 if (k0 > 0) {
 #pragma unroll
-                    for (int q = 0; q < kSBatch; ++q)
-                        w[q] = ld16_stream(Wd + (size_t)s_row[min(rg + kSGroups * (k0 + q), wn - 1)] * d + colc);
+                    for (int q = 0; q < kSBatch; ++q) load_row(q, s_row[min(rg + kSGroups * (k0 + q), wn - 1)]);
                 }
 #pragma unroll
                 for (int q = 0; q < kSBatch; ++q)
-                    if (k0 + q < nk) axpy8(acc, s_a[rg + kSGroups * (k0 + q)], w[q]);
+                    if (k0 + q < nk) {
+                        if constexpr (Q4) axpy8_q4(acc, s_a[rg + kSGroups * (k0 + q)] * wsc[q], wq[q]);
+                        else axpy8(acc, s_a[rg + kSGroups * (k0 + q)], w[q]);
+                    }
             }
         }
         __syncthreads();
@@ -546,6 +600,29 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     y[gc] = sum;
     // every chunk of this tile has read the epoch: the tile's slot advances
     if (tid == 0) st_flag(&slots[tile], epoch);
+}
+
+hipError_t launch_sparse_fused_q4(int kind, const h16* x, int d, int ffn, const uint8_t* qu, const h16* su,
+                                  const float* bup, const uint8_t* qg, const h16* sg, const float* bg,
+                                  const uint8_t* qd, const h16* sd, const int32_t* idx, const int32_t* count,
+                                  float* y, const FusedSparseLayout& L, char* hdr, char* data, hipStream_t s) {
+    uint64_t* atag = reinterpret_cast<uint64_t*>(data + L.atag);
+    float* partial = reinterpret_cast<float*>(data + L.partial);
+    uint32_t* ctr = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_ctr);
+    uint32_t* slots = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_epoch);
+    const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
+    const h16* wu = reinterpret_cast<const h16*>(qu);
+    const h16* wg = reinterpret_cast<const h16*>(qg);
+    const h16* wd = reinterpret_cast<const h16*>(qd);
+    dim3 grid(L.NU + L.T * L.G);
+#define PI_SFQ(K)                                                                                                    \
+    hipLaunchKernelGGL((k_sparse_fused<K, true>), grid, dim3(kSThreads), 0, s, x, d, ffn, wu, bup, wg, bg, wd, idx, \
+                       count, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero, su, sg, sd)
+    if (kind == 2) PI_SFQ(2);
+    else if (kind == 1) PI_SFQ(1);
+    else PI_SFQ(0);
+#undef PI_SFQ
+    return hipGetLastError();
 }
 
 hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,

@@ -231,6 +231,10 @@ hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
                                char* data, hipStream_t s);
+hipError_t launch_sparse_fused_q4(int kind, const h16* x, int d, int ffn, const uint8_t* qu, const h16* su,
+                                  const float* bup, const uint8_t* qg, const h16* sg, const float* bg,
+                                  const uint8_t* qd, const h16* sd, const int32_t* idx, const int32_t* count,
+                                  float* y, const FusedSparseLayout& L, char* hdr, char* data, hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
 // q4.hip

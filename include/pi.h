@@ -269,8 +269,10 @@ pi_status pi_quantize_rows(const pi_half* W, int rows, int d, uint8_t* q, pi_hal
  * fp32.  An active neuron's three rows take 3 * (d / 2 + d / 32) bytes
  * instead of 3 * 2d.  Flags: PI_DENSE (every neuron), PI_DETERMINISTIC
  * (accepted; the path is deterministic).  The workspace is
- * pi_workspace_size(PI_OP_SPARSE, B, d, r, ffn).  Two kernels per call; B
- * tokens share each launch (one grid row per token).
+ * pi_workspace_size(PI_OP_SPARSE, B, d, r, ffn), laid out as pi_ffn_sparse's.
+ * One token with a list: one kernel, the single-token design of
+ * pi_ffn_sparse over INT4 rows.  Otherwise two kernels, B tokens sharing
+ * each launch (one grid row per token).
  * Errors: as pi_ffn_sparse; UNSUPPORTED for d not a multiple of 64; INVALID_ARG
  * for a NULL scale array of a matrix that is used, or another flag.
  */
