@@ -285,6 +285,95 @@ def q4_line(cfg_key, nl, ntok, reps, log_fn):
     return out
 
 
+def stack_run(cfg_key, log_fn):
+    """The whole stack of the workload (64 OPT-66B-shaped layers, ~93 GB
+    resident): every layer profiled on its calibration tokens and reordered
+    hot-first, then the prompt (one batch of prompt tokens per layer, the
+    union path) and the decode steps at batch 1 (predict + sparse per layer,
+    graph-replayed one step at a time).  Inputs are independent per layer:
+    x ~ N(0, I) for every (layer, token)."""
+    import numpy as np
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import CONFIGS, make_calibration, make_layer, make_tokens
+    cfg = CONFIGS[cfg_key]
+    kind, d, r, ffn, NLs = cfg.kind, cfg.d, cfg.r, cfg.ffn, cfg.layers
+    P, S = cfg.prompt_tokens, cfg.decode_steps
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    layers, hot_counts = [], []
+    for l in range(NLs):
+        L = make_layer(cfg, layer=l, device=dev)
+        Wf, bf = (L["W_up"], L["b_up"]) if kind == "relu" else (L["W_gate"], L["b_gate"])
+        counts = R.profile(make_calibration(cfg, device=dev, layer=l), Wf, bf).cpu().numpy()
+        perm, hot = R.reorder(counts, 0.8)
+        layers.append(R.permute_layer(L, torch.from_numpy(perm).to(dev)))
+        hot_counts.append(hot)
+        del L
+        if l % 16 == 15:
+            torch.cuda.synchronize()
+            log_fn(f"stack: {l + 1} layers built, profiled and reordered ({time.perf_counter() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # prompt: P tokens per layer at once
+    Xp = [make_tokens(cfg, P, device=dev, layer=l, stream="prompt") for l in range(NLs)]
+    idxp = torch.empty(P, ffn, dtype=torch.int32, device=dev)
+    cntp = torch.empty(P, dtype=torch.int32, device=dev)
+    yp = torch.empty(P, d, dtype=torch.float32, device=dev)
+    for l in range(2):
+        R.predict(layers[l], Xp[l], idxp, cntp)
+        R.sparse(layers[l], Xp[l], idxp, cntp, yp)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for l in range(NLs):
+        R.predict(layers[l], Xp[l], idxp, cntp)
+        R.sparse(layers[l], Xp[l], idxp, cntp, yp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prompt_ms = e0.elapsed_time(e1)
+    del Xp
+    # decode: S steps, each through every layer, batch 1
+    Xd = [make_tokens(cfg, S, device=dev, layer=l) for l in range(NLs)]
+    idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int32, device=dev)
+    y = torch.empty(1, d, dtype=torch.float32, device=dev)
+    xs = [[Xd[l][t:t + 1].contiguous() for t in range(S)] for l in range(NLs)]
+    for l in range(NLs):
+        R.predict(layers[l], xs[l][0], idx, cnt)
+        R.sparse(layers[l], xs[l][0], idx, cnt, y)
+    torch.cuda.synchronize()
+    counts = []
+    e0.record(stream)
+    for t in range(S):
+        for l in range(NLs):
+            R.predict(layers[l], xs[l][t], idx, cnt)
+            R.sparse(layers[l], xs[l][t], idx, cnt, y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    decode_ms = e0.elapsed_time(e1)
+    for l in range(0, NLs, 8):
+        R.predict(layers[l], xs[l][0], idx, cnt)
+        counts.append(int(cnt.item()))
+    m = 1 if kind == "relu" else 2
+    out = {"workload": cfg.workload, "layers": NLs,
+           "resident_GB": NLs * ((m + 1) * ffn * d * 2 + r * d * 2 + ffn * r * 2) / 1e9,
+           "setup_s": setup_s, "hot_count_mean": float(np.mean(hot_counts)),
+           "prompt": {"tokens": P, "ms": prompt_ms, "tokens_per_s": P * 1000.0 / prompt_ms,
+                      "us_per_layer": prompt_ms * 1000.0 / NLs},
+           "decode": {"steps": S, "ms": decode_ms, "tokens_per_s": S * 1000.0 / decode_ms,
+                      "us_per_layer_step": decode_ms * 1000.0 / (S * NLs),
+                      "sampled_active_mean": float(np.mean(counts)),
+                      "method": "eager calls, HIP events around all steps"}}
+    log_fn(f"stack: prompt {P} tokens x {NLs} layers {prompt_ms:.1f} ms ({P * 1000.0 / prompt_ms:.0f} tok/s); "
+           f"decode {S} steps x {NLs} layers {decode_ms:.1f} ms ({S * 1000.0 / decode_ms:.1f} tok/s, "
+           f"{decode_ms * 1000.0 / (S * NLs):.1f} us per layer step)")
+    del layers, xs, Xd
+    torch.cuda.empty_cache()
+    return out
+
+
 def batch_sweep(cfg_key, batches, steps, nl, log_fn):
     """Decode steps of B tokens on the union path, cache-cold over nl layers."""
     import torch
@@ -375,6 +464,8 @@ def main():
     ap.add_argument("--hot", default="c2",
                     help="config of the hot-prefix line: hot-first layers, predictor trimmed ('' to skip)")
     ap.add_argument("--q4", default="c2", help="config of the INT4-rows line ('' to skip)")
+    ap.add_argument("--stack", default="", help="also run a whole layer stack (c5: 64 layers, ~93 GB), "
+                                                "prompt then decode; off by default")
     ap.add_argument("--prompt", default="c5",
                     help="config of the prompt-phase line: one 128-token batch per layer ('' to skip)")
     ap.add_argument("--sweep-only", action="store_true",
@@ -647,9 +738,16 @@ def main():
         torch.cuda.empty_cache()
         hot = hot_prefix_line(args.hot, 8, 8, 16, log)
 
+    stack = None
+    if args.stack:
+        if not args.sweep and not args.hot:
+            del layers, tokens, xs
+        torch.cuda.empty_cache()
+        stack = stack_run(args.stack, log)
+
     q4 = None
     if args.q4:
-        if not args.sweep and not args.hot:
+        if not args.sweep and not args.hot and not args.stack:
             del layers, tokens, xs
         torch.cuda.empty_cache()
         q4 = q4_line(args.q4, 8, 8, 16, log)
@@ -706,6 +804,7 @@ def main():
         "batch_sweep": sweep,
         "hot_prefix": hot,
         "int4_rows": q4,
+        "stack": stack,
         "prompt_phase": prompt,
     }
     print(json.dumps(out), flush=True)

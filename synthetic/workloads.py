@@ -57,6 +57,7 @@ TENSOR_IDS = {
     "rank_perm": 6,
     "calib": 7,
     "decode": 8,
+    "prompt": 9,
 }
 
 # hidden-unit moments of ReLU(N(0,1)): mean 1/sqrt(2*pi), variance 1/2 - 1/(2*pi)
