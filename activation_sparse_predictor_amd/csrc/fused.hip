@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        int hot) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
-    __shared__ uint32_t s_part[16];
+    __shared__ uint32_t s_part[8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int NA = (r + 3) / 4;
@@ -163,48 +163,55 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
 
     if ((int)blockIdx.x == NA + NT) {
         // ---------------- ordered compaction, 1024 tiles per round: thread k
-        // takes tiles k, k + 256, k + 512 and k + 768 of the round, so the dense
-        // tiles at the front of a hot-first layer spread over many threads
-        // (each writes its tiles' ids one by one, and a wave runs as long as
-        // its busiest lane); one block-wide scan per quarter gives the offsets.
+        // takes tiles 2k and 2k + 1 of each half of the round, one block-wide
+        // scan per half.  The dense front of a hot-first layer then spreads
+        // over many threads (each writes its tiles' ids one by one, and a wave
+        // runs as long as its busiest lane), while two write loops keep the
+        // cost on an unordered layer low.
         const uint32_t epoch = next_epoch(*epoch_word);
         uint32_t base = 0;
         bool good = true;
         for (int t0 = 0; t0 < NT; t0 += 1024) {
             uint64_t m4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + q * 256 + tid, NT - 1)]);
-            uint32_t bits[4], cnt4[4], incl4[4];
+            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + (q >> 1) * 512 + tid * 2 + (q & 1), NT - 1)]);
+            uint32_t bits[4], cnt2[2], incl2[2];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int t = t0 + q * 256 + tid;
+                const int t = t0 + (q >> 1) * 512 + tid * 2 + (q & 1);
                 bits[q] = 0u;
                 if (t < NT) {
                     if (poll_tag(&mtag[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
                     else good = false;
                 }
-                cnt4[q] = (uint32_t)__popc(bits[q]);
-                uint32_t incl = cnt4[q];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                cnt2[h] = (uint32_t)(__popc(bits[2 * h]) + __popc(bits[2 * h + 1]));
+                uint32_t incl = cnt2[h];
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
                     const uint32_t v = __shfl_up(incl, off, 64);
                     if (lane >= off) incl += v;
                 }
-                incl4[q] = incl;
-                if (lane == 63) s_part[q * 4 + wave] = incl;
+                incl2[h] = incl;
+                if (lane == 63) s_part[h * 4 + wave] = incl;
             }
             __syncthreads();
             uint32_t run = base;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t pos = run + incl4[q] - cnt4[q];
-                for (int w2 = 0; w2 < wave; ++w2) pos += s_part[q * 4 + w2];
-                run += s_part[q * 4] + s_part[q * 4 + 1] + s_part[q * 4 + 2] + s_part[q * 4 + 3];
-                uint32_t m = bits[q];
-                const int t = t0 + q * 256 + tid;
-                while (m) {
-                    idx[pos++] = t * kLTile + __builtin_ctz(m);
-                    m &= m - 1;
+            for (int h = 0; h < 2; ++h) {
+                uint32_t pos = run + incl2[h] - cnt2[h];
+                for (int w2 = 0; w2 < wave; ++w2) pos += s_part[h * 4 + w2];
+                run += s_part[h * 4] + s_part[h * 4 + 1] + s_part[h * 4 + 2] + s_part[h * 4 + 3];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    uint32_t m = bits[2 * h + e];
+                    const int t = t0 + h * 512 + tid * 2 + e;
+                    while (m) {
+                        idx[pos++] = t * kLTile + __builtin_ctz(m);
+                        m &= m - 1;
+                    }
                 }
             }
             base = run;
