@@ -88,3 +88,28 @@ def test_full_size_q4():
     c = int(cnt[0].cpu())
     gi = idx[0, :c].cpu().numpy()
     check_y(Y[0].cpu().numpy(), _oracle_q4_y(H, X[0].cpu(), gi), where="c2 q4")
+
+
+def test_q4_single_token_edges():
+    """The fused single-token INT4 kernel: an empty list gives exactly 0, a
+    one-neuron list and a ragged width (d = 576: a partial 512-column tile)
+    match the oracle."""
+    cfg = custom_config("reglu", 576, 1000, 64, mean=0.2, number=101)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 2).to(DEV)
+    x = X[:1].contiguous()
+    idx = torch.zeros(1, cfg.ffn, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y0 = R.sparse_q4(Q, x, idx, cnt)
+    idx[0, 0] = cfg.ffn - 1
+    cnt.fill_(1)
+    y1 = R.sparse_q4(Q, x, idx, cnt)
+    i2, c2 = R.predict(L, X[1:2].contiguous())
+    y2 = R.sparse_q4(Q, X[1:2].contiguous(), i2, c2)
+    torch.cuda.synchronize()
+    assert not torch.any(y0)
+    check_y(y1[0].cpu().numpy(), _oracle_q4_y(H, X[0].cpu(), [cfg.ffn - 1]), where="q4 one neuron")
+    gi = i2[0, :int(c2[0].cpu())].cpu().numpy()
+    check_y(y2[0].cpu().numpy(), _oracle_q4_y(H, X[1].cpu(), gi), where="q4 d=576")
