@@ -334,13 +334,14 @@ __global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* _
 }
 
 // One workgroup per token: the token's 32-bit tile masks in neuron order ->
-// popcount prefix -> ascending idx and count.  Thread k takes words k,
-// k + 256, ... of a round (one block-wide scan per 256 words), so the dense
-// words of a hot-first layer spread over many threads.  The first hotw words
+// popcount prefix -> ascending idx and count.  Thread k takes words 2k and
+// 2k + 1 of each quarter of a 2048-word round (one block-wide scan per
+// quarter), so the dense words of a hot-first layer spread over many threads
+// while each thread writes in four loops.  The first hotw words
 // (the always-listed hot prefix) count as all ones and are not read.
 __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restrict__ masks32, int ffn, int hotw,
                                                        int32_t* __restrict__ idx, int32_t* __restrict__ count) {
-    __shared__ uint32_t s_part[32];
+    __shared__ uint32_t s_part[16];
     const int tok = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ntiles = (ffn + 31) / 32;
@@ -348,36 +349,39 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
     int32_t* out = idx + (size_t)tok * ffn;
     uint32_t base = 0;
     for (int t0 = 0; t0 < ntiles; t0 += 2048) {
-        uint32_t m8[8], c8[8], i8[8];
+        uint32_t m8[8], c4[4], i4[4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int t = t0 + q * 256 + tid;
+        for (int q = 0; q < 8; ++q) {   // words 2k, 2k + 1 of quarter q / 2
+            const int t = t0 + (q >> 1) * 512 + tid * 2 + (q & 1);
             m8[q] = t < hotw ? 0xFFFFFFFFu : (t < ntiles ? mk[t] : 0u);
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            c8[q] = (uint32_t)__popc(m8[q]);
-            uint32_t incl = c8[q];
+        for (int h = 0; h < 4; ++h) {
+            c4[h] = (uint32_t)(__popc(m8[2 * h]) + __popc(m8[2 * h + 1]));
+            uint32_t incl = c4[h];
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const uint32_t v = __shfl_up(incl, off, 64);
                 if (lane >= off) incl += v;
             }
-            i8[q] = incl;
-            if (lane == 63) s_part[q * 4 + wave] = incl;
+            i4[h] = incl;
+            if (lane == 63) s_part[h * 4 + wave] = incl;
         }
         __syncthreads();
         uint32_t run = base;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            uint32_t pos = run + i8[q] - c8[q];
-            for (int w2 = 0; w2 < wave; ++w2) pos += s_part[q * 4 + w2];
-            run += s_part[q * 4] + s_part[q * 4 + 1] + s_part[q * 4 + 2] + s_part[q * 4 + 3];
-            uint32_t m = m8[q];
-            const int t = t0 + q * 256 + tid;
-            while (m) {
-                out[pos++] = t * 32 + __builtin_ctz(m);
-                m &= m - 1;
+        for (int h = 0; h < 4; ++h) {
+            uint32_t pos = run + i4[h] - c4[h];
+            for (int w2 = 0; w2 < wave; ++w2) pos += s_part[h * 4 + w2];
+            run += s_part[h * 4] + s_part[h * 4 + 1] + s_part[h * 4 + 2] + s_part[h * 4 + 3];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                uint32_t m = m8[2 * h + e];
+                const int t = t0 + h * 512 + tid * 2 + e;
+                while (m) {
+                    out[pos++] = t * 32 + __builtin_ctz(m);
+                    m &= m - 1;
+                }
             }
         }
         base = run;
