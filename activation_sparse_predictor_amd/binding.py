@@ -49,6 +49,8 @@ _SIGNATURES = {
     "pi_ffn_sparse": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "pi_ffn_decode": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                            _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "pi_ffn_predict_q4": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
+                               _SZ, _P]),
     "pi_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P]),
     "pi_ffn_sparse_q4": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32,
                               _P, _SZ, _P]),
@@ -133,6 +135,13 @@ def pi_ffn_predict_hot(x, B, d, P1, b1, act, P2, b2, r, ffn, n_hot, tau, idx, co
     return load().pi_ffn_predict_hot(_ptr(x), B, d, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r,
                                      ffn, n_hot, tau, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
                                      _stream(stream))
+
+
+def pi_ffn_predict_q4(x, B, d, q_P1, s_P1, b1, act, q_P2, s_P2, b2, r, ffn, n_hot, tau, idx, count, ws,
+                      ws_bytes, stream=None) -> int:
+    return load().pi_ffn_predict_q4(_ptr(x), B, d, _ptr(q_P1), _ptr(s_P1), _ptr(b1), act, _ptr(q_P2), _ptr(s_P2),
+                                    _ptr(b2), r, ffn, n_hot, tau, _ptr(idx), _ptr(count), _ptr(ws), ws_bytes,
+                                    _stream(stream))
 
 
 def pi_quantize_rows(W, rows, d, q, scales, stream=None) -> int:

@@ -76,8 +76,10 @@ pi_status check_ws(void* ws, size_t ws_bytes, size_t need, const char* op) {
 // Every workspace starts with the fused kernels' synchronisation header; a
 // call's data area follows it.
 size_t predict_data_bytes(int B, int r, int ffn) {
-    if (B == 1) return pi::fused_pred_layout(r, ffn).total;
-    return pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
+    const size_t f = pi::fused_pred_layout(r, ffn).total;   // single token (and INT4 rows at any B)
+    if (B == 1) return f;
+    const size_t b = pi::bpred_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, r, ffn).total;
+    return b > f ? b : f;
 }
 size_t predict_ws_bytes(int B, int r, int ffn) { return pi::kSyncBytes + predict_data_bytes(B, r, ffn); }
 
@@ -187,11 +189,13 @@ pi_status check_sparse_args(int kind, const pi_half* x, int B, int d, int ffn, c
 // The calls proper, on a checked workspace: hdr is its synchronisation header,
 // data the call's data area; clear: zero the tagged words first (single-token
 // paths only).
+// sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
+float logit_threshold(float tau) { return (float)std::log((double)tau / (1.0 - (double)tau)); }
+
 pi_status run_predict(const pi_half* x, int B, int d, const pi_half* P1, const float* b1, int act,
                       const pi_half* P2, const float* b2, int r, int ffn, int hot, float tau, int32_t* idx,
                       int32_t* count, char* hdr, char* data, bool clear, hipStream_t s) {
-    // sigmoid(z) > tau  <=>  z > ln(tau / (1 - tau)), evaluated once in double.
-    const float thr = (float)std::log((double)tau / (1.0 - (double)tau));
+    const float thr = logit_threshold(tau);
     const auto* hx = reinterpret_cast<const pi::h16*>(x);
     const auto* h1 = reinterpret_cast<const pi::h16*>(P1);
     const auto* h2 = reinterpret_cast<const pi::h16*>(P2);
@@ -333,6 +337,40 @@ pi_status pi_ffn_predict_hot(const pi_half* x, int B, int d, const pi_half* P1, 
                        static_cast<hipStream_t>(stream)));
     if (fused) ws_record(ws, key);
     return PI_OK;
+}
+
+pi_status pi_ffn_predict_q4(const pi_half* x, int B, int d, const uint8_t* q_P1, const pi_half* s_P1,
+                            const float* b1, int act, const uint8_t* q_P2, const pi_half* s_P2, const float* b2,
+                            int r, int ffn, int n_hot, float tau, int32_t* idx, int32_t* count, void* ws,
+                            size_t ws_bytes, void* stream) {
+    // the fp16 argument checks, with the code arrays standing in for the weight pointers
+    PI_TRY(check_predict_args(x, B, d, reinterpret_cast<const pi_half*>(q_P1), b1, act,
+                              reinterpret_cast<const pi_half*>(q_P2), b2, r, ffn, tau, idx, count));
+    PI_REQUIRE(d % 64 == 0, PI_ERR_UNSUPPORTED, "d=%d is not a multiple of 64 (the INT4 group)", d);
+    PI_REQUIRE(r % 64 == 0, PI_ERR_UNSUPPORTED, "r=%d is not a multiple of 64 (the INT4 group)", r);
+    PI_REQUIRE(s_P1 != nullptr && s_P2 != nullptr, PI_ERR_INVALID_ARG, "a scale array is NULL");
+    PI_REQUIRE(aligned(s_P1, 2) && aligned(s_P2, 2), PI_ERR_UNSUPPORTED, "a scale array is not 2-byte aligned");
+    PI_REQUIRE(n_hot >= 0 && n_hot <= ffn, PI_ERR_INVALID_ARG, "n_hot=%d outside [0, ffn=%d]", n_hot, ffn);
+    PI_REQUIRE(n_hot % 32 == 0, PI_ERR_UNSUPPORTED, "n_hot=%d is not a multiple of 32", n_hot);
+    PI_TRY(check_ws(ws, ws_bytes, predict_ws_bytes(B, r, ffn), "pi_ffn_predict_q4"));
+    char* hdr = static_cast<char*>(ws);
+    char* data = hdr + pi::kSyncBytes;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // one single-token kernel per token, on the layout, header fields and
+    // epochs of pi_ffn_predict's single-token path
+    const LayoutKey key{PI_OP_PREDICT, 1, 0, r, ffn};
+    const pi::FusedPredLayout L = pi::fused_pred_layout(r, ffn);
+    const float thr = logit_threshold(tau);
+    hipError_t e = hipSuccess;
+    if (ws_needs_clear(ws, key)) e = pi::launch_zero(data, L.total, st);
+    for (int t = 0; t < B && e == hipSuccess; ++t)
+        e = pi::launch_predict_fused_q4(reinterpret_cast<const pi::h16*>(x) + (size_t)t * d, d, q_P1,
+                                        reinterpret_cast<const pi::h16*>(s_P1), b1, act == PI_ACT_RELU, r, q_P2,
+                                        reinterpret_cast<const pi::h16*>(s_P2), b2, ffn, n_hot, thr, L, hdr, data,
+                                        idx + (size_t)t * ffn, count + t, st);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_predict_q4");
+    ws_record(ws, key);
+    return ok();
 }
 
 pi_status pi_ffn_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* W_up,

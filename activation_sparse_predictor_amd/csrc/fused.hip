@@ -104,6 +104,11 @@ static_assert(kLRows * 4 == kLTile, "4 waves per logits tile");
 // 1024 x 28672 predictor, the last 129 logits tiles start as hidden rows
 // retire.  Asking for 5 per CU (102 VGPRs) spills in the logits loop and
 // makes the kernel half again as slow.
+//
+// Q4: P1 and P2 are INT4 rows (P1, P2 then point at the code bytes, two
+// codes a byte, and s1, s2 at the fp16 scales of 64-weight groups); h and z
+// are still accumulated in fp32.
+template <bool Q4>
 __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x, int d,
                                                        const h16* __restrict__ P1,
                                                        const float* __restrict__ b1, int relu, int r,
@@ -112,7 +117,8 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
                                                        uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ count, const float* __restrict__ zero,
-                                                       int hot) {
+                                                       int hot, const h16* __restrict__ s1,
+                                                       const h16* __restrict__ s2) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
     __shared__ uint32_t s_part[8];
@@ -130,6 +136,54 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         u32x4 xs[4];   // x chunks tid + 256 q, requested ahead of the P1 rows
 #pragma unroll
         for (int q = 0; q < 4; ++q) xs[q] = ld16(x + (size_t)min(tid + q * 256, nch - 1) * 8);
+        if constexpr (Q4) {
+            // INT4 row: d / 32 chunks of 16 bytes (32 codes, half a scale group)
+            constexpr int UH = 4;   // chunks per lane per batch
+            const uint8_t* qrow = reinterpret_cast<const uint8_t*>(P1) + (size_t)min(row, r - 1) * (d / 2);
+            const h16* srow = s1 + (size_t)min(row, r - 1) * (d >> 6);
+            const int ncw = d >> 5;
+            // Slots past the row end read its last chunk (valid, unused): no
+            // branch around a load, and each scale stays fp16 until its use, so
+            // no load waits for another.
+            u32x4 w[UH];
+            h16 sc[UH];
+            auto issue = [&](int c0) {
+#pragma unroll
+                for (int u = 0; u < UH; ++u) {
+                    const int c = min(c0 + u * 64, ncw - 1);
+                    w[u] = ld16_stream(qrow + (size_t)c * 16);
+                    sc[u] = srow[c >> 1];
+                }
+            };
+            issue(lane);
+            const uint32_t stored = *epoch_word;
+            const float bias = *(b1 ? b1 + min(row, r - 1) : zero);
+            u32x4* sx = reinterpret_cast<u32x4*>(sh);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (tid + q * 256 < nch) sx[tid + q * 256] = xs[q];
+            for (int i = tid + 1024; i < nch; i += 256) sx[i] = ld16(x + (size_t)i * 8);   // d > 8192
+            __syncthreads();
+            float acc = 0.f;
+            for (int c0 = lane; c0 < ncw; c0 += 64 * UH) {
+                if (c0 != lane) issue(c0);
+#pragma unroll
+                for (int u = 0; u < UH; ++u) {
+                    const int c = c0 + u * 64;
+                    if (c < ncw) {
+                        const uint32_t cw[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                        float p = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) p = dot8_q4(cw[e], sx[c * 4 + e], p);
+                        acc = fmaf((float)sc[u], p, acc);
+                    }
+                }
+            }
+            const float sum = group_sum<64>(acc) + bias;
+            const uint32_t epoch = next_epoch(stored);
+            if (valid && lane == 0) st_tag(&htag[row], epoch, __float_as_uint(relu ? fmaxf(sum, 0.f) : sum));
+            return;
+        }
         u32x4 w[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u)
@@ -280,6 +334,80 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         ok = __syncthreads_and(ok);
         have_h = true;
     };
+    // z of row row0 + k in lane k < 8 (with the bias): the tile's 32-bit mask
+    auto publish = [&](float zk) {
+        if (lane < kLRows) s_act[wave * kLRows + lane] = (row0 + lane < ffn) && (zk + bias > thr);
+        __syncthreads();
+        if (wave == 0) {
+            const uint64_t m = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
+            if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)m);
+        }
+    };
+    if constexpr (Q4) {
+        // INT4 rows of r / 32 chunks (16 bytes, 32 codes).  Half-wave hf takes
+        // rows row0 + hf + 2m (m < 4), lane chunk c = (lane & 31) + 32n: each
+        // h chunk (32 fp32 from LDS) serves four rows.
+        const int hf = lane >> 5;
+        const int ncw = r >> 5, ng = r >> 6;
+        const int NB = (ncw + 31) >> 5;   // column batches (1 for r <= 1024)
+        const uint8_t* qrow[4];
+        const h16* srow[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int rr = min(row0 + hf + 2 * m, ffn - 1);
+            qrow[m] = reinterpret_cast<const uint8_t*>(P2) + (size_t)rr * (r / 2);
+            srow[m] = s2 + (size_t)rr * ng;
+        }
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+        int n = 0;
+        do {
+            // a lane past the row end reads its last chunk (valid, unused)
+            const int c = (lane & 31) + 32 * n;
+            const int cl = min(c, ncw - 1);
+            u32x4 w[4];
+            h16 sc[4];   // converted at use: no load waits for another
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                w[m] = ld16_stream(qrow[m] + (size_t)cl * 16);
+                sc[m] = srow[m][cl >> 1];
+            }
+            if (!have_h) {
+                wait_own_memory();
+                collect_h();
+            }
+            if (c < ncw) {
+                const f32x4* hp = reinterpret_cast<const f32x4*>(sh + c * 32);
+                float hv[32];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const f32x4 v = hp[q];
+                    hv[4 * q] = v.x;
+                    hv[4 * q + 1] = v.y;
+                    hv[4 * q + 2] = v.z;
+                    hv[4 * q + 3] = v.w;
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t cw[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
+                    float p = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int b = 0; b < 8; ++b)   // weight 8e + b: byte b / 2, low nibble for even b
+                            p = fmaf((float)((cw[e] >> (4 * b)) & 0xFu) - 8.f, hv[8 * e + b], p);
+                    a4[m] = fmaf((float)sc[m], p, a4[m]);
+                }
+            }
+        } while (++n < NB);
+        float zk = 0.f;   // lane k < 8: row k is half k & 1's row 2m + (k & 1), m = k / 2
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float z = __shfl(group_sum<32>(a4[m]), (lane & 1) << 5, 64);
+            if (((lane & (kLRows - 1)) >> 1) == m) zk = z;
+        }
+        publish(zk);
+        return;
+    }
     auto accumulate = [&](const u32x4 (&w)[kLRows][kLCols], int m0) {
 #pragma unroll
         for (int m = 0; m < kLCols; ++m) {
@@ -327,12 +455,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         const float z = group_sum<64>(acc[k]);
         if ((lane & (kLRows - 1)) == k) zk = z;
     }
-    if (lane < kLRows) s_act[wave * kLRows + lane] = (row0 + lane < ffn) && (zk + bias > thr);
-    __syncthreads();
-    if (wave == 0) {
-        const uint64_t m = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
-        if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)m);
-    }
+    publish(zk);
 }
 
 // ===========================================================================
@@ -394,21 +517,21 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         int j = j0 + wave;
         int i = 0;
         u32x4 wu[UU], wg[UU];
-        float cu[UU], cg[UU];   // INT4: the chunks' scales
+        h16 cu[UU], cg[UU];   // INT4: the chunks' scales, converted at use
         auto issue = [&](int c0) {
             if constexpr (Q4) {
+                // slots past the row end read its last chunk (valid, unused):
+                // no branch around a load, so no load waits for another
                 const uint8_t* ru = reinterpret_cast<const uint8_t*>(Wup) + (size_t)i * (d / 2);
                 const uint8_t* rg = REGLU ? reinterpret_cast<const uint8_t*>(Wg) + (size_t)i * (d / 2) : nullptr;
 #pragma unroll
                 for (int q = 0; q < UU; ++q) {
-                    const int c = c0 + q * 64;
-                    if (c < ncw) {
-                        wu[q] = ld16_stream(ru + (size_t)c * 16);
-                        cu[q] = (float)su[(size_t)i * ng + (c >> 1)];
-                        if (REGLU) {
-                            wg[q] = ld16_stream(rg + (size_t)c * 16);
-                            cg[q] = (float)sg[(size_t)i * ng + (c >> 1)];
-                        }
+                    const int c = min(c0 + q * 64, ncw - 1);
+                    wu[q] = ld16_stream(ru + (size_t)c * 16);
+                    cu[q] = su[(size_t)i * ng + (c >> 1)];
+                    if (REGLU) {
+                        wg[q] = ld16_stream(rg + (size_t)c * 16);
+                        cg[q] = sg[(size_t)i * ng + (c >> 1)];
                     }
                 }
             } else {
@@ -468,8 +591,8 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
                                 pu = dot8_q4(cw[e], xv, pu);
                                 if (REGLU) pg = dot8_q4(gw[e], xv, pg);
                             }
-                            au = fmaf(cu[q], pu, au);
-                            if (REGLU) ag = fmaf(cg[q], pg, ag);
+                            au = fmaf((float)cu[q], pu, au);
+                            if (REGLU) ag = fmaf((float)cg[q], pg, ag);
                         } else {
                             const u32x4 xv = s_x[c];
                             au = dot8_h(wu[q], xv, au);
@@ -641,8 +764,25 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
     const int NA = (r + 3) / 4;
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
-    hipLaunchKernelGGL(k_predict_fused, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn,
-                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot);
+    hipLaunchKernelGGL(k_predict_fused<false>, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2,
+                       b2, ffn, thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero,
+                       hot, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const h16* s1, const float* b1, bool relu,
+                                   int r, const uint8_t* q2, const h16* s2, const float* b2, int ffn, int hot,
+                                   float thr, const FusedPredLayout& L, char* hdr, char* data, int32_t* idx,
+                                   int32_t* count, hipStream_t s) {
+    uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
+    uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
+    const int NA = (r + 3) / 4;
+    const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
+    const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
+    hipLaunchKernelGGL(k_predict_fused<true>, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d,
+                       reinterpret_cast<const h16*>(q1), b1, (int)relu, r, reinterpret_cast<const h16*>(q2), b2, ffn,
+                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot,
+                       s1, s2);
     return hipGetLastError();
 }
 

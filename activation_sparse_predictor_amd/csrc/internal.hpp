@@ -227,6 +227,10 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
                                 const h16* P2, const float* b2, int ffn, int hot, float thr,
                                 const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
                                 hipStream_t s);
+hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const h16* s1, const float* b1, bool relu,
+                                   int r, const uint8_t* q2, const h16* s2, const float* b2, int ffn, int hot,
+                                   float thr, const FusedPredLayout& L, char* hdr, char* data, int32_t* idx,
+                                   int32_t* count, hipStream_t s);
 hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,

@@ -114,15 +114,37 @@ def quantize_rows(W: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Ten
 
 
 def quantize_layer(layer: dict, stream=None) -> dict:
-    """The layer with its W_up, W_gate and W_down as INT4 rows (q_*, s_*); the
-    predictor and the biases are kept."""
-    out = {k: v for k, v in layer.items() if k not in ("W_up", "W_gate", "W_down")}
-    for k, name in (("W_up", "up"), ("W_gate", "gate"), ("W_down", "down")):
-        if layer.get(k) is not None:
+    """The layer with W_up, W_gate, W_down and the predictor's P1, P2 as INT4
+    rows (q_*, s_*); the biases are kept.  The predictor is quantised only
+    when r is a multiple of 64 (the group); otherwise q_P1 .. s_P2 are None."""
+    out = {k: v for k, v in layer.items() if k not in ("W_up", "W_gate", "W_down", "P1", "P2")}
+    pred_ok = layer.get("P2") is not None and layer["P2"].shape[1] % 64 == 0
+    for k, name in (("W_up", "up"), ("W_gate", "gate"), ("W_down", "down"), ("P1", "P1"), ("P2", "P2")):
+        if layer.get(k) is not None and (pred_ok or k not in ("P1", "P2")):
             out["q_" + name], out["s_" + name] = quantize_rows(layer[k], stream)
         else:
             out["q_" + name], out["s_" + name] = None, None
     return out
+
+
+def predict_q4(layer_q: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
+               count: Optional[torch.Tensor] = None, act: str = "relu", tau: Optional[float] = None,
+               n_hot: int = 0, stream=None):
+    """pi_ffn_predict_q4 over a layer from quantize_layer: idx and count as predict()."""
+    Bt, d = x.shape
+    ffn, r = layer_q["ffn"], layer_q["r"]
+    if idx is None:
+        idx = torch.empty(Bt, ffn, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(Bt, dtype=torch.int32, device=x.device)
+    nbytes = B.pi_workspace_size(B.PI_OP_PREDICT, Bt, d, r, ffn)
+    ws, wsb = workspace("predict_q4", x.device).get(nbytes)
+    t = float(layer_q["tau"] if tau is None else tau)
+    st = B.pi_ffn_predict_q4(_bits(x), Bt, d, layer_q["q_P1"], layer_q["s_P1"], layer_q.get("b1"), B.ACTS[act],
+                             layer_q["q_P2"], layer_q["s_P2"], layer_q.get("b2"), r, ffn, int(n_hot), t, idx,
+                             count, ws, wsb, stream)
+    B.check(st, "pi_ffn_predict_q4")
+    return idx, count
 
 
 def sparse_q4(layer_q: dict, x: torch.Tensor, idx: Optional[torch.Tensor], count: Optional[torch.Tensor],

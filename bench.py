@@ -213,7 +213,8 @@ def hot_prefix_line(cfg_key, nl, ntok, reps, log_fn):
 
 def q4_line(cfg_key, nl, ntok, reps, log_fn):
     """Single-token steps with INT4 FFN rows (pi_quantize_rows once per layer,
-    then pi_ffn_predict + pi_ffn_sparse_q4 per step; the predictor stays fp16),
+    then pi_ffn_predict + pi_ffn_sparse_q4 per step with the fp16 predictor,
+    and pi_ffn_predict_q4 + pi_ffn_sparse_q4 with an INT4 predictor),
     graph-timed over nl rotated layers, beside the INT4 dense FFN."""
     import numpy as np
     import torch
@@ -239,18 +240,22 @@ def q4_line(cfg_key, nl, ntok, reps, log_fn):
     K = nl * ntok
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    counts = []
-    for s in range(K):
-        l, t = s % nl, (s // nl) % ntok
-        R.predict(layers[l], xs[l][t], idx, cnt)
-        counts.append(int(cnt.item()))
+    predictors = {"fp16": R.predict, "int4": R.predict_q4}
+    counts = {}
+    for pk, pf in predictors.items():
+        counts[pk] = []
+        for s in range(K):
+            l, t = s % nl, (s // nl) % ntok
+            pf(layers[l], xs[l][t], idx, cnt)
+            counts[pk].append(int(cnt.item()))
     out = {"workload": cfg.workload + " int4 rows (group 64)"}
-    for name, dense in (("sparse", False), ("dense", True)):
+    for name, pk in (("sparse", "fp16"), ("sparse_int4_predictor", "int4"), ("dense", None)):
+        dense = pk is None
         def run():
             for s in range(K):
                 l, t = s % nl, (s // nl) % ntok
                 if not dense:
-                    R.predict(layers[l], xs[l][t], idx, cnt)
+                    predictors[pk](layers[l], xs[l][t], idx, cnt)
                 R.sparse_q4(layers[l], xs[l][t], idx, cnt, y, dense=dense)
         g = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
@@ -274,11 +279,14 @@ def q4_line(cfg_key, nl, ntok, reps, log_fn):
         if dense:
             T = (m + 1) * ffn * row + 4 * ffn + 6 * d
         else:
-            c = float(np.mean(counts))
-            T = 2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * c * row + 4 * c + 6 * d + 8 * c
+            c = float(np.mean(counts[pk]))
+            P = 2 * r * d + 2 * ffn * r if pk == "fp16" else r * (d // 2 + d // 32) + ffn * (r // 2 + r // 32)
+            T = P + 4 * ffn + (m + 1) * c * row + 4 * c + 6 * d + 8 * c
         out[name] = {"us_per_step": ms * 1000, "tokens_per_s_per_layer": 1000.0 / ms, "touched_MB": T / 1e6,
                      "GBs": T / ms / 1e6}
-        log_fn(f"int4 {name:6s}: {ms * 1000:7.2f} us  {1000.0 / ms:8.0f} tok/s/layer  T {T / 1e6:6.1f} MB  "
+        if not dense:
+            out[name]["mean_active"] = float(np.mean(counts[pk]))
+        log_fn(f"int4 {name:21s}: {ms * 1000:7.2f} us  {1000.0 / ms:8.0f} tok/s/layer  T {T / 1e6:6.1f} MB  "
                f"{T / ms / 1e6:6.0f} GB/s")
     del layers, xs
     torch.cuda.empty_cache()

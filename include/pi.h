@@ -260,6 +260,36 @@ pi_status pi_profile(const pi_half* X, int n, int d, int ffn,
 pi_status pi_quantize_rows(const pi_half* W, int rows, int d, uint8_t* q, pi_half* scales, void* stream);
 
 /*
+ * pi_ffn_predict_q4 -- pi_ffn_predict_hot with the predictor's P1 and P2 as
+ * INT4 rows (as written by pi_quantize_rows: q_P1 r x d / 2 code bytes with
+ * s_P1 r x d / 64 fp16 scales, q_P2 ffn x r / 2 with s_P2 ffn x r / 64).
+ *
+ * Part A section 3.1 of the pages runs the method with INT4 weights; the
+ * predictors of section 4.4 are part of the model's weights, so this
+ * library quantises them like the FFN rows.  The computation is
+ * pi_ffn_predict_hot's with every weight replaced by its dequantised value
+ * (code - 8) * s:
+ *   h = act(P1 x_t + b1),  z = P2 h + b2,  idx_t = [0, n_hot) then the
+ *   ascending i >= n_hot with z_i > ln(tau / (1 - tau)).
+ * h and z are fp32 accumulations; h is never rounded.  The two matrices take
+ * (r d + ffn r) / 2 code bytes plus one fp16 per 64 weights, a quarter of
+ * the fp16 predictor and a little more.
+ * Each token is one kernel (the single-token design of pi_ffn_predict),
+ * so B tokens are B launches on the stream; count[t] = -1 reports an
+ * overrun of that kernel's bounded internal wait.  The workspace is
+ * pi_workspace_size(PI_OP_PREDICT, B, d, r, ffn).
+ *
+ * Errors: as pi_ffn_predict_hot; UNSUPPORTED for d or r not a multiple of
+ * 64; INVALID_ARG for a NULL scale array.
+ */
+pi_status pi_ffn_predict_q4(const pi_half* x, int B, int d,
+                            const uint8_t* q_P1, const pi_half* s_P1, const float* b1, int act,
+                            const uint8_t* q_P2, const pi_half* s_P2, const float* b2,
+                            int r, int ffn, int n_hot, float tau,
+                            int32_t* idx, int32_t* count,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
  * pi_ffn_sparse_q4 -- pi_ffn_sparse over INT4 rows of W_up, W_gate and W_down
  * (as written by pi_quantize_rows; q_* are the code arrays, s_* their scales).
  *

@@ -245,3 +245,76 @@ def test_profile_and_permute_reject_before_launch():
     assert B.pi_permute_rows(A, W, 4, 6, A, stream=0) == B.PI_ERR_UNSUPPORTED
     assert B.pi_permute_rows(A, A + 16, 4, 16, A, stream=0) == B.PI_ERR_INVALID_ARG   # overlap
     assert B.pi_permute_rows(A, W, 0, 16, A, stream=0) == B.PI_ERR_INVALID_ARG
+
+
+def _predict_q4(**kw):
+    args = dict(x=A, B=1, d=64, q_P1=A, s_P1=W, b1=None, act=B.PI_ACT_RELU, q_P2=A, s_P2=W, b2=None, r=64,
+                ffn=128, n_hot=0, tau=0.5, idx=A, count=A, ws=A, ws_bytes=0, stream=0)
+    args.update(kw)
+    return B.pi_ffn_predict_q4(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), B.PI_ERR_INVALID_ARG),
+    (dict(q_P1=None), B.PI_ERR_INVALID_ARG),
+    (dict(q_P2=None), B.PI_ERR_INVALID_ARG),
+    (dict(s_P1=None), B.PI_ERR_INVALID_ARG),
+    (dict(s_P2=None), B.PI_ERR_INVALID_ARG),
+    (dict(idx=None), B.PI_ERR_INVALID_ARG),
+    (dict(B=0), B.PI_ERR_INVALID_ARG),
+    (dict(act=3), B.PI_ERR_INVALID_ARG),
+    (dict(tau=0.0), B.PI_ERR_INVALID_ARG),
+    (dict(n_hot=-32), B.PI_ERR_INVALID_ARG),
+    (dict(n_hot=160), B.PI_ERR_INVALID_ARG),
+    (dict(n_hot=16), B.PI_ERR_UNSUPPORTED),
+    (dict(d=96), B.PI_ERR_UNSUPPORTED),          # a multiple of 8, not of the INT4 group
+    (dict(r=32), B.PI_ERR_UNSUPPORTED),          # likewise for P2's rows
+    (dict(s_P2=W + 1), B.PI_ERR_UNSUPPORTED),
+    (dict(ws=None), B.PI_ERR_WORKSPACE),
+    (dict(ws_bytes=16), B.PI_ERR_WORKSPACE),
+])
+def test_predict_q4_rejects_before_launch(kw, code):
+    assert _predict_q4(**kw) == code
+    assert B.last_error() != ""
+
+
+def _sparse_q4(**kw):
+    args = dict(kind=B.PI_FFN_RELU, x=A, B=1, d=64, ffn=128, q_up=A, s_up=W, b_up=None, q_gate=None,
+                s_gate=None, b_gate=None, q_down=A, s_down=W, idx=A, count=A, y=A, flags=0, ws=A, ws_bytes=0,
+                stream=0)
+    args.update(kw)
+    return B.pi_ffn_sparse_q4(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), B.PI_ERR_INVALID_ARG),
+    (dict(q_up=None), B.PI_ERR_INVALID_ARG),
+    (dict(q_down=None), B.PI_ERR_INVALID_ARG),
+    (dict(s_up=None), B.PI_ERR_INVALID_ARG),
+    (dict(s_down=None), B.PI_ERR_INVALID_ARG),
+    (dict(kind=B.PI_FFN_REGLU, q_gate=A), B.PI_ERR_INVALID_ARG),   # gate codes without scales
+    (dict(kind=B.PI_FFN_SWIGLU), B.PI_ERR_INVALID_ARG),            # gate missing
+    (dict(q_gate=A), B.PI_ERR_INVALID_ARG),                        # gate given for ReLU
+    (dict(flags=B.PI_PER_TOKEN), B.PI_ERR_INVALID_ARG),            # not an INT4 flag
+    (dict(flags=B.PI_CHECK_IDX), B.PI_ERR_INVALID_ARG),
+    (dict(d=96), B.PI_ERR_UNSUPPORTED),
+    (dict(s_down=W + 1), B.PI_ERR_UNSUPPORTED),
+    (dict(y=A + 4), B.PI_ERR_UNSUPPORTED),
+    (dict(ws=None), B.PI_ERR_WORKSPACE),
+    (dict(ws_bytes=64), B.PI_ERR_WORKSPACE),
+])
+def test_sparse_q4_rejects_before_launch(kw, code):
+    assert _sparse_q4(**kw) == code
+    assert B.last_error() != ""
+
+
+def test_quantize_rows_rejects_before_launch():
+    assert B.pi_quantize_rows(None, 4, 64, A, W, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_quantize_rows(A, 0, 64, A, W, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_quantize_rows(A, 4, 0, A, W, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_quantize_rows(A, 4, 96, A, W, stream=0) == B.PI_ERR_UNSUPPORTED
+    assert B.pi_quantize_rows(A, 4, 64, None, W, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_quantize_rows(A, 4, 64, A, None, stream=0) == B.PI_ERR_INVALID_ARG
+    assert B.pi_quantize_rows(A, 4, 64, A + 8, W, stream=0) == B.PI_ERR_UNSUPPORTED
+    assert B.pi_quantize_rows(A, 4, 64, A, W + 1, stream=0) == B.PI_ERR_UNSUPPORTED
+    assert B.pi_quantize_rows(A, 4, 32768, A, W, stream=0) == B.PI_ERR_UNSUPPORTED

@@ -113,3 +113,121 @@ def test_q4_single_token_edges():
     check_y(y1[0].cpu().numpy(), _oracle_q4_y(H, X[0].cpu(), [cfg.ffn - 1]), where="q4 one neuron")
     gi = i2[0, :int(c2[0].cpu())].cpu().numpy()
     check_y(y2[0].cpu().numpy(), _oracle_q4_y(H, X[1].cpu(), gi), where="q4 d=576")
+
+
+# ---------------------------------------------------------------------------
+# pi_ffn_predict_q4: the predictor over INT4 rows of P1 and P2.
+
+def _deq(W):
+    """The oracle's dequantised INT4 rows of an fp16 matrix (host)."""
+    W = W.detach().cpu().numpy() if isinstance(W, torch.Tensor) else W
+    return O.dequantize_rows(*O.quantize_rows(W), W.shape[1])
+
+
+def _q4_logits(H, xh, act="relu"):
+    return O.predictor_logits(xh, _deq(H["P1"]), H.get("b1"), act, _deq(H["P2"]), H["b2"])
+
+
+@pytest.mark.parametrize("d,ffn,r,Bt", [(512, 1000, 64, 1), (576, 1000, 128, 3), (256, 300, 2048, 2),
+                                        (8256, 100, 64, 1)])
+def test_q4_predict_parity(d, ffn, r, Bt):
+    """Ragged last tile (ffn % 32 != 0), the smallest r (two chunks a row),
+    r = 2048 (two column batches per logits lane) and d > 8192 (x staged in
+    two rounds)."""
+    cfg = custom_config("relu", d, ffn, r, mean=0.2, number=110 + r)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, Bt).to(DEV)
+    idx, cnt = R.predict_q4(Q, X)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    for t in range(Bt):
+        c = int(cnt[t].cpu())
+        assert 0 <= c <= ffn
+        check_idx(idx[t, :c].cpu().numpy(), _q4_logits(H, X[t].cpu()), thr, where=f"q4 predict d={d} r={r} t={t}")
+
+
+def test_q4_predict_bias_and_identity_act():
+    """A hidden bias b1 and act = none (h = P1 x + b1, no ReLU)."""
+    cfg = custom_config("relu", 512, 700, 128, mean=0.3, number=120)
+    L = R.to_device(make_layer(cfg), DEV)
+    L["b1"] = (torch.randn(cfg.r, generator=torch.Generator().manual_seed(7)) * 0.05).to(DEV)
+    H = _host(L)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 2).to(DEV)
+    thr = O.logit_threshold(L["tau"])
+    for act in ("relu", "none"):
+        idx, cnt = R.predict_q4(Q, X, act=act)
+        torch.cuda.synchronize()
+        for t in range(2):
+            c = int(cnt[t].cpu())
+            check_idx(idx[t, :c].cpu().numpy(), _q4_logits(H, X[t].cpu(), act), thr, where=f"q4 predict {act} t={t}")
+
+
+def test_q4_predict_hot_prefix():
+    """n_hot = 64: neurons [0, 64) always listed, the rest predicted."""
+    cfg = custom_config("relu", 512, 1000, 64, mean=0.1, number=121)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 2).to(DEV)
+    idx, cnt = R.predict_q4(Q, X, n_hot=64)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    for t in range(2):
+        gi = idx[t, :int(cnt[t].cpu())].cpu().numpy()
+        assert np.array_equal(gi[:64], np.arange(64))
+        z = _q4_logits(H, X[t].cpu())
+        check_idx(gi[64:] - 64, z[64:], thr, where=f"q4 predict hot t={t}")
+
+
+def test_full_size_q4_step():
+    """The OPT-30B-shaped layer (d 7168, ffn 28672, r 1024) with every matrix
+    as INT4 rows: the predicted list against the oracle's logits over the
+    dequantised predictor, and y of the INT4 FFN over that list."""
+    cfg = CONFIGS["c2"]
+    L = make_layer(cfg, layer=0, device=DEV)
+    H = _host(L)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 2, device=DEV, layer=0)
+    thr = O.logit_threshold(L["tau"])
+    for t in range(2):
+        x = X[t:t + 1].contiguous()
+        idx, cnt = R.predict_q4(Q, x)
+        Y = R.sparse_q4(Q, x, idx, cnt)
+        torch.cuda.synchronize()
+        c = int(cnt[0].cpu())
+        gi = idx[0, :c].cpu().numpy()
+        check_idx(gi, _q4_logits(H, X[t].cpu()), thr, where=f"c2 q4 predict t={t}")
+        check_y(Y[0].cpu().numpy(), _oracle_q4_y(H, X[t].cpu(), gi), where=f"c2 q4 step t={t}")
+
+
+def test_q4_predict_graph_replay():
+    """Captured once, replayed three times on new tokens: each replay's list
+    matches the eager call (the epochs advance on the device)."""
+    cfg = custom_config("relu", 512, 1000, 64, mean=0.2, number=122)
+    L = R.to_device(make_layer(cfg), DEV)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 4).to(DEV)
+    x = X[:1].clone()
+    idx = torch.empty(1, cfg.ffn, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(1, dtype=torch.int32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        R.predict_q4(Q, x, idx, cnt)
+        s.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            R.predict_q4(Q, x, idx, cnt)
+    torch.cuda.synchronize()
+    for t in range(1, 4):
+        x.copy_(X[t:t + 1])
+        g.replay()
+        torch.cuda.synchronize()
+        gi, gc = idx.clone(), int(cnt.cpu())
+        ei, ec = R.predict_q4(Q, X[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert gc == int(ec.cpu())
+        assert torch.equal(gi[0, :gc], ei[0, :gc])
