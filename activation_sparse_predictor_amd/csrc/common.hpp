@@ -104,12 +104,48 @@ __device__ __forceinline__ void axpy8(float* acc, float s, u32x4 w) {
     acc[7] = fmaf(s, (float)d.y, acc[7]);
 }
 
+// v plus the v of the lane that the DPP control CTRL pairs with this lane
+// (a partner inside the same 16-lane row, so always in range).  A VALU
+// operand modifier: no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// v[lane] + v[lane ^ 16] (S = 16) or v[lane] + v[lane ^ 32] (S = 32): the
+// gfx950 permlane swaps exchange the odd 16-lane rows of one operand with the
+// even rows of the other (S = 16), or the upper 32 lanes with the lower 32
+// (S = 32).  With both operands v, each lane ends up holding its own value in
+// one result and its partner's in the other.
+template <int S>
+__device__ __forceinline__ float add_swap(float v) {
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (S == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    }
+}
+
 // Sum over aligned groups of W lanes (W a power of two <= 64); every lane of a
-// group ends with the group sum.
+// group ends with the group sum.  Inside a 16-lane row the partners come from
+// DPP: lane ^ 1, lane ^ 2 (quad permutes), then the mirror inside each 8-lane
+// half (i <-> 7 - i) and inside the row (i <-> 15 - i).  After each step a
+// lane holds the sum of a block twice the size, because each mirror pairs
+// every lane with one in the other half of that block.  Rows are then joined
+// across 16 and 32 lanes by the permlane swaps.  All VALU, no LDS round trip.
+// Called with every lane of the wave active.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int off = W / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: a power of two up to the wave");
+    if constexpr (W >= 2) v = add_dpp<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    if constexpr (W >= 4) v = add_dpp<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    if constexpr (W >= 8) v = add_dpp<0x141>(v);   // row_half_mirror
+    if constexpr (W >= 16) v = add_dpp<0x140>(v);  // row_mirror
+    if constexpr (W >= 32) v = add_swap<16>(v);
+    if constexpr (W >= 64) v = add_swap<32>(v);
     return v;
 }
 
