@@ -44,22 +44,33 @@ HBM_PEAK_GBS = 8000.0
 # for the kernel source with this SHA-256 prefix only; for any other source the
 # bench reports traffic as null.
 MEASURED_TRAFFIC = {
-    "source": "activation_sparse_predictor_amd/csrc/fused.hip",
-    "sha256_16": "1a1b5c2b55fc2192",
+    # the sources the single-token kernels are built from, hashed in this order
+    "sources": ["activation_sparse_predictor_amd/csrc/fused.hip", "activation_sparse_predictor_amd/csrc/common.hpp"],
+    "sha256_16": "be14706832559eb6",
     "config": "c2",
-    "bytes_per_launch": {"pi_ffn_predict": 73.00e6, "pi_ffn_sparse": 84.63e6},
+    "bytes_per_launch": {"pi_ffn_predict": 73.00e6, "pi_ffn_sparse": 84.62e6},
 }
 
 
 KERNEL_OF = {"pi_ffn_predict": "k_predict_fused", "pi_ffn_sparse": "k_sparse_fused"}   # one kernel each at B = 1
 
 
+def kernel_source_hash():
+    """SHA-256 prefix over the single-token kernels' sources (None if one is missing)."""
+    import hashlib
+    h = hashlib.sha256()
+    try:
+        for rel in MEASURED_TRAFFIC["sources"]:
+            h.update(open(os.path.join(ROOT, rel), "rb").read())
+    except OSError:
+        return None
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(config_key, entry):
     import hashlib
-    path = os.path.join(ROOT, MEASURED_TRAFFIC["source"])
-    try:
-        h = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
-    except OSError:
+    h = kernel_source_hash()
+    if h is None:
         return None
     if h != MEASURED_TRAFFIC["sha256_16"] or config_key != MEASURED_TRAFFIC["config"]:
         return None
