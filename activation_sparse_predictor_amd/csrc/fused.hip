@@ -386,16 +386,27 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                     hv[4 * q + 2] = v.z;
                     hv[4 * q + 3] = v.w;
                 }
+                // sum_k (code_k - 8) h_k = sum_k code_k h_k - 8 sum_k h_k: the
+                // chunk's sum of h is taken once for its four rows, and a code
+                // is one byte conversion after the word's nibbles are split
+                float hs = 0.f;
+#pragma unroll
+                for (int k = 0; k < 32; ++k) hs += hv[k];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const uint32_t cw[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
                     float p = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = cw[e] & 0x0F0F0F0Fu;          // byte j: the code of weight 8e + 2j
+                        const uint32_t hi = (cw[e] >> 4) & 0x0F0F0F0Fu;   // byte j: the code of weight 8e + 2j + 1
 #pragma unroll
-                        for (int b = 0; b < 8; ++b)   // weight 8e + b: byte b / 2, low nibble for even b
-                            p = fmaf((float)((cw[e] >> (4 * b)) & 0xFu) - 8.f, hv[8 * e + b], p);
-                    a4[m] = fmaf((float)sc[m], p, a4[m]);
+                        for (int j = 0; j < 4; ++j) {
+                            p = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j], p);
+                            p = fmaf((float)((hi >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j + 1], p);
+                        }
+                    }
+                    a4[m] = fmaf((float)sc[m], fmaf(-8.f, hs, p), a4[m]);
                 }
             }
         } while (++n < NB);
