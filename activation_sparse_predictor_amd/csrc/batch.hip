@@ -33,16 +33,18 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 // zeroes the words strictly between the previous entry's word and its own;
 // the words before the first entry's word and after the last one's are
 // zeroed grid-wide.  Workgroups of token 0 also zero the compaction's count
-// slots and the arrival counters of the up GEMM's row blocks.
+// slots, its error word and the arrival counters of the up GEMM's row blocks.
 __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ count, int ffn, int nw,
                                                     uint32_t* __restrict__ tokbits, uint64_t* __restrict__ slots,
-                                                    int nslots, uint32_t* __restrict__ upctr, int nup) {
+                                                    int nslots, uint32_t* __restrict__ upctr, int nup,
+                                                    uint32_t* __restrict__ uerr) {
     const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const int stride = gridDim.x * 256;
     if (t == 0) {
         for (int i = blockIdx.x * 256 + tid; i < nup; i += stride) upctr[i] = 0u;
         for (int i = blockIdx.x * 256 + tid; i < nslots; i += stride) slots[i] = 0ull;
+        if (blockIdx.x == 0 && tid == 0) *uerr = 0u;
     }
     const int cnt = clampi(count[t], 0, ffn);
     const int32_t* lst = idx + (size_t)t * ffn;
@@ -91,7 +93,8 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
 // entries of the ascending union list in parallel, each lane its neuron at
 // its rank.  The last workgroup writes |U|.  A wait that overruns counts the
 // missing workgroup as empty and marks its slot: the list is then short but
-// stays in bounds, and |U| is written as 0.
+// stays in bounds, |U| is written as 0 and the error word is set, which
+// k_union_reduce answers with NaN in every token's y.
 constexpr int kCompactWG = 256;
 constexpr int kCompactTiles = 1024;   // tiles per workgroup held in LDS
 constexpr int kCompactWait = 1 << 16;
@@ -99,7 +102,8 @@ constexpr int kCompactWait = 1 << 16;
 __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restrict__ tokbits, int ffn, int nw, int B,
                                                        uint64_t* __restrict__ slots,
                                                        int32_t* __restrict__ ulist,
-                                                       uint32_t* __restrict__ ucount) {
+                                                       uint32_t* __restrict__ ucount,
+                                                       uint32_t* __restrict__ uerr) {
     __shared__ uint64_t s_m[kCompactTiles];
     __shared__ uint32_t s_wcnt[4];
     __shared__ uint32_t s_base, s_err;
@@ -167,7 +171,10 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
         pos += (uint32_t)__popcll(m);
     }
     if (g == G - 1 && tid == 0) *ucount = s_err ? 0u : s_base + total;
-    if (s_err && tid == 0) __hip_atomic_store(&slots[g], (3ull << 32) | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (s_err && tid == 0) {
+        __hip_atomic_store(&slots[g], (3ull << 32) | total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st_flag(uerr, 1u);   // any workgroup's overrun: every token's y becomes NaN
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -612,12 +619,20 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
 }
 
 // y[t][c] = sum over chunks g (in order) of partial[g][t][c]: one output per
-// thread, the G loads issued 8 at a time.
+// thread, the G loads issued 8 at a time.  NaN for a token whose count is
+// negative (the predictor's overrun report), and for every token when the
+// union compaction overran its wait.
 __global__ __launch_bounds__(256) void k_union_reduce(const float* __restrict__ partial, int B, int Bp,
-                                                      int d, int G, float* __restrict__ y) {
+                                                      int d, int G, float* __restrict__ y,
+                                                      const int32_t* __restrict__ count,
+                                                      const uint32_t* __restrict__ uerr) {
     const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (o >= (size_t)B * d) return;
     const int t = (int)(o / d), c = (int)(o % d);
+    if (count[t] < 0 || *uerr != 0u) {
+        y[o] = __builtin_nanf("");
+        return;
+    }
     float sum = 0.f;
     for (int g0 = 0; g0 < G; g0 += 8) {
         float v[8];
@@ -681,6 +696,7 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
     uint64_t* umasks = reinterpret_cast<uint64_t*>(ws + L.umasks);
     int32_t* ulist = reinterpret_cast<int32_t*>(ws + L.ulist);
     uint32_t* ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
+    uint32_t* uerr = ucount + 1;   // the compaction's error word (the |U| slot is 256 bytes)
     h16* a_hi = reinterpret_cast<h16*>(ws + L.a_hi);
     h16* a_lo = reinterpret_cast<h16*>(ws + L.a_lo);
     float* partial = reinterpret_cast<float*>(ws + L.partial);
@@ -692,8 +708,8 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
     int gc = (ntiles + 3) / 4;   // a tile per wave, up to kCompactWG workgroups
     if (gc > kCompactWG) gc = kCompactWG;
     hipLaunchKernelGGL(k_union_bits, dim3(gb, B), dim3(256), 0, s, idx, count, ffn, nw, tokbits, umasks, gc, upctr,
-                       (ffn + kRingRows - 1) / kRingRows);
-    hipLaunchKernelGGL(k_union_compact, dim3(gc), dim3(256), 0, s, tokbits, ffn, nw, B, umasks, ulist, ucount);
+                       (ffn + kRingRows - 1) / kRingRows, uerr);
+    hipLaunchKernelGGL(k_union_compact, dim3(gc), dim3(256), 0, s, tokbits, ffn, nw, B, umasks, ulist, ucount, uerr);
     RingArgs ra{};
     ra.W[0] = Wup;
     ra.W[1] = Wg;
@@ -733,7 +749,7 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
 #undef PI_DN
     const size_t nout = (size_t)B * d;
     hipLaunchKernelGGL(k_union_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s, partial, B, L.Bp,
-                       d, L.G, y);
+                       d, L.G, y, count, uerr);
     return hipGetLastError();
 }
 

@@ -27,16 +27,19 @@
 // or counter in between.  The epoch is one more than the previous launch's
 // (never 0), kept in the workspace header, so a word left over from an
 // earlier call never passes for a current one, also when the launches are
-// replayed from a captured graph.  In predict the compaction workgroup, which
-// provably runs after every other workgroup has read the epoch, stores it
-// back.  In the FFN the last chunk of each column tile stores it into that
+// replayed from a captured graph.  In predict the compaction workgroup stores
+// it back: it runs after every other workgroup has read the epoch, because it
+// waits for every tile's mask and a tile outside the always-listed prefix
+// waits for every h (when every tile lies in the prefix, no hidden-row
+// workgroup is launched).  In the FFN the last chunk of each column tile stores it into that
 // tile's slot, and a launch takes the oldest slot plus one: while any W_down
 // workgroup of a launch is still running, its tile's slot holds the previous
 // epoch.  A workgroup only waits for
 // workgroups with a smaller index, which are dispatched before it, so the
 // roles overlap (P1 with P2, W_up with W_down) without any risk of circular
 // waiting.  Every wait is bounded: on overrun the kernel reports an error
-// (count = -1, or NaN in y) instead of hanging.
+// instead of hanging (predict: count = -1, which the FFN kernels answer with
+// NaN in y; the FFN: NaN in y).
 //
 // Loads are issued in batches with no uniform condition around any of them:
 // such a branch makes the compiler wait for every earlier load before the
@@ -117,14 +120,13 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
                                                        uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ count, const float* __restrict__ zero,
-                                                       int hot, const h16* __restrict__ s1,
+                                                       int hot, int NA, const h16* __restrict__ s1,
                                                        const h16* __restrict__ s2) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
     __shared__ uint32_t s_part[8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int NA = (r + 3) / 4;
     const int NT = (ffn + kLTile - 1) / kLTile;
 
     if ((int)blockIdx.x < NA) {
@@ -275,7 +277,8 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         if (tid == 0) {
             count[0] = good ? (int32_t)base : -1;
             // every other workgroup has read the epoch: each logits tile has
-            // published its mask, after every hidden row its h
+            // published its mask, and a tile outside the prefix only after
+            // every hidden row its h (without such a tile no hidden row runs)
             st_flag(epoch_word, epoch);
         }
         return;
@@ -513,7 +516,8 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     constexpr bool REGLU = KIND != 0;   // gated: a W_gate row per neuron (ReGLU, SwiGLU)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int cnt = min(max(count[0], 0), ffn);
+    const int craw = count[0];   // negative: the predictor's overrun report, answered with NaN in y
+    const int cnt = min(max(craw, 0), ffn);
     const int PU = (cnt + NU - 1) / NU;   // list positions per up chunk
 
     if ((int)blockIdx.x < NU) {
@@ -738,9 +742,20 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 #pragma unroll
     for (int g = 0; g < kFusedMaxChunks; ++g)
         if (g < Ge) sum += v[g];
-    y[gc] = sum;
+    y[gc] = craw < 0 ? __builtin_nanf("") : sum;
     // every chunk of this tile has read the epoch: the tile's slot advances
     if (tid == 0) st_flag(&slots[tile], epoch);
+}
+
+// Hidden-row workgroups of a predict launch: none when every logits tile lies
+// in the always-listed prefix.  The compaction stores the launch's epoch once
+// it has every mask, and that orders the store after every other workgroup's
+// read of the epoch only because a tile outside the prefix waits for every
+// h; with no such tile a late hidden-row workgroup could read the stored
+// epoch and publish h tagged as the next launch's, so none is launched.
+static int hidden_workgroups(int r, int ffn, int hot) {
+    const int NT = (ffn + kLTile - 1) / kLTile;
+    return NT * kLTile <= hot ? 0 : (r + 3) / 4;
 }
 
 hipError_t launch_sparse_fused_q4(int kind, const h16* x, int d, int ffn, const uint8_t* qu, const h16* su,
@@ -772,12 +787,12 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
                                 hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
-    const int NA = (r + 3) / 4;
+    const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     hipLaunchKernelGGL(k_predict_fused<false>, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2,
                        b2, ffn, thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero,
-                       hot, nullptr, nullptr);
+                       hot, NA, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -787,13 +802,13 @@ hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const
                                    int32_t* count, hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
-    const int NA = (r + 3) / 4;
+    const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     hipLaunchKernelGGL(k_predict_fused<true>, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d,
                        reinterpret_cast<const h16*>(q1), b1, (int)relu, r, reinterpret_cast<const h16*>(q2), b2, ffn,
                        thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot,
-                       s1, s2);
+                       NA, s1, s2);
     return hipGetLastError();
 }
 

@@ -198,7 +198,8 @@ __global__ __launch_bounds__(kDownThreads) void k_down_acc(const h16* __restrict
 #pragma unroll
             for (int u = 0; u < 16; ++u) sum += v[u];
         }
-        y[(size_t)tok * d + gc] = sum;
+        // a negative count is an overrun report of the predictor: answered with NaN
+        y[(size_t)tok * d + gc] = (!DENSE && count[tok] < 0) ? __builtin_nanf("") : sum;
     }
     if (tid == 0) st_flag(my_ctr, 0u);
 }

@@ -35,6 +35,11 @@ _WS: Dict[Tuple[str, int], Workspace] = {}
 
 
 def workspace(tag: str, device=None) -> Workspace:
+    """The workspace kept under `tag` on a device.  Each layout (single-token
+    and batched calls of an entry point, the dense baseline) gets its own tag,
+    so that calls alternating between layouts never make the library clear a
+    workspace, and a captured graph never meets a workspace that another
+    layout wrote between its replays."""
     dev = torch.device(device or "cuda")
     key = (tag, dev.index if dev.index is not None else torch.cuda.current_device())
     if key not in _WS:
@@ -64,7 +69,7 @@ def predict(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor] = None,
     if count is None:
         count = torch.empty(Bt, dtype=torch.int32, device=x.device)
     nbytes = B.pi_workspace_size(B.PI_OP_PREDICT, Bt, d, r, ffn)
-    ws, wsb = workspace("predict", x.device).get(nbytes)
+    ws, wsb = workspace("predict" if Bt == 1 else "predict_batch", x.device).get(nbytes)
     t = float(layer["tau"] if tau is None else tau)
     if n_hot:
         st = B.pi_ffn_predict_hot(_bits(x), Bt, d, layer["P1"], layer.get("b1"), B.ACTS[act], layer["P2"],
@@ -93,7 +98,8 @@ def sparse(layer: dict, x: torch.Tensor, idx: Optional[torch.Tensor],
     if y is None:
         y = torch.empty(Bt, d, dtype=torch.float32, device=x.device)
     nbytes = B.pi_workspace_size(B.PI_OP_SPARSE, Bt, d, layer.get("r", 8), ffn)
-    ws, wsb = workspace("sparse", x.device).get(nbytes)
+    tag = "sparse_dense" if dense else ("sparse" if Bt == 1 or per_token else "sparse_batch")
+    ws, wsb = workspace(tag, x.device).get(nbytes)
     st = B.pi_ffn_sparse(B.KINDS[layer["kind"]], _bits(x), Bt, d, ffn, layer["W_up"],
                          layer.get("b_up"), layer.get("W_gate"), layer.get("b_gate"),
                          layer["W_down"], None if dense else idx, None if dense else count, y,

@@ -1,33 +1,44 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the MI355X sparse-FFN path.
 
-A step is one token through one layer: pi_ffn_predict (predictor MLP,
-threshold, ordered compaction) then pi_ffn_sparse (gathered up GEMV +
-activation, neuron-major W_down accumulate), inputs already resident in HBM.
-The metric is decode tokens/s per layer, with achieved HBM GB/s on the bytes
-the step must touch:
+Headline workload: the OPT-66B-shaped 64-layer FFN stack (ReLU, d 9216,
+ffn 36864, predictor rank 1024, fp16 weights, about 93 GB resident).  Every
+layer is profiled on its 4096 calibration tokens and reordered hot-first
+(pi_profile, pi_reorder, pi_permute_rows); the neurons that fired on at least
+99 % of those tokens, rounded down to whole 32-neuron words, are the layer's
+always-listed prefix.  Then the 128-token prompt runs through the stack on
+the union path, and the decode steps follow at batch 1.
 
-  T = 2 r d + 2 ffn r + 4 ffn            predictor weights + b2
-    + (m + 1) count 2 d + 4 count        active rows of W_up [W_gate] W_down + bias
-    + 2 d + 4 d + 8 count                x, y, index list write + read
+A step is one decode token through all 64 layers: per layer the predictor
+(hidden layer, logits, threshold, ordered compaction) and the neuron-aware
+FFN over the listed rows only, inputs already resident in HBM.  Each step's
+64 layers are captured once as a HIP graph; K steps are K graph replays
+between HIP events on the stream the graphs run on, bracketed by device
+synchronisation.  value = decode tokens/s per layer = 64 K / elapsed, with the
+achieved HBM GB/s on the bytes each layer step must touch:
 
-with m = 1 (ReLU) or 2 (ReGLU) and count the step's own active count.
+  T = 2 r d + (ffn - n_hot)(2 r + 4)    predictor weights + b2 (prefix rows skipped)
+    + (m + 1) count 2 d + 4 count       listed rows of W_up [W_gate] W_down + bias
+    + 2 d + 4 d + 8 count               x, y, index list write + read
 
-Cache-cold protocol: steps rotate over several distinct layers (default 8,
-about 7 GB for the OPT-30B-shaped layer) so the 256 MB Infinity Cache cannot
-hold a layer between its visits.  Timing uses HIP events on the stream the
-library launches on.  The dense FFN (every neuron, no predictor) through the
-same library, and torch's hipBLASLt GEMVs, are timed the same way.  The CPU
-oracle (plain float64 numpy) is timed on a bounded sample of tokens.
+with m = 1 (ReLU) or 2 (gated) and count the layer step's own list length.
+The 64 layers cycle through 93 GB, far beyond the 256 MB Infinity Cache, so
+every layer is read cache-cold.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+Beside the headline: the dense FFN of the same layers through the library
+and through torch (hipBLASLt), graph-timed the same way; per-entry-point
+kernel times from graphs of back-to-back launches (the roofline of the
+dominant kernel); the CPU oracle on a bounded token sample; and the other
+configurations' lines (an OPT-30B-shaped layer, the Falcon-40B-shaped batch
+sweep, the hot prefix, INT4 rows, the prompt phase against torch).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import statistics
 import sys
@@ -39,18 +50,17 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per launch of the single-token kernels, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes on the OPT-30B-shaped layer, each scaled by what the same
-# counter reads for an identity pi_permute_rows copy of known size.  They hold
-# for the kernel source with this SHA-256 prefix only; for any other source the
-# bench reports traffic as null.
+# WRITE_SIZE passes over `bench.py --profile-run` (hot-first layers of the
+# stack), each scaled by what the same counter reads for an identity
+# pi_permute_rows copy of known size.  They hold for the kernel sources with
+# this SHA-256 prefix only; for any other source the bench reports traffic as null.
 MEASURED_TRAFFIC = {
     # the sources the single-token kernels are built from, hashed in this order
     "sources": ["activation_sparse_predictor_amd/csrc/fused.hip", "activation_sparse_predictor_amd/csrc/common.hpp"],
-    "sha256_16": "462d0538a95a109b",
-    "config": "c2",
-    "bytes_per_launch": {"pi_ffn_predict": 73.02e6, "pi_ffn_sparse": 84.63e6},
+    "sha256_16": None,
+    "config": "c5",
+    "bytes_per_launch": {},
 }
-
 
 KERNEL_OF = {"pi_ffn_predict": "k_predict_fused", "pi_ffn_sparse": "k_sparse_fused"}   # one kernel each at B = 1
 
@@ -68,11 +78,8 @@ def kernel_source_hash():
 
 
 def measured_traffic(config_key, entry):
-    import hashlib
     h = kernel_source_hash()
-    if h is None:
-        return None
-    if h != MEASURED_TRAFFIC["sha256_16"] or config_key != MEASURED_TRAFFIC["config"]:
+    if h is None or h != MEASURED_TRAFFIC["sha256_16"] or config_key != MEASURED_TRAFFIC["config"]:
         return None
     return MEASURED_TRAFFIC["bytes_per_launch"].get(entry)
 
@@ -81,10 +88,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def touched_bytes(kind, d, r, ffn, count):
+def touched_bytes(kind, d, r, ffn, count, n_hot=0):
     m = 1 if kind == "relu" else 2
-    return (2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * count * 2 * d + 4 * count
+    return (2 * r * d + (ffn - n_hot) * (2 * r + 4) + (m + 1) * count * 2 * d + 4 * count
             + 2 * d + 4 * d + 8 * count)
+
+
+def predict_bytes(d, r, ffn, count, n_hot=0):
+    return 2 * r * d + (ffn - n_hot) * (2 * r + 4) + 2 * d + 4 * count
+
+
+def sparse_bytes(kind, d, count):
+    m = 1 if kind == "relu" else 2
+    return (m + 1) * count * 2 * d + 4 * count + 8 * count + 2 * d + 4 * d
 
 
 def dense_bytes(kind, d, ffn):
@@ -92,9 +108,62 @@ def dense_bytes(kind, d, ffn):
     return (m + 1) * ffn * 2 * d + 4 * ffn + 2 * d + 4 * d
 
 
-def cpu_baseline(cfg, layer_dev, tokens_dev, budget_s):
+def percentiles(vals, qs=(10, 50, 90)):
+    v = sorted(vals)
+    n = len(v)
+    return {f"p{q}": v[min(n - 1, (q * n) // 100)] for q in qs}
+
+
+class GraphTimer:
+    """Captures a callable into a HIP graph on a side stream and times replays
+    between HIP events recorded on that same stream."""
+
+    def __init__(self, fn, warm=1):
+        import torch
+        self.torch = torch
+        self.stream = torch.cuda.Stream()
+        self.stream.wait_stream(torch.cuda.current_stream())
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            for _ in range(warm):
+                fn()
+            self.stream.synchronize()
+            with torch.cuda.graph(self.graph, stream=self.stream):
+                fn()
+        torch.cuda.synchronize()
+
+    def time(self, reps):
+        """Mean ms per replay over reps replays (one warm replay first)."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            self.graph.replay()
+            e0.record(self.stream)
+            for _ in range(reps):
+                self.graph.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def release(self):
+        del self.graph
+
+
+def torch_dense_ffn(kind, L, x):
+    """The dense FFN through torch's GEMMs (hipBLASLt), fp16 in, fp32 activations."""
+    import torch
+    F = torch.nn.functional
+    if kind == "reglu":
+        a = torch.relu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
+    elif kind == "swiglu":
+        a = F.silu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
+    else:
+        a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
+    return F.linear(a.half(), L["W_down"].t())
+
+
+def cpu_baseline(cfg, layer_dev, tokens_dev, budget_s, what):
     """The oracle as it stands, timed on the host cores over a bounded token sample."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -111,27 +180,314 @@ def cpu_baseline(cfg, layer_dev, tokens_dev, budget_s):
         if el >= budget_s or n >= X.shape[0]:
             break
     return {"value": n / el, "unit": "tokens/s per layer", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} decode tokens of one {cfg.workload} layer (float64 numpy oracle: "
-                      f"predict + sparse FFN), {el:.1f} s"}
+            "sample": f"{n} decode tokens of {what} (float64 numpy oracle: predict + sparse FFN), {el:.1f} s"}
 
 
-def profile_run(layers, tokens, NL, NT, dev):
-    """The workload the hardware-counter passes run: a few warm-up steps, one
-    rotation of decode steps over every layer, then identity row copies of a
-    known size whose FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+def hot_prefix_of(counts_sorted, calib_tokens):
+    """Neurons that fired on >= 99 % of the calibration tokens, in whole 32-neuron words."""
+    import numpy as np
+    return 32 * (int(np.count_nonzero(counts_sorted >= 0.99 * calib_tokens)) // 32)
+
+
+def build_hot_first(cfg, nl, dev, log_fn, label="stack"):
+    """nl layers of cfg, each profiled on its calibration tokens, reordered
+    hot-first and permuted; returns (layers, n_hot per layer, 80 % hot-set sizes)."""
     import torch
     from activation_sparse_predictor_amd import runtime as R
-    d, ffn = layers[0]["d"], layers[0]["ffn"]
+    from synthetic import make_calibration, make_layer
+    t0 = time.perf_counter()
+    layers, hots, hot80 = [], [], []
+    for l in range(nl):
+        L = make_layer(cfg, layer=l, device=dev)
+        Wf, bf = (L["W_up"], L["b_up"]) if cfg.kind == "relu" else (L["W_gate"], L["b_gate"])
+        counts = R.profile(make_calibration(cfg, device=dev, layer=l), Wf, bf).cpu().numpy()
+        perm, hot = R.reorder(counts, 0.8)
+        layers.append(R.permute_layer(L, torch.from_numpy(perm).to(dev)))
+        hots.append(hot_prefix_of(counts[perm], cfg.calib_tokens))
+        hot80.append(hot)
+        del L
+        if l % 16 == 15:
+            torch.cuda.synchronize()
+            log_fn(f"{label}: {l + 1} layers built, profiled and reordered ({time.perf_counter() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    return layers, hots, hot80, time.perf_counter() - t0
+
+
+def stack_headline(cfg, args, dev, log_fn):
+    """The headline: decode steps of one token through the whole hot-first stack,
+    one captured graph per step, plus its baselines and kernel times."""
+    import numpy as np
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import make_tokens
+    kind, d, r, ffn, NLs = cfg.kind, cfg.d, cfg.r, cfg.ffn, cfg.layers
+    m = 1 if kind == "relu" else 2
+    layers, hots, hot80, setup_s = build_hot_first(cfg, NLs, dev, log_fn)
+    log_fn(f"stack: {NLs} layers ready in {setup_s:.1f} s; n_hot mean {np.mean(hots):.0f}, "
+           f"80 % hot set mean {np.mean(hot80):.0f}")
+
+    # ---- prompt: the prompt tokens of every layer at once (union path), one graph
+    P = cfg.prompt_tokens
+    Xp = [make_tokens(cfg, P, device=dev, layer=l, stream="prompt") for l in range(NLs)]
+    idxp = torch.empty(P, ffn, dtype=torch.int32, device=dev)
+    cntp = torch.empty(P, dtype=torch.int32, device=dev)
+    yp = torch.empty(P, d, dtype=torch.float32, device=dev)
+
+    def prompt_pass():
+        for l in range(NLs):
+            R.predict(layers[l], Xp[l], idxp, cntp, n_hot=hots[l])
+            R.sparse(layers[l], Xp[l], idxp, cntp, yp)
+
+    gp = GraphTimer(prompt_pass)
+    prompt_ms = gp.time(2)
+    gp.release()
+    del Xp, idxp, yp
+    log_fn(f"stack prompt: {P} tokens x {NLs} layers {prompt_ms:.2f} ms ({P * 1000.0 / prompt_ms:.0f} tok/s)")
+
+    # ---- decode: one graph per step (one token through every layer)
+    S = cfg.decode_steps
+    K, W = args.steps, args.warmup
+    ng = max(1, min(max(K, W), S))
+    Xd = [make_tokens(cfg, S, device=dev, layer=l) for l in range(NLs)]
+    xs = [[Xd[l][t:t + 1].contiguous() for t in range(ng)] for l in range(NLs)]
+    del Xd
+    idx = torch.empty(NLs, ffn, dtype=torch.int32, device=dev)    # each layer keeps its last list
+    cnt = torch.empty(NLs, dtype=torch.int32, device=dev)
+    y = torch.empty(NLs, d, dtype=torch.float32, device=dev)
+
+    def layer_step(l, x):
+        R.predict(layers[l], x, idx[l:l + 1], cnt[l:l + 1], n_hot=hots[l])
+        R.sparse(layers[l], x, idx[l:l + 1], cnt[l:l + 1], y[l:l + 1])
+
+    # list lengths of every (layer, token) the steps use, for the byte accounting
+    counts = torch.empty(NLs, ng, dtype=torch.int32, device=dev)
+    for t in range(ng):
+        for l in range(NLs):
+            R.predict(layers[l], xs[l][t], idx[l:l + 1], counts[l, t:t + 1], n_hot=hots[l])
+    torch.cuda.synchronize()
+    counts_h = counts.cpu().numpy()
+    if counts_h.min() < 0:
+        raise RuntimeError("the predictor reported an overrun (count -1)")
+    T_layer = np.array([[touched_bytes(kind, d, r, ffn, int(counts_h[l, t]), hots[l]) for t in range(ng)]
+                        for l in range(NLs)])
+
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(cs):
+        for l in range(NLs):                     # eager pass: every workspace holds its layout
+            layer_step(l, xs[l][0])
+        cs.synchronize()
+        for t in range(ng):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cs):
+                for l in range(NLs):
+                    layer_step(l, xs[l][t])
+            graphs.append(g)
+    torch.cuda.synchronize()
+    log_fn(f"stack decode: {ng} step graphs captured ({NLs} layers each)")
+    with torch.cuda.stream(cs):
+        for k in range(W):
+            graphs[k % ng].replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()                     # one process, one GPU: the barrier is the device sync
+    with torch.cuda.stream(cs):
+        ev[0].record(cs)
+        for k in range(K):
+            graphs[k % ng].replay()
+            ev[k + 1].record(cs)
+    torch.cuda.synchronize()
+    step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(K)]
+    total_ms = ev[0].elapsed_time(ev[K])
+    T_step = [float(T_layer[:, k % ng].sum()) for k in range(K)]
+    layer_us = total_ms * 1000.0 / (K * NLs)
+    T_mean = sum(T_step) / (K * NLs)
+    value = K * NLs * 1000.0 / total_ms
+    log_fn(f"stack decode: {K} steps x {NLs} layers in {total_ms:.2f} ms: {layer_us:.2f} us per layer step, "
+           f"{value:.0f} tok/s/layer ({K * 1000.0 / total_ms:.1f} tok/s through the stack), "
+           f"T {T_mean / 1e6:.1f} MB -> {T_mean / layer_us / 1e3:.0f} GB/s")
+    del graphs
+
+    # ---- per entry point: a graph of one launch per layer, back to back
+    reps = 10
+
+    def run_pred():
+        for l in range(NLs):
+            R.predict(layers[l], xs[l][0], idx[l:l + 1], cnt[l:l + 1], n_hot=hots[l])
+
+    def run_sparse():
+        for l in range(NLs):
+            R.sparse(layers[l], xs[l][0], idx[l:l + 1], cnt[l:l + 1], y[l:l + 1])
+
+    run_pred()
+    torch.cuda.synchronize()
+    c0 = cnt.cpu().numpy()
+    g = GraphTimer(run_pred)
+    ms_pred = g.time(reps) / NLs
+    g.release()
+    g = GraphTimer(run_sparse)
+    ms_sp = g.time(reps) / NLs
+    g.release()
+    pb = float(np.mean([predict_bytes(d, r, ffn, int(c0[l]), hots[l]) for l in range(NLs)]))
+    sb = float(np.mean([sparse_bytes(kind, d, int(c0[l])) for l in range(NLs)]))
+    stages = {"pi_ffn_predict": (ms_pred, pb / ms_pred / 1e6, pb), "pi_ffn_sparse": (ms_sp, sb / ms_sp / 1e6, sb)}
+    log_fn(f"stack kernels: predict {ms_pred * 1000:.2f} us ({stages['pi_ffn_predict'][1]:.0f} GB/s), "
+           f"sparse {ms_sp * 1000:.2f} us ({stages['pi_ffn_sparse'][1]:.0f} GB/s) per launch")
+
+    # ---- dense baselines over the same layers, one token each, graph-timed
+    dense = None
+    if not args.no_dense:
+        def run_dense():
+            for l in range(NLs):
+                R.sparse(layers[l], xs[l][0], None, None, y[l:l + 1], dense=True)
+
+        def run_torch():
+            for l in range(NLs):
+                torch_dense_ffn(kind, layers[l], xs[l][0])
+
+        g = GraphTimer(run_dense)
+        ms_dense = g.time(3) / NLs
+        g.release()
+        g = GraphTimer(run_torch)
+        ms_torch = g.time(3) / NLs
+        g.release()
+        db = dense_bytes(kind, d, ffn)
+        ms_layer = layer_us / 1000.0
+        dense = {"pi_dense_us": ms_dense * 1000, "pi_dense_GBs": db / ms_dense / 1e6,
+                 "torch_dense_us": ms_torch * 1000, "torch_dense_GBs": db / ms_torch / 1e6,
+                 "speedup_vs_pi_dense": ms_dense / ms_layer, "speedup_vs_torch_dense": ms_torch / ms_layer,
+                 "ideal_speedup_1_over_active": ffn / float(counts_h.mean()),
+                 "target_speedup_half_ideal": 0.5 * ffn / float(counts_h.mean()),
+                 "method": f"graph of {NLs} launches (one per layer, one token each), replayed 3 times"}
+        log_fn(f"stack dense: library {ms_dense * 1000:.1f} us ({db / ms_dense / 1e6:.0f} GB/s), torch "
+               f"{ms_torch * 1000:.1f} us per layer; sparse step {ms_dense / ms_layer:.2f}x / "
+               f"{ms_torch / ms_layer:.2f}x faster")
+
+    out = {
+        "value": value, "ms_per_step": total_ms / K, "layer_us": layer_us, "T_mean": T_mean,
+        "step_us_percentiles": dict(percentiles([s * 1000.0 for s in step_ms]), steps=K,
+                                    note="per step (one token through all layers) from HIP events between "
+                                         "consecutive graph replays"),
+        "layer_step_us_percentiles": percentiles([s * 1000.0 / NLs for s in step_ms]),
+        "stages": stages, "dense": dense,
+        "info": {"layers": NLs, "setup_s": setup_s, "n_hot_mean": float(np.mean(hots)),
+                 "hot80_mean": float(np.mean(hot80)), "mean_active": float(counts_h.mean()),
+                 "resident_GB": NLs * ((m + 1) * ffn * d * 2 + r * d * 2 + ffn * r * 2) / 1e9,
+                 "step_graphs": ng,
+                 "prompt": {"tokens": P, "ms": prompt_ms, "tokens_per_s": P * 1000.0 / prompt_ms,
+                            "us_per_layer": prompt_ms * 1000.0 / NLs, "method": "one graph of all layers"},
+                 "decode_tokens_per_s": K * 1000.0 / total_ms},
+        "cpu_layer": None,
+    }
+    if not args.no_cpu:
+        out["cpu_layer"] = (layers[0], make_tokens(cfg, 64, device=dev, layer=0))
+    del layers, xs
+    return out
+
+
+def layer_line(cfg_key, nl, nt, reps, no_dense, log_fn):
+    """Single-token steps of one layer shape, cache-cold over nl rotated layers:
+    a graph of nl x min(nt, 8) steps replayed, per-entry-point graphs, and the
+    dense baselines graph-timed the same way."""
+    import numpy as np
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import CONFIGS, make_layer, make_tokens
+    cfg = CONFIGS[cfg_key]
+    kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
+    dev = torch.device("cuda:0")
+    layers = [make_layer(cfg, layer=l, device=dev) for l in range(nl)]
+    toks = [make_tokens(cfg, nt, device=dev, layer=l) for l in range(nl)]
+    xs = [[toks[l][t:t + 1].contiguous() for t in range(nt)] for l in range(nl)]
+    Kg = nl * max(1, min(nt, 8))
+    lt = [(s % nl, (s // nl) % nt) for s in range(Kg)]
+    idx_g = torch.empty(Kg, ffn, dtype=torch.int32, device=dev)
+    cnt_g = torch.empty(Kg, dtype=torch.int32, device=dev)
+    y = torch.empty(1, d, dtype=torch.float32, device=dev)
+
+    def steps():
+        for s, (l, t) in enumerate(lt):
+            R.predict(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1])
+            R.sparse(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1], y)
+
+    def run_pred():
+        for s, (l, t) in enumerate(lt):
+            R.predict(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1])
+
+    def run_sparse():
+        for s, (l, t) in enumerate(lt):
+            R.sparse(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1], y)
+
+    g = GraphTimer(steps)
+    ms_step = g.time(reps) / Kg
+    g.release()
+    c = cnt_g.cpu().numpy()
+    T = float(np.mean([touched_bytes(kind, d, r, ffn, int(v)) for v in c]))
+    g = GraphTimer(run_pred)
+    ms_pred = g.time(reps) / Kg
+    g.release()
+    g = GraphTimer(run_sparse)
+    ms_sp = g.time(reps) / Kg
+    g.release()
+    pb = predict_bytes(d, r, ffn, float(c.mean()))
+    sb = float(np.mean([sparse_bytes(kind, d, int(v)) for v in c]))
+    out = {"workload": cfg.workload, "layers_rotated": nl, "mean_active": float(c.mean()),
+           "us_per_step": ms_step * 1000, "tokens_per_s_per_layer": 1000.0 / ms_step, "touched_MB": T / 1e6,
+           "GBs": T / ms_step / 1e6, "step_frac": T / ms_step / 1e6 / HBM_PEAK_GBS,
+           "kernels_us": {"pi_ffn_predict": ms_pred * 1000, "pi_ffn_sparse": ms_sp * 1000},
+           "kernels_GBs": {"pi_ffn_predict": pb / ms_pred / 1e6, "pi_ffn_sparse": sb / ms_sp / 1e6},
+           "method": f"graph of {Kg} steps over {nl} rotated layers, replayed {reps} times"}
+    log_fn(f"{cfg_key} layer: {ms_step * 1000:.2f} us per step, {1000.0 / ms_step:.0f} tok/s/layer, "
+           f"T {T / 1e6:.1f} MB -> {T / ms_step / 1e6:.0f} GB/s; predict {ms_pred * 1000:.2f} us, "
+           f"sparse {ms_sp * 1000:.2f} us")
+    if not no_dense:
+        def run_dense():
+            for s, (l, t) in enumerate(lt):
+                R.sparse(layers[l], xs[l][t], None, None, y, dense=True)
+
+        def run_torch():
+            for s, (l, t) in enumerate(lt):
+                torch_dense_ffn(kind, layers[l], xs[l][t])
+
+        g = GraphTimer(run_dense)
+        ms_dense = g.time(2) / Kg
+        g.release()
+        g = GraphTimer(run_torch)
+        ms_torch = g.time(2) / Kg
+        g.release()
+        db = dense_bytes(kind, d, ffn)
+        out["dense"] = {"pi_dense_us": ms_dense * 1000, "pi_dense_GBs": db / ms_dense / 1e6,
+                        "torch_dense_us": ms_torch * 1000, "speedup_vs_pi_dense": ms_dense / ms_step,
+                        "speedup_vs_torch_dense": ms_torch / ms_step,
+                        "ideal_speedup_1_over_active": ffn / float(c.mean())}
+        log_fn(f"{cfg_key} dense: library {ms_dense * 1000:.1f} us, torch {ms_torch * 1000:.1f} us; "
+               f"{ms_dense / ms_step:.2f}x / {ms_torch / ms_step:.2f}x")
+    del layers, toks, xs
+    torch.cuda.empty_cache()
+    return out
+
+
+def profile_run(cfg, nl, dev):
+    """The workload the hardware-counter passes run: nl hot-first layers of the
+    stack (profiled, reordered), a few warm-up steps, one counted pass of decode
+    steps over every layer, then identity row copies of a known size whose
+    FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+    import torch
+    from activation_sparse_predictor_amd import runtime as R
+    from synthetic import make_tokens
+    layers, hots, _, _ = build_hot_first(cfg, nl, dev, log)
+    d, ffn = cfg.d, cfg.ffn
     idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
     cnt = torch.empty(1, dtype=torch.int32, device=dev)
     y = torch.empty(1, d, dtype=torch.float32, device=dev)
+    toks = [make_tokens(cfg, 8, device=dev, layer=l) for l in range(nl)]
     counts = []
-    for s in range(NL * 2 + NL * 8):
-        l, t = s % NL, (s // NL) % NT
-        x = tokens[l][t:t + 1].contiguous()
-        R.predict(layers[l], x, idx, cnt)
+    for s in range(nl * 2 + nl * 8):
+        l, t = s % nl, (s // nl) % 8
+        x = toks[l][t:t + 1].contiguous()
+        R.predict(layers[l], x, idx, cnt, n_hot=hots[l])
         R.sparse(layers[l], x, idx, cnt, y)
-        if s >= NL * 2:
+        if s >= nl * 2:
             counts.append(cnt.clone())
     torch.cuda.synchronize()
     rows, row_bytes = 1 << 16, 4096   # 256 MiB
@@ -141,42 +497,30 @@ def profile_run(layers, tokens, NL, NT, dev):
         R.permute_rows(src, perm)
     torch.cuda.synchronize()
     c = torch.cat(counts).float()
-    print(json.dumps({"profile_run": {"decode_steps": len(counts), "mean_count": float(c.mean()),
+    print(json.dumps({"profile_run": {"workload": cfg.workload, "layers": nl, "decode_steps": len(counts),
+                                      "mean_count": float(c.mean()), "n_hot": hots,
                                       "copy_bytes_read": rows * row_bytes, "copy_bytes_written": rows * row_bytes,
                                       "copies": 4}}), flush=True)
 
 
 def hot_prefix_line(cfg_key, nl, ntok, reps, log_fn):
-    """Single-token steps on hot-first layers: each layer profiled on its 4096
-    calibration tokens and reordered, the neurons that fired on >= 99 % of them
-    (whole 32-neuron words) listed without the predictor (pi_ffn_predict_hot),
-    against the same layers with the plain predictor.  Graph-timed, nl rotated
-    layers."""
+    """Single-token steps on hot-first layers with the always-listed prefix
+    (pi_ffn_predict_hot) against the same layers with the plain predictor.
+    Graph-timed, nl rotated layers."""
     import numpy as np
     import torch
     from activation_sparse_predictor_amd import runtime as R
-    from synthetic import CONFIGS, make_calibration, make_layer, make_tokens
+    from synthetic import CONFIGS, make_tokens
     cfg = CONFIGS[cfg_key]
     kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
     dev = torch.device("cuda:0")
-    layers, hots = [], []
-    for l in range(nl):
-        L = make_layer(cfg, layer=l, device=dev)
-        Wf, bf = (L["W_up"], L["b_up"]) if kind == "relu" else (L["W_gate"], L["b_gate"])
-        counts = R.profile(make_calibration(cfg, device=dev, layer=l), Wf, bf).cpu().numpy()
-        perm, _ = R.reorder(counts, 0.8)
-        P = R.permute_layer(L, torch.from_numpy(perm).to(dev))
-        hots.append(32 * (int(np.count_nonzero(counts[perm] >= 0.99 * cfg.calib_tokens)) // 32))
-        layers.append(P)
-        del L
+    layers, hots, _, _ = build_hot_first(cfg, nl, dev, log_fn, label="hot")
     xs = [[make_tokens(cfg, ntok, device=dev, layer=l)[t:t + 1].contiguous() for t in range(ntok)]
           for l in range(nl)]
     idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
     cnt = torch.empty(1, dtype=torch.int32, device=dev)
     y = torch.empty(1, d, dtype=torch.float32, device=dev)
     K = nl * ntok
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     out = {"workload": cfg.workload + " hot-first", "n_hot_mean": float(np.mean(hots)),
            "calibration_tokens": cfg.calib_tokens}
     for name, use_hot in (("plain", False), ("hot_prefix", True)):
@@ -190,29 +534,12 @@ def hot_prefix_line(cfg_key, nl, ntok, reps, log_fn):
             l, t = s % nl, (s // nl) % ntok
             R.predict(layers[l], xs[l][t], idx, cnt, n_hot=hots[l] if use_hot else 0)
             counts.append(int(cnt.item()))
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(stream)
-        with torch.cuda.stream(cs):
-            run()
-            cs.synchronize()
-            with torch.cuda.graph(g, stream=cs):
-                run()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (reps * K)
-        del g
-        m = 1 if kind == "relu" else 2
+        g = GraphTimer(run)
+        ms = g.time(reps) / K
+        g.release()
         cmean = float(np.mean(counts))
         skipped = float(np.mean([hots[s % nl] for s in range(K)])) if use_hot else 0.0
-        T = (2 * r * d + (ffn - skipped) * (2 * r + 4) + (m + 1) * cmean * 2 * d + 4 * cmean
-             + 2 * d + 4 * d + 8 * cmean)
+        T = touched_bytes(kind, d, r, ffn, cmean, skipped)
         out[name] = {"us_per_step": ms * 1000, "tokens_per_s_per_layer": 1000.0 / ms, "mean_active": cmean,
                      "touched_MB": T / 1e6, "GBs": T / ms / 1e6}
         log_fn(f"{name:10s}: {ms * 1000:7.2f} us  {1000.0 / ms:8.0f} tok/s/layer  active {cmean:7.1f}  "
@@ -249,8 +576,6 @@ def q4_line(cfg_key, nl, ntok, reps, log_fn):
     cnt = torch.empty(1, dtype=torch.int32, device=dev)
     y = torch.empty(1, d, dtype=torch.float32, device=dev)
     K = nl * ntok
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     predictors = {"fp16": R.predict, "int4": R.predict_q4}
     counts = {}
     for pk, pf in predictors.items():
@@ -262,37 +587,23 @@ def q4_line(cfg_key, nl, ntok, reps, log_fn):
     out = {"workload": cfg.workload + " int4 rows (group 64)"}
     for name, pk in (("sparse", "fp16"), ("sparse_int4_predictor", "int4"), ("dense", None)):
         dense = pk is None
+
         def run():
             for s in range(K):
                 l, t = s % nl, (s // nl) % ntok
                 if not dense:
                     predictors[pk](layers[l], xs[l][t], idx, cnt)
                 R.sparse_q4(layers[l], xs[l][t], idx, cnt, y, dense=dense)
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(stream)
-        with torch.cuda.stream(cs):
-            run()
-            cs.synchronize()
-            with torch.cuda.graph(g, stream=cs):
-                run()
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (reps * K)
-        del g
+        g = GraphTimer(run)
+        ms = g.time(reps) / K
+        g.release()
         row = d // 2 + d // 32
         if dense:
             T = (m + 1) * ffn * row + 4 * ffn + 6 * d
         else:
             c = float(np.mean(counts[pk]))
-            P = 2 * r * d + 2 * ffn * r if pk == "fp16" else r * (d // 2 + d // 32) + ffn * (r // 2 + r // 32)
-            T = P + 4 * ffn + (m + 1) * c * row + 4 * c + 6 * d + 8 * c
+            Pb = 2 * r * d + 2 * ffn * r if pk == "fp16" else r * (d // 2 + d // 32) + ffn * (r // 2 + r // 32)
+            T = Pb + 4 * ffn + (m + 1) * c * row + 4 * c + 6 * d + 8 * c
         out[name] = {"us_per_step": ms * 1000, "tokens_per_s_per_layer": 1000.0 / ms, "touched_MB": T / 1e6,
                      "GBs": T / ms / 1e6}
         if not dense:
@@ -304,97 +615,9 @@ def q4_line(cfg_key, nl, ntok, reps, log_fn):
     return out
 
 
-def stack_run(cfg_key, log_fn):
-    """The whole stack of the workload (64 OPT-66B-shaped layers, ~93 GB
-    resident): every layer profiled on its calibration tokens and reordered
-    hot-first, then the prompt (one batch of prompt tokens per layer, the
-    union path) and the decode steps at batch 1 (predict + sparse per layer,
-    graph-replayed one step at a time).  Inputs are independent per layer:
-    x ~ N(0, I) for every (layer, token)."""
-    import numpy as np
-    import torch
-    from activation_sparse_predictor_amd import runtime as R
-    from synthetic import CONFIGS, make_calibration, make_layer, make_tokens
-    cfg = CONFIGS[cfg_key]
-    kind, d, r, ffn, NLs = cfg.kind, cfg.d, cfg.r, cfg.ffn, cfg.layers
-    P, S = cfg.prompt_tokens, cfg.decode_steps
-    dev = torch.device("cuda:0")
-    t0 = time.perf_counter()
-    layers, hot_counts = [], []
-    for l in range(NLs):
-        L = make_layer(cfg, layer=l, device=dev)
-        Wf, bf = (L["W_up"], L["b_up"]) if kind == "relu" else (L["W_gate"], L["b_gate"])
-        counts = R.profile(make_calibration(cfg, device=dev, layer=l), Wf, bf).cpu().numpy()
-        perm, hot = R.reorder(counts, 0.8)
-        layers.append(R.permute_layer(L, torch.from_numpy(perm).to(dev)))
-        hot_counts.append(hot)
-        del L
-        if l % 16 == 15:
-            torch.cuda.synchronize()
-            log_fn(f"stack: {l + 1} layers built, profiled and reordered ({time.perf_counter() - t0:.0f} s)")
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t0
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    # prompt: P tokens per layer at once
-    Xp = [make_tokens(cfg, P, device=dev, layer=l, stream="prompt") for l in range(NLs)]
-    idxp = torch.empty(P, ffn, dtype=torch.int32, device=dev)
-    cntp = torch.empty(P, dtype=torch.int32, device=dev)
-    yp = torch.empty(P, d, dtype=torch.float32, device=dev)
-    for l in range(2):
-        R.predict(layers[l], Xp[l], idxp, cntp)
-        R.sparse(layers[l], Xp[l], idxp, cntp, yp)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for l in range(NLs):
-        R.predict(layers[l], Xp[l], idxp, cntp)
-        R.sparse(layers[l], Xp[l], idxp, cntp, yp)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    prompt_ms = e0.elapsed_time(e1)
-    del Xp
-    # decode: S steps, each through every layer, batch 1
-    Xd = [make_tokens(cfg, S, device=dev, layer=l) for l in range(NLs)]
-    idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
-    cnt = torch.empty(1, dtype=torch.int32, device=dev)
-    y = torch.empty(1, d, dtype=torch.float32, device=dev)
-    xs = [[Xd[l][t:t + 1].contiguous() for t in range(S)] for l in range(NLs)]
-    for l in range(NLs):
-        R.predict(layers[l], xs[l][0], idx, cnt)
-        R.sparse(layers[l], xs[l][0], idx, cnt, y)
-    torch.cuda.synchronize()
-    counts = []
-    e0.record(stream)
-    for t in range(S):
-        for l in range(NLs):
-            R.predict(layers[l], xs[l][t], idx, cnt)
-            R.sparse(layers[l], xs[l][t], idx, cnt, y)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    decode_ms = e0.elapsed_time(e1)
-    for l in range(0, NLs, 8):
-        R.predict(layers[l], xs[l][0], idx, cnt)
-        counts.append(int(cnt.item()))
-    m = 1 if kind == "relu" else 2
-    out = {"workload": cfg.workload, "layers": NLs,
-           "resident_GB": NLs * ((m + 1) * ffn * d * 2 + r * d * 2 + ffn * r * 2) / 1e9,
-           "setup_s": setup_s, "hot_count_mean": float(np.mean(hot_counts)),
-           "prompt": {"tokens": P, "ms": prompt_ms, "tokens_per_s": P * 1000.0 / prompt_ms,
-                      "us_per_layer": prompt_ms * 1000.0 / NLs},
-           "decode": {"steps": S, "ms": decode_ms, "tokens_per_s": S * 1000.0 / decode_ms,
-                      "us_per_layer_step": decode_ms * 1000.0 / (S * NLs),
-                      "sampled_active_mean": float(np.mean(counts)),
-                      "method": "eager calls, HIP events around all steps"}}
-    log_fn(f"stack: prompt {P} tokens x {NLs} layers {prompt_ms:.1f} ms ({P * 1000.0 / prompt_ms:.0f} tok/s); "
-           f"decode {S} steps x {NLs} layers {decode_ms:.1f} ms ({S * 1000.0 / decode_ms:.1f} tok/s, "
-           f"{decode_ms * 1000.0 / (S * NLs):.1f} us per layer step)")
-    del layers, xs, Xd
-    torch.cuda.empty_cache()
-    return out
-
-
-def batch_sweep(cfg_key, batches, steps, nl, log_fn):
-    """Decode steps of B tokens on the union path, cache-cold over nl layers."""
+def batch_sweep(cfg_key, batches, reps, nl, log_fn):
+    """Decode steps of B tokens on the union path, cache-cold over nl layers,
+    graph-timed, beside torch's dense GEMMs for the same B tokens."""
     import torch
     from activation_sparse_predictor_amd import runtime as R
     from synthetic import CONFIGS, make_layer, make_tokens
@@ -402,17 +625,15 @@ def batch_sweep(cfg_key, batches, steps, nl, log_fn):
     kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
     m = 1 if kind == "relu" else 2
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
     layers = [make_layer(cfg, layer=l, device=dev) for l in range(nl)]
     out = []
-    F = torch.nn.functional
     for Bt in batches:
-        X = [make_tokens(cfg, Bt, device=dev, layer=l) for l in range(nl)]
+        X = [make_tokens(cfg, Bt, device=dev, layer=l, stream="prompt" if Bt >= 64 else "decode")
+             for l in range(nl)]
         idx = torch.empty(Bt, ffn, dtype=torch.int32, device=dev)
         cnt = torch.empty(Bt, dtype=torch.int32, device=dev)
         y = torch.empty(Bt, d, dtype=torch.float32, device=dev)
-        # union sizes for the byte accounting (host side, once per layer)
-        usize = []
+        usize = []   # union sizes for the byte accounting (host side, once per layer)
         for l in range(nl):
             R.predict(layers[l], X[l], idx, cnt)
             torch.cuda.synchronize()
@@ -422,39 +643,24 @@ def batch_sweep(cfg_key, batches, steps, nl, log_fn):
             for t in range(Bt):
                 sel[ih[t, :c[t]].long()] = True
             usize.append(int(sel.sum()))
-        for s in range(10):
-            R.predict(layers[s % nl], X[s % nl], idx, cnt)
-            R.sparse(layers[s % nl], X[s % nl], idx, cnt, y)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for s in range(steps):
-            R.predict(layers[s % nl], X[s % nl], idx, cnt)
-            R.sparse(layers[s % nl], X[s % nl], idx, cnt, y)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        U = sum(usize[s % nl] for s in range(steps)) / steps
+
+        def run():
+            for l in range(nl):
+                R.predict(layers[l], X[l], idx, cnt)
+                R.sparse(layers[l], X[l], idx, cnt, y)
+
+        def run_torch():
+            for l in range(nl):
+                torch_dense_ffn(kind, layers[l], X[l])
+
+        g = GraphTimer(run)
+        ms = g.time(reps) / nl
+        g.release()
+        g = GraphTimer(run_torch)
+        ms_dense = g.time(max(2, reps // 2)) / nl
+        g.release()
+        U = sum(usize) / nl
         T = 2 * r * d + 2 * ffn * r + 4 * ffn + (m + 1) * U * 2 * d + 4 * U + Bt * (2 * d + 4 * d)
-        # dense reference: torch GEMMs over every neuron for the same B tokens
-        def torch_dense(L, x):
-            if kind == "reglu":
-                a = torch.relu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
-            elif kind == "swiglu":
-                a = F.silu(F.linear(x, L["W_gate"]).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
-            else:
-                a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
-            return F.linear(a.half(), L["W_down"].t())
-        for s in range(5):
-            torch_dense(layers[s % nl], X[s % nl])
-        torch.cuda.synchronize()
-        e0.record(stream)
-        kd = max(10, steps // 4)
-        for s in range(kd):
-            torch_dense(layers[s % nl], X[s % nl])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_dense = e0.elapsed_time(e1) / kd
         row = {"batch": Bt, "us_per_step": ms * 1000, "tokens_per_s_per_layer": Bt * 1000 / ms,
                "union_rows": U, "touched_MB": T / 1e6, "GBs": T / ms / 1e6,
                "torch_dense_us": ms_dense * 1000, "speedup_vs_torch_dense": ms_dense / ms}
@@ -463,46 +669,45 @@ def batch_sweep(cfg_key, batches, steps, nl, log_fn):
         out.append(row)
     del layers
     torch.cuda.empty_cache()
-    return {"workload": cfg.workload, "rows": out}
+    return {"workload": cfg.workload, "method": f"graph of one step per layer over {nl} rotated layers",
+            "rows": out}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", default="c2")
-    ap.add_argument("--layers", type=int, default=8, help="distinct layer copies in the rotation")
-    ap.add_argument("--tokens", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=128, help="timed decode steps (one token through every layer)")
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="c5", help="headline workload (the layer stack)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--layer", default="c2", help="config of the single-layer rotation line ('' to skip)")
     ap.add_argument("--sweep", default="c4", help="config of the batch sweep ('' to skip)")
     ap.add_argument("--sweep-batches", default="1,4,8,16,32")
-    ap.add_argument("--sweep-steps", type=int, default=200)
-    ap.add_argument("--hot", default="c2",
-                    help="config of the hot-prefix line: hot-first layers, predictor trimmed ('' to skip)")
+    ap.add_argument("--hot", default="c2", help="config of the hot-prefix line ('' to skip)")
     ap.add_argument("--q4", default="c2", help="config of the INT4-rows line ('' to skip)")
-    ap.add_argument("--stack", default="", help="also run a whole layer stack (c5: 64 layers, ~93 GB), "
-                                                "prompt then decode; off by default")
     ap.add_argument("--prompt", default="c5",
-                    help="config of the prompt-phase line: one 128-token batch per layer ('' to skip)")
+                    help="config of the prompt-phase line: one prompt batch per layer against torch ('' to skip)")
     ap.add_argument("--sweep-only", action="store_true",
                     help="run only the batch sweep (for a per-kernel profile of the union path)")
     ap.add_argument("--profile-run", action="store_true",
-                    help="short fixed workload for hardware counters: one rotation of decode steps, "
-                         "then 4 identity pi_permute_rows copies of 256 MiB (the calibration copy)")
+                    help="short fixed workload for hardware counters: --profile-layers hot-first layers, one "
+                         "rotation of decode steps, then 4 identity pi_permute_rows copies of 256 MiB")
+    ap.add_argument("--profile-layers", type=int, default=8)
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the path shards by neuron across GPUs but "
               f"this build runs on a single MI355X (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     from activation_sparse_predictor_amd import binding as B
-    from activation_sparse_predictor_amd import runtime as R
-    from synthetic import CONFIGS, make_layer, make_tokens
+    from synthetic import CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -510,320 +715,78 @@ def main():
     B.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.config]
     if args.sweep_only:
-        sw = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")], args.sweep_steps, 4, log)
+        sw = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")], 10, 4, log)
         print(json.dumps({"batch_sweep": sw}), flush=True)
         return
-    cfg = CONFIGS[args.config]
-    kind, d, r, ffn = cfg.kind, cfg.d, cfg.r, cfg.ffn
-    NL, NT = args.layers, args.tokens
-    t_gen = time.perf_counter()
-    layers = [make_layer(cfg, layer=l, device=dev) for l in range(NL)]
-    tokens = [make_tokens(cfg, NT, device=dev, layer=l) for l in range(NL)]
-    torch.cuda.synchronize()
-    log(f"generated {NL} x {cfg.workload} in {time.perf_counter() - t_gen:.1f} s")
-
-    stream = torch.cuda.current_stream()
     if args.profile_run:
-        profile_run(layers, tokens, NL, NT, dev)
+        profile_run(cfg, args.profile_layers, dev)
         return
-    idx = torch.empty(1, ffn, dtype=torch.int32, device=dev)
-    cnt = torch.empty(1, dtype=torch.int32, device=dev)
-    y = torch.empty(1, d, dtype=torch.float32, device=dev)
-    xs = [[tokens[l][t:t + 1].contiguous() for t in range(NT)] for l in range(NL)]
 
-    def step(s):
-        l, t = s % NL, (s // NL) % NT
-        L = layers[l]
-        R.predict(L, xs[l][t], idx, cnt)
-        R.sparse(L, xs[l][t], idx, cnt, y)
+    head = stack_headline(cfg, args, dev, log)
+    cpu_layer = head.pop("cpu_layer")
+    torch.cuda.empty_cache()
+    dom = max(head["stages"], key=lambda k: head["stages"][k][0])
+    st = head["stages"]
 
-    # active counts of every (layer, token) in the rotation, for the byte accounting
-    counts = torch.empty(NL, NT, dtype=torch.int32, device=dev)
-    for l in range(NL):
-        for t in range(NT):
-            R.predict(layers[l], xs[l][t], idx, counts[l, t:t + 1])
-    torch.cuda.synchronize()
-    counts_h = counts.cpu()
-    if int(counts_h.min()) < 0:
-        raise RuntimeError("compaction reported an error count")
-
-    def steps_bytes(s0, K):
-        tot = 0
-        for s in range(s0, s0 + K):
-            tot += touched_bytes(kind, d, r, ffn, int(counts_h[s % NL, (s // NL) % NT]))
-        return tot
-
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0 = args.warmup
-
-    # Eager: one host call per entry point per step.
-    e0.record(stream)
-    for s in range(s0, s0 + args.steps):
-        step(s)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
-
-    # Graph: one rotation of steps (every layer, several tokens each) captured
-    # once and replayed, so the timed region holds only the GPU work of the
-    # steps (the library's kernels take their launch epoch from the workspace,
-    # so replays are valid).  This is the headline number.
-    Kg = NL * max(1, min(NT, 8))
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        for s in range(Kg):
-            step(s)
-        cap.synchronize()
-        with torch.cuda.graph(graph, stream=cap):
-            for s in range(Kg):
-                step(s)
-    torch.cuda.synchronize()
-    reps = max(1, (args.steps + Kg - 1) // Kg)
-    for _ in range(max(1, args.warmup // Kg)):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    n_graph = reps * Kg
-    ms_step = e0.elapsed_time(e1) / n_graph
-    T_avg = steps_bytes(0, Kg) / Kg
-    value = 1000.0 / ms_step
-    log(f"step {ms_step * 1000:.2f} us (graph; eager {ms_eager * 1000:.2f} us), {value:.0f} tok/s/layer, "
-        f"T {T_avg / 1e6:.1f} MB -> {T_avg / ms_step / 1e6:.0f} GB/s")
-    del graph
-
-    # The same steps through pi_ffn_decode (one call per step), graph-timed.
-    def dstep(s):
-        l, t = s % NL, (s // NL) % NT
-        R.decode(layers[l], xs[l][t], y, idx, cnt)
-
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        for s in range(Kg):
-            dstep(s)
-        cap.synchronize()
-        with torch.cuda.graph(graph, stream=cap):
-            for s in range(Kg):
-                dstep(s)
-    torch.cuda.synchronize()
-    for _ in range(max(1, args.warmup // Kg)):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(reps):
-        graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_decode = e0.elapsed_time(e1) / n_graph
-    del graph
-    log(f"decode step (pi_ffn_decode) {ms_decode * 1000:.2f} us, {1000.0 / ms_decode:.0f} tok/s/layer")
-
-    # Per entry point: a graph of Kg back-to-back launches of that entry point
-    # alone (rotating layers and tokens as above), replayed between HIP events
-    # on the launching stream, so that the average covers the kernel itself
-    # and not the host's launch gap.  The sparse launches read the lists the
-    # predict launches wrote, one list per step.
-    idx_g = torch.empty(Kg, ffn, dtype=torch.int32, device=dev)
-    cnt_g = torch.empty(Kg, dtype=torch.int32, device=dev)
-    lt = [(s % NL, (s // NL) % NT) for s in range(Kg)]
-
-    def run_pred():
-        for s, (l, t) in enumerate(lt):
-            R.predict(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1])
-
-    def run_sparse():
-        for s, (l, t) in enumerate(lt):
-            R.sparse(layers[l], xs[l][t], idx_g[s:s + 1], cnt_g[s:s + 1], y)
-
-    def graph_time(fn):
-        g = torch.cuda.CUDAGraph()
-        cs = torch.cuda.Stream()
-        cs.wait_stream(stream)
-        with torch.cuda.stream(cs):
-            fn()
-            cs.synchronize()
-            with torch.cuda.graph(g, stream=cs):
-                fn()
-        torch.cuda.synchronize()
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1) / (reps * Kg)
-
-    run_pred()
-    torch.cuda.synchronize()
-    ms_pred = graph_time(run_pred)
-    ms_sp = graph_time(run_sparse)
-    pred_bytes = 2 * r * d + 2 * ffn * r + 4 * ffn + 2 * d
-    m = 1 if kind == "relu" else 2
-    sp_bytes = [(m + 1) * int(counts_h[l, t]) * (2 * d + 4) + 4 * d for (l, t) in lt]
-    gbs_pred = pred_bytes / ms_pred / 1e6
-    gbs_sp = statistics.mean(sp_bytes) / ms_sp / 1e6
-
-    # the same, eagerly: HIP events between the two calls of each step (the
-    # per-call figure includes the host's launch gap)
-    K2 = min(args.steps, 400)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K2)]
-    for k in range(K2):
-        s = s0 + k
-        l, t = s % NL, (s // NL) % NT
-        ev[3 * k].record(stream)
-        R.predict(layers[l], xs[l][t], idx, cnt)
-        ev[3 * k + 1].record(stream)
-        R.sparse(layers[l], xs[l][t], idx, cnt, y)
-        ev[3 * k + 2].record(stream)
-    torch.cuda.synchronize()
-    eager_steps = sorted(1000 * ev[3 * k].elapsed_time(ev[3 * k + 2]) for k in range(K2))
-    pct = {f"p{q}": eager_steps[min(K2 - 1, (q * K2) // 100)] for q in (10, 50, 90)}
-    eager_us = {"pi_ffn_predict": 1000 * statistics.mean(ev[3 * k].elapsed_time(ev[3 * k + 1]) for k in range(K2)),
-                "pi_ffn_sparse": 1000 * statistics.mean(ev[3 * k + 1].elapsed_time(ev[3 * k + 2])
-                                                        for k in range(K2))}
-    log(f"predict {ms_pred * 1000:.2f} us ({gbs_pred:.0f} GB/s), sparse {ms_sp * 1000:.2f} us "
-        f"({gbs_sp:.0f} GB/s) per launch in graphs; eager per call {eager_us['pi_ffn_predict']:.2f} / "
-        f"{eager_us['pi_ffn_sparse']:.2f} us")
-
-    stages = {"pi_ffn_predict": (ms_pred, gbs_pred, pred_bytes),
-              "pi_ffn_sparse": (ms_sp, gbs_sp, statistics.mean(sp_bytes))}
-    dom = max(stages, key=lambda k: stages[k][0])
-
-    dense = None
-    if not args.no_dense:
-        Kd = min(args.steps, 200)
-        for s in range(20):
-            l = s % NL
-            R.sparse(layers[l], xs[l][0], None, None, y, dense=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for s in range(Kd):
-            l, t = s % NL, (s // NL) % NT
-            R.sparse(layers[l], xs[l][t], None, None, y, dense=True)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_dense = e0.elapsed_time(e1) / Kd
-        # torch hipBLASLt GEMVs of the same dense FFN (fp16 in, fp32 out via fp16 GEMM)
-        F = torch.nn.functional
-        def torch_dense(L, x):
-            if kind == "reglu":
-                a = torch.relu(F.linear(x, L["W_gate"], None).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
-            elif kind == "swiglu":
-                a = F.silu(F.linear(x, L["W_gate"], None).float() + L["b_gate"]) * F.linear(x, L["W_up"]).float()
-            else:
-                a = torch.relu(F.linear(x, L["W_up"]).float() + L["b_up"])
-            return F.linear(a.half(), L["W_down"].t())
-        for s in range(10):
-            torch_dense(layers[s % NL], xs[s % NL][0])
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for s in range(Kd):
-            l, t = s % NL, (s // NL) % NT
-            torch_dense(layers[l], xs[l][t])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_torch = e0.elapsed_time(e1) / Kd
-        db = dense_bytes(kind, d, ffn)
-        dense = {"pi_dense_us": ms_dense * 1000, "pi_dense_GBs": db / ms_dense / 1e6,
-                 "torch_dense_us": ms_torch * 1000, "speedup_vs_pi_dense": ms_dense / ms_step,
-                 "speedup_vs_torch_dense": ms_torch / ms_step,
-                 "ideal_speedup_1_over_active": ffn / float(counts_h.float().mean())}
-        log(f"dense {ms_dense * 1000:.1f} us ({db / ms_dense / 1e6:.0f} GB/s), torch {ms_torch * 1000:.1f} us, "
-            f"speedup {ms_dense / ms_step:.2f}x")
-
-    sweep = None
-    if args.sweep:
-        del layers, tokens, xs
-        torch.cuda.empty_cache()
-        sweep = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")],
-                            args.sweep_steps, 4, log)
-
-    hot = None
-    if args.hot:
-        if not args.sweep:
-            del layers, tokens, xs
-        torch.cuda.empty_cache()
-        hot = hot_prefix_line(args.hot, 8, 8, 16, log)
-
-    stack = None
-    if args.stack:
-        if not args.sweep and not args.hot:
-            del layers, tokens, xs
-        torch.cuda.empty_cache()
-        stack = stack_run(args.stack, log)
-
-    q4 = None
-    if args.q4:
-        if not args.sweep and not args.hot and not args.stack:
-            del layers, tokens, xs
-        torch.cuda.empty_cache()
-        q4 = q4_line(args.q4, 8, 8, 16, log)
-
-    prompt = None
-    if args.prompt:
-        # the prompt of a sequence: 128 tokens through the union path at once,
-        # 3 rotated layers (about 4.4 GB at the OPT-66B shape)
-        torch.cuda.empty_cache()
-        prompt = batch_sweep(args.prompt, [128], 40, 3, log)
+    layer = layer_line(args.layer, 8, 8, 10, args.no_dense, log) if args.layer else None
+    sweep = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")], 10, 4, log) \
+        if args.sweep else None
+    hot = hot_prefix_line(args.hot, 8, 8, 10, log) if args.hot else None
+    q4 = q4_line(args.q4, 8, 8, 10, log) if args.q4 else None
+    # the prompt of a sequence against torch's dense GEMMs: 3 rotated layers
+    prompt = batch_sweep(args.prompt, [CONFIGS[args.prompt].prompt_tokens or 128], 4, 3, log) \
+        if args.prompt else None
 
     cpu = None
-    if not args.no_cpu:
-        cpu_layer = make_layer(cfg, layer=0, device=dev)
-        cpu_tokens = make_tokens(cfg, NT, device=dev, layer=0)
-        cpu = cpu_baseline(cfg, cpu_layer, cpu_tokens, args.cpu_seconds)
+    if cpu_layer is not None:
+        cpu = cpu_baseline(cfg, cpu_layer[0], cpu_layer[1], args.cpu_seconds,
+                           f"layer 0 of the {cfg.workload} (hot-first order)")
         log(f"cpu oracle {cpu['value']:.2f} tok/s/layer on {cpu['cores']} threads")
+        del cpu_layer
 
     out = {
         "metric": "sparse-FFN decode tokens/s per layer + achieved HBM GB/s on touched rows",
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s per layer",
         "n_gpus": 1,
-        "steps": n_graph,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 weights, f32 accumulate",
+        "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": cfg.workload, "kind": kind, "d": d, "ffn": ffn, "r": r,
-                   "batch": 1, "tau": cfg.tau, "layers_rotated": NL, "tokens_per_layer": NT,
-                   "mean_active": float(counts_h.float().mean()),
-                   "touched_MB_per_step": T_avg / 1e6},
-        "achieved_GBs_step": T_avg / ms_step / 1e6,
-        "decode_call": {"us_per_step": ms_decode * 1000, "tokens_per_s_per_layer": 1000.0 / ms_decode,
-                        "GBs": T_avg / ms_decode / 1e6},
-        "timing": {"method": f"hipGraph of {Kg} steps replayed {reps} times, HIP events around the replays",
-                   "ms_per_step_eager": ms_eager,
-                   "step_us_eager_percentiles": dict(pct, steps=K2,
-                                                     note="per step from HIP events around each eager "
-                                                          "predict + sparse pair (launch gaps included)")},
-        "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dom], "entry_point": dom, "achieved": stages[dom][1],
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": stages[dom][1] / HBM_PEAK_GBS, "traffic": measured_traffic(args.config, dom),
-                     "step_frac": T_avg / ms_step / 1e6 / HBM_PEAK_GBS,
-                     "stages_us": {k: v[0] * 1000 for k, v in stages.items()},
-                     "stages_method": f"graph of {Kg} back-to-back launches of one entry point, "
-                                      f"replayed {reps} times between HIP events",
-                     "stages_us_eager_per_call": eager_us},
-        "dense_baseline": dense,
+        "config": {"workload": cfg.workload, "kind": cfg.kind, "d": cfg.d, "ffn": cfg.ffn, "r": cfg.r,
+                   "layers": cfg.layers, "batch": 1, "tau": cfg.tau, "hot_first": True,
+                   "step": f"one decode token through all {cfg.layers} layers (predict + sparse FFN per layer)",
+                   "value_is": f"{cfg.layers} x steps / elapsed (tokens/s per layer)",
+                   "mean_active": head["info"]["mean_active"], "n_hot_mean": head["info"]["n_hot_mean"],
+                   "touched_MB_per_layer_step": head["T_mean"] / 1e6},
+        "us_per_layer_step": head["layer_us"],
+        "achieved_GBs_step": head["T_mean"] / head["layer_us"] / 1e3,
+        "timing": {"method": "one captured HIP graph per step (all layers); steps replayed back to back "
+                             "between HIP events on the graphs' stream, device-synchronised on both sides",
+                   "step_us_percentiles": head["step_us_percentiles"],
+                   "layer_step_us_percentiles": head["layer_step_us_percentiles"]},
+        "roofline": {"bound": "hbm", "kernel": KERNEL_OF[dom], "entry_point": dom, "achieved": st[dom][1],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": st[dom][1] / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.config, dom),
+                     "bytes_per_launch": st[dom][2],
+                     "step_frac": head["T_mean"] / head["layer_us"] / 1e3 / HBM_PEAK_GBS,
+                     "stages_us": {k: v[0] * 1000 for k, v in st.items()},
+                     "stages_GBs": {k: v[1] for k, v in st.items()},
+                     "stages_method": f"graph of {cfg.layers} back-to-back launches of one entry point "
+                                      f"(one per layer), replayed 10 times between HIP events"},
+        "dense_baseline": head["dense"],
         "cpu_baseline": cpu,
+        "stack": head["info"],
+        "layer_line": layer,
         "batch_sweep": sweep,
         "hot_prefix": hot,
         "int4_rows": q4,
-        "stack": stack,
         "prompt_phase": prompt,
     }
     print(json.dumps(out), flush=True)

@@ -112,8 +112,9 @@ typedef enum pi_op {
  * token t in strictly ascending order; count[t] in [0, ffn].  Entries of idx
  * at j >= count[t] are left unspecified.  idx holds B * ffn int32, count B.
  * For B = 1 the call is one kernel (the hidden rows overlap the reads of
- * P2); if one of its bounded internal waits ever ran out, count is set to -1
- * (pi_ffn_sparse treats a negative count as 0).
+ * P2); if one of its bounded internal waits ever ran out, count is set to -1,
+ * and pi_ffn_sparse (every path, pi_ffn_sparse_q4 too) answers a negative
+ * count with y_t = NaN, so the failure cannot pass as a result.
  *
  * Errors: INVALID_ARG for NULL x/P1/P2/idx/count, B/d/r/ffn out of range,
  * act not a pi_pred_act, tau not in (0,1); UNSUPPORTED for d or r not a
@@ -164,7 +165,8 @@ pi_status pi_ffn_predict_hot(const pi_half* x, int B, int d,
  * With flags & PI_DENSE, idx and count are ignored (may be NULL) and every
  * neuron is computed: the dense FFN.  Biases may be NULL (= 0).  W_gate must
  * be non-NULL for REGLU and SWIGLU and NULL for RELU.  Products are fp16 x fp16 with
- * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0).
+ * fp32 accumulation; y is fp32, B x d, fully overwritten (count 0 gives 0;
+ * a negative count[t], the predictor's overrun report, gives y_t = NaN).
  * idx must hold valid, strictly ascending neuron ids (as written by
  * pi_ffn_predict); the call does not re-check them unless flags has
  * PI_CHECK_IDX (then a token whose list breaks this gets y_t = NaN).
@@ -181,7 +183,9 @@ pi_status pi_ffn_predict_hot(const pi_half* x, int B, int d,
  * hi/lo pair, about 22 significant bits).  A neuron outside token t's own
  * list contributes exactly 0 to y_t, so y_t matches the single-token result
  * up to fp32 rounding: the union changes which rows are read, not what is
- * computed (the batched decode of Part A section 4.4).
+ * computed (the batched decode of Part A section 4.4).  The union is formed
+ * by one kernel with a bounded internal wait; were it ever to run out, every
+ * token's y would be NaN.
  *
  * Errors: as pi_ffn_predict, plus INVALID_ARG for an unknown kind or flag,
  * or a W_gate that does not match the kind.

@@ -287,6 +287,51 @@ def test_check_idx_flag(per_token):
     assert np.array_equal(Y2[0], Y0[0]) and np.array_equal(Y3[2], Y0[2])
 
 
+def test_negative_count_gives_nan():
+    """count = -1 is the predictor's report of an overrun wait.  Without
+    PI_CHECK_IDX every FFN path answers it with y_t = NaN (the single-token
+    kernel, PI_PER_TOKEN, the union path, both INT4 paths), while the other
+    tokens of the call keep the results they get when that token's list is
+    empty (bitwise: the union, and so its chunking, is then the same)."""
+    cfg = custom_config("relu", 520, 1000, 64, mean=0.2, number=64)
+    L = R.to_device(make_layer(cfg), DEV)
+    X = make_tokens(cfg, 3).to(DEV)
+    idx, cnt = R.predict(L, X)
+    bad, empty = cnt.clone(), cnt.clone()
+    bad[1], empty[1] = -1, 0
+    for Bt, per_token in ((1, False), (3, True), (3, False)):
+        c_ok, c_bad = empty[:Bt].contiguous(), bad[:Bt].contiguous()
+        if Bt == 1:
+            c_bad = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        Y0 = R.sparse(L, X[:Bt].contiguous(), idx[:Bt].contiguous(), c_ok, per_token=per_token).cpu().numpy()
+        Y1 = R.sparse(L, X[:Bt].contiguous(), idx[:Bt].contiguous(), c_bad, per_token=per_token).cpu().numpy()
+        nan_t = 0 if Bt == 1 else 1
+        assert np.all(np.isnan(Y1[nan_t])), f"B={Bt} per_token={per_token}: count -1 did not give NaN"
+        for t in range(Bt):
+            if t != nan_t:
+                assert np.array_equal(Y1[t], Y0[t]), f"B={Bt} per_token={per_token}: token {t} changed"
+
+
+def test_negative_count_gives_nan_q4():
+    cfg = custom_config("reglu", 512, 1000, 64, mean=0.2, number=65)
+    L = R.to_device(make_layer(cfg), DEV)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 3).to(DEV)
+    idx, cnt = R.predict(L, X)
+    bad, empty = cnt.clone(), cnt.clone()
+    bad[1], empty[1] = -1, 0
+    for Bt in (1, 3):
+        c_ok = empty[:Bt].contiguous()
+        c_bad = bad[:Bt].contiguous() if Bt > 1 else torch.full((1,), -1, dtype=torch.int32, device=DEV)
+        Y0 = R.sparse_q4(Q, X[:Bt].contiguous(), idx[:Bt].contiguous(), c_ok).cpu().numpy()
+        Y1 = R.sparse_q4(Q, X[:Bt].contiguous(), idx[:Bt].contiguous(), c_bad).cpu().numpy()
+        nan_t = 0 if Bt == 1 else 1
+        assert np.all(np.isnan(Y1[nan_t])), f"INT4 B={Bt}: count -1 did not give NaN"
+        for t in range(Bt):
+            if t != nan_t:
+                assert np.array_equal(Y1[t], Y0[t]), f"INT4 B={Bt}: token {t} changed"
+
+
 def test_deterministic_repeats():
     cfg = custom_config("reglu", 1032, 2080, 136, mean=0.3, number=57)
     L = R.to_device(make_layer(cfg), DEV)
@@ -626,3 +671,66 @@ def test_full_size_hot_prefix():
     del L
     _check_hot(P, X[:1].contiguous(), n_hot, where="c2 hot B=1")
     _check_hot(P, X, n_hot, where="c2 hot B=4")
+
+
+# ---------------------------------------------------------------- OPT-66B-shaped stack (d 9216, ffn 36864)
+def test_full_size_stack_prompt_batch():
+    """The 128-token prompt of the OPT-66B-shaped stack in one call per entry
+    point (d 9216, ffn 36864, B = 128: the union covers most rows), the batch
+    the prompt-phase measurement times; sampled tokens against the oracle."""
+    cfg = CONFIGS["c5"]
+    L = make_layer(cfg, layer=3, device=DEV)
+    X = make_tokens(cfg, cfg.prompt_tokens, device=DEV, layer=3, stream="prompt")
+    idx, cnt = R.predict(L, X)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    H = _host(L)
+    del L
+    thr = O.logit_threshold(H["tau"])
+    cnt_h = cnt.cpu().numpy()
+    assert np.all((cnt_h >= 0) & (cnt_h <= cfg.ffn))
+    for t in (0, 41, 85, cfg.prompt_tokens - 1):
+        c = int(cnt_h[t])
+        gi = idx[t, :c].cpu().numpy()
+        xh = X[t].cpu()
+        z = O.predictor_logits(xh, H["P1"], None, "relu", H["P2"], H["b2"])
+        check_idx(gi, z, thr, where=f"c5 prompt t={t}")
+        check_y(Y[t].cpu().numpy(), _oracle_y(H, xh, gi), where=f"c5 prompt t={t}")
+
+
+def _stack_layer_hot_first(cfg, layer):
+    """One layer of the stack as the stack measurement builds it: profiled on
+    its 4096 calibration tokens, reordered hot-first, rows permuted; n_hot is
+    the neurons that fired on >= 99 % of those tokens, in whole mask words."""
+    L = make_layer(cfg, layer=layer, device=DEV)
+    counts = R.profile(make_calibration(cfg, device=DEV, layer=layer), L["W_up"], L["b_up"]).cpu().numpy()
+    perm, hot = R.reorder(counts, 0.8)
+    P = R.permute_layer(L, torch.from_numpy(perm).to(DEV))
+    del L
+    n_hot = 32 * (int(np.count_nonzero(counts[perm] >= 0.99 * cfg.calib_tokens)) // 32)
+    return P, n_hot, hot
+
+
+@pytest.mark.parametrize("layer", [0, 41])
+def test_full_size_stack_layers_hot_first(layer):
+    """Layers of the 64-layer stack, profiled and reordered hot-first, decoded
+    at B = 1 with the plain predictor (n_hot = 0) and with the always-listed
+    prefix (n_hot > 0), each against the oracle."""
+    cfg = CONFIGS["c5"]
+    P, n_hot, hot = _stack_layer_hot_first(cfg, layer)
+    assert 512 <= n_hot <= hot, (n_hot, hot)
+    X = make_tokens(cfg, 2, device=DEV, layer=layer)
+    H = _host(P)
+    thr = O.logit_threshold(P["tau"])
+    for nh in (0, n_hot):
+        for t in range(X.shape[0]):
+            x = X[t:t + 1].contiguous()
+            idx, cnt = R.predict(P, x, n_hot=nh)
+            y = R.sparse(P, x, idx, cnt)
+            torch.cuda.synchronize()
+            c = int(cnt.cpu()[0])
+            gi = idx[0, :c].cpu().numpy()
+            assert np.array_equal(gi[:nh], np.arange(nh))
+            _, z = O.predict_hot(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"], P["tau"], nh)
+            check_idx(gi, z, thr, where=f"c5 layer {layer} n_hot={nh} t={t}")
+            check_y(y[0].cpu().numpy(), _oracle_y(H, X[t].cpu(), gi), where=f"c5 layer {layer} n_hot={nh} t={t}")

@@ -115,6 +115,44 @@ def test_q4_single_token_edges():
     check_y(y2[0].cpu().numpy(), _oracle_q4_y(H, X[1].cpu(), gi), where="q4 d=576")
 
 
+def _oracle_q4_y_rows(H, x, lst):
+    """The oracle's FFN over the dequantised INT4 rows of the listed neurons
+    only (the quantiser works row by row, so a subset of rows quantises as in
+    the whole matrix)."""
+    rows = np.asarray(lst, dtype=np.int64)
+    d = H["d"]
+
+    def deq(k):
+        return None if H.get(k) is None else O.dequantize_rows(*O.quantize_rows(H[k].numpy()[rows]), d)
+
+    def sub(k):
+        return None if H.get(k) is None else H[k].numpy()[rows]
+    return O.sparse_ffn(H["kind"], x, deq("W_up"), sub("b_up"), deq("W_gate"), sub("b_gate"), deq("W_down"),
+                        np.arange(rows.size))
+
+
+@pytest.mark.parametrize("d,n", [(8256, 6143), (8256, 16000), (9216, 6145), (9216, 16000), (9216, 6143)])
+def test_q4_fused_wide_rows_and_long_lists(d, n):
+    """The fused single-token INT4 kernel where its loops take more than one
+    round: d > 8192 (x staged in LDS in a second round) and lists longer than
+    48 chunks x 128 rows, where each W_down row group takes several batches of
+    16 rows in turn (the INT4 counterpart of the fp16 list-length test)."""
+    cfg = custom_config("relu", d, 16384, 16, mean=0.3, number=102)
+    L = make_layer(cfg, device=DEV)
+    Q = R.quantize_layer(L)
+    H = _host(L)
+    del L
+    x = make_tokens(cfg, 1, device=DEV)
+    rng = np.random.default_rng(d + n)
+    lst = np.sort(rng.choice(cfg.ffn, size=n, replace=False))
+    idx = torch.zeros(1, cfg.ffn, dtype=torch.int32, device=DEV)
+    idx[0, :n] = torch.from_numpy(lst.astype(np.int32)).to(DEV)
+    cnt = torch.tensor([n], dtype=torch.int32, device=DEV)
+    y = R.sparse_q4(Q, x, idx, cnt)
+    torch.cuda.synchronize()
+    check_y(y[0].cpu().numpy(), _oracle_q4_y_rows(H, x[0].cpu(), lst), where=f"q4 d={d} list len {n}")
+
+
 # ---------------------------------------------------------------------------
 # pi_ffn_predict_q4: the predictor over INT4 rows of P1 and P2.
 
