@@ -35,6 +35,7 @@ PI_DENSE = 0x1
 PI_PER_TOKEN = 0x2
 PI_DETERMINISTIC = 0x4
 PI_CHECK_IDX = 0x8
+PI_NOALLOC_SCRATCH_BYTES = 4 << 20   # the static scratch of pi_ffn_decode_noalloc, per GPU
 
 KINDS = {"relu": PI_FFN_RELU, "reglu": PI_FFN_REGLU, "swiglu": PI_FFN_SWIGLU}
 ACTS = {"relu": PI_ACT_RELU, "none": PI_ACT_NONE}
@@ -49,6 +50,8 @@ _SIGNATURES = {
     "pi_ffn_sparse": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "pi_ffn_decode": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                            _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "pi_ffn_decode_noalloc": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
+                                   _P, _P, _P, ctypes.c_uint32, _P]),
     "pi_ffn_predict_q4": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
                                _SZ, _P]),
     "pi_quantize_rows": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -167,6 +170,13 @@ def pi_ffn_decode(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W
     return load().pi_ffn_decode(kind, _ptr(x), B, d, ffn, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r, tau,
                                 _ptr(W_up), _ptr(b_up), _ptr(W_gate), _ptr(b_gate), _ptr(W_down), _ptr(idx),
                                 _ptr(count), _ptr(y), flags, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def pi_ffn_decode_noalloc(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down,
+                          idx, count, y, flags, stream=None) -> int:
+    return load().pi_ffn_decode_noalloc(kind, _ptr(x), B, d, ffn, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r,
+                                        tau, _ptr(W_up), _ptr(b_up), _ptr(W_gate), _ptr(b_gate), _ptr(W_down),
+                                        _ptr(idx), _ptr(count), _ptr(y), flags, _stream(stream))
 
 
 def pi_profile(X, n, d, ffn, W_fire, b_fire, counts, ws=None, ws_bytes=0, stream=None) -> int:

@@ -273,6 +273,73 @@ pi_status run_sparse(int kind, const pi_half* x, int B, int d, int ffn, const pi
     return ok();
 }
 
+pi_status check_decode_args(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1, const float* b1,
+                            int act, const pi_half* P2, const float* b2, int r, float tau, const pi_half* W_up,
+                            const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
+                            const int32_t* idx, const int32_t* count, const float* y, uint32_t flags) {
+    PI_TRY(check_predict_args(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count));
+    PI_TRY(check_sparse_args(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags));
+    PI_REQUIRE((flags & PI_DENSE) == 0u, PI_ERR_INVALID_ARG, "PI_DENSE has no predictor step: call pi_ffn_sparse");
+    return PI_OK;
+}
+
+// One decode step on a checked workspace w of at least decode_ws_bytes() bytes.
+pi_status decode_on(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1, const float* b1, int act,
+                    const pi_half* P2, const float* b2, int r, float tau, const pi_half* W_up, const float* b_up,
+                    const pi_half* W_gate, const float* b_gate, const pi_half* W_down, int32_t* idx,
+                    int32_t* count, float* y, uint32_t flags, char* w, hipStream_t s) {
+    // one key for both data areas: where the FFN's starts depends on B, r and ffn
+    const LayoutKey key{PI_OP_DECODE, B, d, r, ffn};
+    const bool fused = B == 1 || sparse_is_fused(B, flags);
+    const bool clear = fused && ws_needs_clear(w, key);
+    if (!fused) ws_forget(w);
+    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, 0, tau, idx, count, w, w + pi::kSyncBytes,
+                       clear && B == 1, s));
+    PI_TRY(run_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w,
+                      w + decode_ffn_offset(B, r, ffn), clear && sparse_is_fused(B, flags), s));
+    if (fused) ws_record(w, key);
+    return PI_OK;
+}
+
+// ---- pi_ffn_decode_noalloc: the decode step's scratch in a static device array.
+// Each GPU the library runs on holds its own copy (kStaticScratchBytes) until
+// the process ends.  Host code never passes the array's name to a kernel: the
+// name is a host-side stand-in, not the device address.  The address comes
+// from hipGetSymbolAddress, once per device with that device current, and is
+// kept per device.
+constexpr size_t kStaticScratchBytes = PI_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's scratch address.  The first call on a device looks it
+// up and zero-fills the array on `s` with a fill kernel (the header's epochs
+// and counters must start at zero; later calls keep what the last one left).
+pi_status static_scratch(hipStream_t s, char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_noalloc: hipGetDevice");
+    PI_REQUIRE(dev >= 0 && dev < kMaxDevices, PI_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_noalloc: hipGetSymbolAddress(scratch)");
+        e = pi::launch_zero(p, kStaticScratchBytes, s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_noalloc: zero-filling the scratch");
+        g_scratch[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch[dev];
+    return PI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -395,23 +462,29 @@ pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn, const
                         const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
                         int32_t* idx, int32_t* count, float* y, uint32_t flags, void* ws, size_t ws_bytes,
                         void* stream) {
-    PI_TRY(check_predict_args(x, B, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count));
-    PI_TRY(check_sparse_args(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags));
-    PI_REQUIRE((flags & PI_DENSE) == 0u, PI_ERR_INVALID_ARG, "PI_DENSE has no predictor step: call pi_ffn_sparse");
+    PI_TRY(check_decode_args(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down,
+                             idx, count, y, flags));
     PI_TRY(check_ws(ws, ws_bytes, decode_ws_bytes(B, d, r, ffn), "pi_ffn_decode"));
-    char* w = static_cast<char*>(ws);
+    return decode_on(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down, idx, count,
+                     y, flags, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+pi_status pi_ffn_decode_noalloc(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1,
+                                const float* b1, int act, const pi_half* P2, const float* b2, int r, float tau,
+                                const pi_half* W_up, const float* b_up, const pi_half* W_gate,
+                                const float* b_gate, const pi_half* W_down, int32_t* idx, int32_t* count, float* y,
+                                uint32_t flags, void* stream) {
+    PI_TRY(check_decode_args(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down,
+                             idx, count, y, flags));
+    const size_t need = decode_ws_bytes(B, d, r, ffn);
+    PI_REQUIRE(need <= kStaticScratchBytes, PI_ERR_WORKSPACE,
+               "pi_ffn_decode_noalloc: these sizes need %zu bytes of scratch, the static scratch holds %zu "
+               "(call pi_ffn_decode with a workspace)", need, kStaticScratchBytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // one key for both data areas: where the FFN's starts depends on B, r and ffn
-    const LayoutKey key{PI_OP_DECODE, B, d, r, ffn};
-    const bool fused = B == 1 || sparse_is_fused(B, flags);
-    const bool clear = fused && ws_needs_clear(ws, key);
-    if (!fused) ws_forget(ws);
-    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, 0, tau, idx, count, w, w + pi::kSyncBytes,
-                       clear && B == 1, s));
-    PI_TRY(run_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w,
-                      w + decode_ffn_offset(B, r, ffn), clear && sparse_is_fused(B, flags), s));
-    if (fused) ws_record(ws, key);
-    return PI_OK;
+    char* w = nullptr;
+    PI_TRY(static_scratch(s, &w));
+    return decode_on(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down, idx, count,
+                     y, flags, w, s);
 }
 
 pi_status pi_quantize_rows(const pi_half* W, int rows, int d, uint8_t* q, pi_half* scales, void* stream) {

@@ -226,6 +226,35 @@ pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn,
                         void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * pi_ffn_decode_noalloc -- pi_ffn_decode for callers that cannot allocate
+ * device memory (code being captured into a graph, tight serving loops,
+ * harnesses that forbid allocation): the same step, arguments, checks and
+ * results (bitwise), with no workspace argument.  Its scratch is a static
+ * device array of PI_NOALLOC_SCRATCH_BYTES inside the library, one copy per
+ * GPU, held until the process ends; the call allocates nothing.
+ *
+ * Limit: the sizes must need at most PI_NOALLOC_SCRATCH_BYTES of workspace
+ * (pi_workspace_size(PI_OP_DECODE, B, d, r, ffn)); a single token (B = 1)
+ * fits up to d = 16384 with ffn up to about 100 000 (d = 9216: about 270 000);
+ * batched sizes mostly do not.  Larger sizes return PI_ERR_WORKSPACE before
+ * anything is launched.
+ *
+ * Every call on one GPU shares that GPU's array and finds what the last call
+ * left in it (the library clears what must start at zero, on the stream, the
+ * first time a GPU is used and whenever the sizes change): calls that overlap
+ * on one GPU (other streams, other host threads) race, so serialise them.
+ */
+#define PI_NOALLOC_SCRATCH_BYTES (4u << 20)
+pi_status pi_ffn_decode_noalloc(int kind, const pi_half* x, int B, int d, int ffn,
+                                const pi_half* P1, const float* b1, int act,
+                                const pi_half* P2, const float* b2, int r, float tau,
+                                const pi_half* W_up, const float* b_up,
+                                const pi_half* W_gate, const float* b_gate,
+                                const pi_half* W_down,
+                                int32_t* idx, int32_t* count, float* y, uint32_t flags,
+                                void* stream);
+
+/*
  * pi_profile -- offline activation counts (Part A section 2.2 "offline
  * profiling data", section 2.3 module 1 and the neuron impact v_i = f_i).
  *
