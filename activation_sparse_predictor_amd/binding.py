@@ -31,6 +31,7 @@ PI_OP_PREDICT = 0
 PI_OP_SPARSE = 1
 PI_OP_PROFILE = 2
 PI_OP_DECODE = 3
+PI_OP_DECODE_HOT = 4
 PI_DENSE = 0x1
 PI_PER_TOKEN = 0x2
 PI_DETERMINISTIC = 0x4
@@ -50,6 +51,12 @@ _SIGNATURES = {
     "pi_ffn_sparse": (_I, [_I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
     "pi_ffn_decode": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                            _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "pi_ffn_decode_hot": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P,
+                               _P, _P, _P, ctypes.c_uint32, _P, _SZ, _P]),
+    "pi_ffn_decode_hot_begin": (_I, [_I, _P, _I, _I, _P, _P, _I, _P, _P, _I, _I, ctypes.c_float, _P, _P, _P, _P, _P,
+                                     _P, _P, _P, _SZ, _P]),
+    "pi_ffn_decode_hot_end": (_I, [_I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint32, _P, _SZ,
+                                   _P]),
     "pi_ffn_decode_noalloc": (_I, [_I, _P, _I, _I, _I, _P, _P, _I, _P, _P, _I, ctypes.c_float, _P, _P, _P, _P, _P,
                                    _P, _P, _P, ctypes.c_uint32, _P]),
     "pi_ffn_predict_q4": (_I, [_P, _I, _I, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, ctypes.c_float, _P, _P, _P,
@@ -170,6 +177,27 @@ def pi_ffn_decode(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W
     return load().pi_ffn_decode(kind, _ptr(x), B, d, ffn, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r, tau,
                                 _ptr(W_up), _ptr(b_up), _ptr(W_gate), _ptr(b_gate), _ptr(W_down), _ptr(idx),
                                 _ptr(count), _ptr(y), flags, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def pi_ffn_decode_hot(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, n_hot, tau, W_up, b_up, W_gate, b_gate, W_down,
+                      idx, count, y, flags, ws, ws_bytes, stream=None) -> int:
+    return load().pi_ffn_decode_hot(kind, _ptr(x), B, d, ffn, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r, n_hot,
+                                    tau, _ptr(W_up), _ptr(b_up), _ptr(W_gate), _ptr(b_gate), _ptr(W_down), _ptr(idx),
+                                    _ptr(count), _ptr(y), flags, _ptr(ws), ws_bytes, _stream(stream))
+
+
+def pi_ffn_decode_hot_begin(kind, x, d, ffn, P1, b1, act, P2, b2, r, n_hot, tau, W_up, b_up, W_gate, b_gate,
+                            W_down, idx, count, ws, ws_bytes, stream=None) -> int:
+    return load().pi_ffn_decode_hot_begin(kind, _ptr(x), d, ffn, _ptr(P1), _ptr(b1), act, _ptr(P2), _ptr(b2), r, n_hot,
+                                          tau, _ptr(W_up), _ptr(b_up), _ptr(W_gate), _ptr(b_gate), _ptr(W_down),
+                                          _ptr(idx), _ptr(count), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def pi_ffn_decode_hot_end(kind, x, d, ffn, r, n_hot, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, ws,
+                          ws_bytes, stream=None) -> int:
+    return load().pi_ffn_decode_hot_end(kind, _ptr(x), d, ffn, r, n_hot, _ptr(W_up), _ptr(b_up), _ptr(W_gate),
+                                        _ptr(b_gate), _ptr(W_down), _ptr(idx), _ptr(count), _ptr(y), flags, _ptr(ws),
+                                        ws_bytes, _stream(stream))
 
 
 def pi_ffn_decode_noalloc(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down,

@@ -100,6 +100,16 @@ size_t sparse_ws_bytes(int B, int d, int ffn) { return pi::kSyncBytes + sparse_d
 size_t decode_ffn_offset(int B, int r, int ffn) { return pi::kSyncBytes + pi::align256(predict_data_bytes(B, r, ffn)); }
 size_t decode_ws_bytes(int B, int d, int r, int ffn) { return decode_ffn_offset(B, r, ffn) + sparse_data_bytes(B, d, ffn); }
 
+// pi_ffn_decode_hot: the header, the predictor's data area, the hot prefix's
+// area (its FFN inside the predictor's kernel), then the FFN's data area.
+size_t decode_hot_area_offset(int B, int r, int ffn) { return decode_ffn_offset(B, r, ffn); }
+size_t decode_hot_ffn_offset(int B, int d, int r, int ffn) {
+    return decode_hot_area_offset(B, r, ffn) + pi::align256(pi::hot_layout(d, ffn).total);
+}
+size_t decode_hot_ws_bytes(int B, int d, int r, int ffn) {
+    return decode_hot_ffn_offset(B, d, r, ffn) + sparse_data_bytes(B, d, ffn);
+}
+
 // Which layout each workspace last held, by its address.  Tags of earlier
 // fused calls can never match a new epoch, but data written by another
 // layout could, so a call that uses tagged words zeroes them whenever the
@@ -159,6 +169,23 @@ pi_status check_predict_args(const pi_half* x, int B, int d, const pi_half* P1, 
     return PI_OK;
 }
 
+// The FFN's kind, weights and biases.
+pi_status check_ffn_weights(int kind, const pi_half* W_up, const float* b_up, const pi_half* W_gate,
+                            const float* b_gate, const pi_half* W_down) {
+    PI_REQUIRE(kind == PI_FFN_RELU || kind == PI_FFN_REGLU || kind == PI_FFN_SWIGLU, PI_ERR_INVALID_ARG,
+               "kind=%d unknown", kind);
+    const bool gated = kind != PI_FFN_RELU;   // ReGLU and SwiGLU take a W_gate row per neuron
+    PI_REQUIRE(gated == (W_gate != nullptr), PI_ERR_INVALID_ARG,
+               gated ? "W_gate is NULL for a gated (ReGLU / SwiGLU) FFN" : "W_gate given for a ReLU FFN");
+    PI_REQUIRE(gated || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
+    PI_TRY(check_half(W_up, "W_up", true));
+    PI_TRY(check_half(W_gate, "W_gate", false));
+    PI_TRY(check_half(W_down, "W_down", true));
+    PI_TRY(check_word(b_up, "b_up", false));
+    PI_TRY(check_word(b_gate, "b_gate", false));
+    return PI_OK;
+}
+
 pi_status check_sparse_args(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* W_up,
                             const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
                             const int32_t* idx, const int32_t* count, const float* y, uint32_t flags) {
@@ -168,16 +195,8 @@ pi_status check_sparse_args(int kind, const pi_half* x, int B, int d, int ffn, c
     PI_REQUIRE((flags & ~(PI_DENSE | PI_PER_TOKEN | PI_DETERMINISTIC | PI_CHECK_IDX)) == 0u, PI_ERR_INVALID_ARG,
                "unknown flags 0x%x", flags);
     const bool dense = (flags & PI_DENSE) != 0u;
-    const bool gated = kind != PI_FFN_RELU;   // ReGLU and SwiGLU take a W_gate row per neuron
-    PI_REQUIRE(gated == (W_gate != nullptr), PI_ERR_INVALID_ARG,
-               gated ? "W_gate is NULL for a gated (ReGLU / SwiGLU) FFN" : "W_gate given for a ReLU FFN");
-    PI_REQUIRE(gated || b_gate == nullptr, PI_ERR_INVALID_ARG, "b_gate given for a ReLU FFN");
+    PI_TRY(check_ffn_weights(kind, W_up, b_up, W_gate, b_gate, W_down));
     PI_TRY(check_half(x, "x", true));
-    PI_TRY(check_half(W_up, "W_up", true));
-    PI_TRY(check_half(W_gate, "W_gate", false));
-    PI_TRY(check_half(W_down, "W_down", true));
-    PI_TRY(check_word(b_up, "b_up", false));
-    PI_TRY(check_word(b_gate, "b_gate", false));
     PI_TRY(check_word(idx, "idx", !dense));
     PI_TRY(check_word(count, "count", !dense));
     PI_REQUIRE(y != nullptr, PI_ERR_INVALID_ARG, "y is NULL");
@@ -301,6 +320,83 @@ pi_status decode_on(int kind, const pi_half* x, int B, int d, int ffn, const pi_
     return PI_OK;
 }
 
+// The two launches of a single-token hot decode step on a checked workspace w
+// of at least decode_hot_ws_bytes(1, ...) bytes.  Begin: the predictor's kernel
+// with the hot prefix's FFN in extra roles (its sum left in the FFN's extra
+// partial slot); it clears the tagged words first when the workspace held
+// another layout.  End: the FFN kernel over list positions [n_hot, count),
+// adding the prefix's sum.
+pi_status hot_begin_on(int kind, const pi_half* x, int d, int ffn, const pi_half* P1, const float* b1, int act,
+                       const pi_half* P2, const float* b2, int r, int n_hot, float tau, const pi_half* W_up,
+                       const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
+                       int32_t* idx, int32_t* count, char* w, hipStream_t s) {
+    const LayoutKey key{PI_OP_DECODE_HOT, 1, d, r, ffn};
+    const bool clear = ws_needs_clear(w, key);
+    const pi::FusedPredLayout PL = pi::fused_pred_layout(r, ffn);
+    const pi::HotLayout HL = pi::hot_layout(d, ffn);
+    const pi::FusedSparseLayout FL = pi::fused_sparse_layout(d, ffn);
+    char* pdata = w + pi::kSyncBytes;
+    char* hot = w + decode_hot_area_offset(1, r, ffn);
+    char* fdata = w + decode_hot_ffn_offset(1, d, r, ffn);
+    hipError_t e = hipSuccess;
+    // the predictor's area, the hot area and the FFN's tagged words are contiguous
+    if (clear) e = pi::launch_zero(pdata, (size_t)(fdata + FL.partial - pdata), s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_hot clearing the workspace");
+    e = pi::launch_predict_fused_hot(kind, reinterpret_cast<const pi::h16*>(x), d, reinterpret_cast<const pi::h16*>(P1),
+                                     b1, act == PI_ACT_RELU, r, reinterpret_cast<const pi::h16*>(P2), b2, ffn, n_hot,
+                                     logit_threshold(tau), PL, w, pdata, idx, count,
+                                     reinterpret_cast<const pi::h16*>(W_up), b_up,
+                                     reinterpret_cast<const pi::h16*>(W_gate), b_gate,
+                                     reinterpret_cast<const pi::h16*>(W_down), HL, hot,
+                                     reinterpret_cast<float*>(fdata + FL.partial), s);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_hot predict");
+    ws_record(w, key);
+    return PI_OK;
+}
+
+pi_status hot_end_on(int kind, const pi_half* x, int d, int ffn, int r, int n_hot, const pi_half* W_up,
+                     const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
+                     const int32_t* idx, const int32_t* count, float* y, uint32_t flags, char* w, hipStream_t s) {
+    const pi::FusedSparseLayout FL = pi::fused_sparse_layout(d, ffn);
+    char* fdata = w + decode_hot_ffn_offset(1, d, r, ffn);
+    hipError_t e = pi::launch_sparse_fused(kind, reinterpret_cast<const pi::h16*>(x), d, ffn,
+                                           reinterpret_cast<const pi::h16*>(W_up), b_up,
+                                           reinterpret_cast<const pi::h16*>(W_gate), b_gate,
+                                           reinterpret_cast<const pi::h16*>(W_down), idx, count, y, FL, w, fdata, s,
+                                           n_hot);
+    if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_hot sparse");
+    if ((flags & PI_CHECK_IDX) != 0u) {
+        e = pi::launch_check_idx(idx, count, 1, ffn, d, y, s);
+        if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_hot index check");
+    }
+    return PI_OK;
+}
+
+// One decode step with an always-listed hot prefix on a checked workspace w
+// of at least decode_hot_ws_bytes() bytes.  One token: begin then end.
+// Several tokens: pi_ffn_predict_hot and pi_ffn_sparse as they are.
+pi_status decode_hot_on(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1, const float* b1,
+                        int act, const pi_half* P2, const float* b2, int r, int n_hot, float tau,
+                        const pi_half* W_up, const float* b_up, const pi_half* W_gate, const float* b_gate,
+                        const pi_half* W_down, int32_t* idx, int32_t* count, float* y, uint32_t flags, char* w,
+                        hipStream_t s) {
+    if (B == 1) {
+        PI_TRY(hot_begin_on(kind, x, d, ffn, P1, b1, act, P2, b2, r, n_hot, tau, W_up, b_up, W_gate, b_gate, W_down, idx,
+                            count, w, s));
+        PI_TRY(hot_end_on(kind, x, d, ffn, r, n_hot, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w, s));
+        return ok();
+    }
+    const LayoutKey key{PI_OP_DECODE_HOT, B, d, r, ffn};
+    const bool fused = sparse_is_fused(B, flags);
+    const bool clear = fused && ws_needs_clear(w, key);
+    if (!fused) ws_forget(w);
+    PI_TRY(run_predict(x, B, d, P1, b1, act, P2, b2, r, ffn, n_hot, tau, idx, count, w, w + pi::kSyncBytes, false, s));
+    PI_TRY(run_sparse(kind, x, B, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags, w,
+                      w + decode_hot_ffn_offset(B, d, r, ffn), clear, s));
+    if (fused) ws_record(w, key);
+    return ok();
+}
+
 // ---- pi_ffn_decode_noalloc: the decode step's scratch in a static device array.
 // Each GPU the library runs on holds its own copy (kStaticScratchBytes) until
 // the process ends.  Host code never passes the array's name to a kernel: the
@@ -377,6 +473,11 @@ pi_status pi_workspace_size(int op, int B, int d, int r, int ffn, size_t* bytes)
             PI_TRY(check_dims(B, d, ffn));
             PI_REQUIRE(r > 0 && r <= PI_MAX_R, PI_ERR_INVALID_ARG, "r=%d outside [1, %d]", r, PI_MAX_R);
             *bytes = decode_ws_bytes(B, d, r, ffn);
+            return ok();
+        case PI_OP_DECODE_HOT:
+            PI_TRY(check_dims(B, d, ffn));
+            PI_REQUIRE(r > 0 && r <= PI_MAX_R, PI_ERR_INVALID_ARG, "r=%d outside [1, %d]", r, PI_MAX_R);
+            *bytes = decode_hot_ws_bytes(B, d, r, ffn);
             return ok();
     }
     return fail(PI_ERR_INVALID_ARG, "unknown op %d", op);
@@ -467,6 +568,51 @@ pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn, const
     PI_TRY(check_ws(ws, ws_bytes, decode_ws_bytes(B, d, r, ffn), "pi_ffn_decode"));
     return decode_on(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down, idx, count,
                      y, flags, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+pi_status pi_ffn_decode_hot(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1, const float* b1,
+                            int act, const pi_half* P2, const float* b2, int r, int n_hot, float tau,
+                            const pi_half* W_up, const float* b_up, const pi_half* W_gate, const float* b_gate,
+                            const pi_half* W_down, int32_t* idx, int32_t* count, float* y, uint32_t flags, void* ws,
+                            size_t ws_bytes, void* stream) {
+    PI_TRY(check_decode_args(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, tau, W_up, b_up, W_gate, b_gate, W_down,
+                             idx, count, y, flags));
+    PI_REQUIRE(n_hot >= 0 && n_hot <= ffn, PI_ERR_INVALID_ARG, "n_hot=%d outside [0, ffn=%d]", n_hot, ffn);
+    PI_REQUIRE(n_hot % 32 == 0, PI_ERR_UNSUPPORTED, "n_hot=%d is not a multiple of 32", n_hot);
+    PI_TRY(check_ws(ws, ws_bytes, decode_hot_ws_bytes(B, d, r, ffn), "pi_ffn_decode_hot"));
+    return decode_hot_on(kind, x, B, d, ffn, P1, b1, act, P2, b2, r, n_hot, tau, W_up, b_up, W_gate, b_gate, W_down,
+                         idx, count, y, flags, static_cast<char*>(ws), static_cast<hipStream_t>(stream));
+}
+
+pi_status pi_ffn_decode_hot_begin(int kind, const pi_half* x, int d, int ffn, const pi_half* P1, const float* b1,
+                                  int act, const pi_half* P2, const float* b2, int r, int n_hot, float tau,
+                                  const pi_half* W_up, const float* b_up, const pi_half* W_gate, const float* b_gate,
+                                  const pi_half* W_down, int32_t* idx, int32_t* count, void* ws, size_t ws_bytes,
+                                  void* stream) {
+    PI_TRY(check_predict_args(x, 1, d, P1, b1, act, P2, b2, r, ffn, tau, idx, count));
+    PI_TRY(check_ffn_weights(kind, W_up, b_up, W_gate, b_gate, W_down));
+    PI_REQUIRE(n_hot >= 0 && n_hot <= ffn, PI_ERR_INVALID_ARG, "n_hot=%d outside [0, ffn=%d]", n_hot, ffn);
+    PI_REQUIRE(n_hot % 32 == 0, PI_ERR_UNSUPPORTED, "n_hot=%d is not a multiple of 32", n_hot);
+    PI_TRY(check_ws(ws, ws_bytes, decode_hot_ws_bytes(1, d, r, ffn), "pi_ffn_decode_hot_begin"));
+    PI_TRY(hot_begin_on(kind, x, d, ffn, P1, b1, act, P2, b2, r, n_hot, tau, W_up, b_up, W_gate, b_gate, W_down, idx,
+                        count, static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+    return ok();
+}
+
+pi_status pi_ffn_decode_hot_end(int kind, const pi_half* x, int d, int ffn, int r, int n_hot, const pi_half* W_up,
+                                const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
+                                const int32_t* idx, const int32_t* count, float* y, uint32_t flags, void* ws,
+                                size_t ws_bytes, void* stream) {
+    PI_TRY(check_sparse_args(kind, x, 1, d, ffn, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags));
+    PI_REQUIRE((flags & (PI_DENSE | PI_PER_TOKEN)) == 0u, PI_ERR_INVALID_ARG,
+               "pi_ffn_decode_hot_end takes PI_CHECK_IDX and PI_DETERMINISTIC only");
+    PI_REQUIRE(r > 0 && r <= PI_MAX_R, PI_ERR_INVALID_ARG, "r=%d outside [1, %d]", r, PI_MAX_R);
+    PI_REQUIRE(n_hot >= 0 && n_hot <= ffn, PI_ERR_INVALID_ARG, "n_hot=%d outside [0, ffn=%d]", n_hot, ffn);
+    PI_REQUIRE(n_hot % 32 == 0, PI_ERR_UNSUPPORTED, "n_hot=%d is not a multiple of 32", n_hot);
+    PI_TRY(check_ws(ws, ws_bytes, decode_hot_ws_bytes(1, d, r, ffn), "pi_ffn_decode_hot_end"));
+    PI_TRY(hot_end_on(kind, x, d, ffn, r, n_hot, W_up, b_up, W_gate, b_gate, W_down, idx, count, y, flags,
+                      static_cast<char*>(ws), static_cast<hipStream_t>(stream)));
+    return ok();
 }
 
 pi_status pi_ffn_decode_noalloc(int kind, const pi_half* x, int B, int d, int ffn, const pi_half* P1,

@@ -3,11 +3,18 @@
 // pi_ffn_predict (B = 1):  k_predict_fused
 //   workgroups [0, NA)        hidden rows, one wave per row of P1:
 //                             h_k = act(P1[k].x + b1_k), published as a tagged word
-//   workgroups [NA, NA + NT)  logits tiles of 32 neurons: collect h, stream the
+//   [NA, NA + NHU)            (pi_ffn_decode_hot only) hot-prefix up rows, one
+//                             wave per neuron i < n_hot: a_i, published as a tagged word
+//   next NT workgroups        logits tiles of 32 neurons: collect h, stream the
 //                             tile's P2 rows, z = P2 h + b2 > thr, publish the
 //                             tile's 32-bit mask as a tagged word (a tile of
 //                             the always-listed hot prefix publishes all ones)
-//   workgroup NA + NT         gathers every mask and writes idx (ascending) and count
+//   the next one              gathers every mask and writes idx (ascending) and count
+//   the last T * G            (pi_ffn_decode_hot only) hot-prefix W_down: column
+//                             tile x chunk of the prefix, accumulated from the
+//                             prefix's a_i; the tile's last chunk adds the chunk
+//                             partials in order into the FFN's extra partial slot,
+//                             which the FFN kernel adds to y (its list from n_hot on)
 //
 // pi_ffn_sparse (B = 1):   k_sparse_fused
 //   workgroups [0, NU)        up chunks, one wave per active row:
@@ -111,7 +118,195 @@ static_assert(kLRows * 4 == kLTile, "4 waves per logits tile");
 // Q4: P1 and P2 are INT4 rows (P1, P2 then point at the code bytes, two
 // codes a byte, and s1, s2 at the fp16 scales of 64-weight groups); h and z
 // are still accumulated in fp32.
-template <bool Q4>
+// The hot prefix's FFN (pi_ffn_decode_hot): rows [0, n) of W_up [W_gate] and
+// W_down, its activations as tagged words with their own epochs (per-tile
+// slots advanced by the W_down tiles' last chunks, as in the FFN kernel), its
+// chunk partials and arrival counters, and y_hot, the FFN kernel's extra slot.
+struct HotArgs {
+    const h16* Wu;
+    const float* bu;
+    const h16* Wg;
+    const float* bg;
+    const h16* Wd;
+    uint64_t* atag;
+    float* partial;
+    uint32_t* ctr;
+    uint32_t* slots;
+    float* yhot;
+    int n, NHU, G, T;
+};
+
+constexpr int kHotUpMaxWG = 384;            // hot up workgroups (4 rows each, one per wave)
+constexpr int kHotCols = kFusedCols;        // W_down columns per hot tile: 64 threads x 8
+constexpr int kHotGroups = 4;               // row groups (waves) of a hot W_down workgroup
+constexpr int kHotBatch = kHotRowsPerChunk / kHotGroups;   // rows in flight per thread
+static_assert(kHotCols == 64 * 8, "one wave spans a hot tile's columns");
+
+// Hot-prefix up rows: workgroup u takes a contiguous range of the prefix, one
+// wave per neuron (the FFN kernel's up role at 256 threads).
+template <int KIND>
+__device__ __forceinline__ void hot_up_role(const HotArgs& H, const h16* __restrict__ x, int d, int u, float* sh,
+                                            const float* __restrict__ zero) {
+    constexpr bool GATED = KIND != 0;
+    constexpr int UU = GATED ? 8 : 16;   // 16-byte chunks per lane per batch
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = H.n;
+    const int PU = (n + H.NHU - 1) / H.NHU;
+    const int j0 = min(n, u * PU), j1 = min(n, j0 + PU);
+    if (j0 >= j1) return;
+    const int nch = d >> 3;
+    u32x4 xs[4];   // x chunks tid + 256 q, requested ahead of the rows
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xs[q] = ld16(x + (size_t)min(tid + q * 256, nch - 1) * 8);
+    int i = min(j0 + wave, j1 - 1);
+    const bool live = j0 + wave < j1;   // wave-uniform
+    u32x4 wu[UU], wg[UU];
+    auto issue = [&](int c0) {
+        const h16* ru = H.Wu + (size_t)i * d;
+        const h16* rgp = GATED ? H.Wg + (size_t)i * d : nullptr;
+#pragma unroll
+        for (int q = 0; q < UU; ++q) {
+            const int c = c0 + q * 64;
+            if (c < nch) {
+                wu[q] = ld16_stream(ru + (size_t)c * 8);
+                if (GATED) wg[q] = ld16_stream(rgp + (size_t)c * 8);
+            }
+        }
+    };
+    float bu = 0.f, bgv = 0.f;
+    auto issue_bias = [&]() {
+        bu = *(H.bu ? H.bu + i : zero);
+        if (GATED) bgv = *(H.bg ? H.bg + i : zero);
+    };
+    issue(lane);
+    issue_bias();
+    const uint32_t slot = H.slots[min(lane, H.T - 1)];
+    u32x4* sx = reinterpret_cast<u32x4*>(sh);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (tid + q * 256 < nch) sx[tid + q * 256] = xs[q];
+    for (int k = tid + 1024; k < nch; k += 256) sx[k] = ld16(x + (size_t)k * 8);   // d > 8192
+    __syncthreads();
+    if (!live) return;
+    for (int j = j0 + wave; j < j1; j += 4) {
+        if (j != j0 + wave) {
+            i = j;
+            issue(lane);
+            issue_bias();
+        }
+        float au = 0.f, ag = 0.f;
+        for (int c0 = lane; c0 < nch; c0 += 64 * UU) {
+            if (c0 != lane) issue(c0);
+#pragma unroll
+            for (int q = 0; q < UU; ++q) {
+                const int c = c0 + q * 64;
+                if (c < nch) {
+                    const u32x4 xv = sx[c];
+                    au = dot8_h(wu[q], xv, au);
+                    if (GATED) ag = dot8_h(wg[q], xv, ag);
+                }
+            }
+        }
+        au = group_sum<64>(au);
+        if (GATED) ag = group_sum<64>(ag);
+        const uint32_t epoch = next_epoch(oldest_slot(slot));
+        if (lane == 0) st_tag(&H.atag[j], epoch, __float_as_uint(ffn_act<KIND>(au + bu, ag + bgv)));
+    }
+}
+
+// Hot-prefix W_down: workgroup (tile, chunk) of the prefix, wave g the chunk's
+// rows g, g + 4, ...; a thread holds 8 columns of 16 rows in flight, requested
+// before the activations are collected.  Each wave collects its own rows'
+// activations (lane q polls row q) and takes them by lane broadcast.  The
+// waves are summed in LDS, the chunk partial is stored, and the tile's last
+// chunk to arrive adds the G partials in chunk order into y_hot and advances
+// the tile's epoch slot.
+__device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, float* sh, int* s_flag) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int rg = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int T = H.T, G = H.G, n = H.n;
+    const int tile = k % T, chunk = k / T;
+    const int PD = (n + G - 1) / G;
+    const int j0 = min(n, chunk * PD), j1 = min(n, j0 + PD);
+    const int col = tile * kHotCols + lane * 8;
+    const int colc = min(col, d - 8);   // load address of a column past the end
+    const int nk = (j1 - j0 - rg + kHotGroups - 1) / kHotGroups;   // this wave's rows j0 + rg + 4m
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    bool ok = true;
+    uint32_t epoch = 0;
+    // the slot is stable while this launch runs (no tile can finish before
+    // this workgroup arrives), so it may be requested ahead of the rows
+    const uint32_t slot = H.slots[min(lane, T - 1)];
+    for (int k0 = 0; k0 == 0 || k0 < nk; k0 += kHotBatch) {
+        u32x4 w[kHotBatch];
+#pragma unroll
+        for (int q = 0; q < kHotBatch; ++q) {
+            const int r = min(j0 + rg + kHotGroups * min(k0 + q, max(nk - 1, 0)), n - 1);
+            w[q] = ld16_stream(H.Wd + (size_t)r * d + colc);
+        }
+        if (k0 == 0) epoch = next_epoch(oldest_slot(slot));
+        const int q = lane & (kHotBatch - 1);
+        const int jr = min(j0 + rg + kHotGroups * (k0 + q), n - 1);
+        uint64_t v = ld_tag(&H.atag[jr]);
+        float a = 0.f;
+        if (lane < kHotBatch && k0 + q < nk) {
+            ok = poll_tag(&H.atag[jr], v, epoch) && ok;
+            a = __uint_as_float((uint32_t)v);
+        }
+#pragma unroll
+        for (int m = 0; m < kHotBatch; ++m)
+            if (k0 + m < nk) axpy8(acc, __shfl(a, m, 64), w[m]);
+    }
+    ok = __syncthreads_and(ok);
+    float* s_red = sh;   // kHotGroups x kHotCols fp32
+    *reinterpret_cast<f32x4*>(&s_red[rg * kHotCols + lane * 8]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(&s_red[rg * kHotCols + lane * 8 + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kHotCols / 256; ++e) {
+        const int c = tid + 256 * e, gc = tile * kHotCols + c;
+        if (gc < d) {
+            float v = 0.f;
+#pragma unroll
+            for (int g = 0; g < kHotGroups; ++g) v += s_red[g * kHotCols + c];
+            st_coherent(&H.partial[(size_t)chunk * d + gc], ok ? v : __builtin_nanf(""));
+        }
+    }
+    wait_own_memory();
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t* c = &H.ctr[(size_t)tile * kCtrStride];
+        const int flag = fetch_add(c, 1u) == (uint32_t)(G - 1);
+        if (flag) st_flag(c, 0u);   // the last arrival puts the counter back for the next call
+        *s_flag = flag;
+    }
+    __syncthreads();
+    if (!*s_flag) return;
+    // the tile's last chunk: both columns' G partials requested in one round
+    float v[kHotCols / 256][kHotMaxChunks];
+#pragma unroll
+    for (int e = 0; e < kHotCols / 256; ++e) {
+        const int gc = min(tile * kHotCols + tid + 256 * e, d - 1);
+#pragma unroll
+        for (int g = 0; g < kHotMaxChunks; ++g) v[e][g] = ld_coherent(&H.partial[(size_t)min(g, G - 1) * d + gc]);
+    }
+#pragma unroll
+    for (int e = 0; e < kHotCols / 256; ++e) {
+        const int gc = tile * kHotCols + tid + 256 * e;
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < kHotMaxChunks; ++g)
+            if (g < G) sum += v[e][g];
+        if (gc < d) H.yhot[gc] = sum;
+    }
+    // every chunk of this tile has read the epoch: the tile's slot advances
+    if (tid == 0) st_flag(&H.slots[tile], epoch);
+}
+
+template <bool Q4, int HK>
 __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x, int d,
                                                        const h16* __restrict__ P1,
                                                        const float* __restrict__ b1, int relu, int r,
@@ -121,15 +316,29 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ count, const float* __restrict__ zero,
                                                        int hot, int NA, const h16* __restrict__ s1,
-                                                       const h16* __restrict__ s2) {
+                                                       const h16* __restrict__ s2, HotArgs H) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
     __shared__ uint32_t s_part[8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int NT = (ffn + kLTile - 1) / kLTile;
+    const int NHU = HK >= 0 ? H.NHU : 0;
+    const int b = blockIdx.x;
+    const int lg0 = NA + NHU;   // first logits tile
+    if constexpr (HK >= 0) {
+        if (b >= NA && b < lg0) {
+            hot_up_role<HK>(H, x, d, b - NA, sh, zero);
+            return;
+        }
+        if (b > lg0 + NT) {
+            __shared__ int s_hflag;
+            hot_down_role(H, d, b - (lg0 + NT + 1), sh, &s_hflag);
+            return;
+        }
+    }
 
-    if ((int)blockIdx.x < NA) {
+    if (b < NA) {
         // ---------------- hidden rows
         const int row = blockIdx.x * 4 + wave;
         const bool valid = row < r;
@@ -186,9 +395,11 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             if (valid && lane == 0) st_tag(&htag[row], epoch, __float_as_uint(relu ? fmaxf(sum, 0.f) : sum));
             return;
         }
-        u32x4 w[16];
+        // 18 chunks per lane: a row of d <= 9216 is requested in one round
+        constexpr int HU = 18;
+        u32x4 w[HU];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
+        for (int u = 0; u < HU; ++u)
             if (lane + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(lane + u * 64) * 8);
         const uint32_t stored = *epoch_word;
         const float bias = *(b1 ? b1 + min(row, r - 1) : zero);
@@ -199,14 +410,14 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         for (int i = tid + 1024; i < nch; i += 256) sx[i] = ld16(x + (size_t)i * 8);   // d > 8192
         __syncthreads();
         float acc = 0.f;
-        for (int c0 = lane; c0 < nch; c0 += 64 * 16) {
+        for (int c0 = lane; c0 < nch; c0 += 64 * HU) {
             if (c0 != lane) {
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
+                for (int u = 0; u < HU; ++u)
                     if (c0 + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(c0 + u * 64) * 8);
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < HU; ++u) {
                 const int c = c0 + u * 64;
                 if (c < nch) acc = dot8_h(w[u], sx[c], acc);
             }
@@ -217,7 +428,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         return;
     }
 
-    if ((int)blockIdx.x == NA + NT) {
+    if (b == lg0 + NT) {
         // ---------------- ordered compaction, 1024 tiles per round: thread k
         // takes tiles 2k and 2k + 1 of each half of the round, one block-wide
         // scan per half.  The dense front of a hot-first layer then spreads
@@ -287,7 +498,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     // ---------------- logits tile: wave w owns neurons tile*32 + 8w + k (k < 8); lane l
     // takes chunks l + 64m of all eight rows, so an h chunk read from LDS serves
     // eight rows
-    const int tile = blockIdx.x - NA;
+    const int tile = b - lg0;
     if ((tile + 1) * kLTile <= hot) {
         // a tile of the always-listed hot prefix (hot is a multiple of 32):
         // every neuron on, no P2 row read, no wait for h
@@ -496,7 +707,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
                                                             const float* __restrict__ bg,
                                                             const h16* __restrict__ Wd,
                                                             const int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ count, int NU,
+                                                            const int32_t* __restrict__ count, int skip, int NU,
                                                             int T, int G, uint64_t* __restrict__ atag,
                                                             float* __restrict__ partial,
                                                             uint32_t* __restrict__ ctr, uint32_t* __restrict__ slots,
@@ -518,12 +729,16 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int craw = count[0];   // negative: the predictor's overrun report, answered with NaN in y
     const int cnt = min(max(craw, 0), ffn);
-    const int PU = (cnt + NU - 1) / NU;   // list positions per up chunk
+    // list positions [0, sk) are the hot prefix, computed by the predictor's kernel
+    // (skip > 0); this launch takes [sk, cnt) and adds the prefix's sum to y
+    const int sk = min(max(skip, 0), cnt);
+    const int nl = cnt - sk;
+    const int PU = (nl + NU - 1) / NU;   // list positions per up chunk
 
     if ((int)blockIdx.x < NU) {
         // ---------------- up chunk: one wave per active row
         const int u = blockIdx.x;
-        const int j0 = min(cnt, u * PU), j1 = min(cnt, j0 + PU);
+        const int j0 = sk + min(nl, u * PU), j1 = min(cnt, j0 + PU);
         if (j0 >= j1) return;
         constexpr int UU = Q4 ? (REGLU ? 2 : 4) : (REGLU ? 8 : 16);   // 16-byte chunks per lane per batch
         const int nch = d >> 3;                     // 8-weight x chunks
@@ -632,10 +847,10 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     // Chunks in use: as many as give every row group at most one batch of
     // rows (the launch has G, the most).  Fewer, fuller chunks stream better,
     // and a second, mostly empty batch would cost as much as a full one.
-    const int Ge = min(G, max(1, (cnt + kSChunkRows - 1) / kSChunkRows));
+    const int Ge = min(G, max(1, (nl + kSChunkRows - 1) / kSChunkRows));
     if (chunk >= Ge) return;
-    const int PD = (cnt + Ge - 1) / Ge;
-    const int j0 = min(cnt, chunk * PD), j1 = min(cnt, j0 + PD);
+    const int PD = (nl + Ge - 1) / Ge;
+    const int j0 = sk + min(nl, chunk * PD), j1 = min(cnt, j0 + PD);
     const int ct = tid % kSColThreads;
     const int rg = __builtin_amdgcn_readfirstlane(tid / kSColThreads);
     const int col = tile * kFusedCols + ct * 8;
@@ -734,14 +949,16 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     if (!s_flag || tid >= kFusedCols || gc >= d) return;
 
     // the tile's last chunk: add the G partials in chunk order, all loads in one round
-    // the partial buffer holds kFusedMaxChunks chunks, so every load is in bounds
-    float v[kFusedMaxChunks];
+    // the partial buffer holds kFusedMaxChunks + 1 chunks, so every load is in bounds;
+    // the last slot is the hot prefix's sum, written by the predictor's kernel
+    float v[kFusedMaxChunks + 1];
 #pragma unroll
-    for (int g = 0; g < kFusedMaxChunks; ++g) v[g] = ld_coherent(&partial[(size_t)g * d + gc]);
+    for (int g = 0; g < kFusedMaxChunks + 1; ++g) v[g] = ld_coherent(&partial[(size_t)g * d + gc]);
     float sum = 0.f;
 #pragma unroll
     for (int g = 0; g < kFusedMaxChunks; ++g)
         if (g < Ge) sum += v[g];
+    if (skip > 0) sum += v[kFusedMaxChunks];
     y[gc] = craw < 0 ? __builtin_nanf("") : sum;
     // every chunk of this tile has read the epoch: the tile's slot advances
     if (tid == 0) st_flag(&slots[tile], epoch);
@@ -773,7 +990,7 @@ hipError_t launch_sparse_fused_q4(int kind, const h16* x, int d, int ffn, const 
     dim3 grid(L.NU + L.T * L.G);
 #define PI_SFQ(K)                                                                                                    \
     hipLaunchKernelGGL((k_sparse_fused<K, true>), grid, dim3(kSThreads), 0, s, x, d, ffn, wu, bup, wg, bg, wd, idx, \
-                       count, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero, su, sg, sd)
+                       count, 0, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero, su, sg, sd)
     if (kind == 2) PI_SFQ(2);
     else if (kind == 1) PI_SFQ(1);
     else PI_SFQ(0);
@@ -790,9 +1007,9 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
     const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
-    hipLaunchKernelGGL(k_predict_fused<false>, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2,
-                       b2, ffn, thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero,
-                       hot, NA, nullptr, nullptr);
+    hipLaunchKernelGGL((k_predict_fused<false, -1>), dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu,
+                       r, P2, b2, ffn, thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count,
+                       zero, hot, NA, nullptr, nullptr, HotArgs{});
     return hipGetLastError();
 }
 
@@ -805,17 +1022,56 @@ hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const
     const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
-    hipLaunchKernelGGL(k_predict_fused<true>, dim3(NA + L.NT + 1), dim3(256), shm, s, x, d,
+    hipLaunchKernelGGL((k_predict_fused<true, -1>), dim3(NA + L.NT + 1), dim3(256), shm, s, x, d,
                        reinterpret_cast<const h16*>(q1), b1, (int)relu, r, reinterpret_cast<const h16*>(q2), b2, ffn,
                        thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot,
-                       NA, s1, s2);
+                       NA, s1, s2, HotArgs{});
+    return hipGetLastError();
+}
+
+hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
+                                    const h16* P2, const float* b2, int ffn, int hot, float thr,
+                                    const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
+                                    const h16* Wup, const float* bup, const h16* Wg, const float* bg, const h16* Wd,
+                                    const HotLayout& HL, char* hot_area, float* ffn_partial, hipStream_t s) {
+    uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
+    uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
+    const int NA = hidden_workgroups(r, ffn, hot);
+    // LDS: x (hidden rows, hot up rows), h (logits), the hot W_down row-group sums
+    size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
+    if (shm < (size_t)kHotGroups * kHotCols * 4) shm = (size_t)kHotGroups * kHotCols * 4;
+    const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
+    HotArgs H{};
+    H.Wu = Wup;
+    H.bu = bup;
+    H.Wg = Wg;
+    H.bg = bg;
+    H.Wd = Wd;
+    H.atag = reinterpret_cast<uint64_t*>(hot_area + HL.atag);
+    H.partial = reinterpret_cast<float*>(hot_area + HL.partial);
+    H.ctr = reinterpret_cast<uint32_t*>(hot_area + HL.ctr);
+    H.slots = reinterpret_cast<uint32_t*>(hot_area + HL.slots);
+    H.yhot = ffn_partial + (size_t)kFusedMaxChunks * d;
+    H.n = hot;
+    H.NHU = hot > 0 ? ((hot + 3) / 4 < kHotUpMaxWG ? (hot + 3) / 4 : kHotUpMaxWG) : 0;
+    H.G = hot > 0 ? hot_chunks(hot) : 0;
+    H.T = HL.T;
+    const dim3 grid(NA + H.NHU + L.NT + 1 + H.T * H.G);
+#define PI_PH(K)                                                                                                    \
+    hipLaunchKernelGGL((k_predict_fused<false, K>), grid, dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn, \
+                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot, NA, \
+                       nullptr, nullptr, H)
+    if (kind == 2) PI_PH(2);
+    else if (kind == 1) PI_PH(1);
+    else PI_PH(0);
+#undef PI_PH
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
-                               char* data, hipStream_t s) {
+                               char* data, hipStream_t s, int skip) {
     uint64_t* atag = reinterpret_cast<uint64_t*>(data + L.atag);
     float* partial = reinterpret_cast<float*>(data + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_ctr);
@@ -824,7 +1080,7 @@ hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16
     dim3 grid(L.NU + L.T * L.G);
 #define PI_SF(K)                                                                                               \
     hipLaunchKernelGGL(k_sparse_fused<K>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx, count, \
-                       L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero)
+                       skip, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero)
     if (kind == 2) PI_SF(2);
     else if (kind == 1) PI_SF(1);
     else PI_SF(0);

@@ -196,6 +196,74 @@ def decode(layer: dict, x: torch.Tensor, y: Optional[torch.Tensor] = None,
     return y, idx, count
 
 
+def decode_hot(layer: dict, x: torch.Tensor, n_hot: int, y: Optional[torch.Tensor] = None,
+               idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+               act: str = "relu", tau: Optional[float] = None, per_token: bool = False,
+               check_idx: bool = False, stream=None):
+    """One decode step of a hot-first layer through pi_ffn_decode_hot: neurons
+    [0, n_hot) always listed (their FFN computed beside the predictor for a
+    single token), the rest predicted.  Returns (y, idx, count)."""
+    Bt, d = x.shape
+    ffn, r = layer["ffn"], layer["r"]
+    if y is None:
+        y = torch.empty(Bt, d, dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty(Bt, ffn, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(Bt, dtype=torch.int32, device=x.device)
+    nbytes = B.pi_workspace_size(B.PI_OP_DECODE_HOT, Bt, d, r, ffn)
+    ws, wsb = workspace("decode_hot" if Bt == 1 else "decode_hot_batch", x.device).get(nbytes)
+    st = B.pi_ffn_decode_hot(B.KINDS[layer["kind"]], _bits(x), Bt, d, ffn, layer["P1"], layer.get("b1"),
+                             B.ACTS[act], layer["P2"], layer.get("b2"), r, int(n_hot),
+                             float(layer["tau"] if tau is None else tau), layer["W_up"], layer.get("b_up"),
+                             layer.get("W_gate"), layer.get("b_gate"), layer["W_down"], idx, count, y,
+                             (B.PI_PER_TOKEN if per_token else 0) | (B.PI_CHECK_IDX if check_idx else 0),
+                             ws, wsb, stream)
+    B.check(st, "pi_ffn_decode_hot")
+    return y, idx, count
+
+
+def hot_workspace(layer: dict, device=None) -> torch.Tensor:
+    """A fresh zero-filled workspace for the single-token hot decode of this
+    layer's shape (for callers that keep one per layer)."""
+    nbytes = B.pi_workspace_size(B.PI_OP_DECODE_HOT, 1, layer["d"], layer["r"], layer["ffn"])
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device or layer["W_up"].device)
+
+
+def decode_hot_begin(layer: dict, x: torch.Tensor, n_hot: int, idx: torch.Tensor, count: torch.Tensor,
+                     ws: Optional[torch.Tensor] = None, act: str = "relu", tau: Optional[float] = None,
+                     stream=None):
+    """First launch of a single-token hot decode step (pi_ffn_decode_hot_begin):
+    the list into idx / count and the hot prefix's FFN sum into the workspace."""
+    d, ffn, r = layer["d"], layer["ffn"], layer["r"]
+    if ws is None:
+        ws, wsb = workspace("decode_hot", x.device).get(B.pi_workspace_size(B.PI_OP_DECODE_HOT, 1, d, r, ffn))
+    else:
+        wsb = ws.numel()
+    st = B.pi_ffn_decode_hot_begin(B.KINDS[layer["kind"]], _bits(x), d, ffn, layer["P1"], layer.get("b1"), B.ACTS[act],
+                                   layer["P2"], layer.get("b2"), r, int(n_hot),
+                                   float(layer["tau"] if tau is None else tau), layer["W_up"], layer.get("b_up"),
+                                   layer.get("W_gate"), layer.get("b_gate"), layer["W_down"], idx, count, ws, wsb,
+                                   stream)
+    B.check(st, "pi_ffn_decode_hot_begin")
+
+
+def decode_hot_end(layer: dict, x: torch.Tensor, n_hot: int, idx: torch.Tensor, count: torch.Tensor,
+                   y: torch.Tensor, ws: Optional[torch.Tensor] = None, check_idx: bool = False, stream=None):
+    """Second launch (pi_ffn_decode_hot_end): the FFN over the list from n_hot on,
+    plus the prefix's sum left by decode_hot_begin on the same workspace."""
+    d, ffn, r = layer["d"], layer["ffn"], layer["r"]
+    if ws is None:
+        ws, wsb = workspace("decode_hot", x.device).get(B.pi_workspace_size(B.PI_OP_DECODE_HOT, 1, d, r, ffn))
+    else:
+        wsb = ws.numel()
+    st = B.pi_ffn_decode_hot_end(B.KINDS[layer["kind"]], _bits(x), d, ffn, r, int(n_hot), layer["W_up"],
+                                 layer.get("b_up"), layer.get("W_gate"), layer.get("b_gate"), layer["W_down"], idx,
+                                 count, y, B.PI_CHECK_IDX if check_idx else 0, ws, wsb, stream)
+    B.check(st, "pi_ffn_decode_hot_end")
+    return y
+
+
 def profile(X: torch.Tensor, W_fire: torch.Tensor, b_fire: Optional[torch.Tensor],
             counts: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     n, d = X.shape

@@ -62,7 +62,9 @@ MEASURED_TRAFFIC = {
     "bytes_per_launch": {},
 }
 
-KERNEL_OF = {"pi_ffn_predict": "k_predict_fused", "pi_ffn_sparse": "k_sparse_fused"}   # one kernel each at B = 1
+# one kernel each at B = 1
+KERNEL_OF = {"pi_ffn_predict": "k_predict_fused", "pi_ffn_sparse": "k_sparse_fused",
+             "pi_ffn_decode_hot_begin": "k_predict_fused", "pi_ffn_decode_hot_end": "k_sparse_fused"}
 
 
 def kernel_source_hash():
@@ -96,6 +98,19 @@ def touched_bytes(kind, d, r, ffn, count, n_hot=0):
 
 def predict_bytes(d, r, ffn, count, n_hot=0):
     return 2 * r * d + (ffn - n_hot) * (2 * r + 4) + 2 * d + 4 * count
+
+
+def hot_begin_bytes(kind, d, r, ffn, count, n_hot):
+    """The first launch of a hot decode step: the predictor (prefix rows of P2
+    skipped) and the prefix's FFN rows."""
+    m = 1 if kind == "relu" else 2
+    return predict_bytes(d, r, ffn, count, n_hot) + (m + 1) * n_hot * 2 * d + 4 * n_hot
+
+
+def hot_end_bytes(kind, d, count, n_hot):
+    """The second launch: the predicted rows after the prefix, the list and x, y."""
+    m = 1 if kind == "relu" else 2
+    return (m + 1) * (count - n_hot) * 2 * d + 4 * (count - n_hot) + 4 * count + 4 * d
 
 
 def sparse_bytes(kind, d, count):
@@ -256,8 +271,7 @@ def stack_headline(cfg, args, dev, log_fn):
     y = torch.empty(NLs, d, dtype=torch.float32, device=dev)
 
     def layer_step(l, x):
-        R.predict(layers[l], x, idx[l:l + 1], cnt[l:l + 1], n_hot=hots[l])
-        R.sparse(layers[l], x, idx[l:l + 1], cnt[l:l + 1], y[l:l + 1])
+        R.decode_hot(layers[l], x, hots[l], y[l:l + 1], idx[l:l + 1], cnt[l:l + 1])
 
     # list lengths of every (layer, token) the steps use, for the byte accounting
     counts = torch.empty(NLs, ng, dtype=torch.int32, device=dev)
@@ -308,31 +322,49 @@ def stack_headline(cfg, args, dev, log_fn):
            f"T {T_mean / 1e6:.1f} MB -> {T_mean / layer_us / 1e3:.0f} GB/s")
     del graphs
 
-    # ---- per entry point: a graph of one launch per layer, back to back
+    # ---- per kernel: the step's two launches as separate entry points
+    # (pi_ffn_decode_hot_begin, pi_ffn_decode_hot_end), one workspace per layer;
+    # a graph of one launch per layer, back to back, for each
     reps = 10
+    wss = [R.hot_workspace(layers[l]) for l in range(NLs)]
 
-    def run_pred():
+    def run_begin():
         for l in range(NLs):
-            R.predict(layers[l], xs[l][0], idx[l:l + 1], cnt[l:l + 1], n_hot=hots[l])
+            R.decode_hot_begin(layers[l], xs[l][0], hots[l], idx[l:l + 1], cnt[l:l + 1], ws=wss[l])
 
-    def run_sparse():
+    def run_end():
         for l in range(NLs):
-            R.sparse(layers[l], xs[l][0], idx[l:l + 1], cnt[l:l + 1], y[l:l + 1])
+            R.decode_hot_end(layers[l], xs[l][0], hots[l], idx[l:l + 1], cnt[l:l + 1], y[l:l + 1], ws=wss[l])
 
-    run_pred()
+    run_begin()
     torch.cuda.synchronize()
     c0 = cnt.cpu().numpy()
-    g = GraphTimer(run_pred)
-    ms_pred = g.time(reps) / NLs
+    g = GraphTimer(run_begin)
+    ms_begin = g.time(reps) / NLs
     g.release()
-    g = GraphTimer(run_sparse)
-    ms_sp = g.time(reps) / NLs
+    g = GraphTimer(run_end)
+    ms_end = g.time(reps) / NLs
     g.release()
-    pb = float(np.mean([predict_bytes(d, r, ffn, int(c0[l]), hots[l]) for l in range(NLs)]))
-    sb = float(np.mean([sparse_bytes(kind, d, int(c0[l])) for l in range(NLs)]))
-    stages = {"pi_ffn_predict": (ms_pred, pb / ms_pred / 1e6, pb), "pi_ffn_sparse": (ms_sp, sb / ms_sp / 1e6, sb)}
-    log_fn(f"stack kernels: predict {ms_pred * 1000:.2f} us ({stages['pi_ffn_predict'][1]:.0f} GB/s), "
-           f"sparse {ms_sp * 1000:.2f} us ({stages['pi_ffn_sparse'][1]:.0f} GB/s) per launch")
+    bb = float(np.mean([hot_begin_bytes(kind, d, r, ffn, int(c0[l]), hots[l]) for l in range(NLs)]))
+    eb = float(np.mean([hot_end_bytes(kind, d, int(c0[l]), hots[l]) for l in range(NLs)]))
+    stages = {"pi_ffn_decode_hot_begin": (ms_begin, bb / ms_begin / 1e6, bb),
+              "pi_ffn_decode_hot_end": (ms_end, eb / ms_end / 1e6, eb)}
+    del wss
+    log_fn(f"stack kernels: begin (predictor + hot prefix) {ms_begin * 1000:.2f} us "
+           f"({stages['pi_ffn_decode_hot_begin'][1]:.0f} GB/s on {bb / 1e6:.1f} MB), end (FFN rest) "
+           f"{ms_end * 1000:.2f} us ({stages['pi_ffn_decode_hot_end'][1]:.0f} GB/s on {eb / 1e6:.1f} MB) per launch")
+
+    # ---- the same steps as two calls (pi_ffn_predict_hot + pi_ffn_sparse: the
+    # prefix's rows gathered with the rest), for comparison
+    def run_two_calls():
+        for l in range(NLs):
+            R.predict(layers[l], xs[l][0], idx[l:l + 1], cnt[l:l + 1], n_hot=hots[l])
+            R.sparse(layers[l], xs[l][0], idx[l:l + 1], cnt[l:l + 1], y[l:l + 1])
+
+    g = GraphTimer(run_two_calls)
+    ms_two = g.time(reps) / NLs
+    g.release()
+    log_fn(f"stack: the same layer steps as pi_ffn_predict_hot + pi_ffn_sparse: {ms_two * 1000:.2f} us")
 
     # ---- dense baselines over the same layers, one token each, graph-timed
     dense = None
@@ -374,6 +406,8 @@ def stack_headline(cfg, args, dev, log_fn):
                  "hot80_mean": float(np.mean(hot80)), "mean_active": float(counts_h.mean()),
                  "resident_GB": NLs * ((m + 1) * ffn * d * 2 + r * d * 2 + ffn * r * 2) / 1e9,
                  "step_graphs": ng,
+                 "entry_point": "pi_ffn_decode_hot (the prefix's FFN beside the predictor)",
+                 "two_calls_us_per_layer_step": ms_two * 1000,
                  "prompt": {"tokens": P, "ms": prompt_ms, "tokens_per_s": P * 1000.0 / prompt_ms,
                             "us_per_layer": prompt_ms * 1000.0 / NLs, "method": "one graph of all layers"},
                  "decode_tokens_per_s": K * 1000.0 / total_ms},
@@ -779,7 +813,8 @@ def main():
                      "stages_us": {k: v[0] * 1000 for k, v in st.items()},
                      "stages_GBs": {k: v[1] for k, v in st.items()},
                      "stages_method": f"graph of {cfg.layers} back-to-back launches of one entry point "
-                                      f"(one per layer), replayed 10 times between HIP events"},
+                                      f"(one per layer, one workspace each), replayed 10 times between HIP "
+                                      f"events on the graph's stream"},
         "dense_baseline": head["dense"],
         "cpu_baseline": cpu,
         "stack": head["info"],

@@ -78,7 +78,8 @@ typedef enum pi_op {
     PI_OP_PREDICT = 0,
     PI_OP_SPARSE = 1,
     PI_OP_PROFILE = 2,
-    PI_OP_DECODE = 3
+    PI_OP_DECODE = 3,
+    PI_OP_DECODE_HOT = 4
 } pi_op;
 
 /* pi_ffn_sparse flags */
@@ -224,6 +225,67 @@ pi_status pi_ffn_decode(int kind, const pi_half* x, int B, int d, int ffn,
                         const pi_half* W_down,
                         int32_t* idx, int32_t* count, float* y, uint32_t flags,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * pi_ffn_decode_hot -- one decode step of a hot-first layer: pi_ffn_predict_hot
+ * (neurons [0, n_hot) always listed, the rest predicted) followed by
+ * pi_ffn_sparse on its list.
+ *
+ * After the offline profile and the hot-first reorder, the neurons at the
+ * front fire on nearly every token: the hot neurons that the pages place
+ * first and keep resident (Part A section 2.3, modules 1-2; Part B).  Their
+ * rows do not depend on the prediction, so for a single token (B = 1) their
+ * FFN runs inside the predictor's kernel, beside the predictor's weight
+ * stream instead of behind it: extra workgroups compute a_i for i < n_hot
+ * and accumulate sum_{i < n_hot} a_i W_down[i, :], and the FFN kernel that
+ * follows takes the list from position n_hot on and adds that sum.
+ *
+ * Results: idx and count exactly as pi_ffn_predict_hot writes them (the
+ * prefix, then the predicted neurons); y is the FFN over that whole list, as
+ * pi_ffn_sparse computes it, up to the order of the fp32 sums (the prefix's
+ * part is summed separately and added once per output).  For B >= 2 the call
+ * is pi_ffn_predict_hot then pi_ffn_sparse (the union path), bitwise.
+ * Arguments, flags and checks: as pi_ffn_decode, plus n_hot as in
+ * pi_ffn_predict_hot (INVALID_ARG outside [0, ffn], UNSUPPORTED when not a
+ * multiple of 32).  n_hot = 0 computes what pi_ffn_decode computes.
+ *
+ * ws: at least pi_workspace_size(PI_OP_DECODE_HOT, B, d, r, ffn) bytes (the
+ * workspace rules above apply).
+ */
+pi_status pi_ffn_decode_hot(int kind, const pi_half* x, int B, int d, int ffn,
+                            const pi_half* P1, const float* b1, int act,
+                            const pi_half* P2, const float* b2, int r, int n_hot, float tau,
+                            const pi_half* W_up, const float* b_up,
+                            const pi_half* W_gate, const float* b_gate,
+                            const pi_half* W_down,
+                            int32_t* idx, int32_t* count, float* y, uint32_t flags,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * pi_ffn_decode_hot_begin / pi_ffn_decode_hot_end -- the two launches of
+ * pi_ffn_decode_hot for one token (B = 1), as separate calls, so a caller can
+ * put other work (or timing) between them.  begin: the prediction (idx,
+ * count, as pi_ffn_predict_hot writes them) and the hot prefix's FFN, whose
+ * sum stays in ws; end: the FFN over list positions [n_hot, count) plus that
+ * sum, into y.  end must follow its begin on the same workspace with the same
+ * layer, token, n_hot, idx and count, and no other call on that workspace in
+ * between; begin followed by end computes exactly what pi_ffn_decode_hot
+ * computes (bitwise).  flags of end: PI_CHECK_IDX, PI_DETERMINISTIC.
+ * ws: pi_workspace_size(PI_OP_DECODE_HOT, 1, d, r, ffn) bytes for both.
+ * Errors: as pi_ffn_decode_hot.
+ */
+pi_status pi_ffn_decode_hot_begin(int kind, const pi_half* x, int d, int ffn,
+                                  const pi_half* P1, const float* b1, int act,
+                                  const pi_half* P2, const float* b2, int r, int n_hot, float tau,
+                                  const pi_half* W_up, const float* b_up,
+                                  const pi_half* W_gate, const float* b_gate,
+                                  const pi_half* W_down, int32_t* idx, int32_t* count,
+                                  void* ws, size_t ws_bytes, void* stream);
+pi_status pi_ffn_decode_hot_end(int kind, const pi_half* x, int d, int ffn, int r, int n_hot,
+                                const pi_half* W_up, const float* b_up,
+                                const pi_half* W_gate, const float* b_gate,
+                                const pi_half* W_down, const int32_t* idx, const int32_t* count,
+                                float* y, uint32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * pi_ffn_decode_noalloc -- pi_ffn_decode for callers that cannot allocate

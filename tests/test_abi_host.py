@@ -318,3 +318,15 @@ def test_quantize_rows_rejects_before_launch():
     assert B.pi_quantize_rows(A, 4, 64, A + 8, W, stream=0) == B.PI_ERR_UNSUPPORTED
     assert B.pi_quantize_rows(A, 4, 64, A, W + 1, stream=0) == B.PI_ERR_UNSUPPORTED
     assert B.pi_quantize_rows(A, 4, 32768, A, W, stream=0) == B.PI_ERR_UNSUPPORTED
+
+
+def test_decode_hot_rejects_before_launch():
+    args = dict(kind=B.PI_FFN_RELU, x=A, B=1, d=64, ffn=128, P1=A, b1=None, act=B.PI_ACT_RELU, P2=A, b2=None, r=16,
+                n_hot=0, tau=0.5, W_up=A, b_up=None, W_gate=None, b_gate=None, W_down=A, idx=A, count=A, y=A,
+                flags=0, ws=A, ws_bytes=0, stream=0)
+    for kw, code in ((dict(n_hot=160), B.PI_ERR_INVALID_ARG), (dict(n_hot=-32), B.PI_ERR_INVALID_ARG),
+                     (dict(n_hot=48), B.PI_ERR_UNSUPPORTED), (dict(flags=B.PI_DENSE), B.PI_ERR_INVALID_ARG),
+                     (dict(), B.PI_ERR_WORKSPACE)):
+        a = dict(args)
+        a.update(kw)
+        assert B.pi_ffn_decode_hot(*a.values()) == code, kw
