@@ -28,6 +28,18 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 
 __device__ __forceinline__ f16x2 as_h2(unsigned int v) { return __builtin_bit_cast(f16x2, v); }
 
+// A buffer resource over `bytes` bytes at base (raw: stride 0, 32-bit data
+// format).  Loads through it take one per-lane offset register and a scalar
+// offset, and a 16-byte load at or past `bytes` returns zeros instead of
+// touching memory, so a row's tail needs no per-lane branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16 bytes at byte offset voff + soff (soff wave-uniform), non-temporal.
+__device__ __forceinline__ u32x4 buf_ld16_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2));
+}
+
 // acc + sum_k w[k] * x[k] over 8 fp16 pairs, fp16 products accumulated in fp32
 // (v_dot2_f32_f16: the products of two fp16 values are exact in fp32).
 __device__ __forceinline__ float dot8_h(u32x4 w, u32x4 x, float acc) {

@@ -8,7 +8,7 @@
 //   next NT workgroups        logits tiles of 32 neurons: collect h, stream the
 //                             tile's P2 rows, z = P2 h + b2 > thr, publish the
 //                             tile's 32-bit mask as a tagged word (a tile of
-//                             the always-listed hot prefix publishes all ones)
+//                             the always-listed hot prefix exits at once)
 //   the next one              gathers every mask and writes idx (ascending) and count
 //   the last T * G            (pi_ffn_decode_hot only) hot-prefix W_down: column
 //                             tile x chunk of the prefix, accumulated from the
@@ -148,7 +148,7 @@ template <int KIND>
 __device__ __forceinline__ void hot_up_role(const HotArgs& H, const h16* __restrict__ x, int d, int u, float* sh,
                                             const float* __restrict__ zero) {
     constexpr bool GATED = KIND != 0;
-    constexpr int UU = GATED ? 8 : 16;   // 16-byte chunks per lane per batch
+    constexpr int UU = GATED ? 9 : 18;   // 16-byte chunks per lane per batch: a row of d <= 9216 in one
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = H.n;
@@ -156,22 +156,23 @@ __device__ __forceinline__ void hot_up_role(const HotArgs& H, const h16* __restr
     const int j0 = min(n, u * PU), j1 = min(n, j0 + PU);
     if (j0 >= j1) return;
     const int nch = d >> 3;
-    u32x4 xs[4];   // x chunks tid + 256 q, requested ahead of the rows
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xs[q] = ld16(x + (size_t)min(tid + q * 256, nch - 1) * 8);
+    // x to LDS by direct-to-LDS loads, 64 chunks a wave (no registers held
+    // across the row batch)
+    const uint32_t sxa = lds_addr(sh);
+    for (int c0 = wave * 64; c0 < nch; c0 += 256) dma16(x + (size_t)min(c0 + lane, nch - 1) * 8, sxa + (uint32_t)c0 * 16u);
+    wait_vm<0>();
     int i = min(j0 + wave, j1 - 1);
     const bool live = j0 + wave < j1;   // wave-uniform
     u32x4 wu[UU], wg[UU];
-    auto issue = [&](int c0) {
-        const h16* ru = H.Wu + (size_t)i * d;
-        const h16* rgp = GATED ? H.Wg + (size_t)i * d : nullptr;
+    auto issue = [&](int c0) {   // c0 = b0 + lane; one buffer resource per row, zeros past its end
+        const uint32_t b0 = (uint32_t)(c0 - lane) * 16u;
+        const auto ru = buf_rsrc(H.Wu + (size_t)i * d, (uint32_t)d * 2u);
 #pragma unroll
-        for (int q = 0; q < UU; ++q) {
-            const int c = c0 + q * 64;
-            if (c < nch) {
-                wu[q] = ld16_stream(ru + (size_t)c * 8);
-                if (GATED) wg[q] = ld16_stream(rgp + (size_t)c * 8);
-            }
+        for (int q = 0; q < UU; ++q) wu[q] = buf_ld16_stream(ru, (uint32_t)lane * 16u, b0 + q * 1024u);
+        if (GATED) {
+            const auto rgp = buf_rsrc(H.Wg + (size_t)i * d, (uint32_t)d * 2u);
+#pragma unroll
+            for (int q = 0; q < UU; ++q) wg[q] = buf_ld16_stream(rgp, (uint32_t)lane * 16u, b0 + q * 1024u);
         }
     };
     float bu = 0.f, bgv = 0.f;
@@ -182,11 +183,7 @@ __device__ __forceinline__ void hot_up_role(const HotArgs& H, const h16* __restr
     issue(lane);
     issue_bias();
     const uint32_t slot = H.slots[min(lane, H.T - 1)];
-    u32x4* sx = reinterpret_cast<u32x4*>(sh);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (tid + q * 256 < nch) sx[tid + q * 256] = xs[q];
-    for (int k = tid + 1024; k < nch; k += 256) sx[k] = ld16(x + (size_t)k * 8);   // d > 8192
+    const u32x4* sx = reinterpret_cast<const u32x4*>(sh);
     __syncthreads();
     if (!live) return;
     for (int j = j0 + wave; j < j1; j += 4) {
@@ -326,6 +323,8 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     const int NHU = HK >= 0 ? H.NHU : 0;
     const int b = blockIdx.x;
     const int lg0 = NA + NHU;   // first logits tile
+    // The hot W_down workgroups come last: placed among the logits tiles (from
+    // any position) they held slots the tiles needed and made the step slower.
     if constexpr (HK >= 0) {
         if (b >= NA && b < lg0) {
             hot_up_role<HK>(H, x, d, b - NA, sh, zero);
@@ -337,6 +336,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             return;
         }
     }
+    const int tile = b - lg0;
 
     if (b < NA) {
         // ---------------- hidden rows
@@ -395,12 +395,13 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             if (valid && lane == 0) st_tag(&htag[row], epoch, __float_as_uint(relu ? fmaxf(sum, 0.f) : sum));
             return;
         }
-        // 18 chunks per lane: a row of d <= 9216 is requested in one round
+        // 18 chunks per lane: a row of d <= 9216 is requested in one round; one
+        // buffer resource per row, chunks past its end load zeros
         constexpr int HU = 18;
+        const auto rp = buf_rsrc(prow, (uint32_t)d * 2u);
         u32x4 w[HU];
 #pragma unroll
-        for (int u = 0; u < HU; ++u)
-            if (lane + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(lane + u * 64) * 8);
+        for (int u = 0; u < HU; ++u) w[u] = buf_ld16_stream(rp, (uint32_t)lane * 16u, u * 1024u);
         const uint32_t stored = *epoch_word;
         const float bias = *(b1 ? b1 + min(row, r - 1) : zero);
         u32x4* sx = reinterpret_cast<u32x4*>(sh);
@@ -413,8 +414,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         for (int c0 = lane; c0 < nch; c0 += 64 * HU) {
             if (c0 != lane) {
 #pragma unroll
-                for (int u = 0; u < HU; ++u)
-                    if (c0 + u * 64 < nch) w[u] = ld16_stream(prow + (size_t)(c0 + u * 64) * 8);
+                for (int u = 0; u < HU; ++u) w[u] = buf_ld16_stream(rp, (uint32_t)lane * 16u, (uint32_t)(c0 - lane + u * 64) * 16u);
             }
 #pragma unroll
             for (int u = 0; u < HU; ++u) {
@@ -429,16 +429,17 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     }
 
     if (b == lg0 + NT) {
-        // ---------------- ordered compaction, 1024 tiles per round: thread k
-        // takes tiles 2k and 2k + 1 of each half of the round, one block-wide
-        // scan per half.  The dense front of a hot-first layer then spreads
-        // over many threads (each writes its tiles' ids one by one, and a wave
-        // runs as long as its busiest lane), while two write loops keep the
-        // cost on an unordered layer low.
+        // ---------------- ordered compaction.  The always-listed prefix [0, hot)
+        // is written first, by every thread in turn (coalesced, no mask read).
+        // The other tiles go 1024 per round: thread k takes tiles 2k and 2k + 1
+        // of each half of the round, one block-wide scan per half, and writes
+        // its tiles' ids one by one (a wave runs as long as its busiest lane;
+        // two write loops keep the cost on an unordered layer low).
         const uint32_t epoch = next_epoch(*epoch_word);
-        uint32_t base = 0;
+        for (int j = tid; j < hot; j += 256) idx[j] = j;
+        uint32_t base = (uint32_t)hot;
         bool good = true;
-        for (int t0 = 0; t0 < NT; t0 += 1024) {
+        for (int t0 = hot / kLTile; t0 < NT; t0 += 1024) {
             uint64_t m4[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + (q >> 1) * 512 + tid * 2 + (q & 1), NT - 1)]);
@@ -487,9 +488,10 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         good = __syncthreads_and(good);
         if (tid == 0) {
             count[0] = good ? (int32_t)base : -1;
-            // every other workgroup has read the epoch: each logits tile has
-            // published its mask, and a tile outside the prefix only after
-            // every hidden row its h (without such a tile no hidden row runs)
+            // every other workgroup that reads the epoch has read it: each
+            // logits tile outside the prefix has published its mask, after
+            // every hidden row its h (without such a tile no hidden row runs;
+            // the prefix's tiles read nothing)
             st_flag(epoch_word, epoch);
         }
         return;
@@ -498,11 +500,10 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     // ---------------- logits tile: wave w owns neurons tile*32 + 8w + k (k < 8); lane l
     // takes chunks l + 64m of all eight rows, so an h chunk read from LDS serves
     // eight rows
-    const int tile = b - lg0;
     if ((tile + 1) * kLTile <= hot) {
         // a tile of the always-listed hot prefix (hot is a multiple of 32):
-        // every neuron on, no P2 row read, no wait for h
-        if (tid == 0) st_tag(&mtag[tile], next_epoch(*epoch_word), 0xFFFFFFFFu);
+        // every neuron on, which the compaction writes without a mask; no P2
+        // row read, no wait for h
         return;
     }
     const int row0 = tile * kLTile + wave * kLRows;   // wave-uniform
@@ -740,7 +741,8 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         const int u = blockIdx.x;
         const int j0 = sk + min(nl, u * PU), j1 = min(cnt, j0 + PU);
         if (j0 >= j1) return;
-        constexpr int UU = Q4 ? (REGLU ? 2 : 4) : (REGLU ? 8 : 16);   // 16-byte chunks per lane per batch
+        // 16-byte chunks per lane per batch: an fp16 row of d <= 9216 goes out in one round
+        constexpr int UU = Q4 ? (REGLU ? 2 : 4) : (REGLU ? 9 : 18);
         const int nch = d >> 3;                     // 8-weight x chunks
         const int ncw = Q4 ? d >> 5 : nch;          // 16-byte weight chunks of a row
         const int ng = d >> 6;                      // INT4 scale groups of a row
@@ -748,7 +750,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         int i = 0;
         u32x4 wu[UU], wg[UU];
         h16 cu[UU], cg[UU];   // INT4: the chunks' scales, converted at use
-        auto issue = [&](int c0) {
+        auto issue = [&](int c0) {   // c0 = b0 + lane, b0 the batch's first chunk (uniform)
             if constexpr (Q4) {
                 // slots past the row end read its last chunk (valid, unused):
                 // no branch around a load, so no load waits for another
@@ -765,15 +767,15 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
                     }
                 }
             } else {
-                const h16* ru = Wup + (size_t)i * d;
-                const h16* rg = REGLU ? Wg + (size_t)i * d : nullptr;
+                // one buffer resource per row: chunks past the row end load zeros
+                const auto ru = buf_rsrc(Wup + (size_t)i * d, (uint32_t)d * 2u);
+                const uint32_t b0 = (uint32_t)(c0 - lane) * 16u;
 #pragma unroll
-                for (int q = 0; q < UU; ++q) {
-                    const int c = c0 + q * 64;
-                    if (c < ncw) {
-                        wu[q] = ld16_stream(ru + (size_t)c * 8);
-                        if (REGLU) wg[q] = ld16_stream(rg + (size_t)c * 8);
-                    }
+                for (int q = 0; q < UU; ++q) wu[q] = buf_ld16_stream(ru, (uint32_t)lane * 16u, b0 + q * 1024u);
+                if (REGLU) {
+                    const auto rg = buf_rsrc(Wg + (size_t)i * d, (uint32_t)d * 2u);
+#pragma unroll
+                    for (int q = 0; q < UU; ++q) wg[q] = buf_ld16_stream(rg, (uint32_t)lane * 16u, b0 + q * 1024u);
                 }
             }
         };
@@ -782,24 +784,27 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
             bu = *(bup ? bup + i : zero);
             if (REGLU) bgv = *(bg ? bg + i : zero);
         };
-        u32x4 xs[2];   // x chunks tid + 512 q, requested ahead of the rows
-#pragma unroll
-        for (int q = 0; q < 2; ++q) xs[q] = ld16(x + (size_t)min(tid + q * kSThreads, nch - 1) * 8);
+        // x goes to LDS by direct-to-LDS loads (no registers held across the
+        // row batch: a d = 9216 row then fits one batch of 18 chunks per
+        // lane).  The row ids are needed before the rows can go out, so
+        // waiting for both costs nothing the rows did not wait for anyway.
+        const uint32_t sxa = lds_addr(s_x);
+        for (int c0 = wave * 64; c0 < nch; c0 += kSThreads)   // 64 chunks a wave, lane l chunk c0 + l
+            dma16(x + (size_t)min(c0 + lane, nch - 1) * 8, sxa + (uint32_t)c0 * 16u);
         const bool live = j < j1;   // wave-uniform
-        i = min(max(idx[min(j, j1 - 1)], 0), ffn - 1);
-        issue(lane);
+        // the row id is wave-uniform: kept in a scalar register, the row's loads
+        // take one base and per-lane offsets
+        i = __builtin_amdgcn_readfirstlane(min(max(idx[min(j, j1 - 1)], 0), ffn - 1));
         issue_bias();
+        wait_vm<0>();
+        issue(lane);
         const uint32_t slot = slots[min(lane, T - 1)];
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            if (tid + q * kSThreads < nch) s_x[tid + q * kSThreads] = xs[q];
-        for (int k = tid + 2 * kSThreads; k < nch; k += kSThreads) s_x[k] = ld16(x + (size_t)k * 8);   // d > 8192
         __syncthreads();
         if (!live) return;
         bool first = true;
         for (; j < j1; j += kSThreads / 64) {
             if (!first) {
-                i = min(max(idx[j], 0), ffn - 1);
+                i = __builtin_amdgcn_readfirstlane(min(max(idx[j], 0), ffn - 1));
                 issue(lane);
                 issue_bias();
             }
@@ -1037,8 +1042,10 @@ hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
     const int NA = hidden_workgroups(r, ffn, hot);
-    // LDS: x (hidden rows, hot up rows), h (logits), the hot W_down row-group sums
-    size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
+    // LDS: x (hidden rows; hot up rows, staged in whole 64-chunk blocks of 1 KB),
+    // h (logits), the hot W_down row-group sums
+    size_t shm = (size_t)((d * 2 + 1023) / 1024) * 1024;
+    if (shm < (size_t)r * 4) shm = (size_t)r * 4;
     if (shm < (size_t)kHotGroups * kHotCols * 4) shm = (size_t)kHotGroups * kHotCols * 4;
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     HotArgs H{};

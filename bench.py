@@ -57,9 +57,9 @@ HBM_PEAK_GBS = 8000.0
 MEASURED_TRAFFIC = {
     # the sources the single-token kernels are built from, hashed in this order
     "sources": ["activation_sparse_predictor_amd/csrc/fused.hip", "activation_sparse_predictor_amd/csrc/common.hpp"],
-    "sha256_16": None,
+    "sha256_16": "2ef76d0fe504e5bb",
     "config": "c5",
-    "bytes_per_launch": {},
+    "bytes_per_launch": {"pi_ffn_decode_hot_begin": 1.464e+08, "pi_ffn_decode_hot_end": 8.484e+07},
 }
 
 # one kernel each at B = 1
@@ -503,9 +503,9 @@ def layer_line(cfg_key, nl, nt, reps, no_dense, log_fn):
 
 def profile_run(cfg, nl, dev):
     """The workload the hardware-counter passes run: nl hot-first layers of the
-    stack (profiled, reordered), a few warm-up steps, one counted pass of decode
-    steps over every layer, then identity row copies of a known size whose
-    FETCH_SIZE / WRITE_SIZE calibrate the counters."""
+    stack (profiled, reordered), 2 warm-up and 8 counted hot decode steps
+    (pi_ffn_decode_hot) per layer, then identity row copies of a known size
+    whose FETCH_SIZE / WRITE_SIZE calibrate the counters."""
     import torch
     from activation_sparse_predictor_amd import runtime as R
     from synthetic import make_tokens
@@ -519,8 +519,7 @@ def profile_run(cfg, nl, dev):
     for s in range(nl * 2 + nl * 8):
         l, t = s % nl, (s // nl) % 8
         x = toks[l][t:t + 1].contiguous()
-        R.predict(layers[l], x, idx, cnt, n_hot=hots[l])
-        R.sparse(layers[l], x, idx, cnt, y)
+        R.decode_hot(layers[l], x, hots[l], y, idx, cnt)
         if s >= nl * 2:
             counts.append(cnt.clone())
     torch.cuda.synchronize()
