@@ -26,7 +26,10 @@
  *    words in it between calls and remembers, by address, which layout each
  *    workspace last held (a call that finds a different one clears what it
  *    needs first, at the cost of one small extra kernel): a separate workspace
- *    per operation avoids those clears.
+ *    per operation avoids those clears.  A call captured into a graph decides
+ *    at capture whether it clears; so between the replays of a graph, a
+ *    workspace the graph uses must not be passed to a call of another layout
+ *    (another operation, shape or batch size).
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
  *    means the default stream).  Nothing is copied to the host: the active
  *    count stays in device memory and later kernels read it there.
