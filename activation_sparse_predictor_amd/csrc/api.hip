@@ -87,9 +87,14 @@ size_t sparse_data_bytes(int B, int d, int ffn) {
     size_t n = pi::sparse_layout(B, d, ffn).total;          // dense baseline
     const size_t f = pi::fused_sparse_layout(d, ffn).total;  // single token / per token
     if (f > n) n = f;
-    if (B >= 2) {                                            // union path
+    if (B >= 2) {   // union path, by groups of kUnionMaxTokens and the last group (its chunk count may differ)
         const size_t u = pi::batch_layout(B < pi::kUnionMaxTokens ? B : pi::kUnionMaxTokens, d, ffn).total;
         if (u > n) n = u;
+        const int tail = B % pi::kUnionMaxTokens;
+        if (B > pi::kUnionMaxTokens && tail > 0) {
+            const size_t ut = pi::batch_layout(tail, d, ffn).total;
+            if (ut > n) n = ut;
+        }
     }
     return n;
 }

@@ -195,31 +195,69 @@ using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, rbw_up(XG), ring_seg(REGLU ? 2 : 1, 
 // token t did not select neuron U_u), stored token-major as an fp16 hi/lo
 // pair: aT[t][u], for every token slot t < Bp (zero past B) and for u up to
 // the next multiple of 8 past |U| (zero past |U|).
+template <int KIND>
+struct UpEpi {
+    const int32_t* ulist;
+    const float* bup;
+    const float* bg;
+    const uint32_t* tokbits;
+    int nw, B, Bp, lda, U, U8;
+    h16* a_hi;
+    h16* a_lo;
+    struct Row {
+        int nrow;
+        float bu, bgv;
+    };
+    // (the ring runs no epilogue when |U| = 0, so U - 1 is a valid entry;
+    // loads are unconditional at clamped addresses and their values masked
+    // afterwards: loads under a branch make the compiler wait for all
+    // outstanding memory operations, the previous outputs' stores included)
+    __device__ Row row(int uu) const {
+        const bool ok = uu < U;
+        const int nrow = settle(ulist[min(uu, U - 1)]);
+        const float bu = settle(bup ? bup[nrow] : 0.f);
+        const float bgv = settle((KIND != 0 && bg) ? bg[nrow] : 0.f);
+        return Row{ok ? nrow : 0, ok ? bu : 0.f, ok ? bgv : 0.f};
+    }
+    // (no early exit: every use of the row's loads sits on the path all
+    // threads take, so the compiler waits for them once)
+    template <int E>
+    __device__ void apply(int uu, const Row& r, const int (&t)[E], const float (&vu)[E], const float (&vg)[E]) const {
+        uint32_t bits[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k)   // the E mask words in flight together
+            bits[k] = tokbits[(size_t)min(t[k], B - 1) * nw + (r.nrow >> 5)];
+#pragma unroll
+        for (int k = 0; k < E; ++k) bits[k] = settle(bits[k]);
+        float av[E];
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            // zero past |U| (the down GEMM reads whole 8-entry chunks) and
+            // for the tokens that did not select the neuron
+            const bool on = uu < U && t[k] < B && ((bits[k] >> (r.nrow & 31)) & 1u);
+            av[k] = on ? ffn_act<KIND>(vu[k] + r.bu, KIND != 0 ? vg[k] + r.bgv : 0.f) : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const h16 hi = (h16)av[k];
+            const h16 lo = (h16)(av[k] - (float)hi);
+            if (t[k] < Bp && uu < U8) {
+                a_hi[(size_t)t[k] * lda + uu] = hi;
+                a_lo[(size_t)t[k] * lda + uu] = lo;
+            }
+        }
+    }
+};
+
 template <class C, int KIND>
 __global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __restrict__ ucount, int ffn,
                                                   const float* __restrict__ bup, const float* __restrict__ bg,
                                                   const uint32_t* __restrict__ tokbits, int nw, int Bp, int lda,
                                                   h16* __restrict__ a_hi, h16* __restrict__ a_lo) {
     __shared__ __align__(16) char lds[C::LDS];
-    const int U = (int)min(*ucount, (uint32_t)ffn), B = a.B;
-    const int32_t* ulist = a.rowlist;
-    const int U8 = min((U + 7) & ~7, lda);
-    ring_gemm<C, true, true>(a, U, lds, [&](int uu, int t, float vu, float vg) {
-        if (t >= Bp || uu >= U8) return;
-        if (uu >= U) {   // the down GEMM reads whole 8-entry chunks: the tail past U is zero
-            a_hi[(size_t)t * lda + uu] = (h16)0.f;
-            a_lo[(size_t)t * lda + uu] = (h16)0.f;
-            return;
-        }
-        float av = 0.f;
-        const int nrow = ulist[uu];
-        if (t < B && ((tokbits[(size_t)t * nw + (nrow >> 5)] >> (nrow & 31)) & 1u)) {
-            av = ffn_act<KIND>(vu + (bup ? bup[nrow] : 0.f), KIND != 0 ? vg + (bg ? bg[nrow] : 0.f) : 0.f);
-        }
-        const h16 hi = (h16)av;
-        a_hi[(size_t)t * lda + uu] = hi;
-        a_lo[(size_t)t * lda + uu] = (h16)(av - (float)hi);
-    });
+    const int U = (int)min(*ucount, (uint32_t)ffn);
+    const UpEpi<KIND> epi{a.rowlist, bup, bg, tokbits, nw, a.B, Bp, lda, U, min((U + 7) & ~7, lda), a_hi, a_lo};
+    ring_gemm<C, true, true>(a, U, lds, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -234,14 +272,27 @@ struct HiddenEpi {
     int relu, r, B, ldh;
     h16* h_hi;
     h16* h_lo;
-    __device__ void operator()(int j, int t, float v, float) const {
-        if (j >= r || t >= B) return;
-        const float sv = v + (b1 ? b1[j] : 0.f);
+    struct Row {
+        float b;
+    };
+    __device__ Row row(int j) const { return Row{settle(b1 ? b1[min(j, r - 1)] : 0.f)}; }
+    // the value first, the store under the condition (see UpEpi)
+    __device__ void store(int j, int t, float v, float b) const {
+        const float sv = v + b;
         const float hv = relu ? fmaxf(sv, 0.f) : sv;
         const h16 hi = (h16)hv;
-        h_hi[(size_t)t * ldh + j] = hi;
-        h_lo[(size_t)t * ldh + j] = (h16)(hv - (float)hi);
+        const h16 lo = (h16)(hv - (float)hi);
+        if (j < r && t < B) {
+            h_hi[(size_t)t * ldh + j] = hi;
+            h_lo[(size_t)t * ldh + j] = lo;
+        }
     }
+    template <int E>
+    __device__ void apply(int j, const Row& rw, const int (&t)[E], const float (&v)[E], const float (&)[E]) const {
+#pragma unroll
+        for (int k = 0; k < E; ++k) store(j, t[k], v[k], rw.b);
+    }
+    __device__ void operator()(int j, int t, float v, float) const { store(j, t, v, row(j).b); }
 };
 
 template <class C>
@@ -321,23 +372,39 @@ __global__ __launch_bounds__(256) void k_bpred_hidden_valu(const h16* __restrict
 // z > thr per (neuron, token); every 32 neurons give one 32-bit mask word per
 // token (bit k = neuron 32*word + k).  Each half of a wave holds 32 neurons
 // of one token: one ballot gives two words.
-template <class C>
 // The rows are neurons hot .. ffn - 1 (a.W[0] starts at P2 row hot, a.nrows =
 // ffn - hot; hot is a multiple of 32, so each half-wave's 32 rows are still
 // one mask word).  The words of the hot prefix are the compaction's.
+struct LogitsEpi {
+    const float* b2;
+    float thr;
+    uint32_t* masks32;
+    int nw, hot, nr, B;
+    struct Row {
+        float b;
+    };
+    __device__ Row row(int i) const { return Row{settle(b2 ? b2[hot + min(i, nr - 1)] : 0.f)}; }
+    template <int E>
+    __device__ void apply(int i, const Row& rw, const int (&t)[E], const float (&v)[E], const float (&)[E]) const {
+        const int n = hot + i, lane = threadIdx.x & 63;
+#pragma unroll
+        for (int k = 0; k < E; ++k) {
+            const float z = v[k] + rw.b;
+            const bool on = (i < nr) & (t[k] < B) & (z > thr);
+            const uint64_t m = __ballot(on);
+            if ((lane & 31) == 0 && i < nr && t[k] < B)
+                masks32[(size_t)t[k] * nw + (n >> 5)] = (uint32_t)(m >> (lane & 32));
+        }
+    }
+};
+
+template <class C>
 __global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* __restrict__ b2, float thr,
                                                       uint32_t* __restrict__ masks32, int ffn, int hot) {
     __shared__ __align__(16) char lds[C::LDS];
     static_assert(C::RB % 32 == 0, "a half-wave must hold 32 neurons of one token");
-    const int nr = a.nrows, B = a.B;
-    const int nw = (ffn + 31) / 32;
-    ring_gemm<C, false, true>(a, nr, lds, [&](int i, int t, float v, float) {
-        const int n = hot + i;
-        const bool on = i < nr && t < B && v + (b2 ? b2[n] : 0.f) > thr;
-        const uint64_t m = __ballot(on);
-        const int lane = threadIdx.x & 63;
-        if ((lane & 31) == 0 && i < nr && t < B) masks32[(size_t)t * nw + (n >> 5)] = (uint32_t)(m >> (lane & 32));
-    });
+    const LogitsEpi epi{b2, thr, masks32, (ffn + 31) / 32, hot, a.nrows, a.B};
+    ring_gemm<C, false, true>(a, a.nrows, lds, epi);
 }
 
 // One workgroup per token: the token's 32-bit tile masks in neuron order ->
@@ -421,24 +488,74 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 constexpr int kDnIds = 4096;   // union ids staged in LDS at a time (a window of the chunk)
 
 // Wave w owns CB blocks of 32 columns (the tile is 128 CB columns): with 128
-// tokens, two blocks per wave halve the activation bytes per W_down byte (the
-// ring is then two stages deep either way; with 64 tokens one block keeps
-// it three deep, which measured faster).
+// tokens, two blocks per wave halve the activation bytes per W_down byte.
+// A stage is KR union entries: 64, or 32 with 128 tokens, where a 64-entry
+// stage (64 KB) would leave room for only two in LDS and the ring would hold
+// a single stage in flight; 32-entry stages give it four.  An activation
+// block is what one wave-wide load moves, TPB tokens x KR entries: 8 tokens
+// x 128 bytes with the chunk slots XOR-swizzled by the token group (32 lanes
+// reading one chunk of 32 tokens then hit 4 different 128-byte slots), or 16
+// tokens x 64 bytes, [chunk][token], whose 256-byte chunk rows are read
+// without bank conflicts as they are.
 template <int XG_>
 struct DownCfg {
     static constexpr int XG = XG_;
     static constexpr int NB = (XG + 3) / 4, BP = 32 * NB;
     static constexpr int CB = XG >= 16 ? 2 : 1;
     static constexpr int CT = 128 * CB;                            // columns per tile
-    static constexpr int KR = 64;                                  // union entries per stage
+    static constexpr int KR = XG >= 16 ? 32 : 64;                  // union entries per stage
+    static constexpr int TPB = 512 / KR;                           // tokens per activation block
     static constexpr int WBLK = (KR / 8) * (CT / 64);              // W_down blocks per stage
-    static constexpr int ABLK = 2 * XG;                            // activation blocks (hi, lo)
+    static constexpr int ABA = (8 * XG + TPB - 1) / TPB;           // activation blocks per array
+    static constexpr int ABLK = 2 * ABA;                           // activation blocks (hi, lo)
     static constexpr int NBLK = ((WBLK + ABLK + 3) / 4) * 4;       // padded to whole waves
     static constexpr int IPW = NBLK / 4;
     static constexpr int STAGE = NBLK * 1024;
-    static constexpr int NS = 3 * STAGE + kDnIds * 4 <= 156 * 1024 ? 3 : 2;
+    // ring depth: four 32-entry stages, else three stages where they fit
+    // (which keeps two workgroups per CU at up to 16 tokens), else two
+    static constexpr int NS = KR == 32 && 4 * STAGE + kDnIds * 4 <= 156 * 1024
+                                  ? 4 : (3 * STAGE + kDnIds * 4 <= 156 * 1024 ? 3 : 2);
     static_assert(WBLK % 4 == 0 && IPW * (NS - 2) < 64, "loads per stage");
+    static_assert(TPB == 8 || TPB == 16, "activation block shapes");
+    // LDS byte offset in an activation block of chunk c (8 entries) of its token t
+    static __device__ __forceinline__ int aoff(int tg, int c, int t) {
+        return TPB == 8 ? ((c ^ (tg & 3)) << 7) + ((t & 7) << 4) : (c << 8) + ((t & 15) << 4);
+    }
 };
+
+// Resident down workgroups per CU, by their LDS (the registers allow more).
+template <int X>
+constexpr int down_per_cu() {
+    return (160 * 1024) / (DownCfg<X>::NS * DownCfg<X>::STAGE + kDnIds * 4);
+}
+static_assert(down_per_cu<1>() == 2 && down_per_cu<2>() == 2 && down_per_cu<16>() == 1, "down occupancy");
+
+// The down grid is (column tiles, G chunks of the union).  A partial wave
+// costs as much as a full one, so G fills whole waves of the workgroup slots
+// of the 256 CUs of an MI355X: of 1 to 4 waves, the best use of the slots,
+// the fewest waves on a near tie (fewer chunk partials to add).  On another
+// device the grid is only less well shaped.
+constexpr int kDeviceCUs = 256;
+int union_down_chunks(int B, int d) {
+    const int xg = ring_xg(B);
+    const int ct = xg == 16 ? DownCfg<16>::CT : (xg == 8 ? DownCfg<8>::CT : (xg == 4 ? DownCfg<4>::CT
+                 : (xg == 2 ? DownCfg<2>::CT : DownCfg<1>::CT)));
+    const int per = xg == 16 ? down_per_cu<16>() : (xg == 8 ? down_per_cu<8>() : (xg == 4 ? down_per_cu<4>()
+                  : (xg == 2 ? down_per_cu<2>() : down_per_cu<1>())));
+    const int tiles = (d + ct - 1) / ct, slots = kDeviceCUs * per;
+    int best = 1;
+    double use = -1.0;
+    for (int k = 1; k <= 4; ++k) {
+        const int g = std::min(64, std::max(1, k * slots / tiles));
+        const int waves = (tiles * g + slots - 1) / slots;
+        const double u = (double)tiles * g / ((double)waves * slots);
+        if (u > use + 0.02) {
+            use = u;
+            best = g;
+        }
+    }
+    return best;
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -504,13 +621,15 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
             kofs[i] = c0 + cs * 64 + (((lane >> 3) ^ (rg & 7)) << 3);
             abase[i] = nullptr;
         } else {
+            // lane j writes LDS bytes 16j.. of the block: token j % TPB, and
+            // the chunk whose slot is j / TPB
             const int bx = b - C::WBLK;
-            const int ix = bx / C::XG, tg = bx % C::XG;
-            const int t = tg * 8 + (lane & 7);
+            const int ix = bx / C::ABA, tg = bx % C::ABA;
+            const int t = tg * C::TPB + (lane % C::TPB);
             const bool real = bx < C::ABLK && t < B;
             abase[i] = real ? (ix ? a_lo : a_hi) + (size_t)t * lda : nullptr;
             wofs[i] = 0;
-            kofs[i] = ((lane >> 3) ^ (tg & 3)) << 3;
+            kofs[i] = (C::TPB == 8 ? ((lane >> 3) ^ (tg & 3)) : lane / C::TPB) << 3;
         }
     }
     auto issue = [&](int st, int q) {
@@ -577,11 +696,11 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
             const int c = 2 * q + kh;    // activation chunk (8 entries)
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
-                const int t = nb * 32 + li, tg = min(t >> 3, C::XG - 1);
+                const int t = nb * 32 + li, tg = min(t / C::TPB, C::ABA - 1);
 #pragma unroll
                 for (int ix = 0; ix < 2; ++ix) {
-                    const int blk = C::WBLK + ix * C::XG + tg;
-                    av[q][nb][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + ((c ^ (tg & 3)) << 7) + ((t & 7) << 4));
+                    const int blk = C::WBLK + ix * C::ABA + tg;
+                    av[q][nb][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + C::aoff(tg, c, t));
                 }
             }
         }

@@ -201,6 +201,15 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
 __device__ __forceinline__ void st_coherent(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Returns v as a plain register value: the compiler waits for the load that
+// produced it here, once, rather than before each later use it has sunk into
+// a branch (there it cannot count the loads and waits for every outstanding
+// memory operation, the stores issued since included).
+template <class T>
+__device__ __forceinline__ T settle(T v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
 // Wait until every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_own_memory() { __builtin_amdgcn_s_waitcnt(0); }
 

@@ -91,20 +91,20 @@ struct BatchLayout {
     size_t upctr;    // ceil(ffn/64) uint32 row-block counters of the up GEMM
     size_t upart;    // pieces of the up GEMM (two matrices for ReGLU)
     size_t total;
-    int W, Bp, lda, T, G;
+    int W, Bp, lda, G;
 };
+
+// Union chunks of the down GEMM for B tokens (batch.hip): its grid is
+// (column tiles, chunks), and the chunk count is picked to fill whole waves
+// of the device (1 to 64 chunks; the partials are chunks x Bp x d).
+int union_down_chunks(int B, int d);
 
 inline BatchLayout batch_layout(int B, int d, int ffn) {
     BatchLayout L;
     L.W = (B + 31) / 32;
     L.Bp = L.W * 32;
     L.lda = (ffn + 7) & ~7;
-    L.T = (d + 127) / 128;
-    // union chunks per 128-column tile: about 512 down workgroups in all,
-    // 8 to 64 chunks (the partials stay G x Bp x d whatever ffn is)
-    L.G = 512 / L.T;
-    if (L.G < 8) L.G = 8;
-    if (L.G > 64) L.G = 64;
+    L.G = union_down_chunks(B, d);
     const size_t tiles = (size_t)(ffn + 63) / 64;
     L.tokbits = 0;
     L.umasks = L.tokbits + align256((size_t)B * ((ffn + 31) / 32) * 4);

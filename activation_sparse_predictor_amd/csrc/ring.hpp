@@ -109,11 +109,16 @@ struct RingArgs {
 // 16-byte aligned; the pieces area (a.part) holds two slots per workgroup of
 // NM x BP x RB fp32 sums.
 //
-// epi(i, t, v0, v1) is called by every thread of the workgroup, uniformly,
-// for every (row i of a finished row block, token slot t < BP), rows fastest:
-// the 32 rows of a half-wave belong to one token.  v0 and v1 are the sums for
-// matrices 0 and 1 (v1 = 0 when NM = 1), 0 for t >= B; i runs to the end of
-// the row block, past nrows, where the sums mean nothing.
+// The epilogue runs one row of a finished row block per thread (thread k:
+// row k % RB, token slots k / RB + j * 256 / RB), so the 32 rows of a
+// half-wave belong to one token.  epi.row(i) is called once per thread and
+// row block and returns what the row's outputs need from memory (ids,
+// biases); epi.apply<E>(i, row, t, v0, v1) then takes E token slots of that
+// row at once, every thread uniformly, so that the loads of the E outputs go
+// out together instead of one latency per output (at 128 tokens a thread
+// holds 64 outputs of each row block).  v0 and v1 are the sums for matrices 0
+// and 1 (v1 = 0 when NM = 1), 0 for t >= B; i runs to the end of the row
+// block, past nrows, where the sums mean nothing.
 template <class C, bool GATHER, bool LAST_FINISHES, class Epi>
 __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* lds, Epi&& epi) {
     __shared__ int s_last;
@@ -128,6 +133,11 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
     // workgroup between the first and last holder of a row block has a piece
     const int G = (int)min((long long)gridDim.x, T), w = (int)blockIdx.x;
     if (w >= G) return;
+    static_assert(256 % C::RB == 0, "a thread keeps one row of the block");
+    constexpr int kTS = 256 / C::RB;                // token-slot stride of a thread
+    constexpr int kNT = C::BP / kTS;                // token slots per thread
+    constexpr int kE = kNT < 16 ? kNT : 16;         // outputs per epilogue batch
+    static_assert(kNT % kE == 0, "whole batches");
     const long long ua = T * w / G, ub = T * (w + 1) / G;
     float* red = reinterpret_cast<float*>(lds);
     const uint32_t lbase = (uint32_t)(size_t)(lds_void_ptr)lds;
@@ -242,10 +252,20 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
             for (int k = 0; k < C::WK; ++k) v += red[(((k * C::NB + tb) * C::RBW + rr) * C::NM + m) * 1024 + e * 64 + ln];
             return v;
         };
+        // this thread's row and token slots: rl, tt + j * TS for j < NT
+        const int rl = tid % C::RB, tt = tid / C::RB, row = rb * C::RB + rl;
         if (st0 == 0 && st1 == nst) {
-            for (int o = tid; o < C::RB * C::BP; o += 256) {
-                const int rl = o % C::RB, t = o / C::RB;
-                epi(rb * C::RB + rl, t, val(0, rl, t), C::NM > 1 ? val(C::NM - 1, rl, t) : 0.f);
+            const auto pr = epi.row(row);
+            for (int j = 0; j < kNT; j += kE) {
+                int t[kE];
+                float v0[kE], v1[kE];
+#pragma unroll
+                for (int k = 0; k < kE; ++k) {
+                    t[k] = tt + (j + k) * kTS;
+                    v0[k] = val(0, rl, t[k]);
+                    v1[k] = C::NM > 1 ? val(C::NM - 1, rl, t[k]) : 0.f;
+                }
+                epi.template apply<kE>(row, pr, t, v0, v1);
             }
         } else {
             // piece slot: kind 0 when the range starts inside this row block
@@ -255,9 +275,9 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
                 return a.part + (size_t)(wg * 2 + kind) * C::NM * C::BP * C::RB;
             };
             float* mine = slot(w);
-            for (int o = tid; o < C::RB * C::BP; o += 256) {
-                const int rl = o % C::RB, t = o / C::RB;
-                if (t < a.B && rb * C::RB + rl < nrows)
+            for (int j = 0; j < kNT; ++j) {
+                const int t = tt + j * kTS;
+                if (t < a.B && row < nrows)
 #pragma unroll
                     for (int m = 0; m < C::NM; ++m) {
                         if (LAST_FINISHES) st_coherent(&mine[(m * C::BP + t) * C::RB + rl], val(m, rl, t));
@@ -280,26 +300,34 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
             }
             __syncthreads();
             if (s_last) {
-                for (int o = tid; o < C::RB * C::BP; o += 256) {
-                    const int rl = o % C::RB, t = o / C::RB;
-                    float v0 = 0.f, v1 = 0.f;
-                    if (t < a.B && rb * C::RB + rl < nrows)
-                        for (int w0 = wf; w0 <= wl; w0 += 4) {   // pieces in order, 4 at a time in flight
-                            float x0[4], x1[4];
+                const auto pr = epi.row(row);
+                for (int j = 0; j < kNT; j += kE) {
+                    int t[kE];
+                    float v0[kE], v1[kE];
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                const float* pc = slot(min(w0 + k, wl));
-                                x0[k] = ld_coherent(&pc[t * C::RB + rl]);
-                                x1[k] = C::NM > 1 ? ld_coherent(&pc[(C::BP + t) * C::RB + rl]) : 0.f;
-                            }
+                    for (int k = 0; k < kE; ++k) {
+                        t[k] = tt + (j + k) * kTS;
+                        v0[k] = 0.f;
+                        v1[k] = 0.f;
+                    }
+                    for (int w0 = wf; w0 <= wl; ++w0) {   // pieces in order, kE outputs' loads in flight
+                        const float* pc = slot(w0);
+                        float x0[kE], x1[kE];
+                        // (unconditional loads inside the slot, masked after:
+                        // loads under a branch would cost a full wait each)
 #pragma unroll
-                            for (int k = 0; k < 4; ++k)
-                                if (w0 + k <= wl) {
-                                    v0 += x0[k];
-                                    v1 += x1[k];
-                                }
+                        for (int k = 0; k < kE; ++k) {
+                            x0[k] = ld_coherent(&pc[t[k] * C::RB + rl]);
+                            x1[k] = C::NM > 1 ? ld_coherent(&pc[(C::BP + t[k]) * C::RB + rl]) : 0.f;
                         }
-                    epi(rb * C::RB + rl, t, v0, v1);
+#pragma unroll
+                        for (int k = 0; k < kE; ++k) {
+                            const bool ok = t[k] < a.B && row < nrows;
+                            v0[k] += ok ? x0[k] : 0.f;
+                            v1[k] += ok ? x1[k] : 0.f;
+                        }
+                    }
+                    epi.template apply<kE>(row, pr, t, v0, v1);
                 }
             }
         }
@@ -346,7 +374,10 @@ __device__ __forceinline__ void ring_finish(const RingArgs& a, int nrows, int G0
                     v1 += x1[j];
                 }
         }
-        epi(rb * C::RB + rl, t, v0, v1);
+        const int i = rb * C::RB + rl;
+        const int tt[1] = {t};
+        const float a0[1] = {v0}, a1[1] = {v1};
+        epi.template apply<1>(i, epi.row(i), tt, a0, a1);
     }
 }
 
