@@ -96,6 +96,9 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
 // stays in bounds, |U| is written as 0 and the error word is set, which
 // k_union_reduce answers with NaN in every token's y.
 constexpr int kCompactWG = 256;
+// Grids shaped to fill whole waves assume the 256 CUs of an MI355X (on
+// another device they are only less well shaped).
+constexpr int kDeviceCUs = 256;
 constexpr int kCompactTiles = 1024;   // tiles per workgroup held in LDS
 constexpr int kCompactWait = 1 << 16;
 
@@ -185,7 +188,11 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
 constexpr int ring_seg(int nm, int nx, int xg, int rbw) {
     return 3 * (nm * 4 * rbw + nx * xg) * 4 <= 156 ? 4 : (3 * (nm * 4 * rbw + nx * xg) * 2 <= 156 ? 2 : 1);
 }
-template <int XG> using HidCfg = RingCfg<1, 1, XG, rbw_hidden(XG), ring_seg(1, 1, XG, rbw_hidden(XG)), 3>;
+// (the hidden layer at 128 tokens: 64-row blocks in four one-segment stages;
+// its few rows make every row block split over many workgroups, and smaller
+// blocks halve the pieces each workgroup writes)
+template <int XG>
+using HidCfg = RingCfg<1, 1, XG, rbw_hidden(XG), XG >= 16 ? 1 : ring_seg(1, 1, XG, rbw_hidden(XG)), XG >= 16 ? 4 : 3>;
 template <int XG> using LogCfg = RingCfg<1, 2, XG, rbw_logits(XG), ring_seg(1, 2, XG, rbw_logits(XG)), 3>;
 template <bool REGLU, int XG>
 using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, rbw_up(XG), ring_seg(REGLU ? 2 : 1, 1, XG, rbw_up(XG)), 3>;
@@ -407,6 +414,151 @@ __global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* _
     ring_gemm<C, false, true>(a, a.nrows, lds, epi);
 }
 
+// Logits for more than 32 tokens with h held in registers.  Workgroup
+// (q, range) takes the 32 tokens of group q and a range of 32-row blocks of
+// P2 (rows hot ..); wave w keeps both halves of h for quarter w of K (r / 4
+// entries: KS = r / 64 MFMA steps, 8 registers a step), so that only P2 goes
+// through LDS.  A stage is one half of K of a 32-row block (32 x r / 2
+// halves, by direct-to-LDS loads: 8 rows x 128 bytes per load, chunk slots
+// swizzled by the row group as in ring.hpp); waves 0-1 multiply the first
+// half, waves 2-3 the second, and the ring of four stages keeps three in
+// flight.  After the second half of a block the four waves' partial sums go
+// through LDS, are added in wave order, and give the mask words as in
+// k_bpred_logits.  No row is split across workgroups, and h is read once per
+// workgroup instead of once per row block.  The token groups of one row
+// range are 8 workgroup indices apart: on one XCD, and dispatched together,
+// so that three of the four reads of a P2 row hit its L2.
+constexpr int kTqMaxR = 1024;                 // h registers: r / 64 <= 16 steps
+constexpr int kTqRedE = 65, kTqRedW = 1040;   // partial sums: [wave][16 elements][65 floats]
+constexpr int kTqStages = 4;
+constexpr int kTqMaxBlocks = 64;              // 32-row blocks per workgroup (their biases sit in LDS)
+inline int logits_tq_ranges(int B) {
+    const int nq = (B + 31) / 32;
+    const int rr8 = kDeviceCUs / (8 * nq);
+    return 8 * (rr8 > 0 ? rr8 : 1);
+}
+// r = 256, 512 or 1024 (KS = r / 64, a compile-time count so that a wave's
+// LDS reads all go out ahead of its MFMAs), at most kTqMaxBlocks row blocks
+// per workgroup
+inline bool logits_tq_fits(int B, int r, int nr) {
+    const long long nrb = (nr + 31) / 32, nrg = logits_tq_ranges(B);
+    return B > 32 && (r == 256 || r == 512 || r == 1024) && (nrb + nrg - 1) / nrg <= kTqMaxBlocks;
+}
+
+__device__ __forceinline__ void wait_lds_ops() {   // lgkmcnt(0) only (vector memory not waited on)
+    __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x3 << 14));
+}
+
+template <int KS>
+__global__ __launch_bounds__(256) void k_bpred_logits_tq(const h16* __restrict__ P2, int nr, int hot,
+                                                         const h16* __restrict__ h_hi,
+                                                         const h16* __restrict__ h_lo, int ldh, int B,
+                                                         int nq, int nranges, const float* __restrict__ b2,
+                                                         float thr, uint32_t* __restrict__ masks32, int ffn) {
+    constexpr int r = KS * 64;
+    constexpr int HB = KS / 2;            // 8-chunk blocks per row group in a half-K stage
+    constexpr int IPW = HB;               // loads per wave per stage (4 row groups x HB blocks)
+    constexpr int STG = 32 * (r / 2) * 2; // bytes per stage
+    __shared__ __align__(16) char lds[kTqStages * 32 * (kTqMaxR / 2) * 2];
+    __shared__ float red[4 * kTqRedW];
+    __shared__ float s_b2[kTqMaxBlocks * 32];
+    static_assert(IPW * (kTqStages - 2) < 64, "loads in flight");
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane & 31, kh = lane >> 5;
+    // workgroup b: XCD slot b % 8, then token group, then range group
+    const int b = blockIdx.x, hi8 = b >> 3;
+    const int q = hi8 % nq, rg = (b & 7) + 8 * (hi8 / nq);
+    const int nrb = (nr + 31) / 32;
+    const int rb0 = (int)((long long)rg * nrb / nranges), rb1 = (int)((long long)(rg + 1) * nrb / nranges);
+    const int ns = 2 * (rb1 - rb0);       // stages: two halves of K per row block
+    if (ns <= 0) return;
+    const h16* W = P2 + (size_t)hot * r;
+    const uint32_t lbase = lds_addr(lds);
+
+    // this wave's h: token q*32 + li, chunk w*(r/32) + 2*step + kh (slots past B read the buffer's padding)
+    f16x8 hh[KS], hl[KS];
+    {
+        const size_t tro = (size_t)(q * 32 + li) * ldh + (size_t)(wave * (r >> 5) + kh) * 8;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            hh[k] = *reinterpret_cast<const f16x8*>(h_hi + tro + k * 16);
+            hl[k] = *reinterpret_cast<const f16x8*>(h_lo + tro + k * 16);
+        }
+    }
+    // the range's biases to LDS, and h settled, before any stage goes out: a
+    // compiler wait for a load inside the stage loop would drain the ring
+    for (int i = tid; i < (ns / 2) * 32; i += 256) s_b2[i] = b2 ? b2[hot + min(rb0 * 32 + i, nr - 1)] : 0.f;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        hh[k] = settle(hh[k]);
+        hl[k] = settle(hl[k]);
+    }
+    __syncthreads();
+    auto issue = [&](int st) {
+        const uint32_t dst = lbase + (uint32_t)((st % kTqStages) * STG);
+        const int rb = rb0 + (st >> 1), half = st & 1;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int blk = wave + 4 * i;
+            const int g = blk / HB, cg = blk % HB;
+            const int row = min(rb * 32 + g * 8 + (lane & 7), nr - 1);
+            const int chunk = half * (r / 16) + cg * 8 + ((lane >> 3) ^ (g & 3));
+            dma16(W + (size_t)row * r + chunk * 8, dst + (uint32_t)blk * 1024u);
+        }
+    };
+    const int nw = (ffn + 31) / 32;
+#pragma unroll
+    for (int j = 0; j < kTqStages - 1; ++j)
+        if (j < ns) issue(j);
+    for (int s = 0; s < ns; ++s) {
+        const int rb = rb0 + (s >> 1), half = s & 1;
+        if (s + kTqStages - 2 < ns) wait_vm<(kTqStages - 2) * IPW>();   // stage s is in
+        else wait_vm<0>();
+        ring_barrier();   // every wave's loads of stage s are in; everyone is past stage s - 1 and the sums
+        if (s + kTqStages - 1 < ns) issue(s + kTqStages - 1);
+        if ((wave >> 1) == half) {
+            const char* buf = lds + (s % kTqStages) * STG;
+            const int g = li >> 3;
+            f16x8 a[KS];
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const int c = (wave & 1) * (r >> 5) + 2 * k + kh;   // chunk within the half
+                a[k] = *reinterpret_cast<const f16x8*>(buf + (g * HB + (c >> 3)) * 1024 +
+                                                       (((c & 7) ^ (g & 3)) << 7) + ((li & 7) << 4));
+            }
+            ring_f32x16 acc = {};
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hh[k], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hl[k], acc, 0, 0, 0);
+            }
+            // element e of lane l: row (e/4)*8 + 4*(l/32) + e%4, token l%32
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[wave * kTqRedW + e * kTqRedE + lane] = acc[e];
+        }
+        if (half == 1) {
+            wait_lds_ops();
+            ring_barrier();
+            // wave w: tokens 4w + k (lanes 0-31) and 4w + k + 16 (lanes 32-63), row li
+            const int e = ((li >> 3) << 2) + (li & 3), hb = ((li >> 2) & 1) << 5;
+            const int grow = rb * 32 + li;
+            const float brow = s_b2[(rb - rb0) * 32 + li];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int n = 4 * wave + k + (kh << 4), t = q * 32 + n;
+                float v = 0.f;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) v += red[p * kTqRedW + e * kTqRedE + hb + n];
+                const bool on = (grow < nr) & (t < B) & (v + brow > thr);
+                const uint64_t m = __ballot(on);
+                if (li == 0 && t < B)
+                    masks32[(size_t)t * nw + ((hot + rb * 32) >> 5)] = (uint32_t)(m >> (lane & 32));
+            }
+        }
+    }
+}
+
 // One workgroup per token: the token's 32-bit tile masks in neuron order ->
 // popcount prefix -> ascending idx and count.  Thread k takes words 2k and
 // 2k + 1 of each quarter of a 2048-word round (one block-wide scan per
@@ -532,10 +684,8 @@ static_assert(down_per_cu<1>() == 2 && down_per_cu<2>() == 2 && down_per_cu<16>(
 
 // The down grid is (column tiles, G chunks of the union).  A partial wave
 // costs as much as a full one, so G fills whole waves of the workgroup slots
-// of the 256 CUs of an MI355X: of 1 to 4 waves, the best use of the slots,
-// the fewest waves on a near tie (fewer chunk partials to add).  On another
-// device the grid is only less well shaped.
-constexpr int kDeviceCUs = 256;
+// of the device: of 1 to 4 waves, the best use of the slots, the fewest
+// waves on a near tie (fewer chunk partials to add).
 int union_down_chunks(int B, int d) {
     const int xg = ring_xg(B);
     const int ct = xg == 16 ? DownCfg<16>::CT : (xg == 8 ? DownCfg<8>::CT : (xg == 4 ? DownCfg<4>::CT
@@ -918,8 +1068,16 @@ hipError_t launch_bpredict(const h16* x, int B, int d, const h16* P1, const floa
     const int gv = (r + 3) / 4;
     const bool valu = B <= 8 && nch <= hid_valu_chunks(B <= 4 ? 4 : 8);
 #define PI_BHV(TB) hipLaunchKernelGGL(k_bpred_hidden_valu<TB>, dim3(gv), dim3(256), 0, s, x, B, d, P1, he, lctr, nlctr)
-#define PI_BL(N) hipLaunchKernelGGL((k_bpred_logits<LogCfg<N>>), dim3(ring_grid<k_bpred_logits<LogCfg<N>>>()), \
-                                    dim3(256), 0, s, la, b2, thr, masks32, ffn, hot)
+#define PI_BL(N)                                                                                          \
+    if (logits_tq_fits(B, r, ffn - hot)) {                                                                \
+        const int nq = (B + 31) / 32, nrg = logits_tq_ranges(B);                                          \
+        auto kq = r == 256 ? k_bpred_logits_tq<4> : (r == 512 ? k_bpred_logits_tq<8> : k_bpred_logits_tq<16>); \
+        hipLaunchKernelGGL(kq, dim3(nq * nrg), dim3(256), 0, s, P2, ffn - hot, hot, h_hi, h_lo, L.ldh, B,  \
+                           nq, nrg, b2, thr, masks32, ffn);                                                \
+    } else {                                                                                              \
+        hipLaunchKernelGGL((k_bpred_logits<LogCfg<N>>), dim3(ring_grid<k_bpred_logits<LogCfg<N>>>()),     \
+                           dim3(256), 0, s, la, b2, thr, masks32, ffn, hot);                              \
+    }
     const int xg = ring_xg(B);
     if (valu) {
         if (B <= 2) PI_BHV(2);

@@ -74,7 +74,7 @@ __host__ __device__ constexpr int ring_xg(int B) {
     return B <= 8 ? 1 : (B <= 16 ? 2 : (B <= 32 ? 4 : (B <= 64 ? 8 : 16)));
 }
 __host__ __device__ constexpr int rbw_up(int xg) { return xg <= 2 ? 1 : (xg == 4 ? 2 : xg / 4); }
-__host__ __device__ constexpr int rbw_hidden(int xg) { return xg <= 4 ? 1 : xg / 4; }
+__host__ __device__ constexpr int rbw_hidden(int xg) { return xg <= 4 ? 1 : 2; }
 __host__ __device__ constexpr int rbw_logits(int xg) { return xg <= 4 ? xg : 4; }
 inline size_t ring_piece_bytes(int nm, int rbw, int B) {
     return (size_t)2 * kRingMaxWG * nm * ring_slots(B) * (32 * rbw) * 4;

@@ -79,7 +79,10 @@ struct RingCfg {
     static constexpr int KST = SEG * 64;              // halves of K per stage
     static constexpr int WK = 4 / NB;                 // waves sharing a token block
     static constexpr int NPW = 4 * SEG / WK;          // chunk pairs per wave per stage
-    static constexpr int RED = 4 * RBW * NM * 1024 * 4;   // bytes of per-wave sums
+    // per-wave sums: one block of 16 rows x 65 floats per (wave, row block of
+    // 32, matrix), 1056 floats apart (see ring_gemm's epilogue)
+    static constexpr int REDE = 65, REDB = 1056;
+    static constexpr int RED = 4 * RBW * NM * REDB * 4;   // bytes of per-wave sums
     static constexpr int LDS = NS * STAGE > RED ? NS * STAGE : RED;
     static_assert(XG == 1 || XG == 2 || XG == 4 || XG == 8 || XG == 16, "token groups: 1, 2 or 4, or whole blocks");
     static_assert(WBLK % 4 == 0 && XBLK % 4 == 0 && IPW * (NS - 2) < 64, "loads per stage");
@@ -240,16 +243,22 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
             for (int m = 0; m < C::NM; ++m)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) red[((wave * C::RBW + rr) * C::NM + m) * 1024 + e * 64 + lane] = acc[rr][m][e];
+                for (int e = 0; e < 16; ++e)
+                    red[((wave * C::RBW + rr) * C::NM + m) * C::REDB + e * C::REDE + ((rr & 1) << 4) + lane] = acc[rr][m][e];
         __syncthreads();
         // sum of row rl, token slot t, matrix m: output (r, n) of a 32 x 32
-        // block is element (r/8)*4 + r%4 of lane n + 32*((r/4)%2)
+        // block is element (r/8)*4 + r%4 of lane n + 32*((r/4)%2).  The
+        // epilogue reads 64 rows of one token per wave instruction: the
+        // element rows 65 floats apart and the odd row blocks shifted by 16
+        // put those 64 reads on 64 different banks (unpadded, the 32 rows of
+        // a row block would all hit one bank)
         auto val = [&](int m, int rl, int t) {
             const int rr = rl >> 5, r = rl & 31, tb = t >> 5, nn = t & 31;
             const int e = ((r >> 3) << 2) + (r & 3), ln = nn + (((r >> 2) & 1) << 5);
             float v = 0.f;
 #pragma unroll
-            for (int k = 0; k < C::WK; ++k) v += red[(((k * C::NB + tb) * C::RBW + rr) * C::NM + m) * 1024 + e * 64 + ln];
+            for (int k = 0; k < C::WK; ++k)
+                v += red[(((k * C::NB + tb) * C::RBW + rr) * C::NM + m) * C::REDB + e * C::REDE + ((rr & 1) << 4) + ln];
             return v;
         };
         // this thread's row and token slots: rl, tt + j * TS for j < NT

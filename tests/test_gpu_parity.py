@@ -226,6 +226,36 @@ def test_batched_predictor_hidden_paths(Bt, d):
         assert all(abs(z[j] - thr) <= 1e-3 for j in diff), f"B={Bt} d={d} t={t}: lists differ outside the band"
 
 
+@pytest.mark.parametrize("r,Bt,n_hot", [(256, 33, 0), (512, 64, 0), (1024, 100, 0), (1024, 128, 64),
+                                         (256, 131, 32), (1024, 40, 992), (512, 96, 960)])
+def test_batched_logits_h_in_registers(r, Bt, n_hot):
+    """More than 32 tokens with r = 256, 512 or 1024 take the logits kernel
+    that holds h in registers (32-token groups, whole 32-row blocks of P2, no
+    K split).  ffn = 1000 leaves a partial last 32-row block; the hot prefix
+    shifts the rows (n_hot = 992: one partial block left).  The
+    index rule per token against the oracle, and agreement with the
+    single-token predictor outside the threshold band."""
+    cfg = custom_config("relu", 264, 1000, r, mean=0.15, number=64)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    X = make_tokens(cfg, Bt).to(DEV)
+    idx, cnt = R.predict(L, X, n_hot=n_hot)
+    torch.cuda.synchronize()
+    thr = O.logit_threshold(L["tau"])
+    cnt_h, idx_h = cnt.cpu().numpy(), idx.cpu().numpy()
+    for t in sorted(set([0, 31, 32, Bt - 1] + list(range(0, Bt, 7)))):
+        c = int(cnt_h[t])
+        mine = idx_h[t, :c]
+        _, z = O.predict_hot(X[t].cpu(), H["P1"], None, "relu", H["P2"], H["b2"], L["tau"], n_hot)
+        check_idx(mine, z, thr, where=f"r={r} B={Bt} n_hot={n_hot} t={t}")
+        assert np.array_equal(mine[:n_hot], np.arange(n_hot)), "prefix not listed"
+        i1, c1 = R.predict(L, X[t:t + 1].contiguous(), n_hot=n_hot)
+        torch.cuda.synchronize()
+        single = i1[0, :int(c1.cpu()[0])].cpu().numpy()
+        diff = set(mine.tolist()) ^ set(single.tolist())
+        assert all(abs(z[j] - thr) <= 1e-3 for j in diff), f"r={r} B={Bt} t={t}: lists differ outside the band"
+
+
 def test_union_path_edge_lists():
     """Empty lists, disjoint lists, identical lists, one full list, a list whose
     32-neuron words run across the 64-entry waves that build the token
