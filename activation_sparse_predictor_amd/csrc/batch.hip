@@ -416,12 +416,12 @@ __global__ __launch_bounds__(256) void k_bpred_logits(RingArgs a, const float* _
 
 // Logits for more than 32 tokens with h held in registers.  Workgroup
 // (q, range) takes the 32 tokens of group q and a range of 32-row blocks of
-// P2 (rows hot ..); wave w keeps both halves of h for quarter w of K (r / 4
-// entries: KS = r / 64 MFMA steps, 8 registers a step), so that only P2 goes
-// through LDS.  A stage is one half of K of a 32-row block (32 x r / 2
-// halves, by direct-to-LDS loads: 8 rows x 128 bytes per load, chunk slots
-// swizzled by the row group as in ring.hpp); waves 0-1 multiply the first
-// half, waves 2-3 the second, and the ring of four stages keeps three in
+// P2 (rows hot ..); wave w keeps both halves of h for eighths w and w + 4 of
+// K (r / 4 entries: KS = r / 64 MFMA steps, 8 registers a step), so that
+// only P2 goes through LDS.  A stage is one half of K of a 32-row block
+// (32 x r / 2 halves, by direct-to-LDS loads in the blocks of ring.hpp: 8
+// rows x 128 bytes per load, slots swizzled by row); in each half every
+// wave multiplies its eighth, and the ring of four stages keeps three in
 // flight.  After the second half of a block the four waves' partial sums go
 // through LDS, are added in wave order, and give the mask words as in
 // k_bpred_logits.  No row is split across workgroups, and h is read once per
@@ -476,15 +476,19 @@ __global__ __launch_bounds__(256) void k_bpred_logits_tq(const h16* __restrict__
     const h16* W = P2 + (size_t)hot * r;
     const uint32_t lbase = lds_addr(lds);
 
-    // this wave's h: token q*32 + li, chunk w*(r/32) + 2*step + kh (slots past B read the buffer's padding)
+    // this wave's h: token q*32 + li; step k < KS/2 of half f is chunk
+    // f*(r/16) + w*(r/64) + 2k + kh, in register f*(KS/2) + k (slots past B
+    // read the buffer's padding)
     f16x8 hh[KS], hl[KS];
     {
-        const size_t tro = (size_t)(q * 32 + li) * ldh + (size_t)(wave * (r >> 5) + kh) * 8;
+        const size_t tro = (size_t)(q * 32 + li) * ldh + (size_t)(wave * (r >> 6) + kh) * 8;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-            hh[k] = *reinterpret_cast<const f16x8*>(h_hi + tro + k * 16);
-            hl[k] = *reinterpret_cast<const f16x8*>(h_lo + tro + k * 16);
-        }
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int k = 0; k < KS / 2; ++k) {
+                hh[f * (KS / 2) + k] = *reinterpret_cast<const f16x8*>(h_hi + tro + f * (r / 2) + k * 16);
+                hl[f * (KS / 2) + k] = *reinterpret_cast<const f16x8*>(h_lo + tro + f * (r / 2) + k * 16);
+            }
     }
     // the range's biases to LDS, and h settled, before any stage goes out: a
     // compiler wait for a load inside the stage loop would drain the ring
@@ -502,8 +506,9 @@ __global__ __launch_bounds__(256) void k_bpred_logits_tq(const h16* __restrict__
         for (int i = 0; i < IPW; ++i) {
             const int blk = wave + 4 * i;
             const int g = blk / HB, cg = blk % HB;
-            const int row = min(rb * 32 + g * 8 + (lane & 7), nr - 1);
-            const int chunk = half * (r / 16) + cg * 8 + ((lane >> 3) ^ (g & 3));
+            const int rr = g * 8 + (lane >> 3);   // the lane's row within the block of 32
+            const int row = min(rb * 32 + rr, nr - 1);
+            const int chunk = half * (r / 16) + cg * 8 + ((lane & 7) ^ blk_swz(rr));
             dma16(W + (size_t)row * r + chunk * 8, dst + (uint32_t)blk * 1024u);
         }
     };
@@ -511,50 +516,50 @@ __global__ __launch_bounds__(256) void k_bpred_logits_tq(const h16* __restrict__
 #pragma unroll
     for (int j = 0; j < kTqStages - 1; ++j)
         if (j < ns) issue(j);
-    for (int s = 0; s < ns; ++s) {
-        const int rb = rb0 + (s >> 1), half = s & 1;
+    // one half of K of row block rb (stage s): every wave multiplies its eighth
+    auto half_stage = [&](int s, auto HALF, ring_f32x16& acc) {
+        constexpr int F = decltype(HALF)::value;
         if (s + kTqStages - 2 < ns) wait_vm<(kTqStages - 2) * IPW>();   // stage s is in
         else wait_vm<0>();
         ring_barrier();   // every wave's loads of stage s are in; everyone is past stage s - 1 and the sums
         if (s + kTqStages - 1 < ns) issue(s + kTqStages - 1);
-        if ((wave >> 1) == half) {
-            const char* buf = lds + (s % kTqStages) * STG;
-            const int g = li >> 3;
-            f16x8 a[KS];
+        const char* buf = lds + (s % kTqStages) * STG;
+        const int g = li >> 3;
+        f16x8 a[KS / 2];
 #pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                const int c = (wave & 1) * (r >> 5) + 2 * k + kh;   // chunk within the half
-                a[k] = *reinterpret_cast<const f16x8*>(buf + (g * HB + (c >> 3)) * 1024 +
-                                                       (((c & 7) ^ (g & 3)) << 7) + ((li & 7) << 4));
-            }
-            ring_f32x16 acc = {};
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hh[k], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hl[k], acc, 0, 0, 0);
-            }
-            // element e of lane l: row (e/4)*8 + 4*(l/32) + e%4, token l%32
-#pragma unroll
-            for (int e = 0; e < 16; ++e) red[wave * kTqRedW + e * kTqRedE + lane] = acc[e];
+        for (int k = 0; k < KS / 2; ++k) {
+            const int c = wave * (r >> 6) + 2 * k + kh;   // chunk within the half
+            a[k] = *reinterpret_cast<const f16x8*>(buf + (g * HB + (c >> 3)) * 1024 + blk_off(li, c & 7));
         }
-        if (half == 1) {
-            wait_lds_ops();
-            ring_barrier();
-            // wave w: tokens 4w + k (lanes 0-31) and 4w + k + 16 (lanes 32-63), row li
-            const int e = ((li >> 3) << 2) + (li & 3), hb = ((li >> 2) & 1) << 5;
-            const int grow = rb * 32 + li;
-            const float brow = s_b2[(rb - rb0) * 32 + li];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int n = 4 * wave + k + (kh << 4), t = q * 32 + n;
-                float v = 0.f;
+        for (int k = 0; k < KS / 2; ++k) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hh[F * (KS / 2) + k], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hl[F * (KS / 2) + k], acc, 0, 0, 0);
+        }
+    };
+    for (int rb = rb0; rb < rb1; ++rb) {
+        const int s = 2 * (rb - rb0);
+        ring_f32x16 acc = {};
+        half_stage(s, std::integral_constant<int, 0>{}, acc);
+        half_stage(s + 1, std::integral_constant<int, 1>{}, acc);
+        // element e of lane l: row (e/4)*8 + 4*(l/32) + e%4, token l%32
 #pragma unroll
-                for (int p = 0; p < 4; ++p) v += red[p * kTqRedW + e * kTqRedE + hb + n];
-                const bool on = (grow < nr) & (t < B) & (v + brow > thr);
-                const uint64_t m = __ballot(on);
-                if (li == 0 && t < B)
-                    masks32[(size_t)t * nw + ((hot + rb * 32) >> 5)] = (uint32_t)(m >> (lane & 32));
-            }
+        for (int e = 0; e < 16; ++e) red[wave * kTqRedW + e * kTqRedE + lane] = acc[e];
+        wait_lds_ops();
+        ring_barrier();
+        // wave w: tokens 4w + k (lanes 0-31) and 4w + k + 16 (lanes 32-63), row li
+        const int e = ((li >> 3) << 2) + (li & 3), hb = ((li >> 2) & 1) << 5;
+        const int grow = rb * 32 + li;
+        const float brow = s_b2[(rb - rb0) * 32 + li];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int n = 4 * wave + k + (kh << 4), t = q * 32 + n;
+            float v = 0.f;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) v += red[p * kTqRedW + e * kTqRedE + hb + n];
+            const bool on = (grow < nr) & (t < B) & (v + brow > thr);
+            const uint64_t m = __ballot(on);
+            if (li == 0 && t < B) masks32[(size_t)t * nw + ((hot + rb * 32) >> 5)] = (uint32_t)(m >> (lane & 32));
         }
     }
 }
@@ -620,10 +625,10 @@ __global__ __launch_bounds__(256) void k_bpred_compact(const uint32_t* __restric
 // Down GEMM.  Y[t][c] = sum_u A[t][u] W_down[U_u][c]: the contraction runs
 // over union entries, i.e. across rows of W_down.  Grid = (128-column tiles,
 // G chunks of the union list); a workgroup streams its chunk's rows of its
-// column tile through an LDS ring, stages of 64 union entries: 8-row x
-// 128-byte blocks of W_down (the ring.hpp block layout, by direct-to-LDS
-// loads, row ids taken from the chunk's list staged in LDS) and the stage's
-// activations, hi and lo (8 tokens x 64 entries per block).
+// column tile through an LDS ring, stages of KR union entries: 8-row x
+// 128-byte blocks of W_down (by direct-to-LDS loads as in ring.hpp, with the
+// slot swizzle dn_wswz; row ids taken from the chunk's list staged in LDS)
+// and the stage's activations, hi and lo (see DownCfg).
 //
 // The matrix cores need K (union entries) along each lane's operand, while
 // W_down holds columns along a row: ds_read_b64_tr_b16 transposes on the LDS
@@ -644,11 +649,11 @@ constexpr int kDnIds = 4096;   // union ids staged in LDS at a time (a window of
 // A stage is KR union entries: 64, or 32 with 128 tokens, where a 64-entry
 // stage (64 KB) would leave room for only two in LDS and the ring would hold
 // a single stage in flight; 32-entry stages give it four.  An activation
-// block is what one wave-wide load moves, TPB tokens x KR entries: 8 tokens
-// x 128 bytes with the chunk slots XOR-swizzled by the token group (32 lanes
-// reading one chunk of 32 tokens then hit 4 different 128-byte slots), or 16
-// tokens x 64 bytes, [chunk][token], whose 256-byte chunk rows are read
-// without bank conflicts as they are.
+// block is what one wave-wide load moves, TPB tokens x KR entries, the lanes
+// of one token on its contiguous bytes (so that the load unit merges them):
+// 8 tokens x 128 bytes laid out as the blocks of ring.hpp, or 16 tokens x 64
+// bytes, [token][slot], chunk c of token t in slot c ^ ((t / 4) % 4), which
+// puts the 16 tokens of one LDS read phase on 16 different 4-bank groups.
 template <int XG_>
 struct DownCfg {
     static constexpr int XG = XG_;
@@ -669,9 +674,13 @@ struct DownCfg {
                                   ? 4 : (3 * STAGE + kDnIds * 4 <= 156 * 1024 ? 3 : 2);
     static_assert(WBLK % 4 == 0 && IPW * (NS - 2) < 64, "loads per stage");
     static_assert(TPB == 8 || TPB == 16, "activation block shapes");
-    // LDS byte offset in an activation block of chunk c (8 entries) of its token t
+    // LDS byte offset in activation block tg of chunk c (8 entries) of token t
     static __device__ __forceinline__ int aoff(int tg, int c, int t) {
-        return TPB == 8 ? ((c ^ (tg & 3)) << 7) + ((t & 7) << 4) : (c << 8) + ((t & 15) << 4);
+        return TPB == 8 ? blk_off(tg * 8 + (t & 7), c) : ((t & 15) << 6) + ((c ^ ((t >> 2) & 3)) << 4);
+    }
+    // the chunk that lane `lane` of activation block tg loads (its slot is lane % (64 / TPB))
+    static __device__ __forceinline__ int achunk(int tg, int lane) {
+        return TPB == 8 ? (lane & 7) ^ blk_swz(tg * 8 + (lane >> 3)) : (lane & 3) ^ ((lane >> 4) & 3);
     }
 };
 
@@ -706,6 +715,13 @@ int union_down_chunks(int B, int d) {
     }
     return best;
 }
+
+// W_down blocks: 8 union entries x 128 bytes (64 columns), [entry][slot] as
+// the blocks of ring.hpp, but chunk c of entry k in slot c ^ dn_wswz(k): the
+// transposing reads below take entries 0-3 (or 4-7) at 4 column quads of two
+// neighbouring chunks per 16 lanes, and entries k and k + 2 (the same half of
+// the 256-byte bank cycle) must then fall in different 64-byte quarters.
+__device__ __forceinline__ int dn_wswz(int k) { return (k & 2) << 1; }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
@@ -766,20 +782,21 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     for (int i = 0; i < C::IPW; ++i) {
         const int b = wave + 4 * i;
         if (i < C::WBLK / 4) {
+            // lane j: entry 8 rg + j / 8 of the stage, slot j % 8 (see dn_wswz)
             const int rg = b / (C::CT / 64), cs = b % (C::CT / 64);
-            wofs[i] = rg * 8 + (lane & 7);
-            kofs[i] = c0 + cs * 64 + (((lane >> 3) ^ (rg & 7)) << 3);
+            wofs[i] = rg * 8 + (lane >> 3);
+            kofs[i] = c0 + cs * 64 + (((lane & 7) ^ dn_wswz(lane >> 3)) << 3);
             abase[i] = nullptr;
         } else {
-            // lane j writes LDS bytes 16j.. of the block: token j % TPB, and
-            // the chunk whose slot is j / TPB
+            // lane j writes LDS bytes 16j.. of the block: token j / (64 / TPB)
+            // of it, slot j % (64 / TPB)
             const int bx = b - C::WBLK;
             const int ix = bx / C::ABA, tg = bx % C::ABA;
-            const int t = tg * C::TPB + (lane % C::TPB);
+            const int t = tg * C::TPB + lane / (64 / C::TPB);
             const bool real = bx < C::ABLK && t < B;
             abase[i] = real ? (ix ? a_lo : a_hi) + (size_t)t * lda : nullptr;
             wofs[i] = 0;
-            kofs[i] = (C::TPB == 8 ? ((lane >> 3) ^ (tg & 3)) : lane / C::TPB) << 3;
+            kofs[i] = C::achunk(tg, lane) << 3;
         }
     }
     auto issue = [&](int st, int q) {
@@ -839,9 +856,10 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
                 // first of this lane's 4 columns in column block cb of the wave
                 const int col = (wave * C::CB + cb) * 32 + 16 * (g & 1) + 4 * (j & 3);
                 const int cs = col >> 6, ch = (col & 63) >> 3, quad = (col >> 2) & 1;
-                const char* wb = buf + (rg * (C::CT / 64) + cs) * 1024 + ((ch ^ (rg & 7)) << 7) + quad * 8;
-                w0[q][cb] = lds_read8_tr(wb + (j >> 2) * 16);
-                w1[q][cb] = lds_read8_tr(wb + ((j >> 2) + 4) * 16);
+                const char* wb = buf + (rg * (C::CT / 64) + cs) * 1024 + quad * 8;
+                const int k0 = j >> 2, k1 = k0 + 4;   // the block's rows this lane reads
+                w0[q][cb] = lds_read8_tr(wb + (k0 << 7) + ((ch ^ dn_wswz(k0)) << 4));
+                w1[q][cb] = lds_read8_tr(wb + (k1 << 7) + ((ch ^ dn_wswz(k1)) << 4));
             }
             const int c = 2 * q + kh;    // activation chunk (8 entries)
 #pragma unroll

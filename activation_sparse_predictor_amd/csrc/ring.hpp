@@ -4,15 +4,16 @@
 // ring by direct-to-LDS loads.
 //
 // Load geometry.  One "block" is what a single wave-wide 16-byte-per-lane load
-// moves: 8 rows x 128 contiguous bytes (lane j: row j % 8, 16-byte chunk j / 8
-// of the segment), written by global_load_lds_dwordx4 to 1 KB of LDS at
-// [chunk slot][row] x 16 bytes.  Eight full 128-byte lines per instruction
-// keep the gather at the rate of contiguous reads; a matrix-core operand
-// loaded straight from memory would touch 32 rows x 32 bytes per instruction,
-// which runs at well under half that rate.  Chunk c of a row in block group g
-// sits in slot c ^ (g & 3), so the 32 lanes that read one operand (32 rows or
-// tokens, one chunk) hit 4 different 128-byte slots of 4 blocks and the LDS
-// reads are free of bank conflicts.
+// moves: 8 rows x 128 contiguous bytes, written by global_load_lds_dwordx4 to
+// 1 KB of LDS, lane j at bytes 16j: row j / 8, slot j % 8 of that row.  The
+// eight lanes of a row cover its whole 128-byte line, so the load unit merges
+// them; with lane j on row j % 8 instead (eight lines, one lane each per
+// 16-byte step) the same loads ran at a third of the rate (measured on
+// MI355X: 38 against 111 GB/s per CU from L2).  Chunk c of row r sits in slot
+// c ^ blk_swz(r) = c ^ ((r / 2) % 8): the 16 lanes of one LDS read phase take
+// rows r0 .. r0 + 15 at one chunk, and their 16-byte pieces land on 16
+// different 4-bank groups (row parity picks the 128-byte half of the
+// 256-byte bank cycle, the swizzle the 16-byte group in it).
 //
 // Stages.  A stage covers SEG 128-byte segments (64*SEG halves of K) of every
 // operand row: NM matrices x RB rows and NX activation arrays x 8*XG tokens
@@ -50,6 +51,12 @@
 namespace pi {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Slot swizzle of the load blocks (see the load geometry above).
+__host__ __device__ constexpr int blk_swz(int r) { return (r >> 1) & 7; }
+// LDS byte offset, within a block, of chunk c of row r (the row's index in
+// its row set, of which the block holds rows 8 * (r / 8) ..)
+__device__ __forceinline__ int blk_off(int r, int c) { return ((r & 7) << 7) + ((c ^ blk_swz(r)) << 4); }
 typedef float ring_f32x16 __attribute__((ext_vector_type(16)));
 
 // Workgroup barrier without the memory fences of __syncthreads (those would
@@ -164,18 +171,19 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
             if (i < C::WBLK / 4) {
                 const int m = b / ((C::RB / 8) * C::SEG), rem = b % ((C::RB / 8) * C::SEG);
                 const int g = rem / C::SEG, sg = rem % C::SEG;
-                const int row = min(rb * C::RB + g * 8 + (lane & 7), nrows - 1);
+                const int rlr = g * 8 + (lane >> 3);   // the lane's row within the row block
+                const int row = min(rb * C::RB + rlr, nrows - 1);
                 const int id = GATHER ? min(max(a.rowlist[row], 0), a.wrows - 1) : row;
                 src[i] = (m == 0 ? a.W[0] : a.W[1]) + (size_t)id * a.ldw;
-                kofs[i] = sg * 64 + (((lane >> 3) ^ (g & 3)) << 3);
+                kofs[i] = sg * 64 + (((lane & 7) ^ blk_swz(rlr)) << 3);
                 ok[i] = true;
             } else {
                 const int bx = b - C::WBLK;
                 const int ix = bx / (C::XG * C::SEG), rem = bx % (C::XG * C::SEG);
                 const int tg = rem / C::SEG, sg = rem % C::SEG;
-                const int t = tg * 8 + (lane & 7);
+                const int t = tg * 8 + (lane >> 3);
                 src[i] = (ix == 0 ? a.X[0] : a.X[1]) + (size_t)min(t, a.B - 1) * a.ldx;
-                kofs[i] = sg * 64 + (((lane >> 3) ^ (tg & 3)) << 3);
+                kofs[i] = sg * 64 + (((lane & 7) ^ blk_swz(t)) << 3);
                 ok[i] = t < a.B;
             }
         }
@@ -215,7 +223,7 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
                 for (int ix = 0; ix < C::NX; ++ix) {
                     const int blk = C::WBLK + (ix * C::XG + tg) * C::SEG + sg;
-                    xv[j][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + ((cc ^ (tg & 3)) << 7) + ((t & 7) << 4));
+                    xv[j][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + blk_off(tg * 8 + (t & 7), cc));
                 }
 #pragma unroll
                 for (int rr = 0; rr < C::RBW; ++rr) {
@@ -223,7 +231,7 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
                     for (int m = 0; m < C::NM; ++m) {
                         const int blk = (m * (C::RB / 8) + g) * C::SEG + sg;
-                        wv[j][rr][m] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + ((cc ^ (g & 3)) << 7) + ((rl & 7) << 4));
+                        wv[j][rr][m] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + blk_off(rl, cc));
                     }
                 }
             }
