@@ -303,6 +303,145 @@ __device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, fl
     if (tid == 0) st_flag(&H.slots[tile], epoch);
 }
 
+// Logits tiles of the INT4 predictor, kQ4Tiles per workgroup.  INT4 rows
+// of r / 32 chunks (16 bytes, 32 codes); half-wave hf of wave w takes rows
+// 32 t + 8 w + hf + 2m (m < 4) of each of its tiles t, lane chunk
+// c = (lane & 31) + 32n.  The first column batch of every tile is requested
+// at once, then h is read (after the rows, so it is fresh), then each h chunk
+// and its sum serve the four rows of every tile.  One h collection per four
+// tiles (a quarter of the workgroups polling h, and four tiles' rows in
+// flight during the wait); the arithmetic per row is the single-tile form's.
+constexpr int kQ4Tiles = 4;
+__device__ __forceinline__ void q4_logits_tiles(int tw, const uint8_t* __restrict__ q2, const h16* __restrict__ s2,
+                                                const float* __restrict__ b2, int ffn, int r, float thr, int hot,
+                                                const uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
+                                                const uint32_t* __restrict__ epoch_word,
+                                                const float* __restrict__ zero, float* sh, uint32_t* s_act) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hf = lane >> 5;
+    const int NT = (ffn + kLTile - 1) / kLTile;
+    const int t0 = tw * kQ4Tiles;
+    // every tile of this workgroup in the always-listed prefix: no P2 row and
+    // no wait for h (the compaction writes the prefix without masks)
+    if (min(t0 + kQ4Tiles, NT) * kLTile <= hot) return;
+    const int ncw = r >> 5, ng = r >> 6;
+    const int NB = (ncw + 31) >> 5;   // column batches (1 for r <= 1024)
+    auto rowof = [&](int qt, int m) { return min((t0 + qt) * kLTile + wave * kLRows + hf + 2 * m, ffn - 1); };
+    const int c0 = lane & 31;
+    // first batch of every tile (a lane past the row end reads its last chunk:
+    // valid, unused), and lane k < 8's bias of row 8w + k of every tile
+    u32x4 w[kQ4Tiles][4];
+    h16 sc[kQ4Tiles][4];
+    float bias[kQ4Tiles];
+    {
+        const int cl = min(c0, ncw - 1);
+#pragma unroll
+        for (int qt = 0; qt < kQ4Tiles; ++qt) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int rr = rowof(qt, m);
+                w[qt][m] = ld16_stream(q2 + (size_t)rr * (r / 2) + (size_t)cl * 16);
+                sc[qt][m] = s2[(size_t)rr * ng + (cl >> 1)];
+            }
+            bias[qt] = *(b2 ? b2 + min((t0 + qt) * kLTile + wave * kLRows + (lane & (kLRows - 1)), ffn - 1) : zero);
+        }
+    }
+    // h, once the rows are in (a poll issued behind them would come back with
+    // them, holding h as it was when the poll was served)
+    wait_own_memory();
+    const uint32_t epoch = next_epoch(*epoch_word);
+    bool ok = true;
+    for (int i0 = tid; i0 < r; i0 += 1024) {
+        uint64_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld_tag(&htag[i0 + q * 256]);   // padded to 1024 words
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = i0 + q * 256;
+            if (i < r) {
+                ok = poll_tag(&htag[i], v[q], epoch) && ok;
+                sh[i] = __uint_as_float((uint32_t)v[q]);
+            }
+        }
+    }
+    ok = __syncthreads_and(ok);
+    float a4[kQ4Tiles][4];
+#pragma unroll
+    for (int qt = 0; qt < kQ4Tiles; ++qt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a4[qt][m] = 0.f;
+    for (int n = 0; n < NB; ++n) {
+        const int c = c0 + 32 * n;
+        if (n > 0) {   // r > 1024: the later batches, one at a time
+            const int cl = min(c, ncw - 1);
+#pragma unroll
+            for (int qt = 0; qt < kQ4Tiles; ++qt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int rr = rowof(qt, m);
+                    w[qt][m] = ld16_stream(q2 + (size_t)rr * (r / 2) + (size_t)cl * 16);
+                    sc[qt][m] = s2[(size_t)rr * ng + (cl >> 1)];
+                }
+        }
+        if (c < ncw) {
+            const f32x4* hp = reinterpret_cast<const f32x4*>(sh + c * 32);
+            float hv[32];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const f32x4 v = hp[q];
+                hv[4 * q] = v.x;
+                hv[4 * q + 1] = v.y;
+                hv[4 * q + 2] = v.z;
+                hv[4 * q + 3] = v.w;
+            }
+            // sum_k (code_k - 8) h_k = sum_k code_k h_k - 8 sum_k h_k: the
+            // chunk's sum of h is taken once for all its rows
+            float hs = 0.f;
+#pragma unroll
+            for (int k = 0; k < 32; ++k) hs += hv[k];
+#pragma unroll
+            for (int qt = 0; qt < kQ4Tiles; ++qt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t cw[4] = {w[qt][m].x, w[qt][m].y, w[qt][m].z, w[qt][m].w};
+                    float p = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = cw[e] & 0x0F0F0F0Fu;          // byte j: the code of weight 8e + 2j
+                        const uint32_t hi = (cw[e] >> 4) & 0x0F0F0F0Fu;   // byte j: the code of weight 8e + 2j + 1
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            p = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j], p);
+                            p = fmaf((float)((hi >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j + 1], p);
+                        }
+                    }
+                    a4[qt][m] = fmaf((float)sc[qt][m], fmaf(-8.f, hs, p), a4[qt][m]);
+                }
+        }
+    }
+#pragma unroll
+    for (int qt = 0; qt < kQ4Tiles; ++qt) {
+        const int tile = t0 + qt;
+        if (tile >= NT) break;
+        float zk = 0.f;   // lane k < 8: row k is half k & 1's row 2m + (k & 1), m = k / 2
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float z = __shfl(group_sum<32>(a4[qt][m]), (lane & 1) << 5, 64);
+            if (((lane & (kLRows - 1)) >> 1) == m) zk = z;
+        }
+        if ((tile + 1) * kLTile <= hot) continue;   // a prefix tile: no mask
+        const int row0 = tile * kLTile + wave * kLRows;
+        if (lane < kLRows) s_act[wave * kLRows + lane] = (row0 + lane < ffn) && (zk + bias[qt] > thr);
+        __syncthreads();
+        if (wave == 0) {
+            const uint64_t mk = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
+            if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)mk);
+        }
+        __syncthreads();   // s_act is the next tile's
+    }
+}
+
 template <bool Q4, int HK>
 __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x, int d,
                                                        const h16* __restrict__ P1,
@@ -320,6 +459,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int NT = (ffn + kLTile - 1) / kLTile;
+    const int NTW = Q4 ? (NT + kQ4Tiles - 1) / kQ4Tiles : NT;   // logits workgroups
     const int NHU = HK >= 0 ? H.NHU : 0;
     const int b = blockIdx.x;
     const int lg0 = NA + NHU;   // first logits tile
@@ -330,9 +470,9 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             hot_up_role<HK>(H, x, d, b - NA, sh, zero);
             return;
         }
-        if (b > lg0 + NT) {
+        if (b > lg0 + NTW) {
             __shared__ int s_hflag;
-            hot_down_role(H, d, b - (lg0 + NT + 1), sh, &s_hflag);
+            hot_down_role(H, d, b - (lg0 + NTW + 1), sh, &s_hflag);
             return;
         }
     }
@@ -428,7 +568,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         return;
     }
 
-    if (b == lg0 + NT) {
+    if (b == lg0 + NTW) {
         // ---------------- ordered compaction.  The always-listed prefix [0, hot)
         // is written first, by every thread in turn (coalesced, no mask read).
         // The other tiles go 1024 per round: thread k takes tiles 2k and 2k + 1
@@ -497,6 +637,11 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         return;
     }
 
+    if constexpr (Q4) {
+        q4_logits_tiles(tile, reinterpret_cast<const uint8_t*>(P2), s2, b2, ffn, r, thr, hot, htag, mtag, epoch_word,
+                        zero, sh, s_act);
+        return;
+    }
     // ---------------- logits tile: wave w owns neurons tile*32 + 8w + k (k < 8); lane l
     // takes chunks l + 64m of all eight rows, so an h chunk read from LDS serves
     // eight rows
@@ -558,82 +703,6 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)m);
         }
     };
-    if constexpr (Q4) {
-        // INT4 rows of r / 32 chunks (16 bytes, 32 codes).  Half-wave hf takes
-        // rows row0 + hf + 2m (m < 4), lane chunk c = (lane & 31) + 32n: each
-        // h chunk (32 fp32 from LDS) serves four rows.
-        const int hf = lane >> 5;
-        const int ncw = r >> 5, ng = r >> 6;
-        const int NB = (ncw + 31) >> 5;   // column batches (1 for r <= 1024)
-        const uint8_t* qrow[4];
-        const h16* srow[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int rr = min(row0 + hf + 2 * m, ffn - 1);
-            qrow[m] = reinterpret_cast<const uint8_t*>(P2) + (size_t)rr * (r / 2);
-            srow[m] = s2 + (size_t)rr * ng;
-        }
-        float a4[4] = {0.f, 0.f, 0.f, 0.f};
-        int n = 0;
-        do {
-            // a lane past the row end reads its last chunk (valid, unused)
-            const int c = (lane & 31) + 32 * n;
-            const int cl = min(c, ncw - 1);
-            u32x4 w[4];
-            h16 sc[4];   // converted at use: no load waits for another
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                w[m] = ld16_stream(qrow[m] + (size_t)cl * 16);
-                sc[m] = srow[m][cl >> 1];
-            }
-            if (!have_h) {
-                wait_own_memory();
-                collect_h();
-            }
-            if (c < ncw) {
-                const f32x4* hp = reinterpret_cast<const f32x4*>(sh + c * 32);
-                float hv[32];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const f32x4 v = hp[q];
-                    hv[4 * q] = v.x;
-                    hv[4 * q + 1] = v.y;
-                    hv[4 * q + 2] = v.z;
-                    hv[4 * q + 3] = v.w;
-                }
-                // sum_k (code_k - 8) h_k = sum_k code_k h_k - 8 sum_k h_k: the
-                // chunk's sum of h is taken once for its four rows, and a code
-                // is one byte conversion after the word's nibbles are split
-                float hs = 0.f;
-#pragma unroll
-                for (int k = 0; k < 32; ++k) hs += hv[k];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t cw[4] = {w[m].x, w[m].y, w[m].z, w[m].w};
-                    float p = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = cw[e] & 0x0F0F0F0Fu;          // byte j: the code of weight 8e + 2j
-                        const uint32_t hi = (cw[e] >> 4) & 0x0F0F0F0Fu;   // byte j: the code of weight 8e + 2j + 1
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            p = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j], p);
-                            p = fmaf((float)((hi >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j + 1], p);
-                        }
-                    }
-                    a4[m] = fmaf((float)sc[m], fmaf(-8.f, hs, p), a4[m]);
-                }
-            }
-        } while (++n < NB);
-        float zk = 0.f;   // lane k < 8: row k is half k & 1's row 2m + (k & 1), m = k / 2
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float z = __shfl(group_sum<32>(a4[m]), (lane & 1) << 5, 64);
-            if (((lane & (kLRows - 1)) >> 1) == m) zk = z;
-        }
-        publish(zk);
-        return;
-    }
     auto accumulate = [&](const u32x4 (&w)[kLRows][kLCols], int m0) {
 #pragma unroll
         for (int m = 0; m < kLCols; ++m) {
@@ -1027,7 +1096,7 @@ hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const
     const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
-    hipLaunchKernelGGL((k_predict_fused<true, -1>), dim3(NA + L.NT + 1), dim3(256), shm, s, x, d,
+    hipLaunchKernelGGL((k_predict_fused<true, -1>), dim3(NA + (L.NT + kQ4Tiles - 1) / kQ4Tiles + 1), dim3(256), shm, s, x, d,
                        reinterpret_cast<const h16*>(q1), b1, (int)relu, r, reinterpret_cast<const h16*>(q2), b2, ffn,
                        thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot,
                        NA, s1, s2, HotArgs{});
