@@ -10,6 +10,11 @@
 //                             tile's 32-bit mask as a tagged word (a tile of
 //                             the always-listed hot prefix exits at once)
 //   the next one              gathers every mask and writes idx (ascending) and count
+//   INT4 predictor            (pi_ffn_predict_q4) four logits tiles a workgroup
+//                             and no gathering workgroup: each workgroup finds
+//                             its place in the list by a look-back over the
+//                             earlier workgroups' counts and writes its own ids;
+//                             the last one writes count
 //   the last T * G            (pi_ffn_decode_hot only) hot-prefix W_down: column
 //                             tile x chunk of the prefix, accumulated from the
 //                             prefix's a_i; the tile's last chunk adds the chunk
@@ -34,11 +39,12 @@
 // or counter in between.  The epoch is one more than the previous launch's
 // (never 0), kept in the workspace header, so a word left over from an
 // earlier call never passes for a current one, also when the launches are
-// replayed from a captured graph.  In predict the compaction workgroup stores
-// it back: it runs after every other workgroup has read the epoch, because it
-// waits for every tile's mask and a tile outside the always-listed prefix
-// waits for every h (when every tile lies in the prefix, no hidden-row
-// workgroup is launched).  In the FFN the last chunk of each column tile stores it into that
+// replayed from a captured graph.  In predict the compaction workgroup (INT4:
+// the last logits workgroup, once its look-back has resolved) stores it back:
+// it runs after every other workgroup has read the epoch, because it waits for
+// every tile's mask (every workgroup's count) and a tile outside the
+// always-listed prefix waits for every h (when every tile lies in the prefix,
+// no hidden-row workgroup is launched).  In the FFN the last chunk of each column tile stores it into that
 // tile's slot, and a launch takes the oldest slot plus one: while any W_down
 // workgroup of a launch is still running, its tile's slot holds the previous
 // epoch.  A workgroup only waits for
@@ -109,6 +115,7 @@ constexpr int kLTile = 32;    // neurons per logits tile (one 32-bit mask), 8 pe
 constexpr int kLRows = 8;     // rows per wave
 constexpr int kLCols = 2;     // 64-lane chunk columns per batch: 16 P2 loads in flight per lane
 static_assert(kLRows * 4 == kLTile, "4 waves per logits tile");
+constexpr int kQ4Tiles = 4;   // logits tiles per workgroup of the INT4 predictor
 
 // At the 107 VGPRs this needs, 4 workgroups fit per CU: of the 1153 of a
 // 1024 x 28672 predictor, the last 129 logits tiles start as hidden rows
@@ -303,6 +310,114 @@ __device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, fl
     if (tid == 0) st_flag(&H.slots[tile], epoch);
 }
 
+// The ordered list, written by the logits workgroups themselves with a
+// single-pass prefix sum over their counts (decoupled look-back: Merrill and
+// Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016).
+// Workgroup w owns tiles [w TPW, w TPW + TPW).  It publishes in desc[w] first
+// its own count (AGG), then the count of every neuron up to its last tile
+// (INC, the flag bit set).  It sums its predecessors' descriptors back to the
+// nearest INC, 256 of them per round (one a thread), and writes its neurons'
+// ids at their positions.  The last workgroup writes the count and stores the
+// epoch: an INC stands for every workgroup before it, so by then every one
+// that reads the epoch has read it.  Workgroups below w0 hold only tiles of
+// the always-listed prefix: their counts are known (32 a tile), they publish
+// nothing and read no epoch.  ERR marks a wait that ran out, here or before;
+// it passes down the chain and makes the count -1.  The INT4 predictor uses
+// it: its workgroups (four tiles each) are all resident at once.  With one
+// tile a workgroup (the fp16 predictor, more workgroups than slots) the
+// look-back waits held slots that later tiles needed and made the step
+// slower, so that predictor keeps its gathering workgroup.
+constexpr uint32_t kDescInc = 1u << 31, kDescErr = 1u << 30, kDescVal = kDescErr - 1u;
+// Descriptors sit 128 bytes apart: with every workgroup polling its
+// predecessors', eight to a cache line made the step 0.7 us slower.
+constexpr int kDescStride = 16;
+static_assert(kQ4Tiles == 4 && kDescStride * 8 == 128, "fused_pred_layout sizes the descriptors so");
+
+template <int TPW>
+__device__ __forceinline__ void list_prefix_tiles(int w, int NT, int NW, int32_t* __restrict__ idx,
+                                                  int32_t* __restrict__ count, uint32_t* __restrict__ epoch_word) {
+    const int j0 = w * TPW * kLTile, j1 = min(w * TPW + TPW, NT) * kLTile;
+    for (int j = j0 + (int)threadIdx.x; j < j1; j += 256) idx[j] = j;
+    if (w == NW - 1 && threadIdx.x == 0) {
+        count[0] = j1;
+        st_flag(epoch_word, next_epoch(*epoch_word));
+    }
+}
+
+// s_mask: the TPW tile masks (LDS, written before a barrier); ok: this
+// workgroup's own waits held (block-uniform); s_red: 8 words of LDS.
+template <int TPW>
+__device__ __forceinline__ void list_tiles(int w, int w0, int NW, const uint32_t* s_mask, bool ok, uint32_t epoch,
+                                           uint64_t* __restrict__ desc, int32_t* __restrict__ idx,
+                                           int32_t* __restrict__ count, uint32_t* __restrict__ epoch_word,
+                                           uint32_t* s_red, int ffn) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t agg = 0;
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) agg += (uint32_t)__popc(s_mask[q]);
+    uint32_t flags = ok ? 0u : kDescErr;
+    uint32_t excl = (uint32_t)(w0 * TPW * kLTile);
+    if (w > w0) {
+        if (tid == 0) st_tag(&desc[(size_t)w * kDescStride], epoch, flags | agg);
+        uint32_t sum = 0;
+        for (int base = w;; base -= 256) {
+            const int j = base - 1 - tid;   // thread 0: the nearest predecessor
+            const bool in = j >= w0;
+            uint64_t v = ld_tag(&desc[(size_t)max(j, w0) * kDescStride]);
+            bool good = true;
+            if (in) good = poll_tag(&desc[(size_t)j * kDescStride], v, epoch);
+            const uint32_t lo = (uint32_t)v;
+            const uint64_t inc = __ballot(in && good && (lo & kDescInc));
+            if (lane == 0) s_red[wave] = inc ? (uint32_t)(wave * 64 + __builtin_ctzll(inc)) : 256u;
+            __syncthreads();
+            const uint32_t first = min(min(s_red[0], s_red[1]), min(s_red[2], s_red[3]));
+            // the descriptors nearer than the nearest INC, and that INC
+            const bool take = in && (uint32_t)tid <= first;
+            uint32_t val = take ? (lo & kDescVal) : 0u;
+            uint32_t bad = take && (!good || (lo & kDescErr)) ? 1u : 0u;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                val += __shfl_xor(val, off, 64);
+                bad |= __shfl_xor(bad, off, 64);
+            }
+            __syncthreads();
+            if (lane == 0) {
+                s_red[wave] = val;
+                s_red[4 + wave] = bad;
+            }
+            __syncthreads();
+            sum += s_red[0] + s_red[1] + s_red[2] + s_red[3];
+            if (s_red[4] | s_red[5] | s_red[6] | s_red[7]) flags = kDescErr;
+            __syncthreads();   // s_red is the next round's
+            if (first < 256u) {   // an INC counts every neuron before it
+                excl = sum;
+                break;
+            }
+            if (base - 256 <= w0) {   // back to the prefix workgroups
+                excl += sum;
+                break;
+            }
+        }
+    }
+    if (tid == 0) st_tag(&desc[(size_t)w * kDescStride], epoch, flags | kDescInc | min(excl + agg, kDescVal));
+    if (!flags && tid < TPW * kLTile) {
+        const int q = tid >> 5, bit = tid & 31;
+        const uint32_t m = s_mask[q];
+        if ((m >> bit) & 1u) {
+            uint32_t pos = excl + (uint32_t)__popc(m & ((1u << bit) - 1u));
+#pragma unroll
+            for (int q2 = 0; q2 < TPW - 1; ++q2)
+                if (q2 < q) pos += (uint32_t)__popc(s_mask[q2]);
+            if (pos < (uint32_t)ffn) idx[pos] = (w * TPW + q) * kLTile + bit;
+        }
+    }
+    if (w == NW - 1 && tid == 0) {
+        count[0] = flags ? -1 : (int32_t)(excl + agg);
+        st_flag(epoch_word, epoch);
+    }
+}
+
 // Logits tiles of the INT4 predictor, kQ4Tiles per workgroup.  INT4 rows
 // of r / 32 chunks (16 bytes, 32 codes); half-wave hf of wave w takes rows
 // 32 t + 8 w + hf + 2m (m < 4) of each of its tiles t, lane chunk
@@ -310,25 +425,40 @@ __device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, fl
 // at once, then h is read (after the rows, so it is fresh), then each h chunk
 // and its sum serve the four rows of every tile.  One h collection per four
 // tiles (a quarter of the workgroups polling h, and four tiles' rows in
-// flight during the wait); the arithmetic per row is the single-tile form's.
-constexpr int kQ4Tiles = 4;
+// flight during the wait).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Bytes 2 UP and 2 UP + 1 of v, each below 16, as floats u * byte.  The fp8
+// (e4m3) conversion reads such a byte as a multiple of the format's smallest
+// step u (a power of two: subnormals, then the first binade, same spacing), so
+// no value is rounded; one instruction converts two codes.
+template <bool UP>
+__device__ __forceinline__ f32x2 code_pair(uint32_t v) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)v, UP);
+}
 __device__ __forceinline__ void q4_logits_tiles(int tw, const uint8_t* __restrict__ q2, const h16* __restrict__ s2,
                                                 const float* __restrict__ b2, int ffn, int r, float thr, int hot,
-                                                const uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
-                                                const uint32_t* __restrict__ epoch_word,
-                                                const float* __restrict__ zero, float* sh, uint32_t* s_act) {
+                                                const uint64_t* __restrict__ htag, uint64_t* __restrict__ desc,
+                                                uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
+                                                int32_t* __restrict__ count, const float* __restrict__ zero, float* sh,
+                                                uint32_t* s_act, uint32_t* s_mask, uint32_t* s_red) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hf = lane >> 5;
     const int NT = (ffn + kLTile - 1) / kLTile;
+    const int NW = (NT + kQ4Tiles - 1) / kQ4Tiles;
+    const int w0 = min(hot / kLTile, NT) / kQ4Tiles;   // workgroups holding only prefix tiles
     const int t0 = tw * kQ4Tiles;
     // every tile of this workgroup in the always-listed prefix: no P2 row and
-    // no wait for h (the compaction writes the prefix without masks)
-    if (min(t0 + kQ4Tiles, NT) * kLTile <= hot) return;
+    // no wait for h
+    if (min(t0 + kQ4Tiles, NT) * kLTile <= hot) {
+        list_prefix_tiles<kQ4Tiles>(tw, NT, NW, idx, count, epoch_word);
+        return;
+    }
     const int ncw = r >> 5, ng = r >> 6;
     const int NB = (ncw + 31) >> 5;   // column batches (1 for r <= 1024)
     auto rowof = [&](int qt, int m) { return min((t0 + qt) * kLTile + wave * kLRows + hf + 2 * m, ffn - 1); };
     const int c0 = lane & 31;
+    const float inv_u = 8.f / code_pair<false>(8u).x;   // 1 / u
     // first batch of every tile (a lane past the row end reads its last chunk:
     // valid, unused), and lane k < 8's bias of row 8w + k of every tile
     u32x4 w[kQ4Tiles][4];
@@ -400,46 +530,73 @@ __device__ __forceinline__ void q4_logits_tiles(int tw, const uint8_t* __restric
             float hs = 0.f;
 #pragma unroll
             for (int k = 0; k < 32; ++k) hs += hv[k];
+            const float nhs8 = -8.f * hs;
+            float p[kQ4Tiles][4];
 #pragma unroll
             for (int qt = 0; qt < kQ4Tiles; ++qt)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const uint32_t cw[4] = {w[qt][m].x, w[qt][m].y, w[qt][m].z, w[qt][m].w};
-                    float p = 0.f;
+                for (int m = 0; m < 4; ++m) p[qt][m] = 0.f;
+            // word e of every row in turn (sixteen independent sums); each
+            // nibble field becomes a byte (lo: weights 8e + 2j, hi: 8e + 2j + 1)
+            // and each byte pair converts in one instruction to u * code
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo = cw[e] & 0x0F0F0F0Fu;          // byte j: the code of weight 8e + 2j
-                        const uint32_t hi = (cw[e] >> 4) & 0x0F0F0F0Fu;   // byte j: the code of weight 8e + 2j + 1
+            for (int e = 0; e < 4; ++e)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            p = fmaf((float)((lo >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j], p);
-                            p = fmaf((float)((hi >> (8 * j)) & 0xFFu), hv[8 * e + 2 * j + 1], p);
-                        }
+                for (int qt = 0; qt < kQ4Tiles; ++qt)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const uint32_t cw = e == 0 ? w[qt][m].x : e == 1 ? w[qt][m].y : e == 2 ? w[qt][m].z : w[qt][m].w;
+                        const uint32_t lo = cw & 0x0F0F0F0Fu;
+                        const uint32_t hi = (cw >> 4) & 0x0F0F0F0Fu;
+                        const f32x2 l01 = code_pair<false>(lo), l23 = code_pair<true>(lo);
+                        const f32x2 h01 = code_pair<false>(hi), h23 = code_pair<true>(hi);
+                        float s = p[qt][m];
+                        s = fmaf(l01.x, hv[8 * e + 0], s);
+                        s = fmaf(h01.x, hv[8 * e + 1], s);
+                        s = fmaf(l01.y, hv[8 * e + 2], s);
+                        s = fmaf(h01.y, hv[8 * e + 3], s);
+                        s = fmaf(l23.x, hv[8 * e + 4], s);
+                        s = fmaf(h23.x, hv[8 * e + 5], s);
+                        s = fmaf(l23.y, hv[8 * e + 6], s);
+                        s = fmaf(h23.y, hv[8 * e + 7], s);
+                        p[qt][m] = s;
                     }
-                    a4[qt][m] = fmaf((float)sc[qt][m], fmaf(-8.f, hs, p), a4[qt][m]);
-                }
+            // p = u * sum_k code_k h_k exactly (u a power of two)
+#pragma unroll
+            for (int qt = 0; qt < kQ4Tiles; ++qt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    a4[qt][m] = fmaf((float)sc[qt][m], fmaf(p[qt][m], inv_u, nhs8), a4[qt][m]);
         }
     }
 #pragma unroll
     for (int qt = 0; qt < kQ4Tiles; ++qt) {
         const int tile = t0 + qt;
-        if (tile >= NT) break;
+        if (tile >= NT) {   // past the last tile
+            if (tid == 0) s_mask[qt] = 0u;
+            continue;
+        }
         float zk = 0.f;   // lane k < 8: row k is half k & 1's row 2m + (k & 1), m = k / 2
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const float z = __shfl(group_sum<32>(a4[qt][m]), (lane & 1) << 5, 64);
             if (((lane & (kLRows - 1)) >> 1) == m) zk = z;
         }
-        if ((tile + 1) * kLTile <= hot) continue;   // a prefix tile: no mask
+        if ((tile + 1) * kLTile <= hot) {   // a prefix tile: every neuron listed
+            if (tid == 0) s_mask[qt] = ~0u;
+            continue;
+        }
         const int row0 = tile * kLTile + wave * kLRows;
         if (lane < kLRows) s_act[wave * kLRows + lane] = (row0 + lane < ffn) && (zk + bias[qt] > thr);
         __syncthreads();
         if (wave == 0) {
             const uint64_t mk = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
-            if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)mk);
+            if (lane == 0) s_mask[qt] = (uint32_t)mk;
         }
         __syncthreads();   // s_act is the next tile's
     }
+    __syncthreads();
+    list_tiles<kQ4Tiles>(tw, w0, NW, s_mask, ok, epoch, desc, idx, count, epoch_word, s_red, ffn);
 }
 
 template <bool Q4, int HK>
@@ -448,18 +605,18 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                                                        const float* __restrict__ b1, int relu, int r,
                                                        const h16* __restrict__ P2,
                                                        const float* __restrict__ b2, int ffn, float thr,
-                                                       uint64_t* __restrict__ htag, uint64_t* __restrict__ mtag,
+                                                       uint64_t* __restrict__ htag, uint64_t* __restrict__ desc,
                                                        uint32_t* __restrict__ epoch_word, int32_t* __restrict__ idx,
                                                        int32_t* __restrict__ count, const float* __restrict__ zero,
                                                        int hot, int NA, const h16* __restrict__ s1,
                                                        const h16* __restrict__ s2, HotArgs H) {
     extern __shared__ float sh[];  // hidden role: x (d fp16); logits role: h (r fp32)
     __shared__ uint32_t s_act[kLTile];
-    __shared__ uint32_t s_part[8];
+    __shared__ uint32_t s_mask[kQ4Tiles];
+    __shared__ uint32_t s_red[8];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int NT = (ffn + kLTile - 1) / kLTile;
-    const int NTW = Q4 ? (NT + kQ4Tiles - 1) / kQ4Tiles : NT;   // logits workgroups
     const int NHU = HK >= 0 ? H.NHU : 0;
     const int b = blockIdx.x;
     const int lg0 = NA + NHU;   // first logits tile
@@ -470,9 +627,9 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             hot_up_role<HK>(H, x, d, b - NA, sh, zero);
             return;
         }
-        if (b > lg0 + NTW) {
+        if (b > lg0 + NT) {
             __shared__ int s_hflag;
-            hot_down_role(H, d, b - (lg0 + NTW + 1), sh, &s_hflag);
+            hot_down_role(H, d, b - (lg0 + NT + 1), sh, &s_hflag);
             return;
         }
     }
@@ -568,7 +725,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         return;
     }
 
-    if (b == lg0 + NTW) {
+    if (!Q4 && b == lg0 + NT) {
         // ---------------- ordered compaction.  The always-listed prefix [0, hot)
         // is written first, by every thread in turn (coalesced, no mask read).
         // The other tiles go 1024 per round: thread k takes tiles 2k and 2k + 1
@@ -582,14 +739,14 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         for (int t0 = hot / kLTile; t0 < NT; t0 += 1024) {
             uint64_t m4[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&mtag[min(t0 + (q >> 1) * 512 + tid * 2 + (q & 1), NT - 1)]);
+            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&desc[min(t0 + (q >> 1) * 512 + tid * 2 + (q & 1), NT - 1)]);
             uint32_t bits[4], cnt2[2], incl2[2];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int t = t0 + (q >> 1) * 512 + tid * 2 + (q & 1);
                 bits[q] = 0u;
                 if (t < NT) {
-                    if (poll_tag(&mtag[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
+                    if (poll_tag(&desc[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
                     else good = false;
                 }
             }
@@ -603,15 +760,15 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
                     if (lane >= off) incl += v;
                 }
                 incl2[h] = incl;
-                if (lane == 63) s_part[h * 4 + wave] = incl;
+                if (lane == 63) s_red[h * 4 + wave] = incl;
             }
             __syncthreads();
             uint32_t run = base;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 uint32_t pos = run + incl2[h] - cnt2[h];
-                for (int w2 = 0; w2 < wave; ++w2) pos += s_part[h * 4 + w2];
-                run += s_part[h * 4] + s_part[h * 4 + 1] + s_part[h * 4 + 2] + s_part[h * 4 + 3];
+                for (int w2 = 0; w2 < wave; ++w2) pos += s_red[h * 4 + w2];
+                run += s_red[h * 4] + s_red[h * 4 + 1] + s_red[h * 4 + 2] + s_red[h * 4 + 3];
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     uint32_t m = bits[2 * h + e];
@@ -638,8 +795,8 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     }
 
     if constexpr (Q4) {
-        q4_logits_tiles(tile, reinterpret_cast<const uint8_t*>(P2), s2, b2, ffn, r, thr, hot, htag, mtag, epoch_word,
-                        zero, sh, s_act);
+        q4_logits_tiles(tile, reinterpret_cast<const uint8_t*>(P2), s2, b2, ffn, r, thr, hot, htag, desc, epoch_word,
+                        idx, count, zero, sh, s_act, s_mask, s_red);
         return;
     }
     // ---------------- logits tile: wave w owns neurons tile*32 + 8w + k (k < 8); lane l
@@ -700,7 +857,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
         __syncthreads();
         if (wave == 0) {
             const uint64_t m = __ballot(lane < kLTile && s_act[lane & (kLTile - 1)] != 0u);
-            if (lane == 0 && ok) st_tag(&mtag[tile], epoch, (uint32_t)m);
+            if (lane == 0 && ok) st_tag(&desc[tile], epoch, (uint32_t)m);
         }
     };
     auto accumulate = [&](const u32x4 (&w)[kLRows][kLCols], int m0) {
@@ -1039,11 +1196,12 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 }
 
 // Hidden-row workgroups of a predict launch: none when every logits tile lies
-// in the always-listed prefix.  The compaction stores the launch's epoch once
-// it has every mask, and that orders the store after every other workgroup's
-// read of the epoch only because a tile outside the prefix waits for every
-// h; with no such tile a late hidden-row workgroup could read the stored
-// epoch and publish h tagged as the next launch's, so none is launched.
+// in the always-listed prefix.  The compaction (INT4: the last logits
+// workgroup) stores the launch's epoch once it has every mask (count), and
+// that orders the store after every other workgroup's read of the epoch only
+// because a tile outside the prefix waits for every h; with no such tile a
+// late hidden-row workgroup could read the stored epoch and publish h tagged
+// as the next launch's, so none is launched.
 static int hidden_workgroups(int r, int ffn, int hot) {
     const int NT = (ffn + kLTile - 1) / kLTile;
     return NT * kLTile <= hot ? 0 : (r + 3) / 4;
@@ -1077,12 +1235,12 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
                                 const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
                                 hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
-    uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
+    uint64_t* desc = reinterpret_cast<uint64_t*>(data + L.desc);
     const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
     hipLaunchKernelGGL((k_predict_fused<false, -1>), dim3(NA + L.NT + 1), dim3(256), shm, s, x, d, P1, b1, (int)relu,
-                       r, P2, b2, ffn, thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count,
+                       r, P2, b2, ffn, thr, htag, desc, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count,
                        zero, hot, NA, nullptr, nullptr, HotArgs{});
     return hipGetLastError();
 }
@@ -1092,13 +1250,13 @@ hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const
                                    float thr, const FusedPredLayout& L, char* hdr, char* data, int32_t* idx,
                                    int32_t* count, hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
-    uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
+    uint64_t* desc = reinterpret_cast<uint64_t*>(data + L.desc);
     const int NA = hidden_workgroups(r, ffn, hot);
     const size_t shm = (size_t)(d * 2 > r * 4 ? d * 2 : r * 4);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
-    hipLaunchKernelGGL((k_predict_fused<true, -1>), dim3(NA + (L.NT + kQ4Tiles - 1) / kQ4Tiles + 1), dim3(256), shm, s, x, d,
+    hipLaunchKernelGGL((k_predict_fused<true, -1>), dim3(NA + (L.NT + kQ4Tiles - 1) / kQ4Tiles), dim3(256), shm, s, x, d,
                        reinterpret_cast<const h16*>(q1), b1, (int)relu, r, reinterpret_cast<const h16*>(q2), b2, ffn,
-                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot,
+                       thr, htag, desc, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot,
                        NA, s1, s2, HotArgs{});
     return hipGetLastError();
 }
@@ -1109,7 +1267,7 @@ hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1
                                     const h16* Wup, const float* bup, const h16* Wg, const float* bg, const h16* Wd,
                                     const HotLayout& HL, char* hot_area, float* ffn_partial, hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
-    uint64_t* mtag = reinterpret_cast<uint64_t*>(data + L.mtag);
+    uint64_t* desc = reinterpret_cast<uint64_t*>(data + L.desc);
     const int NA = hidden_workgroups(r, ffn, hot);
     // LDS: x (hidden rows; hot up rows, staged in whole 64-chunk blocks of 1 KB),
     // h (logits), the hot W_down row-group sums
@@ -1135,7 +1293,7 @@ hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1
     const dim3 grid(NA + H.NHU + L.NT + 1 + H.T * H.G);
 #define PI_PH(K)                                                                                                    \
     hipLaunchKernelGGL((k_predict_fused<false, K>), grid, dim3(256), shm, s, x, d, P1, b1, (int)relu, r, P2, b2, ffn, \
-                       thr, htag, mtag, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot, NA, \
+                       thr, htag, desc, reinterpret_cast<uint32_t*>(hdr + Sync::pred_epoch), idx, count, zero, hot, NA, \
                        nullptr, nullptr, H)
     if (kind == 2) PI_PH(2);
     else if (kind == 1) PI_PH(1);

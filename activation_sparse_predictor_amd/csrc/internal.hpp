@@ -169,15 +169,17 @@ constexpr size_t kSyncBytes = 8192;
 static_assert(Sync::end <= kSyncBytes, "sync header overflow");
 
 struct FusedPredLayout {
-    size_t htag, mtag, total;   // offsets from the data area; the whole layout is tagged words
+    size_t htag, desc, total;   // offsets from the data area; the whole layout is tagged words
     int NT;
 };
 inline FusedPredLayout fused_pred_layout(int r, int ffn) {
     FusedPredLayout L;
     L.NT = (ffn + 31) / 32;
     L.htag = 0;   // padded to a multiple of 1024 words: the collection reads whole rounds
-    L.mtag = align256((size_t)((r + 1023) / 1024) * 1024 * 8);
-    L.total = L.mtag + align256((size_t)L.NT * 8);
+    // the fp16 predictor's tile masks (8 bytes a tile), or the INT4
+    // predictor's look-back descriptors (128 bytes per four tiles)
+    L.desc = align256((size_t)((r + 1023) / 1024) * 1024 * 8);
+    L.total = L.desc + align256((size_t)(L.NT + 3) / 4 * 128);
     return L;
 }
 

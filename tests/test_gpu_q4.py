@@ -220,6 +220,35 @@ def test_q4_predict_hot_prefix():
         check_idx(gi[64:] - 64, z[64:], thr, where=f"q4 predict hot t={t}")
 
 
+@pytest.mark.parametrize("ffn,n_hot", [(1000, 160), (1000, 992), (1024, 1024), (40000, 0), (40000, 4096)])
+def test_q4_predict_list_edges(ffn, n_hot):
+    """The list the INT4 predictor's logits workgroups (four tiles each) write
+    themselves after a look-back over the earlier workgroups' counts: a
+    workgroup of prefix tiles only (n_hot 160), a workgroup whose last tile
+    alone is predicted and ragged (992 of 1000), every tile in the prefix (no
+    hidden rows, count = ffn), and 313 workgroups (more than one look-back
+    round of 256), with and without 32 prefix workgroups."""
+    cfg = custom_config("relu", 256, ffn, 64, mean=0.15, number=123)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    Q = R.quantize_layer(L)
+    X = make_tokens(cfg, 2).to(DEV)
+    thr = O.logit_threshold(L["tau"])
+    for rep in range(2):   # a second launch on the advanced epoch
+        idx, cnt = R.predict_q4(Q, X, n_hot=n_hot)
+        torch.cuda.synchronize()
+        for t in range(2):
+            c = int(cnt[t].cpu())
+            assert n_hot <= c <= ffn, (ffn, n_hot, c)
+            gi = idx[t, :c].cpu().numpy()
+            assert np.array_equal(gi[:n_hot], np.arange(n_hot))
+            if n_hot == ffn:
+                assert c == ffn
+                continue
+            z = _q4_logits(H, X[t].cpu())
+            check_idx(gi[n_hot:] - n_hot, z[n_hot:], thr, where=f"q4 list ffn={ffn} hot={n_hot} t={t} rep={rep}")
+
+
 def test_full_size_q4_step():
     """The OPT-30B-shaped layer (d 7168, ffn 28672, r 1024) with every matrix
     as INT4 rows: the predicted list against the oracle's logits over the
