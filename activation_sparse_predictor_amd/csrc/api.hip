@@ -327,10 +327,10 @@ pi_status decode_on(int kind, const pi_half* x, int B, int d, int ffn, const pi_
 
 // The two launches of a single-token hot decode step on a checked workspace w
 // of at least decode_hot_ws_bytes(1, ...) bytes.  Begin: the predictor's kernel
-// with the hot prefix's FFN in extra roles (its sum left in the FFN's extra
-// partial slot); it clears the tagged words first when the workspace held
-// another layout.  End: the FFN kernel over list positions [n_hot, count),
-// adding the prefix's sum.
+// with the hot prefix's FFN in extra roles (its chunk partials left in the hot
+// area); it clears the tagged words first when the workspace held another
+// layout.  End: the FFN kernel over list positions [n_hot, count), adding the
+// prefix's partials and advancing its epoch slots.
 pi_status hot_begin_on(int kind, const pi_half* x, int d, int ffn, const pi_half* P1, const float* b1, int act,
                        const pi_half* P2, const float* b2, int r, int n_hot, float tau, const pi_half* W_up,
                        const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
@@ -352,8 +352,7 @@ pi_status hot_begin_on(int kind, const pi_half* x, int d, int ffn, const pi_half
                                      logit_threshold(tau), PL, w, pdata, idx, count,
                                      reinterpret_cast<const pi::h16*>(W_up), b_up,
                                      reinterpret_cast<const pi::h16*>(W_gate), b_gate,
-                                     reinterpret_cast<const pi::h16*>(W_down), HL, hot,
-                                     reinterpret_cast<float*>(fdata + FL.partial), s);
+                                     reinterpret_cast<const pi::h16*>(W_down), HL, hot, s);
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_hot predict");
     ws_record(w, key);
     return PI_OK;
@@ -363,12 +362,13 @@ pi_status hot_end_on(int kind, const pi_half* x, int d, int ffn, int r, int n_ho
                      const float* b_up, const pi_half* W_gate, const float* b_gate, const pi_half* W_down,
                      const int32_t* idx, const int32_t* count, float* y, uint32_t flags, char* w, hipStream_t s) {
     const pi::FusedSparseLayout FL = pi::fused_sparse_layout(d, ffn);
+    const pi::HotLayout HL = pi::hot_layout(d, ffn);
     char* fdata = w + decode_hot_ffn_offset(1, d, r, ffn);
     hipError_t e = pi::launch_sparse_fused(kind, reinterpret_cast<const pi::h16*>(x), d, ffn,
                                            reinterpret_cast<const pi::h16*>(W_up), b_up,
                                            reinterpret_cast<const pi::h16*>(W_gate), b_gate,
                                            reinterpret_cast<const pi::h16*>(W_down), idx, count, y, FL, w, fdata, s,
-                                           n_hot);
+                                           n_hot, &HL, w + decode_hot_area_offset(1, r, ffn));
     if (e != hipSuccess) return hip_fail(e, "pi_ffn_decode_hot sparse");
     if ((flags & PI_CHECK_IDX) != 0u) {
         e = pi::launch_check_idx(idx, count, 1, ffn, d, y, s);

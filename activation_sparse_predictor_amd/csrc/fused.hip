@@ -127,8 +127,8 @@ constexpr int kQ4Tiles = 4;   // logits tiles per workgroup of the INT4 predicto
 // are still accumulated in fp32.
 // The hot prefix's FFN (pi_ffn_decode_hot): rows [0, n) of W_up [W_gate] and
 // W_down, its activations as tagged words with their own epochs (per-tile
-// slots advanced by the W_down tiles' last chunks, as in the FFN kernel), its
-// chunk partials and arrival counters, and y_hot, the FFN kernel's extra slot.
+// slots, advanced by the FFN kernel that follows), and its chunk partials,
+// which that kernel adds to y.
 struct HotArgs {
     const h16* Wu;
     const float* bu;
@@ -137,9 +137,7 @@ struct HotArgs {
     const h16* Wd;
     uint64_t* atag;
     float* partial;
-    uint32_t* ctr;
     uint32_t* slots;
-    float* yhot;
     int n, NHU, G, T;
 };
 
@@ -223,10 +221,11 @@ __device__ __forceinline__ void hot_up_role(const HotArgs& H, const h16* __restr
 // rows g, g + 4, ...; a thread holds 8 columns of 16 rows in flight, requested
 // before the activations are collected.  Each wave collects its own rows'
 // activations (lane q polls row q) and takes them by lane broadcast.  The
-// waves are summed in LDS, the chunk partial is stored, and the tile's last
-// chunk to arrive adds the G partials in chunk order into y_hot and advances
-// the tile's epoch slot.
-__device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, float* sh, int* s_flag) {
+// waves are summed in LDS and the chunk partial is stored.  The FFN kernel
+// that follows adds the G partials in chunk order to y and advances the
+// epoch slots: a sum and an arrival count here would end this kernel with two
+// more hand-offs, which cost most while the logits tiles still stream.
+__device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, float* sh) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int rg = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int T = H.T, G = H.G, n = H.n;
@@ -241,8 +240,8 @@ __device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, fl
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
     bool ok = true;
     uint32_t epoch = 0;
-    // the slot is stable while this launch runs (no tile can finish before
-    // this workgroup arrives), so it may be requested ahead of the rows
+    // the slot is stable while this launch runs (the FFN kernel that follows
+    // advances it), so it may be requested ahead of the rows
     const uint32_t slot = H.slots[min(lane, T - 1)];
     for (int k0 = 0; k0 == 0 || k0 < nk; k0 += kHotBatch) {
         u32x4 w[kHotBatch];
@@ -279,35 +278,6 @@ __device__ __forceinline__ void hot_down_role(const HotArgs& H, int d, int k, fl
             st_coherent(&H.partial[(size_t)chunk * d + gc], ok ? v : __builtin_nanf(""));
         }
     }
-    wait_own_memory();
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t* c = &H.ctr[(size_t)tile * kCtrStride];
-        const int flag = fetch_add(c, 1u) == (uint32_t)(G - 1);
-        if (flag) st_flag(c, 0u);   // the last arrival puts the counter back for the next call
-        *s_flag = flag;
-    }
-    __syncthreads();
-    if (!*s_flag) return;
-    // the tile's last chunk: both columns' G partials requested in one round
-    float v[kHotCols / 256][kHotMaxChunks];
-#pragma unroll
-    for (int e = 0; e < kHotCols / 256; ++e) {
-        const int gc = min(tile * kHotCols + tid + 256 * e, d - 1);
-#pragma unroll
-        for (int g = 0; g < kHotMaxChunks; ++g) v[e][g] = ld_coherent(&H.partial[(size_t)min(g, G - 1) * d + gc]);
-    }
-#pragma unroll
-    for (int e = 0; e < kHotCols / 256; ++e) {
-        const int gc = tile * kHotCols + tid + 256 * e;
-        float sum = 0.f;
-#pragma unroll
-        for (int g = 0; g < kHotMaxChunks; ++g)
-            if (g < G) sum += v[e][g];
-        if (gc < d) H.yhot[gc] = sum;
-    }
-    // every chunk of this tile has read the epoch: the tile's slot advances
-    if (tid == 0) st_flag(&H.slots[tile], epoch);
 }
 
 // The ordered list, written by the logits workgroups themselves with a
@@ -628,8 +598,7 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
             return;
         }
         if (b > lg0 + NT) {
-            __shared__ int s_hflag;
-            hot_down_role(H, d, b - (lg0 + NT + 1), sh, &s_hflag);
+            hot_down_role(H, d, b - (lg0 + NT + 1), sh);
             return;
         }
     }
@@ -942,7 +911,9 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
                                                             const float* __restrict__ zero,
                                                             const h16* __restrict__ su = nullptr,
                                                             const h16* __restrict__ sg = nullptr,
-                                                            const h16* __restrict__ sd = nullptr) {
+                                                            const h16* __restrict__ sd = nullptr,
+                                                            const float* __restrict__ hpart = nullptr, int hG = 0,
+                                                            uint32_t* __restrict__ hslots = nullptr, int hT = 0) {
     // up role: x (d fp16); W_down role: row-group partials, window ids and activations
     __shared__ __align__(16) char s_mem[kSGroups * kFusedCols * 4 + kSWindow * 8];
     static_assert(sizeof(s_mem) >= PI_MAX_D * 2, "x does not fit the up role's LDS");
@@ -1080,6 +1051,17 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
     // and a second, mostly empty batch would cost as much as a full one.
     const int Ge = min(G, max(1, (nl + kSChunkRows - 1) / kSChunkRows));
     if (chunk >= Ge) return;
+    // skip > 0: the hot prefix's FFN ran in the predictor's kernel, which has
+    // ended.  Its epoch slots (read by nothing in this launch) advance here, by
+    // tile 0's chunk 0 (present for every count): requested now, stored once
+    // the chunk's rows are done, off the rows' path.
+    const bool hot_slots = hT > 0 && k == 0;   // workgroup-uniform
+    const uint32_t hsv = (hot_slots ? hslots : slots)[min(lane, (hot_slots ? hT : T) - 1)];   // no branch around it
+    // skip > 0: chunk 0 of each tile adds the prefix's hG chunk partials (in
+    // chunk order) for the tile's columns into the partial slot the last chunk
+    // reads after the G others, once its rows are done (requested at the start,
+    // the 24 values held across the rows made the OPT-30B-shaped step slower)
+    const bool hot_sum = hG > 0 && chunk == 0;   // workgroup-uniform
     const int PD = (nl + Ge - 1) / Ge;
     const int j0 = sk + min(nl, chunk * PD), j1 = min(cnt, j0 + PD);
     const int ct = tid % kSColThreads;
@@ -1156,6 +1138,21 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
         __syncthreads();
     }
     if (epoch == 0u) epoch = next_epoch(oldest_slot(slots[min(lane, T - 1)]));   // empty chunk (uniform)
+    if (hot_slots && wave == 0) {
+        const uint32_t he = next_epoch(oldest_slot(hsv));
+        if (lane < hT) st_flag(&hslots[lane], he);
+    }
+    if (hot_sum && tile * kFusedCols + tid < d) {
+        float hv[kHotMaxChunks];
+        const int hc = tile * kFusedCols + tid;
+#pragma unroll
+        for (int g = 0; g < kHotMaxChunks; ++g) hv[g] = hpart[(size_t)min(g, hG - 1) * d + hc];
+        float hs = 0.f;
+#pragma unroll
+        for (int g = 0; g < kHotMaxChunks; ++g)
+            if (g < hG) hs += hv[g];
+        st_coherent(&partial[(size_t)kFusedMaxChunks * d + tile * kFusedCols + tid], hs);
+    }
     ok = __syncthreads_and(ok);
     *reinterpret_cast<f32x4*>(&s_red[rg][ct * 8]) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4*>(&s_red[rg][ct * 8 + 4]) = f32x4{acc[4], acc[5], acc[6], acc[7]};
@@ -1181,7 +1178,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 
     // the tile's last chunk: add the G partials in chunk order, all loads in one round
     // the partial buffer holds kFusedMaxChunks + 1 chunks, so every load is in bounds;
-    // the last slot is the hot prefix's sum, written by the predictor's kernel
+    // the last slot is the hot prefix's sum, stored by chunk 0
     float v[kFusedMaxChunks + 1];
 #pragma unroll
     for (int g = 0; g < kFusedMaxChunks + 1; ++g) v[g] = ld_coherent(&partial[(size_t)g * d + gc]);
@@ -1189,7 +1186,7 @@ __global__ __launch_bounds__(kSThreads) void k_sparse_fused(const h16* __restric
 #pragma unroll
     for (int g = 0; g < kFusedMaxChunks; ++g)
         if (g < Ge) sum += v[g];
-    if (skip > 0) sum += v[kFusedMaxChunks];
+    if (hG > 0) sum += v[kFusedMaxChunks];
     y[gc] = craw < 0 ? __builtin_nanf("") : sum;
     // every chunk of this tile has read the epoch: the tile's slot advances
     if (tid == 0) st_flag(&slots[tile], epoch);
@@ -1265,7 +1262,7 @@ hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1
                                     const h16* P2, const float* b2, int ffn, int hot, float thr,
                                     const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
                                     const h16* Wup, const float* bup, const h16* Wg, const float* bg, const h16* Wd,
-                                    const HotLayout& HL, char* hot_area, float* ffn_partial, hipStream_t s) {
+                                    const HotLayout& HL, char* hot_area, hipStream_t s) {
     uint64_t* htag = reinterpret_cast<uint64_t*>(data + L.htag);
     uint64_t* desc = reinterpret_cast<uint64_t*>(data + L.desc);
     const int NA = hidden_workgroups(r, ffn, hot);
@@ -1283,9 +1280,7 @@ hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1
     H.Wd = Wd;
     H.atag = reinterpret_cast<uint64_t*>(hot_area + HL.atag);
     H.partial = reinterpret_cast<float*>(hot_area + HL.partial);
-    H.ctr = reinterpret_cast<uint32_t*>(hot_area + HL.ctr);
     H.slots = reinterpret_cast<uint32_t*>(hot_area + HL.slots);
-    H.yhot = ffn_partial + (size_t)kFusedMaxChunks * d;
     H.n = hot;
     H.NHU = hot > 0 ? ((hot + 3) / 4 < kHotUpMaxWG ? (hot + 3) / 4 : kHotUpMaxWG) : 0;
     H.G = hot > 0 ? hot_chunks(hot) : 0;
@@ -1305,16 +1300,21 @@ hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1
 hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
-                               char* data, hipStream_t s, int skip) {
+                               char* data, hipStream_t s, int skip, const HotLayout* HL, char* hot_area) {
     uint64_t* atag = reinterpret_cast<uint64_t*>(data + L.atag);
     float* partial = reinterpret_cast<float*>(data + L.partial);
     uint32_t* ctr = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_ctr);
     uint32_t* slots = reinterpret_cast<uint32_t*>(hdr + Sync::ffn_epoch);
     const float* zero = reinterpret_cast<const float*>(hdr + Sync::zero);
+    const bool hot = skip > 0 && HL != nullptr;
+    const float* hpart = hot ? reinterpret_cast<const float*>(hot_area + HL->partial) : nullptr;
+    uint32_t* hslots = hot ? reinterpret_cast<uint32_t*>(hot_area + HL->slots) : nullptr;
+    const int hG = hot ? hot_chunks(skip) : 0, hT = hot ? HL->T : 0;
     dim3 grid(L.NU + L.T * L.G);
 #define PI_SF(K)                                                                                               \
     hipLaunchKernelGGL(k_sparse_fused<K>, grid, dim3(kSThreads), 0, s, x, d, ffn, Wup, bup, Wg, bg, Wd, idx, count, \
-                       skip, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero)
+                       skip, L.NU, L.T, L.G, atag, partial, ctr, slots, y, zero, nullptr, nullptr, nullptr, hpart,   \
+                       hG, hslots, hT)
     if (kind == 2) PI_SF(2);
     else if (kind == 1) PI_SF(1);
     else PI_SF(0);

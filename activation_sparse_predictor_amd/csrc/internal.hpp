@@ -197,29 +197,29 @@ inline FusedSparseLayout fused_sparse_layout(int d, int ffn) {
     L.atag = 0;
     L.partial = align256((size_t)ffn * 8);
     // padded: the reduction reads every chunk slot, and one more, kFusedMaxChunks,
-    // which holds the hot prefix's sum when the predictor's kernel computed it
+    // which holds the hot prefix's sum (chunk 0 adds the predictor's kernel's
+    // chunk partials into it)
     L.total = L.partial + align256((size_t)(kFusedMaxChunks + 1) * d * 4);
     return L;
 }
 
 // ---- the always-listed hot prefix's FFN inside the predictor's kernel
 // (pi_ffn_decode_hot, B = 1).  Its own area of the decode workspace, behind
-// the predictor's data area: the W_down tiles' arrival counters and epoch
-// slots, the prefix's activations as tagged words, and the chunk partials.
-// Zero-filled with the other tagged words whenever the workspace held another
-// layout; after that each counter is put back to 0 by its last arrival and
-// each slot advances by one per launch.
+// the predictor's data area: the W_down tiles' epoch slots, the prefix's
+// activations as tagged words, and the chunk partials, which the FFN kernel
+// that follows adds to y.  Zero-filled with the other tagged words whenever
+// the workspace held another layout; after that the slots advance by one per
+// step (in the FFN kernel, once the predictor's kernel has ended).
 constexpr int kHotRowsPerChunk = 64;   // 4 row groups x 16 rows in flight
-constexpr int kHotMaxChunks = 24;   // a tile's last chunk reads 2 x 24 partials in one round
+constexpr int kHotMaxChunks = 24;   // the FFN's last chunk of a tile reads 24 of them in its round
 struct HotLayout {
-    size_t ctr, slots, atag, partial, total;   // offsets from the hot area's start
+    size_t slots, atag, partial, total;   // offsets from the hot area's start
     int T;
 };
 inline HotLayout hot_layout(int d, int ffn) {
     HotLayout L;
     L.T = (d + kFusedCols - 1) / kFusedCols;
-    L.ctr = 0;
-    L.slots = (size_t)kFusedMaxTiles * kCtrStride * 4;
+    L.slots = 0;
     L.atag = L.slots + 256;
     L.partial = L.atag + align256((size_t)ffn * 8);
     L.total = L.partial + align256((size_t)kHotMaxChunks * d * 4);
@@ -261,24 +261,26 @@ hipError_t launch_predict_fused(const h16* x, int d, const h16* P1, const float*
                                 const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
                                 hipStream_t s);
 // The same launch with the hot prefix's FFN ([0, hot) rows of W_up [W_gate]
-// W_down) computed in the kernel's extra roles: its sum goes to slot
-// kFusedMaxChunks of the FFN's partials (ffn_partial), which the following
-// launch_sparse_fused(..., skip = hot) adds to y.
+// W_down) computed in the kernel's extra roles: its chunk partials stay in the
+// hot area, and the following launch_sparse_fused(..., skip = hot) adds them
+// to y and advances the hot area's epoch slots.
 hipError_t launch_predict_fused_hot(int kind, const h16* x, int d, const h16* P1, const float* b1, bool relu, int r,
                                     const h16* P2, const float* b2, int ffn, int hot, float thr,
                                     const FusedPredLayout& L, char* hdr, char* data, int32_t* idx, int32_t* count,
                                     const h16* Wup, const float* bup, const h16* Wg, const float* bg, const h16* Wd,
-                                    const HotLayout& HL, char* hot_area, float* ffn_partial, hipStream_t s);
+                                    const HotLayout& HL, char* hot_area, hipStream_t s);
 hipError_t launch_predict_fused_q4(const h16* x, int d, const uint8_t* q1, const h16* s1, const float* b1, bool relu,
                                    int r, const uint8_t* q2, const h16* s2, const float* b2, int ffn, int hot,
                                    float thr, const FusedPredLayout& L, char* hdr, char* data, int32_t* idx,
                                    int32_t* count, hipStream_t s);
 // skip > 0: list positions [0, skip) (the hot prefix) were computed by
-// launch_predict_fused_hot, whose sum is added to y.
+// launch_predict_fused_hot, whose chunk partials (in hot_area, laid out by HL)
+// are added to y.
 hipError_t launch_sparse_fused(int kind, const h16* x, int d, int ffn, const h16* Wup, const float* bup,
                                const h16* Wg, const float* bg, const h16* Wd, const int32_t* idx,
                                const int32_t* count, float* y, const FusedSparseLayout& L, char* hdr,
-                               char* data, hipStream_t s, int skip = 0);
+                               char* data, hipStream_t s, int skip = 0, const HotLayout* HL = nullptr,
+                               char* hot_area = nullptr);
 hipError_t launch_sparse_fused_q4(int kind, const h16* x, int d, int ffn, const uint8_t* qu, const h16* su,
                                   const float* bup, const uint8_t* qg, const h16* sg, const float* bg,
                                   const uint8_t* qd, const h16* sd, const int32_t* idx, const int32_t* count,

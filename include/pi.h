@@ -269,8 +269,10 @@ pi_status pi_ffn_decode_hot(int kind, const pi_half* x, int B, int d, int ffn,
  * pi_ffn_decode_hot for one token (B = 1), as separate calls, so a caller can
  * put other work (or timing) between them.  begin: the prediction (idx,
  * count, as pi_ffn_predict_hot writes them) and the hot prefix's FFN, whose
- * sum stays in ws; end: the FFN over list positions [n_hot, count) plus that
- * sum, into y.  end must follow its begin on the same workspace with the same
+ * chunk partials stay in ws; end: the FFN over list positions [n_hot, count)
+ * plus the prefix's sum of those partials, into y.  end must follow its begin
+ * (a second begin before end gives unspecified results) on the same
+ * workspace with the same
  * layer, token, n_hot, idx and count, and no other call on that workspace in
  * between; begin followed by end computes exactly what pi_ffn_decode_hot
  * computes (bitwise).  flags of end: PI_CHECK_IDX, PI_DETERMINISTIC.
