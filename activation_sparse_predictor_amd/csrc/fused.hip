@@ -697,59 +697,44 @@ __global__ __launch_bounds__(256) void k_predict_fused(const h16* __restrict__ x
     if (!Q4 && b == lg0 + NT) {
         // ---------------- ordered compaction.  The always-listed prefix [0, hot)
         // is written first, by every thread in turn (coalesced, no mask read).
-        // The other tiles go 1024 per round: thread k takes tiles 2k and 2k + 1
-        // of each half of the round, one block-wide scan per half, and writes
-        // its tiles' ids one by one (a wave runs as long as its busiest lane;
-        // two write loops keep the cost on an unordered layer low).
+        // The other tiles go 256 per round, in tile order, thread k taking tile
+        // k: one block-wide scan and one tile's ids per thread per round.  The
+        // tiles publish roughly in order, so the rounds keep pace with them and
+        // only the last round's scan and writes follow the last mask (the dense
+        // tiles right after a hot-first prefix are long written by then).  The
+        // next round's mask is requested before this round's ids go out.
         const uint32_t epoch = next_epoch(*epoch_word);
         for (int j = tid; j < hot; j += 256) idx[j] = j;
         uint32_t base = (uint32_t)hot;
         bool good = true;
-        for (int t0 = hot / kLTile; t0 < NT; t0 += 1024) {
-            uint64_t m4[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) m4[q] = ld_tag(&desc[min(t0 + (q >> 1) * 512 + tid * 2 + (q & 1), NT - 1)]);
-            uint32_t bits[4], cnt2[2], incl2[2];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int t = t0 + (q >> 1) * 512 + tid * 2 + (q & 1);
-                bits[q] = 0u;
-                if (t < NT) {
-                    if (poll_tag(&desc[t], m4[q], epoch)) bits[q] = (uint32_t)m4[q];
-                    else good = false;
-                }
+        const int tb = hot / kLTile;
+        uint64_t mnext = ld_tag(&desc[min(tb + tid, NT - 1)]);
+        for (int t0 = tb, k = 0; t0 < NT; t0 += 256, ++k) {
+            const int t = t0 + tid;
+            uint64_t m = mnext;
+            mnext = ld_tag(&desc[min(t + 256, NT - 1)]);
+            uint32_t bits = 0u;
+            if (t < NT) {
+                if (poll_tag(&desc[t], m, epoch)) bits = (uint32_t)m;
+                else good = false;
             }
+            const uint32_t c = (uint32_t)__popc(bits);
+            uint32_t incl = c;
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                cnt2[h] = (uint32_t)(__popc(bits[2 * h]) + __popc(bits[2 * h + 1]));
-                uint32_t incl = cnt2[h];
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t v = __shfl_up(incl, off, 64);
-                    if (lane >= off) incl += v;
-                }
-                incl2[h] = incl;
-                if (lane == 63) s_red[h * 4 + wave] = incl;
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t v = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += v;
             }
+            uint32_t* sw = s_red + (k & 1) * 4;   // alternate halves: one barrier a round
+            if (lane == 63) sw[wave] = incl;
             __syncthreads();
-            uint32_t run = base;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t pos = run + incl2[h] - cnt2[h];
-                for (int w2 = 0; w2 < wave; ++w2) pos += s_red[h * 4 + w2];
-                run += s_red[h * 4] + s_red[h * 4 + 1] + s_red[h * 4 + 2] + s_red[h * 4 + 3];
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    uint32_t m = bits[2 * h + e];
-                    const int t = t0 + h * 512 + tid * 2 + e;
-                    while (m) {
-                        idx[pos++] = t * kLTile + __builtin_ctz(m);
-                        m &= m - 1;
-                    }
-                }
+            uint32_t pos = base + incl - c;
+            for (int w2 = 0; w2 < wave; ++w2) pos += sw[w2];
+            base += sw[0] + sw[1] + sw[2] + sw[3];
+            while (bits) {
+                idx[pos++] = t * kLTile + __builtin_ctz(bits);
+                bits &= bits - 1u;
             }
-            base = run;
-            __syncthreads();
         }
         good = __syncthreads_and(good);
         if (tid == 0) {
