@@ -669,6 +669,26 @@ def test_hot_prefix(kind, Bt, n_hot):
     _check_hot(P, X, n_hot, where=f"hot {kind} B={Bt} n_hot={n_hot}")
 
 
+@pytest.mark.parametrize("ffn,n_hot", [(8192, 0), (8224, 0), (9000, 64), (16416, 96), (24608, 7200)])
+def test_compaction_rounds(ffn, n_hot):
+    """The single-token compaction goes through the tiles past the prefix in
+    rounds of 256: exactly one round (256 tiles), a one-tile last round (257),
+    a ragged last tile (9000 = 281 x 32 + 8), a prefix that shifts the rounds
+    and leaves a ragged last round (513 tiles from tile 3), and a long prefix
+    (tile 225 of 769) on a hot-first layer."""
+    cfg = custom_config("relu", 64, ffn, 16, mean=0.15, exponent=1.3, number=131)
+    L = R.to_device(make_layer(cfg), DEV)
+    P = _hot_first(cfg, L, 256)[0] if n_hot >= 1024 else L
+    _check_hot(P, make_tokens(cfg, 1).to(DEV), n_hot, where=f"compaction ffn={ffn} n_hot={n_hot}")
+    # pi_ffn_decode_hot's predictor launch (the same compaction, with the prefix's FFN beside it)
+    x = make_tokens(cfg, 2).to(DEV)[1:2].contiguous()
+    y, i1, c1 = R.decode_hot(P, x, n_hot)
+    i0, c0 = R.predict(P, x, n_hot=n_hot)
+    torch.cuda.synchronize()
+    c = int(c0.cpu()[0])
+    assert int(c1.cpu()[0]) == c and torch.equal(i1[0, :c], i0[0, :c])
+
+
 def test_hot_prefix_zero_and_whole():
     """n_hot = 0 is pi_ffn_predict (bitwise); n_hot = ffn lists every neuron."""
     cfg = custom_config("relu", 256, 1024, 64, mean=0.1, number=98)
