@@ -799,7 +799,8 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
             kofs[i] = C::achunk(tg, lane) << 3;
         }
     }
-    auto issue = [&](int st, int q) {
+    // stage st's sources: the union ids of its weight blocks from the window
+    auto prep = [&](int st, const h16* (&p)[C::IPW]) {
         const int wst = st * C::KR / kDnIds;   // uniform: every wave issues the same stage
         if (wst != window) {
             // every wave has issued the previous window's last stage (it read
@@ -813,20 +814,27 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
 #pragma unroll
         for (int i = 0; i < C::WBLK / 4; ++i)
             id[i] = clampi(s_ids[min(st * C::KR + wofs[i] - window * kDnIds, kDnIds - 1)], 0, ffn - 1);
-        const uint32_t dst = lbase + q * C::STAGE;
 #pragma unroll
         for (int i = 0; i < C::IPW; ++i) {
-            const h16* p;
             if (i < C::WBLK / 4) {
                 const bool ok = st * C::KR + wofs[i] < n_ids && kofs[i] < d;
-                p = ok ? Wd + (size_t)id[i] * d + kofs[i] : zsrc;
+                p[i] = ok ? Wd + (size_t)id[i] * d + kofs[i] : zsrc;
             } else {
                 const int e = st * C::KR + kofs[i];
-                p = (abase[i] && e < n_ids) ? abase[i] + u0 + e : zsrc;
+                p[i] = (abase[i] && e < n_ids) ? abase[i] + u0 + e : zsrc;
             }
-            if (i < C::WBLK / 4) dma16_stream(p, dst + (wave + 4 * i) * 1024);   // W_down: read once
-            else dma16(p, dst + (wave + 4 * i) * 1024);
         }
+    };
+    auto issue1 = [&](const h16* p, int q, int i) {
+        const uint32_t dst = lbase + q * C::STAGE;
+        if (i < C::WBLK / 4) dma16_stream(p, dst + (wave + 4 * i) * 1024);   // W_down: read once
+        else dma16(p, dst + (wave + 4 * i) * 1024);
+    };
+    auto issue = [&](int st, int q) {
+        const h16* p[C::IPW];
+        prep(st, p);
+#pragma unroll
+        for (int i = 0; i < C::IPW; ++i) issue1(p[i], q, i);
     };
 
     f32x16 acc[C::CB][C::NB];
@@ -840,11 +848,18 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
 #pragma unroll
     for (int jj = 0; jj < C::NS - 1; ++jj)
         if (jj < n) issue(jj, jj);
-    for (int s = 0; s < n; ++s) {
+    // stage s; MORE: a stage s + NS - 1 exists.  All of the stage's LDS
+    // reads go out first, then its MFMAs run back to back, with the next
+    // stage's loads spread between them when there are at least two MFMAs
+    // per load, else issued at once after the barrier (see ring.hpp)
+    constexpr int NMF = C::KR / 16 * C::CB * C::NB * 2;   // MFMAs per wave per stage
+    constexpr bool kSpread = NMF >= 2 * C::IPW;
+    auto stage = [&](int s, auto MORE) {
         if (s + C::NS - 2 < n) wait_vm<(C::NS - 2) * C::IPW>();
         else wait_vm<0>();
         ring_barrier();
-        if (s + C::NS - 1 < n) issue(s + C::NS - 1, (s + C::NS - 1) % C::NS);
+        const int qn = (s + C::NS - 1) % C::NS;
+        if constexpr (decltype(MORE)::value && !kSpread) issue(s + C::NS - 1, qn);
         const char* buf = lds + (s % C::NS) * C::STAGE;
         f16x4 w0[C::KR / 16][C::CB], w1[C::KR / 16][C::CB];
         f16x8 av[C::KR / 16][C::NB][2];
@@ -872,6 +887,9 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
                 }
             }
         }
+        const h16* pn[C::IPW];
+        if constexpr (decltype(MORE)::value && kSpread) prep(s + C::NS - 1, pn);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < C::KR / 16; ++q)
 #pragma unroll
@@ -879,11 +897,24 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
                 const f16x8 a8 = {w0[q][cb][0], w0[q][cb][1], w0[q][cb][2], w0[q][cb][3],
                                   w1[q][cb][0], w1[q][cb][1], w1[q][cb][2], w1[q][cb][3]};
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb) {
-                    acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][0], acc[cb][nb], 0, 0, 0);
-                    acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][1], acc[cb][nb], 0, 0, 0);
-                }
+                for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                    for (int ix = 0; ix < 2; ++ix) {
+                        const int f = ((q * C::CB + cb) * C::NB + nb) * 2 + ix;
+                        if constexpr (decltype(MORE)::value && kSpread) {
+#pragma unroll
+                            for (int i = 0; i < C::IPW; ++i)
+                                if (i * NMF / C::IPW == f) issue1(pn[i], qn, i);
+                        }
+                        acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][ix], acc[cb][nb], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
             }
+    };
+    {
+        int s = 0;
+        for (; s + C::NS - 1 < n; ++s) stage(s, std::true_type{});
+        for (; s < n; ++s) stage(s, std::false_type{});
     }
     // acc[cb][nb] element e of lane l: column (wave*CB + cb)*32 + 8*(e/4) + 4*(l/32) + e%4
     // of the tile, token nb*32 + l%32; four consecutive columns per 16-byte store

@@ -86,6 +86,7 @@ struct RingCfg {
     static constexpr int KST = SEG * 64;              // halves of K per stage
     static constexpr int WK = 4 / NB;                 // waves sharing a token block
     static constexpr int NPW = 4 * SEG / WK;          // chunk pairs per wave per stage
+    static constexpr int NMF = NPW * RBW * NM * NX;   // MFMAs per wave per stage
     // per-wave sums: one block of 16 rows x 65 floats per (wave, row block of
     // 32, matrix), 1056 floats apart (see ring_gemm's epilogue)
     static constexpr int REDE = 65, REDB = 1056;
@@ -187,15 +188,16 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
                 ok[i] = t < a.B;
             }
         }
-        auto issue = [&](int st, int q) {
+        auto issue1 = [&](int st, int q, int i) {
             const uint32_t dst = lbase + q * C::STAGE;
+            const int k = st * C::KST + kofs[i];
+            const h16* p = (ok[i] && k < a.K) ? src[i] + k : a.zsrc;
+            if (i < C::WBLK / 4) dma16_stream(p, dst + (wave + 4 * i) * 1024);   // weights: read once
+            else dma16(p, dst + (wave + 4 * i) * 1024);
+        };
+        auto issue = [&](int st, int q) {
 #pragma unroll
-            for (int i = 0; i < C::IPW; ++i) {
-                const int k = st * C::KST + kofs[i];
-                const h16* p = (ok[i] && k < a.K) ? src[i] + k : a.zsrc;
-                if (i < C::WBLK / 4) dma16_stream(p, dst + (wave + 4 * i) * 1024);   // weights: read once
-                else dma16(p, dst + (wave + 4 * i) * 1024);
-            }
+            for (int i = 0; i < C::IPW; ++i) issue1(st, q, i);
         };
 
         ring_f32x16 acc[C::RBW][C::NM];
@@ -208,11 +210,21 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
         for (int j = 0; j < C::NS - 1; ++j)
             if (j < n) issue(st0 + j, j);
-        for (int s = 0; s < n; ++s) {
+        // stage s; MORE: a stage s + NS - 1 exists.  All of the stage's LDS
+        // reads go out first, so that its MFMAs then run back to back instead
+        // of each waiting for its read.  With at least two MFMAs per load the
+        // next stage's loads go out between the MFMAs: a load instruction
+        // holds its wave while the load unit takes its 1 KB, and the MFMAs
+        // issued before it run on meanwhile (issued all together, the loads
+        // and the MFMAs took turns).  With fewer, the loads go out at once,
+        // as early as the ring allows.
+        constexpr bool kSpread = C::NMF >= 2 * C::IPW;
+        auto stage = [&](int s, auto MORE) {
             if (s + C::NS - 2 < n) wait_vm<(C::NS - 2) * C::IPW>();
             else wait_vm<0>();
             ring_barrier();   // stage s is in LDS; every wave is done with stage s - 1
-            if (s + C::NS - 1 < n) issue(st0 + s + C::NS - 1, (s + C::NS - 1) % C::NS);
+            const int sn = st0 + s + C::NS - 1, qn = (s + C::NS - 1) % C::NS;
+            if constexpr (decltype(MORE)::value && !kSpread) issue(sn, qn);
             const char* buf = lds + (s % C::NS) * C::STAGE;
             f16x8 xv[C::NPW][C::NX], wv[C::NPW][C::RBW][C::NM];
 #pragma unroll
@@ -235,6 +247,7 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
                     }
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < C::NPW; ++j)
 #pragma unroll
@@ -242,9 +255,20 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 #pragma unroll
                     for (int m = 0; m < C::NM; ++m)
 #pragma unroll
-                        for (int ix = 0; ix < C::NX; ++ix)
+                        for (int ix = 0; ix < C::NX; ++ix) {
+                            const int f = ((j * C::RBW + rr) * C::NM + m) * C::NX + ix;
+                            if constexpr (decltype(MORE)::value && kSpread) {
+#pragma unroll
+                                for (int i = 0; i < C::IPW; ++i)
+                                    if (i * C::NMF / C::IPW == f) issue1(sn, qn, i);
+                            }
                             acc[rr][m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wv[j][rr][m], xv[j][ix], acc[rr][m], 0, 0, 0);
-        }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+        };
+        int s = 0;
+        for (; s + C::NS - 1 < n; ++s) stage(s, std::true_type{});
+        for (; s < n; ++s) stage(s, std::false_type{});
         ring_barrier();   // the ring is no longer read: its memory holds the sums now
 #pragma unroll
         for (int rr = 0; rr < C::RBW; ++rr)
@@ -259,7 +283,8 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
         // epilogue reads 64 rows of one token per wave instruction: the
         // element rows 65 floats apart and the odd row blocks shifted by 16
         // put those 64 reads on 64 different banks (unpadded, the 32 rows of
-        // a row block would all hit one bank)
+        // a row block would all hit one bank).  The blocks of the waves that
+        // split K are added in wave order.
         auto val = [&](int m, int rl, int t) {
             const int rr = rl >> 5, r = rl & 31, tb = t >> 5, nn = t & 31;
             const int e = ((r >> 3) << 2) + (r & 3), ln = nn + (((r >> 2) & 1) << 5);
@@ -269,38 +294,49 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
                 v += red[(((k * C::NB + tb) * C::RBW + rr) * C::NM + m) * C::REDB + e * C::REDE + ((rr & 1) << 4) + ln];
             return v;
         };
-        // this thread's row and token slots: rl, tt + j * TS for j < NT
-        const int rl = tid % C::RB, tt = tid / C::RB, row = rb * C::RB + rl;
-        if (st0 == 0 && st1 == nst) {
-            const auto pr = epi.row(row);
-            for (int j = 0; j < kNT; j += kE) {
-                int t[kE];
-                float v0[kE], v1[kE];
+        // this thread's row and token slots: rl, tt + j * TS for j < NT (made
+        // opaque in every unit: hoisted out of the unit loop, the epilogue's
+        // addresses stayed live across the whole loop and were spilled)
+        int rl = tid % C::RB, tt = tid / C::RB;
+        asm volatile("" : "+v"(rl), "+v"(tt));
+        const int row = rb * C::RB + rl;
+        const bool whole = st0 == 0 && st1 == nst;
+        // piece slot: kind 0 when the range starts inside this row block
+        // (its first piece), 1 when it ends inside it (its last piece)
+        auto slot = [&](int wg) {
+            const int kind = (T * wg / G) >= (long long)rb * nst ? 0 : 1;
+            return a.part + (size_t)(wg * 2 + kind) * C::NM * C::BP * C::RB;
+        };
+        // token slots j0 .. j1 - 1 of the sums in LDS: outputs of a whole row
+        // block, or this workgroup's piece of a split one
+        auto emit = [&](int j0, int j1, const auto& pr) {
+            if (whole) {
+                for (int j = j0; j < j1; j += kE) {
+                    int t[kE];
+                    float v0[kE], v1[kE];
 #pragma unroll
-                for (int k = 0; k < kE; ++k) {
-                    t[k] = tt + (j + k) * kTS;
-                    v0[k] = val(0, rl, t[k]);
-                    v1[k] = C::NM > 1 ? val(C::NM - 1, rl, t[k]) : 0.f;
-                }
-                epi.template apply<kE>(row, pr, t, v0, v1);
-            }
-        } else {
-            // piece slot: kind 0 when the range starts inside this row block
-            // (its first piece), 1 when it ends inside it (its last piece)
-            auto slot = [&](int wg) {
-                const int kind = (T * wg / G) >= (long long)rb * nst ? 0 : 1;
-                return a.part + (size_t)(wg * 2 + kind) * C::NM * C::BP * C::RB;
-            };
-            float* mine = slot(w);
-            for (int j = 0; j < kNT; ++j) {
-                const int t = tt + j * kTS;
-                if (t < a.B && row < nrows)
-#pragma unroll
-                    for (int m = 0; m < C::NM; ++m) {
-                        if (LAST_FINISHES) st_coherent(&mine[(m * C::BP + t) * C::RB + rl], val(m, rl, t));
-                        else mine[(m * C::BP + t) * C::RB + rl] = val(m, rl, t);
+                    for (int k = 0; k < kE; ++k) {
+                        t[k] = tt + (j + k) * kTS;
+                        v0[k] = val(0, rl, t[k]);
+                        v1[k] = C::NM > 1 ? val(C::NM - 1, rl, t[k]) : 0.f;
                     }
+                    epi.template apply<kE>(row, pr, t, v0, v1);
+                }
+            } else {
+                float* mine = slot(w);
+                for (int j = j0; j < j1; ++j) {
+                    const int t = tt + j * kTS;
+                    if (t < a.B && row < nrows)
+#pragma unroll
+                        for (int m = 0; m < C::NM; ++m) {
+                            if (LAST_FINISHES) st_coherent(&mine[(m * C::BP + t) * C::RB + rl], val(m, rl, t));
+                            else mine[(m * C::BP + t) * C::RB + rl] = val(m, rl, t);
+                        }
+                }
             }
+        };
+        emit(0, kNT, epi.row(row));
+        if (!whole) {
             if (!LAST_FINISHES) {
                 __syncthreads();   // the sums are read: the ring may be loaded again
                 continue;
