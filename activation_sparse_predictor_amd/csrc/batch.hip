@@ -499,30 +499,32 @@ __global__ __launch_bounds__(256) void k_bpred_logits_tq(const h16* __restrict__
         hl[k] = settle(hl[k]);
     }
     __syncthreads();
-    auto issue = [&](int st) {
+    auto issue1 = [&](int st, int i) {
         const uint32_t dst = lbase + (uint32_t)((st % kTqStages) * STG);
         const int rb = rb0 + (st >> 1), half = st & 1;
+        const int blk = wave + 4 * i;
+        const int g = blk / HB, cg = blk % HB;
+        const int rr = g * 8 + (lane >> 3);   // the lane's row within the block of 32
+        const int row = min(rb * 32 + rr, nr - 1);
+        const int chunk = half * (r / 16) + cg * 8 + ((lane & 7) ^ blk_swz(rr));
+        dma16(W + (size_t)row * r + chunk * 8, dst + (uint32_t)blk * 1024u);
+    };
+    auto issue = [&](int st) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int blk = wave + 4 * i;
-            const int g = blk / HB, cg = blk % HB;
-            const int rr = g * 8 + (lane >> 3);   // the lane's row within the block of 32
-            const int row = min(rb * 32 + rr, nr - 1);
-            const int chunk = half * (r / 16) + cg * 8 + ((lane & 7) ^ blk_swz(rr));
-            dma16(W + (size_t)row * r + chunk * 8, dst + (uint32_t)blk * 1024u);
-        }
+        for (int i = 0; i < IPW; ++i) issue1(st, i);
     };
     const int nw = (ffn + 31) / 32;
 #pragma unroll
     for (int j = 0; j < kTqStages - 1; ++j)
         if (j < ns) issue(j);
-    // one half of K of row block rb (stage s): every wave multiplies its eighth
-    auto half_stage = [&](int s, auto HALF, ring_f32x16& acc) {
+    // one half of K of row block rb (stage s): every wave multiplies its
+    // eighth.  The LDS reads go out first; the next stage's loads go out
+    // between the MFMAs, one per two (as in ring.hpp)
+    auto half_stage_m = [&](int s, auto HALF, ring_f32x16& acc, auto MORE) {
         constexpr int F = decltype(HALF)::value;
         if (s + kTqStages - 2 < ns) wait_vm<(kTqStages - 2) * IPW>();   // stage s is in
         else wait_vm<0>();
         ring_barrier();   // every wave's loads of stage s are in; everyone is past stage s - 1 and the sums
-        if (s + kTqStages - 1 < ns) issue(s + kTqStages - 1);
         const char* buf = lds + (s % kTqStages) * STG;
         const int g = li >> 3;
         f16x8 a[KS / 2];
@@ -531,11 +533,21 @@ __global__ __launch_bounds__(256) void k_bpred_logits_tq(const h16* __restrict__
             const int c = wave * (r >> 6) + 2 * k + kh;   // chunk within the half
             a[k] = *reinterpret_cast<const f16x8*>(buf + (g * HB + (c >> 3)) * 1024 + blk_off(li, c & 7));
         }
+        __builtin_amdgcn_sched_barrier(0);
+        static_assert(KS / 2 == IPW, "one load per two MFMAs");
 #pragma unroll
         for (int k = 0; k < KS / 2; ++k) {
+            if constexpr (decltype(MORE)::value) issue1(s + kTqStages - 1, k);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hh[F * (KS / 2) + k], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[k], hl[F * (KS / 2) + k], acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    // (a separate copy for the last stages, which load nothing: a load under
+    // a branch inside the MFMA sequence would be gathered into one block)
+    auto half_stage = [&](int s, auto HALF, ring_f32x16& acc) {
+        if (s + kTqStages - 1 < ns) half_stage_m(s, HALF, acc, std::true_type{});
+        else half_stage_m(s, HALF, acc, std::false_type{});
     };
     for (int rb = rb0; rb < rb1; ++rb) {
         const int s = 2 * (rb - rb0);
