@@ -22,7 +22,10 @@
 // group again: their sums are never used).
 // The ring holds NS stages; stage s + NS - 1 is loaded while stage s is
 // multiplied, and each wave waits only for its own loads of stage s (vmcnt),
-// then a workgroup barrier makes every wave's loads visible.
+// then a workgroup barrier makes every wave's loads visible.  Within a stage
+// all of its LDS operand reads go out first and the MFMAs then run back to
+// back; with at least two MFMAs per load, stage s + NS - 1's loads go out one
+// at a time between them, else all at once after the barrier.
 //
 // MFMA.  v_mfma_f32_32x32x16_f16: lane l supplies row (or token) l % 32 and 8
 // halves of K from chunk 2p + l / 32 of chunk pair p; the contraction order
