@@ -9,10 +9,11 @@
 //                                  activation, zeroed where t did not select U_u
 //   k_union_down    (MFMA)         Y[t] = sum_u A[u][t] * W_down[U_u, :]
 //
-// Each token's result equals its single-token result up to fp32 rounding:
-// a neuron outside a token's own list contributes exactly 0 to that token.
-// A is kept as an fp16 pair (hi + lo, about 22 significant bits) so that the
-// fp16 matrix-core down product loses no accuracy against fp32 activations.
+// Each token's result equals its single-token result up to rounding: a
+// neuron outside a token's own list contributes exactly 0 to that token.  A
+// is stored in fp16 for the matrix-core down product (each activation
+// rounded once, a relative error of at most 2^-11 per term, so about 3e-4 in
+// y's relative L2 norm); the weights are fp16 already and the sums fp32.
 #include "common.hpp"
 #include "internal.hpp"
 #include "ring.hpp"
@@ -199,9 +200,9 @@ using UpCfg = RingCfg<REGLU ? 2 : 1, 1, XG, rbw_up(XG), ring_seg(REGLU ? 2 : 1, 
 
 // Up GEMM over the union rows: A[u][t] = W_up[U_u] . x_t (+ the gate
 // product for ReGLU), then bias, activation and the token mask (zero where
-// token t did not select neuron U_u), stored token-major as an fp16 hi/lo
-// pair: aT[t][u], for every token slot t < Bp (zero past B) and for u up to
-// the next multiple of 8 past |U| (zero past |U|).
+// token t did not select neuron U_u), stored token-major in fp16: aT[t][u],
+// for every token slot t < Bp (zero past B) and for u up to the next multiple
+// of 8 past |U| (zero past |U|).
 template <int KIND>
 struct UpEpi {
     const int32_t* ulist;
@@ -209,8 +210,7 @@ struct UpEpi {
     const float* bg;
     const uint32_t* tokbits;
     int nw, B, Bp, lda, U, U8;
-    h16* a_hi;
-    h16* a_lo;
+    h16* a;
     struct Row {
         int nrow;
         float bu, bgv;
@@ -246,12 +246,8 @@ struct UpEpi {
         }
 #pragma unroll
         for (int k = 0; k < E; ++k) {
-            const h16 hi = (h16)av[k];
-            const h16 lo = (h16)(av[k] - (float)hi);
-            if (t[k] < Bp && uu < U8) {
-                a_hi[(size_t)t[k] * lda + uu] = hi;
-                a_lo[(size_t)t[k] * lda + uu] = lo;
-            }
+            const h16 h = (h16)av[k];
+            if (t[k] < Bp && uu < U8) a[(size_t)t[k] * lda + uu] = h;
         }
     }
 };
@@ -260,10 +256,10 @@ template <class C, int KIND>
 __global__ __launch_bounds__(256) void k_union_up(RingArgs a, const uint32_t* __restrict__ ucount, int ffn,
                                                   const float* __restrict__ bup, const float* __restrict__ bg,
                                                   const uint32_t* __restrict__ tokbits, int nw, int Bp, int lda,
-                                                  h16* __restrict__ a_hi, h16* __restrict__ a_lo) {
+                                                  h16* __restrict__ aT) {
     __shared__ __align__(16) char lds[C::LDS];
     const int U = (int)min(*ucount, (uint32_t)ffn);
-    const UpEpi<KIND> epi{a.rowlist, bup, bg, tokbits, nw, a.B, Bp, lda, U, min((U + 7) & ~7, lda), a_hi, a_lo};
+    const UpEpi<KIND> epi{a.rowlist, bup, bg, tokbits, nw, a.B, Bp, lda, U, min((U + 7) & ~7, lda), aT};
     ring_gemm<C, true, true>(a, U, lds, epi);
 }
 
@@ -676,7 +672,7 @@ struct DownCfg {
     static constexpr int TPB = 512 / KR;                           // tokens per activation block
     static constexpr int WBLK = (KR / 8) * (CT / 64);              // W_down blocks per stage
     static constexpr int ABA = (8 * XG + TPB - 1) / TPB;           // activation blocks per array
-    static constexpr int ABLK = 2 * ABA;                           // activation blocks (hi, lo)
+    static constexpr int ABLK = ABA;                               // activation blocks
     static constexpr int NBLK = ((WBLK + ABLK + 3) / 4) * 4;       // padded to whole waves
     static constexpr int IPW = NBLK / 4;
     static constexpr int STAGE = NBLK * 1024;
@@ -746,8 +742,7 @@ template <class C>
 __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, int d, int ffn,
                                                     const int32_t* __restrict__ ulist,
                                                     const uint32_t* __restrict__ ucount,
-                                                    const h16* __restrict__ a_hi,
-                                                    const h16* __restrict__ a_lo, int B, int Bp, int lda,
+                                                    const h16* __restrict__ aT, int B, int Bp, int lda,
                                                     float* __restrict__ partial, int G,
                                                     const h16* __restrict__ zsrc) {
     __shared__ __align__(16) char lds[C::NS * C::STAGE];
@@ -803,10 +798,10 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
             // lane j writes LDS bytes 16j.. of the block: token j / (64 / TPB)
             // of it, slot j % (64 / TPB)
             const int bx = b - C::WBLK;
-            const int ix = bx / C::ABA, tg = bx % C::ABA;
+            const int tg = bx;
             const int t = tg * C::TPB + lane / (64 / C::TPB);
             const bool real = bx < C::ABLK && t < B;
-            abase[i] = real ? (ix ? a_lo : a_hi) + (size_t)t * lda : nullptr;
+            abase[i] = real ? aT + (size_t)t * lda : nullptr;
             wofs[i] = 0;
             kofs[i] = C::achunk(tg, lane) << 3;
         }
@@ -864,7 +859,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
     // reads go out first, then its MFMAs run back to back, with the next
     // stage's loads spread between them when there are at least two MFMAs
     // per load, else issued at once after the barrier (see ring.hpp)
-    constexpr int NMF = C::KR / 16 * C::CB * C::NB * 2;   // MFMAs per wave per stage
+    constexpr int NMF = C::KR / 16 * C::CB * C::NB;   // MFMAs per wave per stage
     constexpr bool kSpread = NMF >= 2 * C::IPW;
     auto stage = [&](int s, auto MORE) {
         if (s + C::NS - 2 < n) wait_vm<(C::NS - 2) * C::IPW>();
@@ -874,7 +869,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
         if constexpr (decltype(MORE)::value && !kSpread) issue(s + C::NS - 1, qn);
         const char* buf = lds + (s % C::NS) * C::STAGE;
         f16x4 w0[C::KR / 16][C::CB], w1[C::KR / 16][C::CB];
-        f16x8 av[C::KR / 16][C::NB][2];
+        f16x8 av[C::KR / 16][C::NB];
 #pragma unroll
         for (int q = 0; q < C::KR / 16; ++q) {
             const int rg = 2 * q + kh;   // row group of this lane half's 8 entries
@@ -892,11 +887,7 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
                 const int t = nb * 32 + li, tg = min(t / C::TPB, C::ABA - 1);
-#pragma unroll
-                for (int ix = 0; ix < 2; ++ix) {
-                    const int blk = C::WBLK + ix * C::ABA + tg;
-                    av[q][nb][ix] = *reinterpret_cast<const f16x8*>(buf + blk * 1024 + C::aoff(tg, c, t));
-                }
+                av[q][nb] = *reinterpret_cast<const f16x8*>(buf + (C::WBLK + tg) * 1024 + C::aoff(tg, c, t));
             }
         }
         const h16* pn[C::IPW];
@@ -909,18 +900,16 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
                 const f16x8 a8 = {w0[q][cb][0], w0[q][cb][1], w0[q][cb][2], w0[q][cb][3],
                                   w1[q][cb][0], w1[q][cb][1], w1[q][cb][2], w1[q][cb][3]};
 #pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
+                for (int nb = 0; nb < C::NB; ++nb) {
+                    const int f = (q * C::CB + cb) * C::NB + nb;
+                    if constexpr (decltype(MORE)::value && kSpread) {
 #pragma unroll
-                    for (int ix = 0; ix < 2; ++ix) {
-                        const int f = ((q * C::CB + cb) * C::NB + nb) * 2 + ix;
-                        if constexpr (decltype(MORE)::value && kSpread) {
-#pragma unroll
-                            for (int i = 0; i < C::IPW; ++i)
-                                if (i * NMF / C::IPW == f) issue1(pn[i], qn, i);
-                        }
-                        acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb][ix], acc[cb][nb], 0, 0, 0);
-                        __builtin_amdgcn_sched_barrier(0);
+                        for (int i = 0; i < C::IPW; ++i)
+                            if (i * NMF / C::IPW == f) issue1(pn[i], qn, i);
                     }
+                    acc[cb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, av[q][nb], acc[cb][nb], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
     };
     {
@@ -1027,8 +1016,7 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
     int32_t* ulist = reinterpret_cast<int32_t*>(ws + L.ulist);
     uint32_t* ucount = reinterpret_cast<uint32_t*>(ws + L.ucount);
     uint32_t* uerr = ucount + 1;   // the compaction's error word (the |U| slot is 256 bytes)
-    h16* a_hi = reinterpret_cast<h16*>(ws + L.a_hi);
-    h16* a_lo = reinterpret_cast<h16*>(ws + L.a_lo);
+    h16* aT = reinterpret_cast<h16*>(ws + L.aT);
     float* partial = reinterpret_cast<float*>(ws + L.partial);
     uint32_t* upctr = reinterpret_cast<uint32_t*>(ws + L.upctr);
     const int nw = (ffn + 31) / 32;
@@ -1057,11 +1045,11 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
 #define PI_UP(K, N)                                                                                        \
     hipLaunchKernelGGL((k_union_up<UpCfg<(K != 0), N>, K>), dim3(ring_grid<k_union_up<UpCfg<(K != 0), N>, K>>()), \
                        dim3(256), \
-                       0, s, ra, ucount, ffn, bup, bg, tokbits, nw, L.Bp, L.lda, a_hi, a_lo)
+                       0, s, ra, ucount, ffn, bup, bg, tokbits, nw, L.Bp, L.lda, aT)
 #define PI_DN(X)                                                                                        \
     hipLaunchKernelGGL((k_union_down<DownCfg<X>>), dim3((d + DownCfg<X>::CT - 1) / DownCfg<X>::CT, L.G), dim3(256), \
                        0, s, Wd, d, ffn, ulist, ucount, \
-                       a_hi, a_lo, B, L.Bp, L.lda, partial, L.G, ra.zsrc)
+                       aT, B, L.Bp, L.lda, partial, L.G, ra.zsrc)
     const int xg = ring_xg(B);
     if (kind == 2) {
         if (xg == 1) PI_UP(2, 1); else if (xg == 2) PI_UP(2, 2); else if (xg == 4) PI_UP(2, 4);

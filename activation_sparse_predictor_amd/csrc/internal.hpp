@@ -84,8 +84,7 @@ struct BatchLayout {
     size_t umasks;   // tiles uint64 union bitmaps
     size_t ulist;    // ffn int32 ascending union list
     size_t ucount;   // uint32 |U|
-    size_t a_hi;     // Bp x lda fp16 activations, high part
-    size_t a_lo;     // Bp x lda fp16 activations, low part
+    size_t aT;       // Bp x lda fp16 activations, token-major
     size_t partial;  // G x Bp x d fp32 chunk partials of the down GEMM
     size_t ctr;      // kCtrWords uint32 arrival counters
     size_t upctr;    // ceil(ffn/64) uint32 row-block counters of the up GEMM
@@ -110,9 +109,8 @@ inline BatchLayout batch_layout(int B, int d, int ffn) {
     L.umasks = L.tokbits + align256((size_t)B * ((ffn + 31) / 32) * 4);
     L.ulist = L.umasks + align256(tiles * 8);
     L.ucount = L.ulist + align256((size_t)ffn * 4);
-    L.a_hi = L.ucount + 256;
-    L.a_lo = L.a_hi + align256((size_t)L.Bp * L.lda * 2);
-    L.partial = L.a_lo + align256((size_t)L.Bp * L.lda * 2);
+    L.aT = L.ucount + 256;
+    L.partial = L.aT + align256((size_t)L.Bp * L.lda * 2);
     L.ctr = L.partial + align256((size_t)L.G * L.Bp * d * 4);
     L.upctr = L.ctr + align256((size_t)kCtrWords * 4);
     L.upart = L.upctr + align256((size_t)((ffn + kRingRows - 1) / kRingRows) * 4);
