@@ -38,7 +38,8 @@
 // Work split (stream-K).  A unit is one stage of one RB-row block.  The
 // T = row blocks x stages units are cut into gridDim.x equal ranges, one per
 // workgroup, so every workgroup streams the same number of bytes whatever the
-// row count.  A row block whose stages all fall in one range is finished in
+// row count (unless the row blocks fill at least 3/4 of the grid: then each
+// workgroup takes one whole row block, see ring_gemm).  A row block whose stages all fall in one range is finished in
 // place; otherwise each piece writes its fp32 sums to a slot of its own and
 // the last piece to arrive on the row block's counter adds the pieces in
 // workgroup order (fixed order: deterministic) and finishes the row block,
@@ -144,8 +145,16 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
     const int nst = (a.K + C::KST - 1) / C::KST;
     const long long T = (long long)nrb * nst;
     // no more workgroups than units, so that no range is empty and every
-    // workgroup between the first and last holder of a row block has a piece
-    const int G = (int)min((long long)gridDim.x, T), w = (int)blockIdx.x;
+    // workgroup between the first and last holder of a row block has a piece.
+    // When the row blocks fill at least 3/4 of the grid they are not split:
+    // one whole row block per workgroup (up to a third more stages each,
+    // against the split blocks at both ends of a workgroup's range, whose
+    // pieces, arrivals and last-arriver reads cost ~20 us each at 128 tokens
+    // against ~8 us for a block finished in place).  (Only where the last
+    // piece finishes: ring_finish assumes the even split.)
+    const int gd = (int)gridDim.x;
+    const bool whole_blocks = LAST_FINISHES && nrb <= gd && 4 * nrb >= 3 * gd;
+    const int G = whole_blocks ? nrb : (int)min((long long)gd, T), w = (int)blockIdx.x;
     if (w >= G) return;
     static_assert(256 % C::RB == 0, "a thread keeps one row of the block");
     constexpr int kTS = 256 / C::RB;                // token-slot stride of a thread
