@@ -200,6 +200,29 @@ def test_batched_union_path(kind, Bt):
         check_y(Yp_h[t], ref, where=f"per-token B={Bt} t={t}")
 
 
+@pytest.mark.parametrize("kind,ffn", [("relu", 24576), ("relu", 24448), ("reglu", 24576)])
+def test_union_whole_row_block_threshold(kind, ffn):
+    """128 tokens whose union is every neuron: 192 row blocks of 128 (3/4 of
+    the 256 resident up-GEMM workgroups: one whole row block each) and 191
+    (below the threshold: the even split with pieces and last arrivers), with
+    a ragged K (d = 520).  y of sampled tokens against the oracle."""
+    cfg = custom_config(kind, 520, ffn, 32, mean=0.7, exponent=0.3, number=66)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    X = make_tokens(cfg, 128).to(DEV)
+    idx, cnt = R.predict(L, X)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    cnt_h, idx_h = cnt.cpu().numpy(), idx.cpu().numpy()
+    union = np.zeros(ffn, dtype=bool)
+    for t in range(128):
+        union[idx_h[t, :cnt_h[t]]] = True
+    assert union.all(), f"union {union.sum()} of {ffn}: the row-block count this test needs is not reached"
+    for t in (0, 77, 127):
+        mine = idx_h[t, :cnt_h[t]]
+        check_y(Y[t].cpu().numpy(), _oracle_y(H, X[t].cpu(), mine), where=f"{kind} ffn={ffn} t={t}")
+
+
 @pytest.mark.parametrize("Bt,d", [(3, 520), (5, 520), (3, 8200), (7, 9216), (6, 9224), (8, 16384)])
 def test_batched_predictor_hidden_paths(Bt, d):
     """Groups of up to 8 tokens take the hidden layer on the vector units when
