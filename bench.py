@@ -722,6 +722,8 @@ def main():
     ap.add_argument("--q4", default="c2", help="config of the INT4-rows line ('' to skip)")
     ap.add_argument("--prompt", default="c5",
                     help="config of the prompt-phase line: one prompt batch per layer against torch ('' to skip)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="run only the single-layer rotation line (for a per-kernel profile of the B = 1 calls)")
     ap.add_argument("--sweep-only", action="store_true",
                     help="run only the batch sweep (for a per-kernel profile of the union path)")
     ap.add_argument("--profile-run", action="store_true",
@@ -752,6 +754,9 @@ def main():
     if args.sweep_only:
         sw = batch_sweep(args.sweep, [int(b) for b in args.sweep_batches.split(",")], 10, 4, log)
         print(json.dumps({"batch_sweep": sw}), flush=True)
+        return
+    if args.layer_only:
+        print(json.dumps({"layer": layer_line(args.layer, 8, 8, 10, args.no_dense, log)}), flush=True)
         return
     if args.profile_run:
         profile_run(cfg, args.profile_layers, dev)
