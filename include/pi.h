@@ -88,7 +88,8 @@ typedef enum pi_op {
 /* pi_ffn_sparse flags */
 #define PI_DENSE 0x1u      /* ignore idx/count and compute every neuron (dense FFN baseline) */
 #define PI_PER_TOKEN 0x2u  /* B >= 2: run every token through the single-token kernel instead of
-                              the union path (same results up to fp32 rounding) */
+                              the union path (same results up to rounding: the union path
+                              rounds each activation to fp16 once) */
 #define PI_DETERMINISTIC 0x4u  /* accepted for callers that ask for it: every path is deterministic
                                   already (fixed reduction orders, no floating-point atomics) */
 #define PI_CHECK_IDX 0x8u  /* after the FFN, check each token's list against the contract
@@ -183,11 +184,12 @@ pi_status pi_ffn_predict_hot(const pi_half* x, int B, int d,
  * For B >= 2 (unless PI_DENSE or PI_PER_TOKEN) the tokens are taken in
  * groups of up to 128: the union U of the group's lists is formed on the
  * device, the rows of U are read once, and the up/gate and W_down products
- * run on the matrix cores (fp16 x fp16 -> fp32; a_i is carried as an fp16
- * hi/lo pair, about 22 significant bits).  A neuron outside token t's own
- * list contributes exactly 0 to y_t, so y_t matches the single-token result
- * up to fp32 rounding: the union changes which rows are read, not what is
- * computed (the batched decode of Part A section 4.4).  The union is formed
+ * run on the matrix cores (fp16 x fp16 -> fp32; each activation a_i is
+ * rounded once to fp16 for the W_down product, a relative error of at most
+ * 2^-11 per term, about 2e-4 in y's relative L2 norm).  A neuron outside
+ * token t's own list contributes exactly 0 to y_t, so y_t matches the
+ * single-token result up to that rounding: the union changes which rows are
+ * read, not what is computed (the batched decode of Part A section 4.4).  The union is formed
  * by one kernel with a bounded internal wait; were it ever to run out, every
  * token's y would be NaN.
  *
