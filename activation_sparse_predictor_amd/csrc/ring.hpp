@@ -403,6 +403,10 @@ __device__ __forceinline__ void ring_gemm(const RingArgs& a, int nrows, char* ld
 // Finishes the row blocks that a ring_gemm<C, ..., false> launch of G0
 // workgroups left in pieces: one thread per (row block, token < B, row),
 // grid-stride; each sums its pieces in workgroup order, 8 loads in flight.
+// A thread finds its workgroup range once: only its first piece can be the
+// second (tail) slot of its workgroup, every later workgroup starts inside
+// the row block.  (Per-piece 64-bit divisions had made this kernel
+// instruction-bound.)
 template <class C, class Epi>
 __device__ __forceinline__ void ring_finish(const RingArgs& a, int nrows, int G0, Epi&& epi) {
     const int nrb = (nrows + C::RB - 1) / C::RB;
@@ -410,30 +414,43 @@ __device__ __forceinline__ void ring_finish(const RingArgs& a, int nrows, int G0
     const long long T = (long long)nrb * nst;
     if (T == 0) return;
     const int G = (int)min((long long)G0, T);
-    const long long total = (long long)nrb * a.B * C::RB;
-    for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (long long)gridDim.x * blockDim.x) {
-        const int rb = (int)(e / ((long long)a.B * C::RB));
-        const int rem = (int)(e % ((long long)a.B * C::RB));
+    const bool narrow = T * (G + 1) < (1ll << 32);   // the unit arithmetic fits 32 bits
+    const int BR = a.B * C::RB;   // outputs per row block
+    const int total = nrb * BR;
+    constexpr size_t kSlot = (size_t)C::NM * C::BP * C::RB;
+    constexpr int kBatch = 8;   // pieces in flight (16 measured no faster)
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
+        const int rb = e / BR, rem = e - rb * BR;
         const int t = rem / C::RB, rl = rem % C::RB;
-        const int wf = (int)((((long long)rb * nst + 1) * G + T - 1) / T) - 1;
-        const int wl = (int)((((long long)(rb + 1) * nst) * G + T - 1) / T) - 1;
+        // workgroups wf .. wl hold the row block's units u0 .. u0 + nst - 1;
+        // kf: workgroup wf's slot for it (1 when its range starts earlier)
+        int wf, wl, kf;
+        if (narrow) {
+            const uint32_t u0 = (uint32_t)(rb * nst), Tu = (uint32_t)T, Gu = (uint32_t)G;
+            wf = (int)(((u0 + 1) * Gu + Tu - 1) / Tu) - 1;
+            wl = (int)(((u0 + nst) * Gu + Tu - 1) / Tu) - 1;
+            kf = Tu * (uint32_t)wf / Gu >= u0 ? 0 : 1;
+        } else {
+            const long long u0 = (long long)rb * nst;
+            wf = (int)(((u0 + 1) * G + T - 1) / T) - 1;
+            wl = (int)(((u0 + nst) * G + T - 1) / T) - 1;
+            kf = T * wf / G >= u0 ? 0 : 1;
+        }
         if (wf == wl || rb * C::RB + rl >= nrows) continue;   // finished in place, or past the rows
-        auto piece = [&](int wg, int m) {
-            const int kind = (T * wg / G) >= (long long)rb * nst ? 0 : 1;
-            return a.part[(size_t)(wg * 2 + kind) * C::NM * C::BP * C::RB + (m * C::BP + t) * C::RB + rl];
-        };
+        const float* p0 = a.part + (size_t)(t * C::RB + rl);
+        const float* p1 = p0 + (size_t)(C::NM - 1) * C::BP * C::RB;
         float v0 = 0.f, v1 = 0.f;
-        for (int w0 = wf; w0 <= wl; w0 += 8) {
-            float x0[8], x1[8];
+        for (int w0 = wf; w0 <= wl; w0 += kBatch) {
+            float x0[kBatch], x1[kBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < kBatch; ++j) {
                 const int wg = min(w0 + j, wl);
-                x0[j] = piece(wg, 0);
-                x1[j] = C::NM > 1 ? piece(wg, C::NM - 1) : 0.f;
+                const size_t off = (size_t)(wg * 2 + (wg == wf ? kf : 0)) * kSlot;
+                x0[j] = p0[off];
+                x1[j] = C::NM > 1 ? p1[off] : 0.f;
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (w0 + j <= wl) {
                     v0 += x0[j];
                     v1 += x1[j];
