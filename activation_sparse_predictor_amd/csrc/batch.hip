@@ -30,7 +30,8 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 // neuron 32w + k.  Every word is written, so no clearing pass is needed: the
 // lists are strictly ascending, so the entries of one word form a run; the
 // run's first entry ORs the run's bits (a segmented OR over the wave, then
-// the entries past the wave's end, at most 31) and writes the word, and also
+// the entries past the wave's end, at most 31, loaded with the wave's own
+// entries) and writes the word, and also
 // zeroes the words strictly between the previous entry's word and its own;
 // the words before the first entry's word and after the last one's are
 // zeroed grid-wide.  Workgroups of token 0 also zero the compaction's count
@@ -52,14 +53,15 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
     uint32_t* out = tokbits + (size_t)t * nw;
     // ids are read clamped to [0, ffn): a list that breaks the contract gives
     // wrong bits but no access outside the bitmaps (PI_CHECK_IDX reports it)
-    const int wfirst = cnt > 0 ? clampi(lst[0], 0, ffn - 1) >> 5 : nw;
-    const int wlast = cnt > 0 ? clampi(lst[cnt - 1], 0, ffn - 1) >> 5 : -1;
-    for (int w = blockIdx.x * 256 + tid; w < nw; w += stride)
-        if (w < wfirst || w > wlast) out[w] = 0u;
     for (int j0 = blockIdx.x * 256 + (tid & ~63); j0 < cnt; j0 += stride) {   // whole waves
-        const int j = j0 + lane;
-        const bool in = j < cnt;
+        // one round of loads: the wave's 64 entries, the 32 after them (a word
+        // holds at most 32 entries, so the run at the wave's end ends there)
+        // and, in lane 0, the entry before the wave
+        const int j = j0 + lane, ja = j0 + 64 + lane;
+        const bool in = j < cnt, ina = lane < 32 && ja < cnt;
         const int i = in ? clampi(lst[j], 0, ffn - 1) : 0;
+        const int ia = ina ? clampi(lst[ja], 0, ffn - 1) : 0;
+        const int ip = lane == 0 && j0 > 0 ? clampi(lst[j0 - 1], 0, ffn - 1) : 0;
         const int w = in ? (i >> 5) : -1 - lane;   // lanes past the list match no one
         uint32_t bits = in ? (1u << (i & 31)) : 0u;
 #pragma unroll
@@ -70,18 +72,23 @@ __global__ __launch_bounds__(256) void k_union_bits(const int32_t* __restrict__ 
         }
         const int wup = __shfl_up(w, 1, 64);
         const int w63 = __shfl(w, 63, 64);
+        // the bits of the run that goes on past the wave: the entries after
+        // it in word w63
+        uint32_t xb = ina && (ia >> 5) == w63 ? 1u << (ia & 31) : 0u;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) xb |= __shfl_xor(xb, off, 64);
         if (!in) continue;
-        const int wprev = j == 0 ? -1 : (lane == 0 ? clampi(lst[j - 1], 0, ffn - 1) >> 5 : wup);
+        const int wprev = j == 0 ? -1 : (lane == 0 ? ip >> 5 : wup);
         if (wprev == w) continue;   // not the first entry of its word
-        if (w63 == w)               // the run goes on past this wave
-            for (int jj = j0 + 64; jj < cnt; ++jj) {
-                const int ii = clampi(lst[jj], 0, ffn - 1);
-                if ((ii >> 5) != w) break;
-                bits |= 1u << (ii & 31);
-            }
+        if (w63 == w) bits |= xb;
         out[w] = bits;
-        for (int g = max(wprev + 1, wfirst); g < w; ++g) out[g] = 0u;
+        for (int g = j == 0 ? w : wprev + 1; g < w; ++g) out[g] = 0u;   // (the first entry: none)
     }
+    // the words before the first entry's word and after the last one's
+    const int wfirst = cnt > 0 ? clampi(lst[0], 0, ffn - 1) >> 5 : nw;
+    const int wlast = cnt > 0 ? clampi(lst[cnt - 1], 0, ffn - 1) >> 5 : -1;
+    for (int w = blockIdx.x * 256 + tid; w < nw; w += stride)
+        if (w < wfirst || w > wlast) out[w] = 0u;
 }
 
 // Union compaction in one pass.  Workgroup g of G (at most kCompactWG, all
