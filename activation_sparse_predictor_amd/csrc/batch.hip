@@ -944,30 +944,43 @@ __global__ __launch_bounds__(256) void k_union_down(const h16* __restrict__ Wd, 
         }
 }
 
-// y[t][c] = sum over chunks g (in order) of partial[g][t][c]: one output per
-// thread, the G loads issued 8 at a time.  NaN for a token whose count is
-// negative (the predictor's overrun report), and for every token when the
-// union compaction overran its wait.
+// y[t][c] = sum over chunks g (in order) of partial[g][t][c]: four outputs
+// (16 bytes) per thread, the G loads issued 8 at a time; 32-bit index
+// arithmetic (B x d is far below 2^31; a 64-bit division per thread had made
+// this kernel instruction-bound).  NaN for a token whose count is negative
+// (the predictor's overrun report), and for every token when the union
+// compaction overran its wait.  d is a multiple of 8 and y 16-byte aligned.
 __global__ __launch_bounds__(256) void k_union_reduce(const float* __restrict__ partial, int B, int Bp,
                                                       int d, int G, float* __restrict__ y,
                                                       const int32_t* __restrict__ count,
                                                       const uint32_t* __restrict__ uerr) {
-    const size_t o = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (o >= (size_t)B * d) return;
-    const int t = (int)(o / d), c = (int)(o % d);
+    const int dq = d >> 2;
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (q >= B * dq) return;
+    const int t = q / dq, c = (q - t * dq) * 4;
+    f32x4* yo = reinterpret_cast<f32x4*>(y + (size_t)t * d + c);
     if (count[t] < 0 || *uerr != 0u) {
-        y[o] = __builtin_nanf("");
+        const float nan = __builtin_nanf("");
+        *yo = f32x4{nan, nan, nan, nan};
         return;
     }
-    float sum = 0.f;
+    const float* p = partial + (size_t)t * d + c;
+    const size_t gs = (size_t)Bp * d;   // one chunk's partials
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
     for (int g0 = 0; g0 < G; g0 += 8) {
-        float v[8];
+        f32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (g0 + u < G) ? partial[((size_t)(g0 + u) * Bp + t) * d + c] : 0.f;
+        for (int u = 0; u < 8; ++u)
+            v[u] = g0 + u < G ? *reinterpret_cast<const f32x4*>(p + (size_t)(g0 + u) * gs) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sum += v[u];
+        for (int u = 0; u < 8; ++u) {
+            sum.x += v[u].x;
+            sum.y += v[u].y;
+            sum.z += v[u].z;
+            sum.w += v[u].w;
+        }
     }
-    y[o] = sum;
+    *yo = sum;
 }
 
 // PI_CHECK_IDX: one workgroup per token checks its list against the contract
@@ -1072,8 +1085,8 @@ hipError_t launch_union(int kind, const h16* x, int B, int d, int ffn, const h16
     else if (xg == 8) PI_DN(8); else PI_DN(16);
 #undef PI_UP
 #undef PI_DN
-    const size_t nout = (size_t)B * d;
-    hipLaunchKernelGGL(k_union_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, s, partial, B, L.Bp,
+    const int nq = B * (d / 4);   // four outputs per thread
+    hipLaunchKernelGGL(k_union_reduce, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, partial, B, L.Bp,
                        d, L.G, y, count, uerr);
     return hipGetLastError();
 }
