@@ -304,6 +304,35 @@ def test_union_path_edge_lists():
         check_y(Yh[t], _oracle_y(H, X[t].cpu(), lists[t]), where=f"edge list t={t}")
 
 
+def test_union_bitmap_runs_across_waves():
+    """The token bitmaps are built 64 list entries a wave; a 32-neuron word's
+    run that crosses a wave's end is completed from the (at most 31) entries
+    after it.  Lists whose run there goes on for 31 entries (the most), for 1,
+    for none (a word boundary at the wave's end), one that ends inside those
+    31, and dense lists long enough that every wave takes several rounds."""
+    cfg = custom_config("relu", 1032, 1000, 16, mean=0.3, number=63)
+    L = R.to_device(make_layer(cfg), DEV)
+    H = _host(L)
+    ffn = cfg.ffn
+    lists = [list(range(1, ffn)),                              # entry 63 = neuron 64: 31 more of word 2
+             list(range(31, ffn)),                             # entry 63 = neuron 94: 1 more of word 2
+             list(range(32, ffn)),                             # entry 63 = neuron 95: word 2 ends there
+             list(range(0, 63)) + list(range(96, 128)) + list(range(700, 990, 3)),
+             list(range(0, 63)) + list(range(96, 110)),        # the list ends inside the run
+             list(range(5, 69)) + list(range(70, 80))]         # a run of word 2 split 5 / 10 by the wave's end
+    Bt = len(lists)
+    X = make_tokens(cfg, Bt).to(DEV)
+    idx = torch.zeros(Bt, ffn, dtype=torch.int32, device=DEV)
+    for t, l in enumerate(lists):
+        idx[t, :len(l)] = torch.tensor(l, dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([len(l) for l in lists], dtype=torch.int32, device=DEV)
+    Y = R.sparse(L, X, idx, cnt)
+    torch.cuda.synchronize()
+    Yh = Y.cpu().numpy()
+    for t in range(Bt):
+        check_y(Yh[t], _oracle_y(H, X[t].cpu(), lists[t]), where=f"run list t={t}")
+
+
 @pytest.mark.parametrize("per_token", [False, True])
 def test_check_idx_flag(per_token):
     """PI_CHECK_IDX: tokens whose lists break the contract (an id out of range,
