@@ -127,11 +127,17 @@ __global__ __launch_bounds__(256) void k_union_compact(const uint32_t* __restric
     for (int k = 0; k < tw; ++k) {
         const int tl = wave * tw + k, tile = t0 + tl;
         if (tile >= t1) break;
+        // two tokens a lane, their four words loaded together; tokens past B
+        // read token B - 1 again (the OR is unchanged) and a high word past
+        // the bitmap reads the low one (dropped)
+        const int wl = 2 * tile, wh = min(2 * tile + 1, nw - 1);
+        const bool hv = 2 * tile + 1 < nw;
         uint64_t m = 0;
-        for (int t = lane; t < B; t += 64) {
-            const uint32_t lo = tokbits[(size_t)t * nw + 2 * tile];
-            const uint32_t hi = 2 * tile + 1 < nw ? tokbits[(size_t)t * nw + 2 * tile + 1] : 0u;
-            m |= lo | ((uint64_t)hi << 32);
+        for (int tb0 = 0; tb0 < B; tb0 += 128) {
+            const size_t ra = (size_t)min(tb0 + lane, B - 1) * nw, rb = (size_t)min(tb0 + 64 + lane, B - 1) * nw;
+            const uint32_t la = tokbits[ra + wl], ha = tokbits[ra + wh];
+            const uint32_t lb = tokbits[rb + wl], hb = tokbits[rb + wh];
+            m |= (uint64_t)(la | lb) | ((uint64_t)(hv ? ha | hb : 0u) << 32);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) m |= __shfl_xor(m, off, 64);
